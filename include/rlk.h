@@ -1,0 +1,170 @@
+/*
+ * rlk.h -- C ABI of the fused row-wise log-softmax library for AMD MI355X
+ * (gfx950).  Plain pointers and sizes only; no HIP or torch types appear in
+ * the signatures (the stream is passed as a void* that holds a hipStream_t).
+ *
+ * What is computed (sources are web pages on the subject, cited by title and
+ * section):
+ *   - "Final Logit Softcap" (RL-Kernel operator documentation), Summary and
+ *     Tensor and Precision Contract: the elementwise cap y = c * tanh(x / c)
+ *     with a runtime cap, its derivative 1 - tanh^2(x / c), fp32 internal
+ *     math and one trailing cast;
+ *   - "Add Triton kernels for vocab-parallel logprobs, entropy and KL"
+ *     (DeepSpeed pull request 8838), Changes and the review comment on
+ *     reading each logit once: per-token logprobs (k = 1 and top-k),
+ *     entropy and KL against a second logit tensor, computed from online
+ *     row statistics (running max, sum of exponentials and a weighted sum)
+ *     in a single read of each logit, with a support-mismatch rule;
+ *   - "perf(logp): fused zero-workspace backward for the generic CUDA fused
+ *     logp" (RL-Kernel pull request 495), Summary and Behavior changes: the
+ *     backward g * (onehot - softmax) written straight in the logits dtype
+ *     with no [N, V] temporary, and targets outside [0, V) (such as -100)
+ *     giving output 0 and an exactly zero gradient.
+ *
+ * Conventions common to every entry point:
+ *   - Tensor pointers are DEVICE pointers owned by the caller.  The library
+ *     allocates, frees and copies nothing and keeps no state between calls.
+ *   - Logits are fp32 or bf16 (rlk_dtype).  All arithmetic is fp32; head
+ *     outputs are fp32; gradients with respect to the logits are written in
+ *     the logits dtype with a single round-to-nearest-even cast.
+ *   - A logits matrix is [N, V] row-major with row stride ld >= V elements
+ *     (padding between rows is never read).  Gradients are written
+ *     contiguous [N, V].  Inputs are never modified; outputs must not alias
+ *     inputs.
+ *   - softcap: 0.0f turns the fused cap off; any other value must be finite
+ *     and > 0.  The standalone softcap calls require a finite cap > 0.
+ *   - N == 0 (or n == 0) returns RLK_OK without any HIP call.
+ *   - Every argument is validated on the host before anything is launched;
+ *     on error nothing is launched and rlk_last_error() describes the
+ *     problem.  The launch goes to the device that owns the first tensor
+ *     pointer (all pointers must live on it, else RLK_ERR_DEVICE); the
+ *     caller's current device is restored afterwards.  Calls are
+ *     asynchronous on `stream` (0 = the null stream); faults inside a kernel
+ *     surface at the caller's next synchronisation.
+ *   - A *_bwd call must receive the `stats` buffer written by the matching
+ *     *_fwd call with identical inputs and arguments, ordered after it (same
+ *     stream, or after a synchronisation).
+ *   - Results are deterministic and batch-invariant: a row's outputs depend
+ *     only on that row's data, V and the arguments, never on N, on the other
+ *     rows or on the row stride.
+ */
+#ifndef RLK_H
+#define RLK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RLK_ABI_VERSION 1
+
+/* Largest top-k width accepted by rlk_logp_fwd / rlk_logp_bwd. */
+#define RLK_MAX_TOPK 4096
+
+typedef enum { RLK_F32 = 0, RLK_BF16 = 1 } rlk_dtype;
+
+typedef enum {
+    RLK_OK = 0,
+    RLK_ERR_ARG = 1,    /* null pointer, bad cap, bad enum value          */
+    RLK_ERR_DTYPE = 2,  /* dtype outside rlk_dtype (fp16, fp64, ints...)  */
+    RLK_ERR_SHAPE = 3,  /* N < 0, V < 1, ld < V, k out of range, overflow */
+    RLK_ERR_DEVICE = 4, /* pointer not device memory, or on another GPU   */
+    RLK_ERR_LAUNCH = 5  /* the HIP runtime refused a launch               */
+} rlk_status;
+
+typedef enum { RLK_HEAD_LOGP = 0, RLK_HEAD_ENTROPY = 1, RLK_HEAD_KL = 2 } rlk_head;
+
+/* RLK_KL_REVERSE: KL(policy || ref) = sum p (log p - log q).
+ * RLK_KL_FORWARD: KL(ref || policy) = sum q (log q - log p). */
+typedef enum { RLK_KL_REVERSE = 0, RLK_KL_FORWARD = 1 } rlk_kl_dir;
+
+/* ABI version of the loaded library (RLK_ABI_VERSION at build time). */
+int rlk_abi_version(void);
+
+/* Bytes of the per-row forward->backward record for `head` (N rows of
+ * width V); the caller allocates it in device memory.  The layout is
+ * private to the library.  Returns 0 for N <= 0 or an unknown head. */
+size_t rlk_stats_bytes(rlk_head head, int64_t N, int64_t V);
+
+/* Static text of a status code. */
+const char* rlk_status_str(rlk_status s);
+
+/* Detail of the last error raised on the calling host thread ("" if none). */
+const char* rlk_last_error(void);
+
+/* ------------------------------------------------------------- softcap
+ * "Final Logit Softcap", Summary and Tensor and Precision Contract.
+ * y[i] = cap * tanh(x[i] / cap) for n elements, x in x_dtype, y in y_dtype
+ * (RLK_F32: the fp32 output of the fused kernel; x_dtype: the cast-back
+ * `forward` variant).  fp32 math with one trailing cast.  -inf maps to -cap.
+ * cap must be finite and > 0 (else RLK_ERR_ARG). */
+rlk_status rlk_softcap_fwd(const void* x, rlk_dtype x_dtype, void* y, rlk_dtype y_dtype,
+                           int64_t n, float cap, void* stream);
+
+/* grad_x[i] = grad_y[i] * (1 - tanh^2(x[i] / cap)), recomputed from the saved
+ * input x; grad_y is fp32, grad_x is written in x_dtype. */
+rlk_status rlk_softcap_bwd(const void* x, rlk_dtype x_dtype, const float* grad_y, void* grad_x,
+                           int64_t n, float cap, void* stream);
+
+/* ------------------------------------------------------------ logprobs
+ * Pull request 8838 (Changes) and pull request 495 (Summary, Behavior
+ * changes).  targets is int64 [N, k] (k = 1: per-token logprobs; k > 1:
+ * top-k ids, 1 <= k <= RLK_MAX_TOPK).  With y = softcap(x) (or x):
+ *   logp[i, j] = y[i, t_ij] - logsumexp(y[i, :])  if 0 <= t_ij < V,
+ *   logp[i, j] = 0                                otherwise (ignored),
+ * NaN for a valid target in a row whose logits are all -inf, -inf for a
+ * valid target on a masked (-inf) column.  stats: rlk_stats_bytes(LOGP). */
+rlk_status rlk_logp_fwd(const void* logits, rlk_dtype dtype, int64_t N, int64_t V, int64_t ld,
+                        const int64_t* targets, int64_t k, float softcap, float* logp,
+                        void* stats, void* stream);
+
+/* grad_logits[i, v] = (h_iv - p_iv * G_i) * dy/dx, where G_i is the sum of
+ * grad_logp[i, j] over valid slots and h_iv the sum over valid slots with
+ * t_ij == v (duplicates add, ascending j, in fp32 before the single cast).
+ * A row without any valid slot is exactly zero; otherwise a row whose logits
+ * are all -inf is NaN.  grad_logp is fp32 [N, k]; grad_logits is [N, V]
+ * contiguous in `dtype`. */
+rlk_status rlk_logp_bwd(const void* logits, rlk_dtype dtype, int64_t N, int64_t V, int64_t ld,
+                        const int64_t* targets, int64_t k, float softcap, const void* stats,
+                        const float* grad_logp, void* grad_logits, void* stream);
+
+/* -------------------------------------------------------------- entropy
+ * Pull request 8838, review comment: H = log S - W / S computed from one
+ * read of each logit.  entropy[i] = -sum_v p_iv log p_iv (0 log 0 = 0);
+ * NaN for a row whose logits are all -inf. */
+rlk_status rlk_entropy_fwd(const void* logits, rlk_dtype dtype, int64_t N, int64_t V, int64_t ld,
+                           float softcap, float* entropy, void* stats, void* stream);
+
+/* grad_logits[i, v] = -g_i p_iv (log p_iv + H_i) * dy/dx (masked columns: 0;
+ * rows whose logits are all -inf: NaN). */
+rlk_status rlk_entropy_bwd(const void* logits, rlk_dtype dtype, int64_t N, int64_t V, int64_t ld,
+                           float softcap, const void* stats, const float* grad_entropy,
+                           void* grad_logits, void* stream);
+
+/* ------------------------------------------------------------------- KL
+ * Pull request 8838, review comment: KL(A || B) = W / S_A - log S_A +
+ * log S_B from one read of both tensors.  kl[i] is NaN if either row is all
+ * -inf, +inf if the second distribution masks a column the first supports
+ * (decided on the logits, even where the probability underflows), else the
+ * sum above.  policy and ref share dtype and V; each has its own row stride
+ * and its own cap. */
+rlk_status rlk_kl_fwd(const void* policy, const void* ref, rlk_dtype dtype, int64_t N, int64_t V,
+                      int64_t ld_policy, int64_t ld_ref, rlk_kl_dir dir, float softcap_policy,
+                      float softcap_ref, float* kl, void* stats, void* stream);
+
+/* Gradient with respect to the policy logits only (the reference is
+ * detached):  reverse: g p (log p - log q - D) * dy/dx  (masked policy
+ * columns: 0; support-mismatch rows: NaN on the policy's support, 0 off it);
+ * forward: g (p - q) * dy/dx.  Rows where either input is all -inf: NaN. */
+rlk_status rlk_kl_bwd(const void* policy, const void* ref, rlk_dtype dtype, int64_t N, int64_t V,
+                      int64_t ld_policy, int64_t ld_ref, rlk_kl_dir dir, float softcap_policy,
+                      float softcap_ref, const void* stats, const float* grad_kl,
+                      void* grad_policy, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RLK_H */

@@ -1,0 +1,112 @@
+"""The C ABI on the host (no GPU needed): exports, helpers and validation.
+
+Every argument check of include/rlk.h runs on the host before any HIP call,
+so the error codes and the empty-input path are testable without a GPU.
+"""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from vocab_log_softmax_amd import rlk
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OK, ARG, DTYPE, SHAPE, DEVICE = 0, 1, 2, 3, 4
+F = ctypes.c_float
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return rlk.load_library()
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "rlk.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rlk_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for fn in ("rlk_softcap_fwd", "rlk_softcap_bwd", "rlk_logp_fwd", "rlk_logp_bwd",
+               "rlk_entropy_fwd", "rlk_entropy_bwd", "rlk_kl_fwd", "rlk_kl_bwd"):
+        assert fn in names
+    assert set(names) == set(rlk.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for fn in declared_functions():
+        assert hasattr(lib, fn), fn
+
+
+def test_helpers(lib):
+    assert lib.rlk_abi_version() == 1
+    assert lib.rlk_stats_bytes(0, 10, 7) == 320
+    assert lib.rlk_stats_bytes(2, 3, 7) == 96
+    assert lib.rlk_stats_bytes(0, 0, 7) == 0
+    assert lib.rlk_stats_bytes(9, 3, 7) == 0
+    assert lib.rlk_status_str(3) == b"RLK_ERR_SHAPE"
+    assert lib.rlk_status_str(42) == b"RLK_ERR_UNKNOWN"
+
+
+def _logp_fwd(lib, dtype=1, N=4, V=10, ld=10, k=1, cap=0.0, ptrs=True):
+    p = ctypes.c_void_p(16) if ptrs else None
+    return lib.rlk_logp_fwd(p, dtype, N, V, ld, p, k, F(cap), p, p, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=2), DTYPE), (dict(dtype=-1), DTYPE),
+    (dict(N=-1), SHAPE), (dict(V=0), SHAPE), (dict(ld=9), SHAPE), (dict(V=2**31, ld=2**31), SHAPE),
+    (dict(k=0), SHAPE), (dict(k=4097), SHAPE), (dict(N=2**40, ld=2**30, V=10), SHAPE),
+    (dict(cap=-1.0), ARG), (dict(cap=float("nan")), ARG), (dict(cap=float("inf")), ARG),
+    (dict(ptrs=False), ARG),
+])
+def test_logp_fwd_rejects(lib, kw, code):
+    assert _logp_fwd(lib, **kw) == code
+    assert rlk.rlk_last_error() != ""
+
+
+def test_empty_inputs_launch_nothing(lib):
+    # N == 0 is OK even with null pointers: nothing is touched, no HIP call.
+    assert _logp_fwd(lib, N=0, ptrs=False) == OK
+    assert lib.rlk_logp_bwd(None, 0, 0, 5, 5, None, 3, F(20.0), None, None, None, None) == OK
+    assert lib.rlk_entropy_fwd(None, 1, 0, 5, 5, F(0), None, None, None) == OK
+    assert lib.rlk_entropy_bwd(None, 1, 0, 5, 5, F(0), None, None, None, None) == OK
+    assert lib.rlk_kl_fwd(None, None, 1, 0, 5, 5, 5, 0, F(0), F(0), None, None, None) == OK
+    assert lib.rlk_kl_bwd(None, None, 1, 0, 5, 5, 5, 1, F(0), F(0), None, None, None, None) == OK
+    assert lib.rlk_softcap_fwd(None, 1, None, 0, 0, F(30.0), None) == OK
+    assert lib.rlk_softcap_bwd(None, 1, None, None, 0, F(30.0), None) == OK
+    assert rlk.rlk_last_error() == ""
+
+
+def test_other_entry_points_validate(lib):
+    p = ctypes.c_void_p(16)
+    assert lib.rlk_softcap_fwd(p, 1, p, 0, 8, F(0.0), None) == ARG        # cap must be > 0
+    assert lib.rlk_softcap_fwd(p, 1, p, 3, 8, F(30.0), None) == DTYPE
+    assert lib.rlk_softcap_bwd(p, 5, p, p, 8, F(30.0), None) == DTYPE
+    assert lib.rlk_softcap_bwd(p, 1, p, p, -1, F(30.0), None) == SHAPE
+    assert lib.rlk_entropy_fwd(p, 1, 4, 8, 7, F(0), p, p, None) == SHAPE   # ld < V
+    assert lib.rlk_entropy_bwd(p, 1, 4, 8, 8, F(-3.0), p, p, p, None) == ARG
+    assert lib.rlk_kl_fwd(p, p, 1, 4, 8, 8, 8, 2, F(0), F(0), p, p, None) == ARG  # bad dir
+    assert lib.rlk_kl_fwd(p, p, 1, 4, 8, 8, 6, 0, F(0), F(0), p, p, None) == SHAPE
+    assert lib.rlk_kl_bwd(p, p, 1, 4, 8, 8, 8, 0, F(0), F(float("nan")), p, p, p, None) == ARG
+    assert lib.rlk_kl_bwd(p, p, 1, 4, 8, 8, 8, 0, F(0), F(0), p, None, p, None) == ARG
+
+
+def test_host_memory_is_rejected_before_launch(lib):
+    # Plain host memory is not device memory: RLK_ERR_DEVICE, nothing launched.
+    x = np.zeros((4, 16), np.float32)
+    t = np.zeros((4, 1), np.int64)
+    o = np.zeros((4, 1), np.float32)
+    s = np.zeros(128, np.uint8)
+    st = lib.rlk_logp_fwd(x.ctypes.data, 0, 4, 16, 16, t.ctypes.data, 1, F(0), o.ctypes.data,
+                          s.ctypes.data, None)
+    assert st == DEVICE
+
+
+def test_binding_raises_with_status():
+    err = rlk.RLKError("rlk_logp_fwd", 3, "detail")
+    assert "RLK_ERR_SHAPE" in str(err) and err.status == 3

@@ -1,0 +1,416 @@
+// rlk_api.cpp -- the C ABI declared in include/rlk.h: host-side argument
+// validation, device binding and the launches.
+//
+// Validation happens entirely on the host before any HIP call, so a bad
+// argument never reaches a kernel ("Final Logit Softcap", Tensor and Precision
+// Contract: an invalid cap is rejected up front rather than turning into NaN
+// inside a kernel).  Empty inputs return before any HIP call.  The launch
+// goes to the device that owns the tensors, not to whichever device happens
+// to be current (the device-guard lesson of RL-Kernel pull requests 495 and
+// 507), and the caller's current device is restored.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+
+#include "rlk.h"
+#include "rlk_launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+rlk_status fail(rlk_status s, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+rlk_status ok() {
+    g_err[0] = '\0';
+    return RLK_OK;
+}
+
+bool dtype_ok(int d) { return d == RLK_F32 || d == RLK_BF16; }
+int64_t esize(int d) { return d == RLK_F32 ? 4 : 2; }
+
+// A fused-head cap: 0 = off, otherwise finite and > 0.
+rlk_status check_head_cap(float c, const char* name) {
+    if (c == 0.0f) return RLK_OK;
+    if (!std::isfinite(c) || !(c > 0.0f))
+        return fail(RLK_ERR_ARG, "%s must be 0 (off) or finite and > 0, got %g", name, (double)c);
+    return RLK_OK;
+}
+
+rlk_status check_matrix(int64_t N, int64_t V, int64_t ld, int64_t es, const char* name) {
+    if (N < 0) return fail(RLK_ERR_SHAPE, "N must be >= 0, got %lld", (long long)N);
+    if (V < 1) return fail(RLK_ERR_SHAPE, "V must be >= 1, got %lld", (long long)V);
+    if (V > INT32_MAX) return fail(RLK_ERR_SHAPE, "V must be < 2^31, got %lld", (long long)V);
+    if (ld < V)
+        return fail(RLK_ERR_SHAPE, "%s row stride %lld is smaller than V = %lld", name,
+                    (long long)ld, (long long)V);
+    if (N > 0 && ld > INT64_MAX / es / N)
+        return fail(RLK_ERR_SHAPE, "%s: N * ld overflows 64-bit offsets", name);
+    return RLK_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+float cap_k(float c) { return c != 0.0f ? -2.0f * 1.44269504088896340736f / c : 0.0f; }
+float cap_sc(float c) { return c != 0.0f ? c * 1.44269504088896340736f : 1.44269504088896340736f; }
+
+// Device that owns `ptr` (device or managed memory only).
+rlk_status pointer_device(const void* ptr, const char* name, int* dev) {
+    hipPointerAttribute_t attr;
+    hipError_t e = hipPointerGetAttributes(&attr, ptr);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(RLK_ERR_DEVICE, "%s is not a HIP allocation (%s)", name, hipGetErrorString(e));
+    }
+    if (attr.type != hipMemoryTypeDevice && attr.type != hipMemoryTypeManaged)
+        return fail(RLK_ERR_DEVICE, "%s is not device memory", name);
+    *dev = attr.device;
+    return RLK_OK;
+}
+
+// Binds the device owning every listed pointer for the lifetime of the
+// object and restores the caller's device afterwards.
+class DeviceBinding {
+  public:
+    rlk_status bind(std::initializer_list<std::pair<const void*, const char*>> ptrs) {
+        int dev = -1;
+        for (const auto& pn : ptrs) {
+            if (pn.first == nullptr) continue;
+            int d = -1;
+            rlk_status s = pointer_device(pn.first, pn.second, &d);
+            if (s != RLK_OK) return s;
+            if (dev < 0)
+                dev = d;
+            else if (d != dev)
+                return fail(RLK_ERR_DEVICE, "%s is on device %d but the first tensor is on %d",
+                            pn.second, d, dev);
+        }
+        if (dev < 0) return fail(RLK_ERR_DEVICE, "no device pointer given");
+        if (hipGetDevice(&prev_) != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(RLK_ERR_DEVICE, "hipGetDevice failed");
+        }
+        if (prev_ != dev) {
+            if (hipSetDevice(dev) != hipSuccess) {
+                (void)hipGetLastError();
+                return fail(RLK_ERR_DEVICE, "hipSetDevice(%d) failed", dev);
+            }
+            switched_ = true;
+        }
+        return RLK_OK;
+    }
+    ~DeviceBinding() {
+        if (switched_) (void)hipSetDevice(prev_);
+    }
+
+  private:
+    int prev_ = -1;
+    bool switched_ = false;
+};
+
+rlk_status launched(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(RLK_ERR_LAUNCH, "%s launch failed: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int rlk_abi_version(void) { return RLK_ABI_VERSION; }
+
+size_t rlk_stats_bytes(rlk_head head, int64_t N, int64_t V) {
+    (void)V;
+    if (N <= 0) return 0;
+    if (head != RLK_HEAD_LOGP && head != RLK_HEAD_ENTROPY && head != RLK_HEAD_KL) return 0;
+    return static_cast<size_t>(N) * 32u;
+}
+
+const char* rlk_status_str(rlk_status s) {
+    switch (s) {
+        case RLK_OK: return "RLK_OK";
+        case RLK_ERR_ARG: return "RLK_ERR_ARG";
+        case RLK_ERR_DTYPE: return "RLK_ERR_DTYPE";
+        case RLK_ERR_SHAPE: return "RLK_ERR_SHAPE";
+        case RLK_ERR_DEVICE: return "RLK_ERR_DEVICE";
+        case RLK_ERR_LAUNCH: return "RLK_ERR_LAUNCH";
+    }
+    return "RLK_ERR_UNKNOWN";
+}
+
+const char* rlk_last_error(void) { return g_err; }
+
+// ------------------------------------------------------------- softcap
+
+rlk_status rlk_softcap_fwd(const void* x, rlk_dtype x_dtype, void* y, rlk_dtype y_dtype,
+                           int64_t n, float cap, void* stream) {
+    if (!dtype_ok(x_dtype) || !dtype_ok(y_dtype))
+        return fail(RLK_ERR_DTYPE, "softcap dtypes must be RLK_F32 or RLK_BF16");
+    if (!std::isfinite(cap) || !(cap > 0.0f))
+        return fail(RLK_ERR_ARG, "softcap cap must be finite and > 0, got %g", (double)cap);
+    if (n < 0) return fail(RLK_ERR_SHAPE, "n must be >= 0, got %lld", (long long)n);
+    if (n == 0) return ok();
+    if (!x || !y) return fail(RLK_ERR_ARG, "x and y must be non-null when n > 0");
+    DeviceBinding dev;
+    rlk_status s = dev.bind({{x, "x"}, {y, "y"}});
+    if (s != RLK_OK) return s;
+    const bool al = aligned16(x) && aligned16(y);
+    return launched(rlk::launch_softcap_fwd(x, x_dtype, y, y_dtype, n, cap, al,
+                                            static_cast<hipStream_t>(stream)),
+                    "softcap_fwd");
+}
+
+rlk_status rlk_softcap_bwd(const void* x, rlk_dtype x_dtype, const float* grad_y, void* grad_x,
+                           int64_t n, float cap, void* stream) {
+    if (!dtype_ok(x_dtype)) return fail(RLK_ERR_DTYPE, "x dtype must be RLK_F32 or RLK_BF16");
+    if (!std::isfinite(cap) || !(cap > 0.0f))
+        return fail(RLK_ERR_ARG, "softcap cap must be finite and > 0, got %g", (double)cap);
+    if (n < 0) return fail(RLK_ERR_SHAPE, "n must be >= 0, got %lld", (long long)n);
+    if (n == 0) return ok();
+    if (!x || !grad_y || !grad_x) return fail(RLK_ERR_ARG, "null pointer with n > 0");
+    DeviceBinding dev;
+    rlk_status s = dev.bind({{x, "x"}, {grad_y, "grad_y"}, {grad_x, "grad_x"}});
+    if (s != RLK_OK) return s;
+    const bool al = aligned16(x) && aligned16(grad_y) && aligned16(grad_x);
+    return launched(rlk::launch_softcap_bwd(x, x_dtype, grad_y, grad_x, n, cap, al,
+                                            static_cast<hipStream_t>(stream)),
+                    "softcap_bwd");
+}
+
+// ------------------------------------------------------------ logprobs
+
+static rlk_status logp_common(const void* logits, rlk_dtype dtype, int64_t N, int64_t V,
+                              int64_t ld, const int64_t* targets, int64_t k, float softcap) {
+    if (!dtype_ok(dtype)) return fail(RLK_ERR_DTYPE, "logits dtype must be RLK_F32 or RLK_BF16");
+    rlk_status s = check_matrix(N, V, ld, esize(dtype), "logits");
+    if (s != RLK_OK) return s;
+    if (k < 1 || k > RLK_MAX_TOPK)
+        return fail(RLK_ERR_SHAPE, "k must be in [1, %d], got %lld", RLK_MAX_TOPK, (long long)k);
+    if (N > 0 && k > INT64_MAX / N) return fail(RLK_ERR_SHAPE, "N * k overflows");
+    s = check_head_cap(softcap, "softcap");
+    if (s != RLK_OK) return s;
+    (void)logits;
+    (void)targets;
+    return RLK_OK;
+}
+
+rlk_status rlk_logp_fwd(const void* logits, rlk_dtype dtype, int64_t N, int64_t V, int64_t ld,
+                        const int64_t* targets, int64_t k, float softcap, float* logp,
+                        void* stats, void* stream) {
+    rlk_status s = logp_common(logits, dtype, N, V, ld, targets, k, softcap);
+    if (s != RLK_OK) return s;
+    if (N == 0) return ok();
+    if (!logits || !targets || !logp || !stats)
+        return fail(RLK_ERR_ARG, "logits, targets, logp and stats must be non-null when N > 0");
+    DeviceBinding dev;
+    s = dev.bind({{logits, "logits"}, {targets, "targets"}, {logp, "logp"}, {stats, "stats"}});
+    if (s != RLK_OK) return s;
+    rlk::FwdParams p{};
+    p.x = logits;
+    p.N = N;
+    p.V = V;
+    p.ldx = ld;
+    p.targets = targets;
+    p.k = k;
+    p.kx = cap_k(softcap);
+    p.scx = cap_sc(softcap);
+    p.out = logp;
+    p.stats = stats;
+    const bool al = aligned16(logits) && (ld * esize(dtype)) % 16 == 0;
+    return launched(rlk::launch_fwd(rlk::kHeadLogp, dtype, softcap != 0.0f, false, al, p,
+                                    static_cast<hipStream_t>(stream)),
+                    "logp_fwd");
+}
+
+rlk_status rlk_logp_bwd(const void* logits, rlk_dtype dtype, int64_t N, int64_t V, int64_t ld,
+                        const int64_t* targets, int64_t k, float softcap, const void* stats,
+                        const float* grad_logp, void* grad_logits, void* stream) {
+    rlk_status s = logp_common(logits, dtype, N, V, ld, targets, k, softcap);
+    if (s != RLK_OK) return s;
+    if (N == 0) return ok();
+    if (!logits || !targets || !stats || !grad_logp || !grad_logits)
+        return fail(RLK_ERR_ARG, "null pointer with N > 0");
+    DeviceBinding dev;
+    s = dev.bind({{logits, "logits"}, {targets, "targets"}, {stats, "stats"},
+                  {grad_logp, "grad_logp"}, {grad_logits, "grad_logits"}});
+    if (s != RLK_OK) return s;
+    rlk::BwdParams p{};
+    p.x = logits;
+    p.N = N;
+    p.V = V;
+    p.ldx = ld;
+    p.targets = targets;
+    p.k = k;
+    p.kx = cap_k(softcap);
+    p.scx = cap_sc(softcap);
+    p.stats = stats;
+    p.g = grad_logp;
+    p.gx = grad_logits;
+    const bool al = aligned16(logits) && (ld * esize(dtype)) % 16 == 0 && aligned16(grad_logits) &&
+                    (V * esize(dtype)) % 16 == 0;
+    return launched(rlk::launch_bwd(rlk::kHeadLogp, dtype, softcap != 0.0f, false, al, p,
+                                    static_cast<hipStream_t>(stream)),
+                    "logp_bwd");
+}
+
+// -------------------------------------------------------------- entropy
+
+rlk_status rlk_entropy_fwd(const void* logits, rlk_dtype dtype, int64_t N, int64_t V, int64_t ld,
+                           float softcap, float* entropy, void* stats, void* stream) {
+    if (!dtype_ok(dtype)) return fail(RLK_ERR_DTYPE, "logits dtype must be RLK_F32 or RLK_BF16");
+    rlk_status s = check_matrix(N, V, ld, esize(dtype), "logits");
+    if (s != RLK_OK) return s;
+    s = check_head_cap(softcap, "softcap");
+    if (s != RLK_OK) return s;
+    if (N == 0) return ok();
+    if (!logits || !entropy || !stats)
+        return fail(RLK_ERR_ARG, "logits, entropy and stats must be non-null when N > 0");
+    DeviceBinding dev;
+    s = dev.bind({{logits, "logits"}, {entropy, "entropy"}, {stats, "stats"}});
+    if (s != RLK_OK) return s;
+    rlk::FwdParams p{};
+    p.x = logits;
+    p.N = N;
+    p.V = V;
+    p.ldx = ld;
+    p.k = 1;
+    p.kx = cap_k(softcap);
+    p.scx = cap_sc(softcap);
+    p.out = entropy;
+    p.stats = stats;
+    const bool al = aligned16(logits) && (ld * esize(dtype)) % 16 == 0;
+    return launched(rlk::launch_fwd(rlk::kHeadEntropy, dtype, softcap != 0.0f, false, al, p,
+                                    static_cast<hipStream_t>(stream)),
+                    "entropy_fwd");
+}
+
+rlk_status rlk_entropy_bwd(const void* logits, rlk_dtype dtype, int64_t N, int64_t V, int64_t ld,
+                           float softcap, const void* stats, const float* grad_entropy,
+                           void* grad_logits, void* stream) {
+    if (!dtype_ok(dtype)) return fail(RLK_ERR_DTYPE, "logits dtype must be RLK_F32 or RLK_BF16");
+    rlk_status s = check_matrix(N, V, ld, esize(dtype), "logits");
+    if (s != RLK_OK) return s;
+    s = check_head_cap(softcap, "softcap");
+    if (s != RLK_OK) return s;
+    if (N == 0) return ok();
+    if (!logits || !stats || !grad_entropy || !grad_logits)
+        return fail(RLK_ERR_ARG, "null pointer with N > 0");
+    DeviceBinding dev;
+    s = dev.bind({{logits, "logits"}, {stats, "stats"}, {grad_entropy, "grad_entropy"},
+                  {grad_logits, "grad_logits"}});
+    if (s != RLK_OK) return s;
+    rlk::BwdParams p{};
+    p.x = logits;
+    p.N = N;
+    p.V = V;
+    p.ldx = ld;
+    p.k = 1;
+    p.kx = cap_k(softcap);
+    p.scx = cap_sc(softcap);
+    p.stats = stats;
+    p.g = grad_entropy;
+    p.gx = grad_logits;
+    const bool al = aligned16(logits) && (ld * esize(dtype)) % 16 == 0 && aligned16(grad_logits) &&
+                    (V * esize(dtype)) % 16 == 0;
+    return launched(rlk::launch_bwd(rlk::kHeadEntropy, dtype, softcap != 0.0f, false, al, p,
+                                    static_cast<hipStream_t>(stream)),
+                    "entropy_bwd");
+}
+
+// ------------------------------------------------------------------- KL
+
+static rlk_status kl_common(rlk_dtype dtype, int64_t N, int64_t V, int64_t ld_policy,
+                            int64_t ld_ref, rlk_kl_dir dir, float cp, float cr) {
+    if (!dtype_ok(dtype)) return fail(RLK_ERR_DTYPE, "logits dtype must be RLK_F32 or RLK_BF16");
+    rlk_status s = check_matrix(N, V, ld_policy, esize(dtype), "policy");
+    if (s != RLK_OK) return s;
+    s = check_matrix(N, V, ld_ref, esize(dtype), "ref");
+    if (s != RLK_OK) return s;
+    if (dir != RLK_KL_REVERSE && dir != RLK_KL_FORWARD)
+        return fail(RLK_ERR_ARG, "dir must be RLK_KL_REVERSE or RLK_KL_FORWARD, got %d", (int)dir);
+    s = check_head_cap(cp, "softcap_policy");
+    if (s != RLK_OK) return s;
+    return check_head_cap(cr, "softcap_ref");
+}
+
+rlk_status rlk_kl_fwd(const void* policy, const void* ref, rlk_dtype dtype, int64_t N, int64_t V,
+                      int64_t ld_policy, int64_t ld_ref, rlk_kl_dir dir, float softcap_policy,
+                      float softcap_ref, float* kl, void* stats, void* stream) {
+    rlk_status s = kl_common(dtype, N, V, ld_policy, ld_ref, dir, softcap_policy, softcap_ref);
+    if (s != RLK_OK) return s;
+    if (N == 0) return ok();
+    if (!policy || !ref || !kl || !stats)
+        return fail(RLK_ERR_ARG, "policy, ref, kl and stats must be non-null when N > 0");
+    DeviceBinding dev;
+    s = dev.bind({{policy, "policy"}, {ref, "ref"}, {kl, "kl"}, {stats, "stats"}});
+    if (s != RLK_OK) return s;
+    rlk::FwdParams p{};
+    p.x = policy;
+    p.y = ref;
+    p.N = N;
+    p.V = V;
+    p.ldx = ld_policy;
+    p.ldy = ld_ref;
+    p.k = 1;
+    p.kx = cap_k(softcap_policy);
+    p.ky = cap_k(softcap_ref);
+    p.scx = cap_sc(softcap_policy);
+    p.scy = cap_sc(softcap_ref);
+    p.out = kl;
+    p.stats = stats;
+    const int64_t es = esize(dtype);
+    const bool al = aligned16(policy) && aligned16(ref) && (ld_policy * es) % 16 == 0 &&
+                    (ld_ref * es) % 16 == 0;
+    const int head = dir == RLK_KL_REVERSE ? rlk::kHeadKLReverse : rlk::kHeadKLForward;
+    return launched(rlk::launch_fwd(head, dtype, softcap_policy != 0.0f, softcap_ref != 0.0f, al,
+                                    p, static_cast<hipStream_t>(stream)),
+                    "kl_fwd");
+}
+
+rlk_status rlk_kl_bwd(const void* policy, const void* ref, rlk_dtype dtype, int64_t N, int64_t V,
+                      int64_t ld_policy, int64_t ld_ref, rlk_kl_dir dir, float softcap_policy,
+                      float softcap_ref, const void* stats, const float* grad_kl,
+                      void* grad_policy, void* stream) {
+    rlk_status s = kl_common(dtype, N, V, ld_policy, ld_ref, dir, softcap_policy, softcap_ref);
+    if (s != RLK_OK) return s;
+    if (N == 0) return ok();
+    if (!policy || !ref || !stats || !grad_kl || !grad_policy)
+        return fail(RLK_ERR_ARG, "null pointer with N > 0");
+    DeviceBinding dev;
+    s = dev.bind({{policy, "policy"}, {ref, "ref"}, {stats, "stats"}, {grad_kl, "grad_kl"},
+                  {grad_policy, "grad_policy"}});
+    if (s != RLK_OK) return s;
+    rlk::BwdParams p{};
+    p.x = policy;
+    p.y = ref;
+    p.N = N;
+    p.V = V;
+    p.ldx = ld_policy;
+    p.ldy = ld_ref;
+    p.k = 1;
+    p.kx = cap_k(softcap_policy);
+    p.ky = cap_k(softcap_ref);
+    p.scx = cap_sc(softcap_policy);
+    p.scy = cap_sc(softcap_ref);
+    p.stats = stats;
+    p.g = grad_kl;
+    p.gx = grad_policy;
+    const int64_t es = esize(dtype);
+    const bool al = aligned16(policy) && aligned16(ref) && (ld_policy * es) % 16 == 0 &&
+                    (ld_ref * es) % 16 == 0 && aligned16(grad_policy) && (V * es) % 16 == 0;
+    const int head = dir == RLK_KL_REVERSE ? rlk::kHeadKLReverse : rlk::kHeadKLForward;
+    return launched(rlk::launch_bwd(head, dtype, softcap_policy != 0.0f, softcap_ref != 0.0f, al,
+                                    p, static_cast<hipStream_t>(stream)),
+                    "kl_bwd");
+}
+
+}  // extern "C"

@@ -1,0 +1,289 @@
+// rlk_bwd.hip -- fused zero-workspace backward row kernels.
+//
+// "perf(logp): fused zero-workspace backward for the generic CUDA fused logp"
+// (RL-Kernel pull request 495), Summary: the gradient g (onehot - softmax) is
+// written straight in the logits dtype with no [N, V] fp32 temporary; rows
+// whose targets are all outside [0, V) get an exactly zero gradient (Behavior
+// changes).  Here the softmax is not recomputed from two more passes: the
+// forward saved (m log2 e, log2 S) per row, so each logit is read once and
+// each gradient written once, and p comes from the very same FMA as in the
+// forward (bitwise-consistent with the forward output).
+//
+// Heads (all times the upstream g of the row and, with a softcap, the
+// derivative 1 - tanh^2 of "Final Logit Softcap", Summary):
+//   logprobs: h_v - p_v G, with the top-k one-hot sums h added in fp32 before
+//             the single cast ("Add Triton kernels for vocab-parallel
+//             logprobs, entropy and KL", Changes);
+//   entropy:  -p_v (log p_v + H);
+//   reverse KL(P||R): p_v (log p_v - log q_v - D);
+//   forward KL(R||P): p_v - q_v.
+#include "rlk_device.h"
+#include "rlk_launch.h"
+
+namespace rlk {
+
+// Load the U chunks of one group (raw values, -inf beyond V).
+template <int BLOCK, int U, typename S, bool ALIGNED>
+__device__ __forceinline__ void load_raw(const S* __restrict__ row, int64_t V, int64_t g0,
+                                         bool full, float (&x)[U][kChunk]) {
+    const int tid = threadIdx.x;
+    if (ALIGNED && full) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) load_chunk(row + (g0 + u * BLOCK + tid) * kChunk, x[u]);
+    } else {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t c0 = (g0 + u * BLOCK + tid) * kChunk;
+#pragma unroll
+            for (int e = 0; e < kChunk; ++e) {
+                const int64_t col = c0 + e;
+                x[u][e] = col < V ? load_one(row + col) : neg_inf();
+            }
+        }
+    }
+}
+
+// Store the U chunks of one group (elements beyond V are not written).
+template <int BLOCK, int U, typename S, bool ALIGNED>
+__device__ __forceinline__ void store_group(S* __restrict__ row, int64_t V, int64_t g0, bool full,
+                                            const float (&v)[U][kChunk]) {
+    const int tid = threadIdx.x;
+    if (ALIGNED && full) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) store_chunk(row + (g0 + u * BLOCK + tid) * kChunk, v[u]);
+    } else {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t c0 = (g0 + u * BLOCK + tid) * kChunk;
+#pragma unroll
+            for (int e = 0; e < kChunk; ++e)
+                if (c0 + e < V) store_one(row + c0 + e, v[u][e]);
+        }
+    }
+}
+
+// Row modes.
+enum : int { kModeNormal = 0, kModeZero = 1, kModeNaN = 2, kModeMismatch = 3 };
+
+template <int BLOCK, int U, typename T, int HEAD, bool CAPA, bool CAPB, bool ALIGNED>
+__global__ __launch_bounds__(BLOCK) void bwd_kernel(BwdParams p) {
+    using S = typename T::storage;
+    constexpr bool KL = HEAD == kHeadKLReverse || HEAD == kHeadKLForward;
+    constexpr int NW = BLOCK / 64;
+    extern __shared__ int smem_topk[];  // logp: int32 target (-1: ignored) [k], fp32 g [k]
+    __shared__ float red_g[NW];
+    __shared__ float red_n[NW];
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int64_t nchunks = (p.V + kChunk - 1) / kChunk, nfull = p.V / kChunk;
+    const RowStats* stats = static_cast<const RowStats*>(p.stats);
+    int* tg = smem_topk;
+    float* gg = reinterpret_cast<float*>(smem_topk + p.k);
+
+    for (int64_t row = blockIdx.x; row < p.N; row += gridDim.x) {
+        const RowStats rs = stats[row];
+        const S* __restrict__ xa = static_cast<const S*>(p.x) + row * p.ldx;
+        const S* __restrict__ xb = KL ? static_cast<const S*>(p.y) + row * p.ldy : nullptr;
+        S* __restrict__ gx = static_cast<S*>(p.gx) + row * p.V;
+
+        int mode = kModeNormal;
+        float G = 0.0f;
+        if (HEAD == kHeadLogp) {
+            // Stage the slots and sum G over valid ones with a fixed tree.
+            float part = 0.0f, cnt = 0.0f;
+            for (int64_t j = tid; j < p.k; j += BLOCK) {
+                const int64_t t = p.targets[row * p.k + j];
+                const bool valid = t >= 0 && t < p.V;
+                const float g = p.g[row * p.k + j];
+                tg[j] = valid ? static_cast<int>(t) : -1;
+                gg[j] = g;
+                if (valid) {
+                    part += g;
+                    cnt += 1.0f;
+                }
+            }
+            part = wave_sum(part);
+            cnt = wave_sum(cnt);
+            if (lane == 0) {
+                red_g[wid] = part;
+                red_n[wid] = cnt;
+            }
+            __syncthreads();
+            float n = red_n[0];
+            G = red_g[0];
+#pragma unroll
+            for (int w = 1; w < NW; ++w) {
+                G += red_g[w];
+                n += red_n[w];
+            }
+            if (n == 0.0f)
+                mode = kModeZero;
+            else if (rs.flags & kFlagEmptyA)
+                mode = kModeNaN;
+        } else if (HEAD == kHeadEntropy) {
+            if (rs.flags & kFlagEmptyA) mode = kModeNaN;
+        } else {
+            if (rs.flags & (kFlagEmptyA | kFlagEmptyB))
+                mode = kModeNaN;
+            else if (HEAD == kHeadKLReverse && (rs.flags & kFlagMismatch))
+                mode = kModeMismatch;
+        }
+
+        // Per-row coefficients.
+        const float g_row = (HEAD == kHeadLogp) ? 0.0f : p.g[row];
+        float A = 0.0f, B = 0.0f;
+        if (HEAD == kHeadLogp) {
+            A = CAPA ? -4.0f * G : -G;  // cap: slope 4 r (1 - r)
+        } else if (HEAD == kHeadEntropy) {
+            A = -g_row * kLn2;
+            B = -g_row * rs.value;
+        } else if (HEAD == kHeadKLReverse) {
+            A = g_row * kLn2;
+            B = -g_row * rs.value;
+        } else {
+            A = CAPA ? 4.0f * g_row : g_row;
+        }
+
+        for (int64_t g0 = 0; g0 < nchunks; g0 += (int64_t)U * BLOCK) {
+            const bool full = g0 + (int64_t)U * BLOCK <= nfull;
+            float v[U][kChunk];
+            if (mode == kModeNormal) {
+                float xa_[U][kChunk];
+                load_raw<BLOCK, U, S, ALIGNED>(xa, p.V, g0, full, xa_);
+                float xb_[KL ? U : 1][kChunk];
+                if (KL) load_raw<BLOCK, KL ? U : 1, S, ALIGNED>(xb, p.V, g0, full, xb_);
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+#pragma unroll
+                    for (int e = 0; e < kChunk; ++e) {
+                        float a = xa_[u][e], r = 0.0f;
+                        if (CAPA) {
+                            const CapVal c = cap_fast(a, p.kx);
+                            a = c.a;
+                            r = c.r;
+                        }
+                        const float ta = __builtin_fmaf(a, p.scx, -rs.mLa) - rs.log2Sa;
+                        float out;
+                        if (HEAD == kHeadLogp) {
+                            out = A * ex2(ta);
+                        } else if (HEAD == kHeadEntropy) {
+                            const float tc = fmaxf(ta, kClampT);
+                            out = ex2(tc) * __builtin_fmaf(A, tc, B);
+                        } else {
+                            float b = xb_[KL ? u : 0][e];
+                            if (CAPB) b = cap_fast(b, p.ky).a;
+                            const float tb = __builtin_fmaf(b, p.scy, -rs.mLb) - rs.log2Sb;
+                            if (HEAD == kHeadKLReverse) {
+                                const float l = fmaxf(ta - tb, kClampT);
+                                out = ex2(ta) * __builtin_fmaf(A, l, B);
+                            } else {
+                                out = A * (ex2(ta) - ex2(tb));
+                            }
+                        }
+                        if (CAPA) out *= (HEAD == kHeadLogp || HEAD == kHeadKLForward)
+                                             ? r * (1.0f - r)
+                                             : cap_fast_slope(r);
+                        v[u][e] = out;
+                    }
+            } else if (mode == kModeMismatch) {
+                float xa_[U][kChunk];
+                load_raw<BLOCK, U, S, ALIGNED>(xa, p.V, g0, full, xa_);
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+#pragma unroll
+                    for (int e = 0; e < kChunk; ++e)
+                        v[u][e] = (!CAPA && xa_[u][e] == neg_inf()) ? 0.0f : qnan();
+            } else {
+                const float fill = mode == kModeZero ? 0.0f : qnan();
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+#pragma unroll
+                    for (int e = 0; e < kChunk; ++e) v[u][e] = fill;
+            }
+            store_group<BLOCK, U, S, ALIGNED>(gx, p.V, g0, full, v);
+        }
+
+        if (HEAD == kHeadLogp && mode == kModeNormal) {
+            // Target columns: rewrite the bulk value with its one-hot term.
+            // The barrier orders these stores after this workgroup's bulk
+            // stores of the same addresses.
+            __syncthreads();
+            for (int64_t j = tid; j < p.k; j += BLOCK) {
+                const int t = tg[j];
+                if (t < 0) continue;
+                bool first = true;
+                float h = 0.0f;
+                for (int64_t jj = 0; jj < p.k; ++jj) {
+                    if (tg[jj] == t) {
+                        if (jj < j) first = false;
+                        h += gg[jj];
+                    }
+                }
+                if (!first) continue;
+                float a = load_one(xa + t), slope = 1.0f;
+                if (CAPA) {
+                    const CapVal c = cap_fast(a, p.kx);
+                    a = c.a;
+                    slope = cap_fast_slope(c.r);
+                }
+                const float pt = ex2(__builtin_fmaf(a, p.scx, -rs.mLa) - rs.log2Sa);
+                store_one(gx + t, __builtin_fmaf(-pt, G, h) * slope);
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// ------------------------------------------------------------- dispatch
+
+template <typename T, bool CAPX, bool CAPY, bool AL>
+static hipError_t bwd_dispatch_head(int head, const BwdParams& p, hipStream_t s) {
+    const dim3 grid(row_grid(p.N)), block(kBlock);
+    switch (head) {
+        case kHeadLogp: {
+            const size_t lds = static_cast<size_t>(p.k) * (sizeof(int) + sizeof(float));
+            hipLaunchKernelGGL((bwd_kernel<kBlock, kUnroll1, T, kHeadLogp, CAPX, false, AL>), grid,
+                               block, lds, s, p);
+            break;
+        }
+        case kHeadEntropy:
+            hipLaunchKernelGGL((bwd_kernel<kBlock, kUnroll1, T, kHeadEntropy, CAPX, false, AL>),
+                               grid, block, 0, s, p);
+            break;
+        case kHeadKLReverse:
+            hipLaunchKernelGGL((bwd_kernel<kBlock, kUnrollKL, T, kHeadKLReverse, CAPX, CAPY, AL>),
+                               grid, block, 0, s, p);
+            break;
+        case kHeadKLForward:
+            hipLaunchKernelGGL((bwd_kernel<kBlock, kUnrollKL, T, kHeadKLForward, CAPX, CAPY, AL>),
+                               grid, block, 0, s, p);
+            break;
+        default:
+            return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <typename T, bool CAPX, bool CAPY>
+static hipError_t bwd_dispatch_al(int head, bool al, const BwdParams& p, hipStream_t s) {
+    return al ? bwd_dispatch_head<T, CAPX, CAPY, true>(head, p, s)
+              : bwd_dispatch_head<T, CAPX, CAPY, false>(head, p, s);
+}
+
+template <typename T>
+static hipError_t bwd_dispatch_cap(int head, bool cx, bool cy, bool al, const BwdParams& p,
+                                   hipStream_t s) {
+    const bool kl = head == kHeadKLReverse || head == kHeadKLForward;
+    if (!kl) cy = false;
+    if (cx && cy) return bwd_dispatch_al<T, true, true>(head, al, p, s);
+    if (cx) return bwd_dispatch_al<T, true, false>(head, al, p, s);
+    if (cy) return bwd_dispatch_al<T, false, true>(head, al, p, s);
+    return bwd_dispatch_al<T, false, false>(head, al, p, s);
+}
+
+hipError_t launch_bwd(int head, int dtype, bool cap_x, bool cap_y, bool aligned,
+                      const BwdParams& p, hipStream_t stream) {
+    if (dtype == 0) return bwd_dispatch_cap<F32>(head, cap_x, cap_y, aligned, p, stream);
+    return bwd_dispatch_cap<BF16>(head, cap_x, cap_y, aligned, p, stream);
+}
+
+}  // namespace rlk

@@ -1,0 +1,285 @@
+// rlk_device.h -- device-side building blocks shared by the forward, backward
+// and softcap kernels (gfx950, wave64).
+//
+// Element -> lane map.  A row of V logits is cut into chunks of 8 consecutive
+// elements (one 16-byte load for bf16, two for fp32).  In a workgroup of
+// BLOCK threads, lane `tid` owns chunks tid, tid + BLOCK, tid + 2 BLOCK, ...,
+// consumed in groups of U chunks.  This map, the group size, the per-lane
+// accumulation order and the reduction tree depend only on V and on the
+// compile-time BLOCK and U: never on N, on the row stride, on the pointer
+// alignment or on the dtype.  So every row's result is deterministic and
+// batch-invariant, and an fp32 and a bf16 row holding the same values give
+// identical statistics.
+//
+// Online statistics in base 2 (the single-read scheme of the review comment
+// on "Add Triton kernels for vocab-parallel logprobs, entropy and KL",
+// DeepSpeed pull request 8838, re-derived here with exp2):
+//   a_v  = x_v, or tanh(x_v / c) when the softcap is on (then y = c a);
+//   sc   = log2(e), or c log2(e);  so y_v log2(e) = a_v sc;
+//   mL   = m sc with m the running maximum of a (a rounded constant that is
+//          used consistently everywhere, so its rounding cancels);
+//   t_v  = a_v sc - mL (one FMA), S = sum 2^t_v, W = sum 2^t_v t_v.
+//   When the maximum grows by d = mL_old - mL_new (< 0):
+//          S <- 2^d S,  W <- 2^d (W + d S).
+//   Then logsumexp(y) = ln2 (mL + log2 S) and the entropy is
+//          H = ln2 (log2 S - W / S).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rlk {
+
+constexpr float kLog2e = 1.44269504088896340736f;
+constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kClampT = -256.0f;  // 2^-256 is 0 in fp32: clamping t below it is exact
+constexpr int kChunk = 8;
+
+__device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
+__device__ __forceinline__ float pos_inf() { return __builtin_inff(); }
+__device__ __forceinline__ float qnan() { return __builtin_nanf(""); }
+
+// Raw hardware exp2 / reciprocal (v_exp_f32, v_rcp_f32, about 1 ulp).
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// ---------------------------------------------------------------- dtypes
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+struct F32 {
+    using storage = float;
+    static constexpr int kBytes = 4;
+};
+struct BF16 {
+    using storage = uint16_t;
+    static constexpr int kBytes = 2;
+};
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+    return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+// Round-to-nearest-even pack (v_cvt_pk_bf16_f32 on gfx950; NaN stays NaN).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    bf16x2_t v;
+    v.x = static_cast<__bf16>(lo);
+    v.y = static_cast<__bf16>(hi);
+    return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+
+// Load one full chunk of 8 elements from a 16-byte aligned address.
+__device__ __forceinline__ void load_chunk(const float* p, float (&f)[kChunk]) {
+    const float4 a = *reinterpret_cast<const float4*>(p);
+    const float4 b = *(reinterpret_cast<const float4*>(p) + 1);
+    f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+    f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+}
+__device__ __forceinline__ void load_chunk(const uint16_t* p, float (&f)[kChunk]) {
+    const uint4 w = *reinterpret_cast<const uint4*>(p);
+    f[0] = bf16_lo(w.x); f[1] = bf16_hi(w.x);
+    f[2] = bf16_lo(w.y); f[3] = bf16_hi(w.y);
+    f[4] = bf16_lo(w.z); f[5] = bf16_hi(w.z);
+    f[6] = bf16_lo(w.w); f[7] = bf16_hi(w.w);
+}
+__device__ __forceinline__ float load_one(const float* p) { return *p; }
+__device__ __forceinline__ float load_one(const uint16_t* p) { return bf16_to_f32(*p); }
+
+// Store one full chunk of 8 values to a 16-byte aligned address.
+__device__ __forceinline__ void store_chunk(float* p, const float (&f)[kChunk]) {
+    *reinterpret_cast<float4*>(p) = make_float4(f[0], f[1], f[2], f[3]);
+    *(reinterpret_cast<float4*>(p) + 1) = make_float4(f[4], f[5], f[6], f[7]);
+}
+__device__ __forceinline__ void store_chunk(uint16_t* p, const float (&f)[kChunk]) {
+    uint4 w;
+    w.x = pack_bf16x2(f[0], f[1]);
+    w.y = pack_bf16x2(f[2], f[3]);
+    w.z = pack_bf16x2(f[4], f[5]);
+    w.w = pack_bf16x2(f[6], f[7]);
+    *reinterpret_cast<uint4*>(p) = w;
+}
+__device__ __forceinline__ void store_one(float* p, float f) { *p = f; }
+__device__ __forceinline__ void store_one(uint16_t* p, float f) { *p = f32_to_bf16(f); }
+
+// ---------------------------------------------------------------- softcap
+//
+// "Final Logit Softcap", Summary: y = c tanh(x / c), dy/dx = 1 - tanh^2.
+//
+// Fused prologue form.  With r = 1 / (1 + 2^(k x)), k = -2 log2(e) / c:
+//   tanh(x / c) = 2 r - 1   and   1 - tanh^2(x / c) = 4 r (1 - r).
+// Both ends are exact (x = +inf: r = 1, tanh = 1; x = -inf: r = 0,
+// tanh = -1; slope 0).  The absolute error of tanh is a few 1e-8, which is
+// what the softmax sees (it depends on absolute errors of y).
+struct CapVal {
+    float a;  // tanh(x / c)
+    float r;  // 1 / (1 + 2^(k x))
+};
+__device__ __forceinline__ CapVal cap_fast(float x, float k) {
+    const float e = ex2(x * k);
+    const float r = rcp(1.0f + e);
+    return {__builtin_fmaf(2.0f, r, -1.0f), r};
+}
+__device__ __forceinline__ float cap_fast_slope(float r) { return 4.0f * r * (1.0f - r); }
+
+// Standalone form, accurate in RELATIVE terms (the output y itself is
+// compared at 1e-5 relative).  For |u| < 0.55 an odd polynomial
+// u + u^3 P(u^2) whose five coefficients were fitted to tanh on [0, 0.55]
+// (weighted least squares, max relative error 7e-8 in fp32 Horner form);
+// above, tanh|u| = (1 - e) / (1 + e) with e = 2^(-2 log2(e) |u|) <= 1/3 and
+// the slope 4 e / (1 + e)^2 (no cancellation near saturation).
+__device__ __forceinline__ float tanh_precise(float u, float* slope) {
+    const float au = fabsf(u);
+    const float u2 = u * u;
+    float p = -6.0180192813277245e-03f;
+    p = __builtin_fmaf(p, u2, 2.0877523347735405e-02f);
+    p = __builtin_fmaf(p, u2, -5.3801555186510086e-02f);
+    p = __builtin_fmaf(p, u2, 1.3332062959671020e-01f);
+    p = __builtin_fmaf(p, u2, -3.3333301544189453e-01f);
+    const float ts = __builtin_fmaf(u * u2, p, u);
+    const float e = ex2(-2.0f * kLog2e * au);
+    const float r = rcp(1.0f + e);
+    const float tl = __builtin_copysignf(__builtin_fmaf(-e, r, r), u);
+    const bool small = au < 0.55f;
+    *slope = small ? __builtin_fmaf(-ts, ts, 1.0f) : 4.0f * e * r * r;
+    return small ? ts : tl;
+}
+
+// ------------------------------------------------------- online statistics
+
+// Running statistics of one tensor row (per lane, then merged).
+//   m: max of a (-inf while nothing finite has been seen), mL = m sc
+//   (0 while m = -inf, so t stays -inf instead of NaN), S, W as above.
+struct Stat1 {
+    float m, mL, S, W;
+};
+
+__device__ __forceinline__ Stat1 stat1_init() { return {neg_inf(), 0.0f, 0.0f, 0.0f}; }
+
+// Merge two partial states (exact up to rounding; empty parts drop out).
+template <bool WITH_W>
+__device__ __forceinline__ Stat1 stat1_merge(const Stat1& A, const Stat1& B) {
+    if (A.m == neg_inf()) return B;
+    if (B.m == neg_inf()) return A;
+    const bool a_big = A.m >= B.m;
+    Stat1 o;
+    o.m = a_big ? A.m : B.m;
+    o.mL = a_big ? A.mL : B.mL;
+    const float dA = A.mL - o.mL, dB = B.mL - o.mL;  // <= 0, finite
+    const float sA = ex2(dA), sB = ex2(dB);
+    o.S = A.S * sA + B.S * sB;
+    o.W = WITH_W ? sA * __builtin_fmaf(dA, A.S, A.W) + sB * __builtin_fmaf(dB, B.S, B.W) : 0.0f;
+    return o;
+}
+
+// Statistics of a KL row pair: a side (policy) and b side (reference).
+//   W = sum 2^ta (ta - tb)  (reverse: weights from the policy) or
+//   W = sum 2^tb (tb - ta)  (forward: weights from the reference);
+//   flag = max (reverse) / min (forward) of ta - tb: +inf / -inf exactly
+//   when one side is finite where the other is -inf (support mismatch).
+struct StatKL {
+    float ma, mLa, Sa, mb, mLb, Sb, W, flag;
+};
+
+template <bool REVERSE>
+__device__ __forceinline__ StatKL statkl_init() {
+    return {neg_inf(), 0.0f, 0.0f, neg_inf(), 0.0f, 0.0f, 0.0f, REVERSE ? neg_inf() : pos_inf()};
+}
+
+template <bool REVERSE>
+__device__ __forceinline__ StatKL statkl_merge(const StatKL& A, const StatKL& B) {
+    StatKL o;
+    o.flag = REVERSE ? fmaxf(A.flag, B.flag) : fminf(A.flag, B.flag);
+    // a side
+    const bool a_empty_A = A.ma == neg_inf(), a_empty_B = B.ma == neg_inf();
+    const bool a_big = A.ma >= B.ma;
+    o.ma = a_big ? A.ma : B.ma;
+    o.mLa = a_empty_A ? B.mLa : (a_empty_B ? A.mLa : (a_big ? A.mLa : B.mLa));
+    const float dA = a_empty_A ? 0.0f : A.mLa - o.mLa;
+    const float dB = a_empty_B ? 0.0f : B.mLa - o.mLa;
+    const float saA = a_empty_A ? 0.0f : ex2(dA), saB = a_empty_B ? 0.0f : ex2(dB);
+    // b side
+    const bool b_empty_A = A.mb == neg_inf(), b_empty_B = B.mb == neg_inf();
+    const bool b_big = A.mb >= B.mb;
+    o.mb = b_big ? A.mb : B.mb;
+    o.mLb = b_empty_A ? B.mLb : (b_empty_B ? A.mLb : (b_big ? A.mLb : B.mLb));
+    const float eA = b_empty_A ? 0.0f : A.mLb - o.mLb;
+    const float eB = b_empty_B ? 0.0f : B.mLb - o.mLb;
+    const float sbA = b_empty_A ? 0.0f : ex2(eA), sbB = b_empty_B ? 0.0f : ex2(eB);
+    o.Sa = A.Sa * saA + B.Sa * saB;
+    o.Sb = A.Sb * sbA + B.Sb * sbB;
+    // A part with no finite weight carries W = 0 (or a mismatch, which
+    // overrides the value anyway): drop it instead of scaling 0 by garbage.
+    float wA, wB;
+    if (REVERSE) {
+        wA = (a_empty_A || b_empty_A) ? 0.0f : saA * __builtin_fmaf(dA - eA, A.Sa, A.W);
+        wB = (a_empty_B || b_empty_B) ? 0.0f : saB * __builtin_fmaf(dB - eB, B.Sa, B.W);
+    } else {
+        wA = (a_empty_A || b_empty_A) ? 0.0f : sbA * __builtin_fmaf(eA - dA, A.Sb, A.W);
+        wB = (a_empty_B || b_empty_B) ? 0.0f : sbB * __builtin_fmaf(eB - dB, B.Sb, B.W);
+    }
+    o.W = wA + wB;
+    return o;
+}
+
+// ---------------------------------------------------- wave64 shuffles
+
+__device__ __forceinline__ float shfl_xor(float v, int mask) {
+    return __shfl_xor(v, mask, 64);
+}
+
+template <bool WITH_W>
+__device__ __forceinline__ Stat1 wave_reduce(Stat1 s) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        Stat1 o;
+        o.m = shfl_xor(s.m, off);
+        o.mL = shfl_xor(s.mL, off);
+        o.S = shfl_xor(s.S, off);
+        o.W = WITH_W ? shfl_xor(s.W, off) : 0.0f;
+        s = stat1_merge<WITH_W>(s, o);
+    }
+    return s;
+}
+
+template <bool REVERSE>
+__device__ __forceinline__ StatKL wave_reduce_kl(StatKL s) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        StatKL o;
+        o.ma = shfl_xor(s.ma, off);
+        o.mLa = shfl_xor(s.mLa, off);
+        o.Sa = shfl_xor(s.Sa, off);
+        o.mb = shfl_xor(s.mb, off);
+        o.mLb = shfl_xor(s.mLb, off);
+        o.Sb = shfl_xor(s.Sb, off);
+        o.W = shfl_xor(s.W, off);
+        o.flag = shfl_xor(s.flag, off);
+        s = statkl_merge<REVERSE>(s, o);
+    }
+    return s;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += shfl_xor(v, off);
+    return v;
+}
+
+// ----------------------------------------------------------- row record
+
+// Per-row record written by a forward call and read by its backward call.
+// 32 bytes per row, 16-byte aligned.
+struct alignas(16) RowStats {
+    float mLa, log2Sa;  // first (or only) tensor: scaled max, log2 of the sum
+    float mLb, log2Sb;  // KL reference tensor
+    float value;        // entropy H, or KL D (natural log units)
+    uint32_t flags;     // kFlag* bits
+    float pad0, pad1;
+};
+constexpr uint32_t kFlagEmptyA = 1u, kFlagEmptyB = 2u, kFlagMismatch = 4u;
+
+}  // namespace rlk

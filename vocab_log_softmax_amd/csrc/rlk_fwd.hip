@@ -1,0 +1,307 @@
+// rlk_fwd.hip -- forward row kernels: one read of each logit, online
+// statistics, head outputs and the per-row record for the backward.
+//
+// Single-read statistics follow the review comment "Suggested change: read
+// each logit once in the entropy / KL forward" on "Add Triton kernels for
+// vocab-parallel logprobs, entropy and KL" (DeepSpeed pull request 8838):
+// the running max, the sum of exponentials and a probability-weighted sum of
+// centred logits, all rescaled when the max grows, give
+//   entropy  H = log S - W / S,
+//   KL(A||B) = W / S_A - log S_A + log S_B,
+// and a support-mismatch flag decided on the logits.  The logprobs head reads
+// the target logit after the row statistics (pull request 495, Behavior
+// changes: targets outside [0, V) give 0).
+#include "rlk_device.h"
+#include "rlk_launch.h"
+
+namespace rlk {
+
+// Load the U chunks of one group for lane `tid`: a[u][e] = element
+// (g0 + u BLOCK + tid) * 8 + e, softcapped when CAP, -inf beyond V.
+template <int BLOCK, int U, typename S, bool CAP, bool ALIGNED>
+__device__ __forceinline__ void load_group(const S* __restrict__ row, int64_t V, int64_t g0,
+                                           bool full, float k, float (&a)[U][kChunk]) {
+    const int tid = threadIdx.x;
+    if (ALIGNED && full) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) load_chunk(row + (g0 + u * BLOCK + tid) * kChunk, a[u]);
+        if (CAP) {
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int e = 0; e < kChunk; ++e) a[u][e] = cap_fast(a[u][e], k).a;
+        }
+    } else {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t c0 = (g0 + u * BLOCK + tid) * kChunk;
+#pragma unroll
+            for (int e = 0; e < kChunk; ++e) {
+                const int64_t col = c0 + e;
+                float v = neg_inf();
+                if (col < V) {
+                    v = load_one(row + col);
+                    if (CAP) v = cap_fast(v, k).a;
+                }
+                a[u][e] = v;
+            }
+        }
+    }
+}
+
+// Fold one group into a single-tensor state.
+template <int U, bool WITH_W>
+__device__ __forceinline__ void update1(Stat1& st, const float (&a)[U][kChunk], float sc) {
+    float gm = a[0][0];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int e = 0; e < kChunk; ++e) gm = fmaxf(gm, a[u][e]);
+    if (gm > st.m) {
+        const float mLn = gm * sc;
+        if (st.m != neg_inf()) {
+            const float d = st.mL - mLn;
+            const float s = ex2(d);
+            if (WITH_W) st.W = s * __builtin_fmaf(d, st.S, st.W);
+            st.S *= s;
+        }
+        st.m = gm;
+        st.mL = mLn;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int e = 0; e < kChunk; ++e) {
+            float t = __builtin_fmaf(a[u][e], sc, -st.mL);
+            if (WITH_W) t = fmaxf(t, kClampT);
+            const float ex = ex2(t);
+            st.S += ex;
+            if (WITH_W) st.W = __builtin_fmaf(ex, t, st.W);
+        }
+}
+
+// Fold one group into a KL state (a: policy, b: reference).
+template <int U, bool REVERSE>
+__device__ __forceinline__ void update_kl(StatKL& st, const float (&a)[U][kChunk],
+                                          const float (&b)[U][kChunk], float sca, float scb) {
+    float gma = a[0][0], gmb = b[0][0];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int e = 0; e < kChunk; ++e) {
+            gma = fmaxf(gma, a[u][e]);
+            gmb = fmaxf(gmb, b[u][e]);
+        }
+    if (gma > st.ma) {
+        const float mLn = gma * sca;
+        if (st.ma != neg_inf()) {
+            const float d = st.mLa - mLn;
+            const float s = ex2(d);
+            if (REVERSE)
+                st.W = s * __builtin_fmaf(d, st.Sa, st.W);
+            else
+                st.W = __builtin_fmaf(-d, st.Sb, st.W);
+            st.Sa *= s;
+        }
+        st.ma = gma;
+        st.mLa = mLn;
+    }
+    if (gmb > st.mb) {
+        const float mLn = gmb * scb;
+        if (st.mb != neg_inf()) {
+            const float d = st.mLb - mLn;
+            const float s = ex2(d);
+            if (REVERSE)
+                st.W = __builtin_fmaf(-d, st.Sa, st.W);
+            else
+                st.W = s * __builtin_fmaf(d, st.Sb, st.W);
+            st.Sb *= s;
+        }
+        st.mb = gmb;
+        st.mLb = mLn;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int e = 0; e < kChunk; ++e) {
+            const float ta = __builtin_fmaf(a[u][e], sca, -st.mLa);
+            const float tb = __builtin_fmaf(b[u][e], scb, -st.mLb);
+            const float ea = ex2(ta), eb = ex2(tb);
+            st.Sa += ea;
+            st.Sb += eb;
+            const float d = ta - tb;
+            if (REVERSE) {
+                st.flag = fmaxf(st.flag, d);
+                st.W = __builtin_fmaf(ea, fmaxf(d, kClampT), st.W);
+            } else {
+                st.flag = fminf(st.flag, d);
+                st.W = __builtin_fmaf(eb, fmaxf(-d, kClampT), st.W);
+            }
+        }
+}
+
+// Logprobs / entropy forward: one workgroup per row.
+template <int BLOCK, int U, typename T, int HEAD, bool CAP, bool ALIGNED>
+__global__ __launch_bounds__(BLOCK) void fwd1_kernel(FwdParams p) {
+    using S = typename T::storage;
+    constexpr bool WITH_W = HEAD == kHeadEntropy;
+    constexpr int NW = BLOCK / 64;
+    __shared__ Stat1 red[NW];
+    __shared__ float bc[2];
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int64_t nchunks = (p.V + kChunk - 1) / kChunk, nfull = p.V / kChunk;
+    RowStats* stats = static_cast<RowStats*>(p.stats);
+    for (int64_t row = blockIdx.x; row < p.N; row += gridDim.x) {
+        const S* __restrict__ x = static_cast<const S*>(p.x) + row * p.ldx;
+        Stat1 st = stat1_init();
+        for (int64_t g0 = 0; g0 < nchunks; g0 += (int64_t)U * BLOCK) {
+            float a[U][kChunk];
+            const bool full = g0 + (int64_t)U * BLOCK <= nfull;
+            load_group<BLOCK, U, S, CAP, ALIGNED>(x, p.V, g0, full, p.kx, a);
+            update1<U, WITH_W>(st, a, p.scx);
+        }
+        st = wave_reduce<WITH_W>(st);
+        if (lane == 0) red[wid] = st;
+        __syncthreads();
+        if (tid == 0) {
+            Stat1 r = red[0];
+#pragma unroll
+            for (int w = 1; w < NW; ++w) r = stat1_merge<WITH_W>(r, red[w]);
+            const bool empty = r.m == neg_inf();
+            const float log2S = log2f(r.S);  // -inf for an empty row
+            RowStats rs;
+            rs.mLa = r.mL;
+            rs.log2Sa = log2S;
+            rs.mLb = 0.0f;
+            rs.log2Sb = 0.0f;
+            rs.flags = empty ? kFlagEmptyA : 0u;
+            rs.value = 0.0f;
+            rs.pad0 = rs.pad1 = 0.0f;
+            if (HEAD == kHeadEntropy) {
+                const float H = empty ? qnan() : kLn2 * (log2S - r.W / r.S);
+                rs.value = H;
+                p.out[row] = H;
+            }
+            stats[row] = rs;
+            bc[0] = r.mL;
+            bc[1] = log2S;
+        }
+        __syncthreads();
+        if (HEAD == kHeadLogp) {
+            const float mL = bc[0], log2S = bc[1];
+            for (int64_t j = tid; j < p.k; j += BLOCK) {
+                const int64_t t = p.targets[row * p.k + j];
+                float o = 0.0f;
+                if (t >= 0 && t < p.V) {
+                    float a = load_one(x + t);
+                    if (CAP) a = cap_fast(a, p.kx).a;
+                    o = (__builtin_fmaf(a, p.scx, -mL) - log2S) * kLn2;
+                }
+                p.out[row * p.k + j] = o;
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// KL forward (either direction): one workgroup per row pair.
+template <int BLOCK, int U, typename T, bool REVERSE, bool CAPA, bool CAPB, bool ALIGNED>
+__global__ __launch_bounds__(BLOCK) void fwdkl_kernel(FwdParams p) {
+    using S = typename T::storage;
+    constexpr int NW = BLOCK / 64;
+    __shared__ StatKL red[NW];
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int64_t nchunks = (p.V + kChunk - 1) / kChunk, nfull = p.V / kChunk;
+    RowStats* stats = static_cast<RowStats*>(p.stats);
+    for (int64_t row = blockIdx.x; row < p.N; row += gridDim.x) {
+        const S* __restrict__ xa = static_cast<const S*>(p.x) + row * p.ldx;
+        const S* __restrict__ xb = static_cast<const S*>(p.y) + row * p.ldy;
+        StatKL st = statkl_init<REVERSE>();
+        for (int64_t g0 = 0; g0 < nchunks; g0 += (int64_t)U * BLOCK) {
+            float a[U][kChunk], b[U][kChunk];
+            const bool full = g0 + (int64_t)U * BLOCK <= nfull;
+            load_group<BLOCK, U, S, CAPA, ALIGNED>(xa, p.V, g0, full, p.kx, a);
+            load_group<BLOCK, U, S, CAPB, ALIGNED>(xb, p.V, g0, full, p.ky, b);
+            update_kl<U, REVERSE>(st, a, b, p.scx, p.scy);
+        }
+        st = wave_reduce_kl<REVERSE>(st);
+        if (lane == 0) red[wid] = st;
+        __syncthreads();
+        if (tid == 0) {
+            StatKL r = red[0];
+#pragma unroll
+            for (int w = 1; w < NW; ++w) r = statkl_merge<REVERSE>(r, red[w]);
+            const bool empty_a = r.ma == neg_inf(), empty_b = r.mb == neg_inf();
+            const bool mismatch = REVERSE ? r.flag == pos_inf() : r.flag == neg_inf();
+            const float log2Sa = log2f(r.Sa), log2Sb = log2f(r.Sb);
+            const float D = REVERSE ? kLn2 * (r.W / r.Sa - log2Sa + log2Sb)
+                                    : kLn2 * (r.W / r.Sb - log2Sb + log2Sa);
+            const float out = (empty_a || empty_b) ? qnan() : (mismatch ? pos_inf() : D);
+            RowStats rs;
+            rs.mLa = r.mLa;
+            rs.log2Sa = log2Sa;
+            rs.mLb = r.mLb;
+            rs.log2Sb = log2Sb;
+            rs.value = out;
+            rs.flags = (empty_a ? kFlagEmptyA : 0u) | (empty_b ? kFlagEmptyB : 0u) |
+                       (mismatch ? kFlagMismatch : 0u);
+            rs.pad0 = rs.pad1 = 0.0f;
+            stats[row] = rs;
+            p.out[row] = out;
+        }
+        __syncthreads();
+    }
+}
+
+// ------------------------------------------------------------- dispatch
+
+template <typename T, bool CAPX, bool CAPY, bool AL>
+static hipError_t fwd_dispatch_head(int head, const FwdParams& p, hipStream_t s) {
+    const dim3 grid(row_grid(p.N)), block(kBlock);
+    switch (head) {
+        case kHeadLogp:
+            hipLaunchKernelGGL((fwd1_kernel<kBlock, kUnroll1, T, kHeadLogp, CAPX, AL>), grid,
+                               block, 0, s, p);
+            break;
+        case kHeadEntropy:
+            hipLaunchKernelGGL((fwd1_kernel<kBlock, kUnroll1, T, kHeadEntropy, CAPX, AL>), grid,
+                               block, 0, s, p);
+            break;
+        case kHeadKLReverse:
+            hipLaunchKernelGGL((fwdkl_kernel<kBlock, kUnrollKL, T, true, CAPX, CAPY, AL>), grid,
+                               block, 0, s, p);
+            break;
+        case kHeadKLForward:
+            hipLaunchKernelGGL((fwdkl_kernel<kBlock, kUnrollKL, T, false, CAPX, CAPY, AL>), grid,
+                               block, 0, s, p);
+            break;
+        default:
+            return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <typename T, bool CAPX, bool CAPY>
+static hipError_t fwd_dispatch_al(int head, bool al, const FwdParams& p, hipStream_t s) {
+    return al ? fwd_dispatch_head<T, CAPX, CAPY, true>(head, p, s)
+              : fwd_dispatch_head<T, CAPX, CAPY, false>(head, p, s);
+}
+
+template <typename T>
+static hipError_t fwd_dispatch_cap(int head, bool cx, bool cy, bool al, const FwdParams& p,
+                                   hipStream_t s) {
+    const bool kl = head == kHeadKLReverse || head == kHeadKLForward;
+    if (!kl) cy = false;  // the second cap only exists for KL
+    if (cx && cy) return fwd_dispatch_al<T, true, true>(head, al, p, s);
+    if (cx) return fwd_dispatch_al<T, true, false>(head, al, p, s);
+    if (cy) return fwd_dispatch_al<T, false, true>(head, al, p, s);
+    return fwd_dispatch_al<T, false, false>(head, al, p, s);
+}
+
+hipError_t launch_fwd(int head, int dtype, bool cap_x, bool cap_y, bool aligned,
+                      const FwdParams& p, hipStream_t stream) {
+    if (dtype == 0) return fwd_dispatch_cap<F32>(head, cap_x, cap_y, aligned, p, stream);
+    return fwd_dispatch_cap<BF16>(head, cap_x, cap_y, aligned, p, stream);
+}
+
+}  // namespace rlk

@@ -1,0 +1,366 @@
+"""Python binding of the C ABI in ``include/rlk.h`` (argument marshalling only).
+
+The functions below carry the C names (``rlk_logp_fwd`` ...).  They check torch
+dtypes and shapes, pass raw device pointers, row strides and the current HIP
+stream of the tensors' device, and raise ``RLKError`` on a non-OK status.
+Every step of the computation runs in ``librlk.so``; there is no fallback: if
+the library is missing, the import of the functions fails loudly.
+
+Convenience layers (allocate outputs with torch, then call the same entry
+points): ``logp_fwd`` / ``logp_bwd`` / ``entropy_fwd`` / ... and the autograd
+functions ``logprobs``, ``entropy``, ``kl_divergence`` and ``softcap``.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.environ.get("RLK_LIB", os.path.join(_PKG, "librlk.so"))
+
+RLK_F32, RLK_BF16 = 0, 1
+RLK_HEAD_LOGP, RLK_HEAD_ENTROPY, RLK_HEAD_KL = 0, 1, 2
+RLK_KL_REVERSE, RLK_KL_FORWARD = 0, 1
+RLK_MAX_TOPK = 4096
+STATUS = {0: "RLK_OK", 1: "RLK_ERR_ARG", 2: "RLK_ERR_DTYPE", 3: "RLK_ERR_SHAPE",
+          4: "RLK_ERR_DEVICE", 5: "RLK_ERR_LAUNCH"}
+
+EXPORTS = ("rlk_abi_version", "rlk_stats_bytes", "rlk_status_str", "rlk_last_error",
+           "rlk_softcap_fwd", "rlk_softcap_bwd", "rlk_logp_fwd", "rlk_logp_bwd",
+           "rlk_entropy_fwd", "rlk_entropy_bwd", "rlk_kl_fwd", "rlk_kl_bwd")
+
+
+class RLKError(RuntimeError):
+    def __init__(self, fn: str, status: int, detail: str):
+        self.status = status
+        super().__init__(f"{fn}: {STATUS.get(status, status)}: {detail}")
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load librlk.so (once) and declare the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with __graft_entry__.build() "
+                          "(there is no fallback implementation)")
+    lib = ctypes.CDLL(path)
+    vp, i64, f32, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int
+    sig = {
+        "rlk_abi_version": ([], ci),
+        "rlk_stats_bytes": ([ci, i64, i64], ctypes.c_size_t),
+        "rlk_status_str": ([ci], ctypes.c_char_p),
+        "rlk_last_error": ([], ctypes.c_char_p),
+        "rlk_softcap_fwd": ([vp, ci, vp, ci, i64, f32, vp], ci),
+        "rlk_softcap_bwd": ([vp, ci, vp, vp, i64, f32, vp], ci),
+        "rlk_logp_fwd": ([vp, ci, i64, i64, i64, vp, i64, f32, vp, vp, vp], ci),
+        "rlk_logp_bwd": ([vp, ci, i64, i64, i64, vp, i64, f32, vp, vp, vp, vp], ci),
+        "rlk_entropy_fwd": ([vp, ci, i64, i64, i64, f32, vp, vp, vp], ci),
+        "rlk_entropy_bwd": ([vp, ci, i64, i64, i64, f32, vp, vp, vp, vp], ci),
+        "rlk_kl_fwd": ([vp, vp, ci, i64, i64, i64, i64, ci, f32, f32, vp, vp, vp], ci),
+        "rlk_kl_bwd": ([vp, vp, ci, i64, i64, i64, i64, ci, f32, f32, vp, vp, vp, vp], ci),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = lib
+    return lib
+
+
+def _call(name: str, *args) -> None:
+    lib = load_library()
+    st = getattr(lib, name)(*args)
+    if st != 0:
+        raise RLKError(name, st, lib.rlk_last_error().decode())
+
+
+# ------------------------------------------------------------ marshalling
+
+def _dtype_code(t: torch.Tensor, what: str) -> int:
+    if t.dtype == torch.float32:
+        return RLK_F32
+    if t.dtype == torch.bfloat16:
+        return RLK_BF16
+    raise TypeError(f"{what} must be float32 or bfloat16, got {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t: torch.Tensor):
+    if t.device.type != "cuda":
+        raise ValueError(f"tensor must be on a GPU device, got {t.device}")
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _rows(x: torch.Tensor, what: str) -> torch.Tensor:
+    """2-D view whose vocabulary dimension is unit-stride (copy only if not)."""
+    if x.dim() != 2:
+        raise ValueError(f"{what} must be 2-D [N, V], got shape {tuple(x.shape)}")
+    if x.stride(1) != 1 or x.stride(0) < x.shape[1]:
+        x = x.contiguous()
+    return x
+
+
+def _ld(x: torch.Tensor) -> int:
+    return x.stride(0) if x.shape[0] > 1 else max(x.stride(0), x.shape[1])
+
+
+def _need(t: torch.Tensor, dtype, shape, what: str):
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous {dtype} {tuple(shape)}, "
+                         f"got {t.dtype} {tuple(t.shape)}")
+
+
+def rlk_abi_version() -> int:
+    return int(load_library().rlk_abi_version())
+
+
+def rlk_stats_bytes(head: int, N: int, V: int) -> int:
+    return int(load_library().rlk_stats_bytes(head, N, V))
+
+
+def rlk_status_str(status: int) -> str:
+    return load_library().rlk_status_str(status).decode()
+
+
+def rlk_last_error() -> str:
+    return load_library().rlk_last_error().decode()
+
+
+def rlk_softcap_fwd(x: torch.Tensor, y: torch.Tensor, cap: float) -> None:
+    if not x.is_contiguous() or not y.is_contiguous() or x.numel() != y.numel():
+        raise ValueError("x and y must be contiguous with the same number of elements")
+    _call("rlk_softcap_fwd", _ptr(x), _dtype_code(x, "x"), _ptr(y), _dtype_code(y, "y"),
+          x.numel(), float(cap), _stream(x))
+
+
+def rlk_softcap_bwd(x: torch.Tensor, grad_y: torch.Tensor, grad_x: torch.Tensor,
+                    cap: float) -> None:
+    _need(grad_y, torch.float32, x.shape, "grad_y")
+    _need(grad_x, x.dtype, x.shape, "grad_x")
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous")
+    _call("rlk_softcap_bwd", _ptr(x), _dtype_code(x, "x"), _ptr(grad_y), _ptr(grad_x),
+          x.numel(), float(cap), _stream(x))
+
+
+def rlk_logp_fwd(logits, targets, softcap, logp, stats) -> None:
+    N, V = logits.shape
+    k = targets.shape[1]
+    _need(targets, torch.int64, (N, k), "targets")
+    _need(logp, torch.float32, (N, k), "logp")
+    _call("rlk_logp_fwd", _ptr(logits), _dtype_code(logits, "logits"), N, V, _ld(logits),
+          _ptr(targets), k, float(softcap), _ptr(logp), _ptr(stats), _stream(logits))
+
+
+def rlk_logp_bwd(logits, targets, softcap, stats, grad_logp, grad_logits) -> None:
+    N, V = logits.shape
+    k = targets.shape[1]
+    _need(targets, torch.int64, (N, k), "targets")
+    _need(grad_logp, torch.float32, (N, k), "grad_logp")
+    _need(grad_logits, logits.dtype, (N, V), "grad_logits")
+    _call("rlk_logp_bwd", _ptr(logits), _dtype_code(logits, "logits"), N, V, _ld(logits),
+          _ptr(targets), k, float(softcap), _ptr(stats), _ptr(grad_logp), _ptr(grad_logits),
+          _stream(logits))
+
+
+def rlk_entropy_fwd(logits, softcap, entropy, stats) -> None:
+    N, V = logits.shape
+    _need(entropy, torch.float32, (N,), "entropy")
+    _call("rlk_entropy_fwd", _ptr(logits), _dtype_code(logits, "logits"), N, V, _ld(logits),
+          float(softcap), _ptr(entropy), _ptr(stats), _stream(logits))
+
+
+def rlk_entropy_bwd(logits, softcap, stats, grad_entropy, grad_logits) -> None:
+    N, V = logits.shape
+    _need(grad_entropy, torch.float32, (N,), "grad_entropy")
+    _need(grad_logits, logits.dtype, (N, V), "grad_logits")
+    _call("rlk_entropy_bwd", _ptr(logits), _dtype_code(logits, "logits"), N, V, _ld(logits),
+          float(softcap), _ptr(stats), _ptr(grad_entropy), _ptr(grad_logits), _stream(logits))
+
+
+def rlk_kl_fwd(policy, ref, direction, softcap_policy, softcap_ref, kl, stats) -> None:
+    N, V = policy.shape
+    if tuple(ref.shape) != (N, V) or ref.dtype != policy.dtype:
+        raise ValueError("policy and ref must have the same shape and dtype")
+    _need(kl, torch.float32, (N,), "kl")
+    _call("rlk_kl_fwd", _ptr(policy), _ptr(ref), _dtype_code(policy, "policy"), N, V,
+          _ld(policy), _ld(ref), int(direction), float(softcap_policy), float(softcap_ref),
+          _ptr(kl), _ptr(stats), _stream(policy))
+
+
+def rlk_kl_bwd(policy, ref, direction, softcap_policy, softcap_ref, stats, grad_kl,
+               grad_policy) -> None:
+    N, V = policy.shape
+    _need(grad_kl, torch.float32, (N,), "grad_kl")
+    _need(grad_policy, policy.dtype, (N, V), "grad_policy")
+    _call("rlk_kl_bwd", _ptr(policy), _ptr(ref), _dtype_code(policy, "policy"), N, V,
+          _ld(policy), _ld(ref), int(direction), float(softcap_policy), float(softcap_ref),
+          _ptr(stats), _ptr(grad_kl), _ptr(grad_policy), _stream(policy))
+
+
+# ------------------------------------------------ allocating convenience layer
+
+def new_stats(head: int, N: int, V: int, device) -> torch.Tensor:
+    return torch.empty(max(1, rlk_stats_bytes(head, N, V)), dtype=torch.uint8, device=device)
+
+
+def _targets2d(targets: torch.Tensor, N: int) -> torch.Tensor:
+    t = targets.reshape(N, -1)
+    return t.contiguous() if t.dtype == torch.int64 else t.to(torch.int64).contiguous()
+
+
+def logp_fwd(logits, targets, softcap=0.0):
+    logits = _rows(logits, "logits")
+    N, V = logits.shape
+    t = _targets2d(targets, N)
+    out = torch.empty(t.shape, dtype=torch.float32, device=logits.device)
+    stats = new_stats(RLK_HEAD_LOGP, N, V, logits.device)
+    rlk_logp_fwd(logits, t, softcap, out, stats)
+    return out.reshape(targets.shape), stats
+
+
+def logp_bwd(logits, targets, grad_logp, stats, softcap=0.0):
+    logits = _rows(logits, "logits")
+    N, V = logits.shape
+    t = _targets2d(targets, N)
+    g = grad_logp.reshape(t.shape).to(torch.float32).contiguous()
+    gx = torch.empty((N, V), dtype=logits.dtype, device=logits.device)
+    rlk_logp_bwd(logits, t, softcap, stats, g, gx)
+    return gx
+
+
+def entropy_fwd(logits, softcap=0.0):
+    logits = _rows(logits, "logits")
+    N, V = logits.shape
+    out = torch.empty(N, dtype=torch.float32, device=logits.device)
+    stats = new_stats(RLK_HEAD_ENTROPY, N, V, logits.device)
+    rlk_entropy_fwd(logits, softcap, out, stats)
+    return out, stats
+
+
+def entropy_bwd(logits, grad_entropy, stats, softcap=0.0):
+    logits = _rows(logits, "logits")
+    N, V = logits.shape
+    gx = torch.empty((N, V), dtype=logits.dtype, device=logits.device)
+    rlk_entropy_bwd(logits, softcap, stats, grad_entropy.to(torch.float32).contiguous(), gx)
+    return gx
+
+
+def kl_fwd(policy, ref, direction=RLK_KL_REVERSE, softcap_policy=0.0, softcap_ref=0.0):
+    policy, ref = _rows(policy, "policy"), _rows(ref, "ref")
+    N, V = policy.shape
+    out = torch.empty(N, dtype=torch.float32, device=policy.device)
+    stats = new_stats(RLK_HEAD_KL, N, V, policy.device)
+    rlk_kl_fwd(policy, ref, direction, softcap_policy, softcap_ref, out, stats)
+    return out, stats
+
+
+def kl_bwd(policy, ref, grad_kl, stats, direction=RLK_KL_REVERSE, softcap_policy=0.0,
+           softcap_ref=0.0):
+    policy, ref = _rows(policy, "policy"), _rows(ref, "ref")
+    N, V = policy.shape
+    gx = torch.empty((N, V), dtype=policy.dtype, device=policy.device)
+    rlk_kl_bwd(policy, ref, direction, softcap_policy, softcap_ref, stats,
+               grad_kl.to(torch.float32).contiguous(), gx)
+    return gx
+
+
+def softcap_fwd(x, cap=30.0, out_dtype=torch.float32):
+    x = x.contiguous()
+    y = torch.empty(x.shape, dtype=out_dtype, device=x.device)
+    rlk_softcap_fwd(x, y, cap)
+    return y
+
+
+def softcap_bwd(x, grad_y, cap=30.0):
+    x = x.contiguous()
+    gx = torch.empty_like(x)
+    rlk_softcap_bwd(x, grad_y.to(torch.float32).contiguous(), gx, cap)
+    return gx
+
+
+# ------------------------------------------------------------------ autograd
+
+class _LogProbs(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, logits, targets, softcap):
+        out, stats = logp_fwd(logits, targets, softcap)
+        ctx.save_for_backward(logits, targets, stats)
+        ctx.softcap = softcap
+        return out
+
+    @staticmethod
+    def backward(ctx, g):
+        logits, targets, stats = ctx.saved_tensors
+        gx = logp_bwd(logits, targets, g, stats, ctx.softcap)
+        return gx.reshape(logits.shape), None, None
+
+
+class _Entropy(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, logits, softcap):
+        out, stats = entropy_fwd(logits, softcap)
+        ctx.save_for_backward(logits, stats)
+        ctx.softcap = softcap
+        return out
+
+    @staticmethod
+    def backward(ctx, g):
+        logits, stats = ctx.saved_tensors
+        return entropy_bwd(logits, g, stats, ctx.softcap), None
+
+
+class _KL(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, policy, ref, direction, cp, cr):
+        out, stats = kl_fwd(policy, ref, direction, cp, cr)
+        ctx.save_for_backward(policy, ref, stats)
+        ctx.args = (direction, cp, cr)
+        return out
+
+    @staticmethod
+    def backward(ctx, g):
+        policy, ref, stats = ctx.saved_tensors
+        direction, cp, cr = ctx.args
+        return kl_bwd(policy, ref, g, stats, direction, cp, cr), None, None, None, None
+
+
+class _Softcap(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, x, cap):
+        ctx.save_for_backward(x)
+        ctx.cap = cap
+        return softcap_fwd(x, cap)
+
+    @staticmethod
+    def backward(ctx, g):
+        (x,) = ctx.saved_tensors
+        return softcap_bwd(x, g, ctx.cap), None
+
+
+def logprobs(logits, targets, softcap=0.0):
+    """log softmax(softcap(logits))[targets] per row; ignored targets give 0."""
+    return _LogProbs.apply(logits, targets, softcap)
+
+
+def entropy(logits, softcap=0.0):
+    return _Entropy.apply(logits, softcap)
+
+
+def kl_divergence(policy, ref, direction=RLK_KL_REVERSE, softcap_policy=0.0, softcap_ref=0.0):
+    """KL per row; the gradient flows to ``policy`` only (``ref`` is detached)."""
+    return _KL.apply(policy, ref.detach(), direction, softcap_policy, softcap_ref)
+
+
+def softcap(x, cap=30.0):
+    return _Softcap.apply(x, cap)
