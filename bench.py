@@ -1,0 +1,255 @@
+#!/usr/bin/env python3
+"""Benchmark: fused logprobs forward + backward on one MI355X.
+
+A step is one forward + backward pass of the hot path over one batch: the
+single-read row statistics with the target gather (rlk_logp_fwd), then the
+fused zero-workspace backward (rlk_logp_bwd), on the logprobs k=1 workload
+bf16 logits [8192, 151936] (seeded synthetic inputs, already resident in HBM).
+
+Prints ONE JSON line with the throughput in algorithmic GB/s (every logit
+read once by the forward, read once and written once by the backward, plus the
+per-row side arrays), the dominant kernel's roofline figures measured with HIP
+events on the launch stream, and the fp64 CPU oracle timed on a bounded sample
+of the same workload on the host cores.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+HBM_PEAK_GBS = 8000.0
+METRIC = "fwd+bwd ms and HBM GB/s (% of 8 TB/s) for logp/entropy/KL at N x V"
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "vocab_log_softmax_amd", "csrc")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(CSRC)):
+        if f.endswith((".hip", ".h", ".cpp")):
+            with open(os.path.join(CSRC, f), "rb") as fh:
+                h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(workload: str, kernel: str):
+    """HBM bytes per launch from a committed rocprofv3 --pmc summary, or None.
+
+    The summary must name the same kernel sources (hash) as this tree; a
+    changed kernel makes its counters stale.
+    """
+    path = os.path.join(PROFILES, f"{kernel}_{workload}_pmc.txt")
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    m_hash = re.search(r"^source_hash:\s*(\S+)", txt, re.M)
+    m_rd = re.search(r"^hbm_read_bytes_per_launch:\s*([0-9.eE+]+)", txt, re.M)
+    m_wr = re.search(r"^hbm_write_bytes_per_launch:\s*([0-9.eE+]+)", txt, re.M)
+    if not (m_hash and m_rd and m_wr) or m_hash.group(1) != kernel_source_hash():
+        return None
+    return float(m_rd.group(1)) + float(m_wr.group(1))
+
+
+def side_bytes(w, N):
+    """Per-step bytes of the per-row side arrays (targets, grads, outputs, stats)."""
+    k = w.k
+    if w.head == "logp":
+        fwd = N * (8 * k + 4 * k + 32)
+        bwd = N * (8 * k + 4 * k + 32)
+    else:
+        fwd = N * (4 + 32)
+        bwd = N * (4 + 32)
+    return fwd, bwd
+
+
+def run_oracle_sample(w, d, max_rows: int, threads: int):
+    """Time the fp64 oracle's fwd+bwd on the first max_rows rows (host cores)."""
+    import oracle
+
+    orc = oracle.get()
+    orc.set_threads(threads)
+    n = min(max_rows, d["N"])
+    x = d["logits"][:n].double().cpu().numpy()
+    g = d["grad"][:n].double().cpu().numpy()
+    t0 = time.perf_counter()
+    if w.head == "logp":
+        t = d["targets"][:n].cpu().numpy()
+        orc.logp_fwd(x, t, w.cap)
+        orc.logp_bwd(x, t, g, w.cap)
+    elif w.head == "entropy":
+        orc.entropy_fwd(x, w.cap)
+        orc.entropy_bwd(x, g, w.cap)
+    else:
+        r = d["ref"][:n].double().cpu().numpy()
+        orc.kl_fwd(x, r, 0, 0.0, 0.0)
+        orc.kl_bwd(x, r, g, 0, 0.0, 0.0)
+    dt = time.perf_counter() - t0
+    return n, dt
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c2_logp_bf16")
+    ap.add_argument("--oracle-rows", type=int, default=4096,
+                    help="rows of the workload timed on the CPU oracle")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain device copy of a known size (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(rows shard across GPUs with no exchange; see the design notes). "
+              "Run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from vocab_log_softmax_amd import rlk, workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    rlk.load_library()
+    dev = torch.device("cuda:0")
+    if args.copy_probe:
+        # A plain copy of exactly 2 GiB each way: the HBM counters of this
+        # kernel (2 GiB read, 2 GiB written per launch) calibrate FETCH_SIZE
+        # and WRITE_SIZE for the traffic field.
+        src = torch.empty(2 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_each_way": src.numel(), "launches": 3}))
+        return 0
+    w = workloads.WORKLOADS[args.workload]
+    d = workloads.make_inputs(args.workload, dev)
+    x = d["logits"]
+    N, V = x.shape
+    es = x.element_size()
+    stream = torch.cuda.current_stream(dev)
+
+    if w.head == "logp":
+        tg, g = d["targets"], d["grad"]
+        out = torch.empty(tg.shape, dtype=torch.float32, device=dev)
+        st = rlk.new_stats(rlk.RLK_HEAD_LOGP, N, V, dev)
+        gx = torch.empty_like(x)
+        fwd = lambda: rlk.rlk_logp_fwd(x, tg, w.cap, out, st)          # noqa: E731
+        bwd = lambda: rlk.rlk_logp_bwd(x, tg, w.cap, st, g, gx)        # noqa: E731
+        n_in, fwd_name, bwd_name = 1, "fwd1_kernel", "bwd_kernel"
+    elif w.head == "entropy":
+        g = d["grad"]
+        out = torch.empty(N, dtype=torch.float32, device=dev)
+        st = rlk.new_stats(rlk.RLK_HEAD_ENTROPY, N, V, dev)
+        gx = torch.empty_like(x)
+        fwd = lambda: rlk.rlk_entropy_fwd(x, w.cap, out, st)           # noqa: E731
+        bwd = lambda: rlk.rlk_entropy_bwd(x, w.cap, st, g, gx)         # noqa: E731
+        n_in, fwd_name, bwd_name = 1, "fwd1_kernel", "bwd_kernel"
+    else:
+        ref, g = d["ref"], d["grad"]
+        out = torch.empty(N, dtype=torch.float32, device=dev)
+        st = rlk.new_stats(rlk.RLK_HEAD_KL, N, V, dev)
+        gx = torch.empty_like(x)
+        fwd = lambda: rlk.rlk_kl_fwd(x, ref, 0, 0.0, 0.0, out, st)     # noqa: E731
+        bwd = lambda: rlk.rlk_kl_bwd(x, ref, 0, 0.0, 0.0, st, g, gx)   # noqa: E731
+        n_in, fwd_name, bwd_name = 2, "fwdkl_kernel", "bwd_kernel"
+
+    sf, sb = side_bytes(w, N)
+    fwd_bytes = n_in * N * V * es + sf            # read every input logit once
+    bwd_bytes = (n_in + 1) * N * V * es + sb      # read again, write the gradient once
+    step_bytes = fwd_bytes + bwd_bytes
+
+    for _ in range(args.warmup):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e in ev:
+        e[0].record(stream)
+        fwd()
+        e[1].record(stream)
+        bwd()
+        e[2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / len(ev)
+    bwd_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / len(ev)
+    ms_per_step = wall * 1e3 / args.steps
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+
+    bwd_gbs = bwd_bytes / (bwd_ms * 1e-3) / 1e9
+    fwd_gbs = fwd_bytes / (fwd_ms * 1e-3) / 1e9
+    traffic = traffic_from_profiles(args.workload, bwd_name)
+    roofline = {
+        "bound": "hbm",
+        "kernel": f"{bwd_name} ({w.head} backward)",
+        "achieved": round(bwd_gbs, 1),
+        "peak": HBM_PEAK_GBS,
+        "unit": "GB/s",
+        "frac": round(bwd_gbs / HBM_PEAK_GBS, 4),
+        "traffic": traffic,
+        "algorithmic_bytes_per_launch": bwd_bytes,
+        "avg_launch_ms": round(bwd_ms, 4),
+        "second_kernel": {"kernel": f"{fwd_name} ({w.head} forward)", "avg_launch_ms":
+                          round(fwd_ms, 4), "achieved": round(fwd_gbs, 1),
+                          "frac": round(fwd_gbs / HBM_PEAK_GBS, 4),
+                          "algorithmic_bytes_per_launch": fwd_bytes},
+    }
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        threads = min(len(os.sched_getaffinity(0)), 16)
+        n, dt = run_oracle_sample(w, d, args.oracle_rows, threads)
+        sample_bytes = step_bytes * n / N
+        cpu = {"value": round(sample_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
+               "kind": "oracle",
+               "sample": f"fp64 oracle fwd+bwd on the first {n} of {N} rows of the same "
+                         f"workload ({n * V} logits), {dt:.2f} s wall"}
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{args.workload}: {w.head} fwd+bwd, "
+                        f"{'bf16' if es == 2 else 'fp32'} logits [{N}, {V}]"
+                        + (f", k={w.k}" if w.head == "logp" else "")
+                        + (f", softcap {w.cap:g}" if w.cap else ""),
+            "N": N, "V": V, "logits_dtype": "bf16" if es == 2 else "fp32",
+            "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+            "algorithmic_bytes_per_step": step_bytes,
+        },
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -24,4 +24,6 @@ def dev():
 @pytest.fixture(scope="session")
 def orc():
     import oracle
-    return oracle.get()
+    o = oracle.get()
+    o.set_threads(min(16, len(os.sched_getaffinity(0))))
+    return o

@@ -1,0 +1,151 @@
+"""Determinism and invariance of the HIP path (bitwise, no tolerance).
+
+The claims ("L0 repeatable, L1 batch-invariant" in the vocabulary of RL-Kernel
+pull request 507):
+  * repeat: the same call twice gives identical bits;
+  * batch invariance: a row's outputs and gradient do not depend on which
+    other rows are in the batch, on their order, or on N;
+  * layout invariance: a padded row stride (ld > V, padding filled with NaN,
+    so any stray read shows up; the technique of the strided-view test in
+    DeepSpeed pull request 8838) and a misaligned base pointer give the same
+    bits as the contiguous aligned call;
+  * dtype: a bf16 tensor and the fp32 tensor holding the same values give
+    identical head outputs, and the bf16 gradient is the round-to-nearest-even
+    of the fp32 one (the side effect reported on the same pull request).
+"""
+
+import pytest
+import torch
+
+from vocab_log_softmax_amd import rlk
+
+pytestmark = pytest.mark.gpu
+
+
+def _gen(seed):
+    return torch.Generator().manual_seed(seed)
+
+
+def run_all(x, ref, t, g_t, g_r, cap):
+    """Outputs and gradients of every head for logits x (and ref for KL)."""
+    out = {}
+    lp, st = rlk.logp_fwd(x, t, cap)
+    out["logp"] = lp
+    out["logp_grad"] = rlk.logp_bwd(x, t, g_t, st, cap)
+    h, st = rlk.entropy_fwd(x, cap)
+    out["ent"] = h
+    out["ent_grad"] = rlk.entropy_bwd(x, g_r, st, cap)
+    for d in (0, 1):
+        k, st = rlk.kl_fwd(x, ref, d, cap, 0.0)
+        out[f"kl{d}"] = k
+        out[f"kl{d}_grad"] = rlk.kl_bwd(x, ref, g_r, st, d, cap, 0.0)
+    torch.cuda.synchronize()
+    return out
+
+
+def make(N, V, dtype, seed, dev, k=3):
+    x = (torch.randn(N, V, generator=_gen(seed)) * 4).to(dtype)
+    ref = (x.float() + torch.randn(N, V, generator=_gen(seed + 1)) * 0.5).to(dtype)
+    x[1, : V // 3] = float("-inf")
+    ref[1, : V // 3] = float("-inf")
+    t = torch.randint(0, V, (N, k), generator=_gen(seed + 2))
+    t[0, 1] = -100
+    g_t = torch.randn(N, k, generator=_gen(seed + 3))
+    g_r = torch.randn(N, generator=_gen(seed + 4))
+    return [a.to(dev) for a in (x, ref, t, g_t, g_r)]
+
+
+def assert_bitwise(a, b, what):
+    assert a.shape == b.shape and a.dtype == b.dtype, what
+    ai = a.contiguous().view(torch.int16 if a.element_size() == 2 else torch.int32)
+    bi = b.contiguous().view(torch.int16 if b.element_size() == 2 else torch.int32)
+    ne = (ai != bi)
+    assert not bool(ne.any()), f"{what}: {int(ne.sum())} elements differ bitwise"
+
+
+@pytest.mark.parametrize("V", [1031, 32000, 151936])
+@pytest.mark.parametrize("cap", [0.0, 30.0])
+def test_repeat_is_bitwise(dev, V, cap):
+    args = make(16, V, torch.bfloat16, V, dev)
+    a = run_all(*args, cap)
+    b = run_all(*args, cap)
+    for k in a:
+        assert_bitwise(a[k], b[k], f"repeat {k}")
+
+
+@pytest.mark.parametrize("V", [4097, 151936])
+def test_batch_invariance(dev, V):
+    N = 40
+    x, ref, t, g_t, g_r = make(N, V, torch.bfloat16, 7, dev)
+    full = run_all(x, ref, t, g_t, g_r, 20.0)
+    perm = torch.randperm(N, generator=_gen(1)).to(dev)
+    shuf = run_all(x[perm].contiguous(), ref[perm].contiguous(), t[perm].contiguous(),
+                   g_t[perm].contiguous(), g_r[perm].contiguous(), 20.0)
+    sub = torch.tensor([3, 17, 1, 39], device=dev)
+    part = run_all(x[sub].contiguous(), ref[sub].contiguous(), t[sub].contiguous(),
+                   g_t[sub].contiguous(), g_r[sub].contiguous(), 20.0)
+    single = run_all(x[5:6].contiguous(), ref[5:6].contiguous(), t[5:6].contiguous(),
+                     g_t[5:6].contiguous(), g_r[5:6].contiguous(), 20.0)
+    for k in full:
+        assert_bitwise(full[k][perm], shuf[k], f"permuted {k}")
+        assert_bitwise(full[k][sub], part[k], f"subset {k}")
+        assert_bitwise(full[k][5:6], single[k], f"single row {k}")
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("V,pad", [(4096, 8), (4099, 5), (151936, 64)])
+def test_padded_stride_reads_nothing_outside_the_row(dev, dtype, V, pad):
+    N = 12
+    x, ref, t, g_t, g_r = make(N, V, dtype, V + pad, dev)
+    want = run_all(x, ref, t, g_t, g_r, 0.0)
+    xp = torch.full((N, V + pad), float("nan"), dtype=dtype, device=dev)
+    rp = torch.full((N, V + pad), float("nan"), dtype=dtype, device=dev)
+    xp[:, :V] = x
+    rp[:, :V] = ref
+    got = run_all(xp[:, :V], rp[:, :V], t, g_t, g_r, 0.0)
+    for k in want:
+        assert_bitwise(want[k], got[k], f"padded {k}")
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+def test_misaligned_base_pointer(dev, dtype):
+    N, V = 9, 8192
+    x, ref, t, g_t, g_r = make(N, V, dtype, 99, dev)
+    want = run_all(x, ref, t, g_t, g_r, 30.0)
+    bx = torch.empty(N * V + 1, dtype=dtype, device=dev)
+    br = torch.empty(N * V + 1, dtype=dtype, device=dev)
+    xs = bx[1:].view(N, V)
+    rs = br[1:].view(N, V)
+    xs.copy_(x)
+    rs.copy_(ref)
+    assert xs.data_ptr() % 16 != 0
+    got = run_all(xs, rs, t, g_t, g_r, 30.0)
+    for k in want:
+        assert_bitwise(want[k], got[k], f"misaligned {k}")
+
+
+@pytest.mark.parametrize("cap", [0.0, 20.0])
+def test_bf16_equals_fp32_of_same_values(dev, cap):
+    N, V = 10, 75968
+    x, ref, t, g_t, g_r = make(N, V, torch.bfloat16, 5, dev)
+    b = run_all(x, ref, t, g_t, g_r, cap)
+    f = run_all(x.float(), ref.float(), t, g_t, g_r, cap)
+    for k in b:
+        if k.endswith("grad"):
+            assert_bitwise(b[k], f[k].to(torch.bfloat16), f"bf16 grad == RNE(fp32 grad) {k}")
+        else:
+            assert_bitwise(b[k], f[k], f"bf16 vs fp32 output {k}")
+
+
+def test_outputs_independent_of_stats_buffer_history(dev):
+    # the forward record is fully rewritten: garbage in the buffer changes nothing
+    x, ref, t, g_t, g_r = make(6, 5000, torch.bfloat16, 3, dev)
+    lp, st = rlk.logp_fwd(x, t)
+    g1 = rlk.logp_bwd(x, t, g_t, st)
+    st2 = torch.full_like(st, 0xAB)
+    out2 = torch.empty_like(lp)
+    rlk.rlk_logp_fwd(x, t, 0.0, out2, st2)
+    g2 = rlk.logp_bwd(x, t, g_t, st2)
+    torch.cuda.synchronize()
+    assert_bitwise(lp, out2, "logp")
+    assert_bitwise(g1, g2, "grad")

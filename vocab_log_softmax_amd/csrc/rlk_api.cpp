@@ -60,8 +60,13 @@ rlk_status check_matrix(int64_t N, int64_t V, int64_t ld, int64_t es, const char
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Softcap constants of the row kernels: k = -2 log2(e) / c gives
+// r = 1 / (1 + 2^(k x)), and the statistic input is x log2(e) (cap off) or
+// r with scale 2 c log2(e) (cap on; see rlk_device.h).
 float cap_k(float c) { return c != 0.0f ? -2.0f * 1.44269504088896340736f / c : 0.0f; }
-float cap_sc(float c) { return c != 0.0f ? c * 1.44269504088896340736f : 1.44269504088896340736f; }
+float cap_sc(float c) {
+    return c != 0.0f ? 2.0f * c * 1.44269504088896340736f : 1.44269504088896340736f;
+}
 
 // Device that owns `ptr` (device or managed memory only).
 rlk_status pointer_device(const void* ptr, const char* name, int* dev) {

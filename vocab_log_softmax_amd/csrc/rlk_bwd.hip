@@ -5,7 +5,7 @@
 // written straight in the logits dtype with no [N, V] fp32 temporary; rows
 // whose targets are all outside [0, V) get an exactly zero gradient (Behavior
 // changes).  Here the softmax is not recomputed from two more passes: the
-// forward saved (m log2 e, log2 S) per row, so each logit is read once and
+// forward saved (max log2 e, log2 S) per row, so each logit is read once and
 // each gradient written once, and p comes from the very same FMA as in the
 // forward (bitwise-consistent with the forward output).
 //
@@ -22,88 +22,58 @@
 
 namespace rlk {
 
-// Load the U chunks of one group (raw values, -inf beyond V).
-template <int BLOCK, int U, typename S, bool ALIGNED>
-__device__ __forceinline__ void load_raw(const S* __restrict__ row, int64_t V, int64_t g0,
-                                         bool full, float (&x)[U][kChunk]) {
-    const int tid = threadIdx.x;
-    if (ALIGNED && full) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) load_chunk(row + (g0 + u * BLOCK + tid) * kChunk, x[u]);
-    } else {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t c0 = (g0 + u * BLOCK + tid) * kChunk;
-#pragma unroll
-            for (int e = 0; e < kChunk; ++e) {
-                const int64_t col = c0 + e;
-                x[u][e] = col < V ? load_one(row + col) : neg_inf();
-            }
-        }
-    }
-}
-
-// Store the U chunks of one group (elements beyond V are not written).
-template <int BLOCK, int U, typename S, bool ALIGNED>
-__device__ __forceinline__ void store_group(S* __restrict__ row, int64_t V, int64_t g0, bool full,
-                                            const float (&v)[U][kChunk]) {
-    const int tid = threadIdx.x;
-    if (ALIGNED && full) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) store_chunk(row + (g0 + u * BLOCK + tid) * kChunk, v[u]);
-    } else {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t c0 = (g0 + u * BLOCK + tid) * kChunk;
-#pragma unroll
-            for (int e = 0; e < kChunk; ++e)
-                if (c0 + e < V) store_one(row + c0 + e, v[u][e]);
-        }
-    }
-}
+// Lanes that sum the upstream gradient of the k slots (fixed tree).
+constexpr int kGLanes = 256;
 
 // Row modes.
 enum : int { kModeNormal = 0, kModeZero = 1, kModeNaN = 2, kModeMismatch = 3 };
 
 template <int BLOCK, int U, typename T, int HEAD, bool CAPA, bool CAPB, bool ALIGNED>
-__global__ __launch_bounds__(BLOCK) void bwd_kernel(BwdParams p) {
+__global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void bwd_kernel(BwdParams p) {
     using S = typename T::storage;
     constexpr bool KL = HEAD == kHeadKLReverse || HEAD == kHeadKLForward;
-    constexpr int NW = BLOCK / 64;
+    constexpr int UB = KL ? U : 1;  // reference group (KL only)
+    static_assert(BLOCK >= kGLanes, "the G tree needs kGLanes threads");
     extern __shared__ int smem_topk[];  // logp: int32 target (-1: ignored) [k], fp32 g [k]
-    __shared__ float red_g[NW];
-    __shared__ float red_n[NW];
+    __shared__ float red_g[kGLanes / 64];
+    __shared__ float red_n[kGLanes / 64];
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int64_t step = (int64_t)U * BLOCK;
     const int64_t nchunks = (p.V + kChunk - 1) / kChunk, nfull = p.V / kChunk;
     const RowStats* stats = static_cast<const RowStats*>(p.stats);
     int* tg = smem_topk;
     float* gg = reinterpret_cast<float*>(smem_topk + p.k);
 
     for (int64_t row = blockIdx.x; row < p.N; row += gridDim.x) {
-        const RowStats rs = stats[row];
         const S* __restrict__ xa = static_cast<const S*>(p.x) + row * p.ldx;
         const S* __restrict__ xb = KL ? static_cast<const S*>(p.y) + row * p.ldy : nullptr;
         S* __restrict__ gx = static_cast<S*>(p.gx) + row * p.V;
 
+        const RowStats rs = stats[row];
+
         int mode = kModeNormal;
         float G = 0.0f;
         if (HEAD == kHeadLogp) {
-            // Stage the slots and sum G over valid ones with a fixed tree.
+            // Stage the slots and sum G over the valid ones.  The tree is fixed
+            // by kGLanes (slot j is summed by lane j mod kGLanes, in order),
+            // not by BLOCK, so G has the same bits for every launch shape.
             float part = 0.0f, cnt = 0.0f;
-            for (int64_t j = tid; j < p.k; j += BLOCK) {
-                const int64_t t = p.targets[row * p.k + j];
-                const bool valid = t >= 0 && t < p.V;
-                const float g = p.g[row * p.k + j];
-                tg[j] = valid ? static_cast<int>(t) : -1;
-                gg[j] = g;
-                if (valid) {
-                    part += g;
-                    cnt += 1.0f;
+            if (tid < kGLanes) {
+                for (int64_t j = tid; j < p.k; j += kGLanes) {
+                    const int64_t t = p.targets[row * p.k + j];
+                    const bool valid = t >= 0 && t < p.V;
+                    const float g = p.g[row * p.k + j];
+                    tg[j] = valid ? static_cast<int>(t) : -1;
+                    gg[j] = g;
+                    if (valid) {
+                        part += g;
+                        cnt += 1.0f;
+                    }
                 }
             }
             part = wave_sum(part);
             cnt = wave_sum(cnt);
-            if (lane == 0) {
+            if (lane == 0 && wid < kGLanes / 64) {
                 red_g[wid] = part;
                 red_n[wid] = cnt;
             }
@@ -111,7 +81,7 @@ __global__ __launch_bounds__(BLOCK) void bwd_kernel(BwdParams p) {
             float n = red_n[0];
             G = red_g[0];
 #pragma unroll
-            for (int w = 1; w < NW; ++w) {
+            for (int w = 1; w < kGLanes / 64; ++w) {
                 G += red_g[w];
                 n += red_n[w];
             }
@@ -128,78 +98,90 @@ __global__ __launch_bounds__(BLOCK) void bwd_kernel(BwdParams p) {
                 mode = kModeMismatch;
         }
 
-        // Per-row coefficients.
+        // Per-row coefficients (the slope 4 r (1 - r) has its 4 folded in).
         const float g_row = (HEAD == kHeadLogp) ? 0.0f : p.g[row];
         float A = 0.0f, B = 0.0f;
         if (HEAD == kHeadLogp) {
-            A = CAPA ? -4.0f * G : -G;  // cap: slope 4 r (1 - r)
+            A = CAPA ? -4.0f * G : -G;
         } else if (HEAD == kHeadEntropy) {
-            A = -g_row * kLn2;
-            B = -g_row * rs.value;
+            A = (CAPA ? -4.0f : -1.0f) * g_row * kLn2;
+            B = (CAPA ? -4.0f : -1.0f) * g_row * rs.value;
         } else if (HEAD == kHeadKLReverse) {
-            A = g_row * kLn2;
-            B = -g_row * rs.value;
+            A = (CAPA ? 4.0f : 1.0f) * g_row * kLn2;
+            B = (CAPA ? -4.0f : -1.0f) * g_row * rs.value;
         } else {
             A = CAPA ? 4.0f * g_row : g_row;
         }
 
-        for (int64_t g0 = 0; g0 < nchunks; g0 += (int64_t)U * BLOCK) {
-            const bool full = g0 + (int64_t)U * BLOCK <= nfull;
-            float v[U][kChunk];
-            if (mode == kModeNormal) {
-                float xa_[U][kChunk];
-                load_raw<BLOCK, U, S, ALIGNED>(xa, p.V, g0, full, xa_);
-                float xb_[KL ? U : 1][kChunk];
-                if (KL) load_raw<BLOCK, KL ? U : 1, S, ALIGNED>(xb, p.V, g0, full, xb_);
+        // Gradient of one group from its logit values.
+        auto grad_group = [&](const float (&a)[U][kChunk], const float (&b)[UB][kChunk],
+                              float (&v)[U][kChunk]) {
 #pragma unroll
-                for (int u = 0; u < U; ++u)
+            for (int u = 0; u < U; ++u)
 #pragma unroll
-                    for (int e = 0; e < kChunk; ++e) {
-                        float a = xa_[u][e], r = 0.0f;
-                        if (CAPA) {
-                            const CapVal c = cap_fast(a, p.kx);
-                            a = c.a;
-                            r = c.r;
-                        }
-                        const float ta = __builtin_fmaf(a, p.scx, -rs.mLa) - rs.log2Sa;
-                        float out;
-                        if (HEAD == kHeadLogp) {
-                            out = A * ex2(ta);
-                        } else if (HEAD == kHeadEntropy) {
-                            const float tc = fmaxf(ta, kClampT);
-                            out = ex2(tc) * __builtin_fmaf(A, tc, B);
+                for (int e = 0; e < kChunk; ++e) {
+                    const float ta = __builtin_fmaf(a[u][e], p.scx, -rs.mLa) - rs.log2Sa;
+                    float o;
+                    if (HEAD == kHeadLogp) {
+                        o = A * ex2(ta);
+                    } else if (HEAD == kHeadEntropy) {
+                        const float tc = CAPA ? ta : fmaxf(ta, kClampT);
+                        o = ex2(tc) * __builtin_fmaf(A, tc, B);
+                    } else {
+                        const float tb = __builtin_fmaf(b[KL ? u : 0][e], p.scy, -rs.mLb) - rs.log2Sb;
+                        if (HEAD == kHeadKLReverse) {
+                            const float l = CAPA ? ta - tb : fmaxf(ta - tb, kClampT);
+                            o = ex2(ta) * __builtin_fmaf(A, l, B);
                         } else {
-                            float b = xb_[KL ? u : 0][e];
-                            if (CAPB) b = cap_fast(b, p.ky).a;
-                            const float tb = __builtin_fmaf(b, p.scy, -rs.mLb) - rs.log2Sb;
-                            if (HEAD == kHeadKLReverse) {
-                                const float l = fmaxf(ta - tb, kClampT);
-                                out = ex2(ta) * __builtin_fmaf(A, l, B);
-                            } else {
-                                out = A * (ex2(ta) - ex2(tb));
-                            }
+                            o = A * (ex2(ta) - ex2(tb));
                         }
-                        if (CAPA) out *= (HEAD == kHeadLogp || HEAD == kHeadKLForward)
-                                             ? r * (1.0f - r)
-                                             : cap_fast_slope(r);
-                        v[u][e] = out;
                     }
-            } else if (mode == kModeMismatch) {
-                float xa_[U][kChunk];
-                load_raw<BLOCK, U, S, ALIGNED>(xa, p.V, g0, full, xa_);
-#pragma unroll
-                for (int u = 0; u < U; ++u)
-#pragma unroll
-                    for (int e = 0; e < kChunk; ++e)
-                        v[u][e] = (!CAPA && xa_[u][e] == neg_inf()) ? 0.0f : qnan();
+                    if (CAPA) o *= a[u][e] * (1.0f - a[u][e]);  // slope / 4 (4 is in A, B)
+                    v[u][e] = o;
+                }
+        };
+
+        if (mode == kModeNormal) {
+            if (KL) {
+                for_each_group2<BLOCK, U, S, CAPA, CAPB, ALIGNED, kBwdPipe>(
+                    xa, xb, p.V, p.kx, p.ky,
+                    [&](int64_t g0, bool full, const float (&a)[U][kChunk],
+                        const float (&b)[U][kChunk]) {
+                        float v[U][kChunk];
+                        grad_group(a, reinterpret_cast<const float(&)[UB][kChunk]>(b), v);
+                        store_group<BLOCK, U, S, ALIGNED>(gx, p.V, g0, full, v);
+                    });
             } else {
-                const float fill = mode == kModeZero ? 0.0f : qnan();
-#pragma unroll
-                for (int u = 0; u < U; ++u)
-#pragma unroll
-                    for (int e = 0; e < kChunk; ++e) v[u][e] = fill;
+                for_each_group<BLOCK, U, S, CAPA, ALIGNED, kBwdPipe>(
+                    xa, p.V, p.kx, [&](int64_t g0, bool full, const float (&a)[U][kChunk]) {
+                        float v[U][kChunk];
+                        const float b[UB][kChunk] = {};
+                        grad_group(a, b, v);
+                        store_group<BLOCK, U, S, ALIGNED>(gx, p.V, g0, full, v);
+                    });
             }
-            store_group<BLOCK, U, S, ALIGNED>(gx, p.V, g0, full, v);
+        } else if (mode == kModeMismatch) {
+            // Reverse KL with a support mismatch: NaN on the policy's support,
+            // 0 on its masked columns.
+            for_each_group<BLOCK, U, S, false, ALIGNED, kBwdPipe>(
+                xa, p.V, 0.0f, [&](int64_t g0, bool full, const float (&a)[U][kChunk]) {
+                    float v[U][kChunk];
+#pragma unroll
+                    for (int u = 0; u < U; ++u)
+#pragma unroll
+                        for (int e = 0; e < kChunk; ++e)
+                            v[u][e] = (!CAPA && a[u][e] == neg_inf()) ? 0.0f : qnan();
+                    store_group<BLOCK, U, S, ALIGNED>(gx, p.V, g0, full, v);
+                });
+        } else {
+            const float fill = mode == kModeZero ? 0.0f : qnan();
+            float v[U][kChunk];
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int e = 0; e < kChunk; ++e) v[u][e] = fill;
+            for (int64_t g0 = 0; g0 < nchunks; g0 += step)
+                store_group<BLOCK, U, S, ALIGNED>(gx, p.V, g0, g0 + step <= nfull, v);
         }
 
         if (HEAD == kHeadLogp && mode == kModeNormal) {
@@ -221,9 +203,8 @@ __global__ __launch_bounds__(BLOCK) void bwd_kernel(BwdParams p) {
                 if (!first) continue;
                 float a = load_one(xa + t), slope = 1.0f;
                 if (CAPA) {
-                    const CapVal c = cap_fast(a, p.kx);
-                    a = c.a;
-                    slope = cap_fast_slope(c.r);
+                    a = cap_r(a, p.kx);
+                    slope = cap_slope_r(a);
                 }
                 const float pt = ex2(__builtin_fmaf(a, p.scx, -rs.mLa) - rs.log2Sa);
                 store_one(gx + t, __builtin_fmaf(-pt, G, h) * slope);
@@ -234,28 +215,33 @@ __global__ __launch_bounds__(BLOCK) void bwd_kernel(BwdParams p) {
 }
 
 // ------------------------------------------------------------- dispatch
+//
+// The backward is elementwise given the row record (and G has a fixed tree),
+// so its launch shape does not change any result and is chosen per call:
+// 1024-thread workgroups for the plain streaming rows, 512 when a wide top-k
+// fix-up follows each row (fewer idle lanes per row, more rows per CU).
 
-template <typename T, bool CAPX, bool CAPY, bool AL>
+template <int BB, int U1, int UKL, typename T, bool CAPX, bool CAPY, bool AL>
 static hipError_t bwd_dispatch_head(int head, const BwdParams& p, hipStream_t s) {
-    const dim3 grid(row_grid(p.N)), block(kBlock);
+    const dim3 grid(row_grid(p.N)), block(BB);
     switch (head) {
         case kHeadLogp: {
             const size_t lds = static_cast<size_t>(p.k) * (sizeof(int) + sizeof(float));
-            hipLaunchKernelGGL((bwd_kernel<kBlock, kUnroll1, T, kHeadLogp, CAPX, false, AL>), grid,
-                               block, lds, s, p);
+            hipLaunchKernelGGL((bwd_kernel<BB, U1, T, kHeadLogp, CAPX, false, AL>), grid, block,
+                               lds, s, p);
             break;
         }
         case kHeadEntropy:
-            hipLaunchKernelGGL((bwd_kernel<kBlock, kUnroll1, T, kHeadEntropy, CAPX, false, AL>),
-                               grid, block, 0, s, p);
+            hipLaunchKernelGGL((bwd_kernel<BB, U1, T, kHeadEntropy, CAPX, false, AL>), grid, block,
+                               0, s, p);
             break;
         case kHeadKLReverse:
-            hipLaunchKernelGGL((bwd_kernel<kBlock, kUnrollKL, T, kHeadKLReverse, CAPX, CAPY, AL>),
-                               grid, block, 0, s, p);
+            hipLaunchKernelGGL((bwd_kernel<BB, UKL, T, kHeadKLReverse, CAPX, CAPY, AL>), grid,
+                               block, 0, s, p);
             break;
         case kHeadKLForward:
-            hipLaunchKernelGGL((bwd_kernel<kBlock, kUnrollKL, T, kHeadKLForward, CAPX, CAPY, AL>),
-                               grid, block, 0, s, p);
+            hipLaunchKernelGGL((bwd_kernel<BB, UKL, T, kHeadKLForward, CAPX, CAPY, AL>), grid,
+                               block, 0, s, p);
             break;
         default:
             return hipErrorInvalidValue;
@@ -265,8 +251,16 @@ static hipError_t bwd_dispatch_head(int head, const BwdParams& p, hipStream_t s)
 
 template <typename T, bool CAPX, bool CAPY>
 static hipError_t bwd_dispatch_al(int head, bool al, const BwdParams& p, hipStream_t s) {
-    return al ? bwd_dispatch_head<T, CAPX, CAPY, true>(head, p, s)
-              : bwd_dispatch_head<T, CAPX, CAPY, false>(head, p, s);
+    const bool wide_topk = head == kHeadLogp && p.k >= kBwdWideTopk;
+    if (wide_topk)
+        return al ? bwd_dispatch_head<kBwdBlockTopk, kBwdUnrollTopk, kBwdUnrollTopk, T, CAPX, CAPY,
+                                      true>(head, p, s)
+                  : bwd_dispatch_head<kBwdBlockTopk, kBwdUnrollTopk, kBwdUnrollTopk, T, CAPX, CAPY,
+                                      false>(head, p, s);
+    return al ? bwd_dispatch_head<kBwdBlock, kBwdUnroll1, kBwdUnrollKL, T, CAPX, CAPY, true>(head, p,
+                                                                                            s)
+              : bwd_dispatch_head<kBwdBlock, kBwdUnroll1, kBwdUnrollKL, T, CAPX, CAPY, false>(head,
+                                                                                             p, s);
 }
 
 template <typename T>

@@ -72,15 +72,39 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
+// Streaming hints for the bulk row traffic (every logit is touched once per
+// kernel, so caching it only evicts other data).  Compile-time switches.
+#ifndef RLK_NT_LOAD
+#define RLK_NT_LOAD 1
+#endif
+#ifndef RLK_NT_STORE
+#define RLK_NT_STORE 1
+#endif
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <typename V>
+__device__ __forceinline__ V ld16(const V* p) {
+    if (RLK_NT_LOAD) return __builtin_nontemporal_load(p);
+    return *p;
+}
+template <typename V>
+__device__ __forceinline__ void st16(V* p, V v) {
+    if (RLK_NT_STORE)
+        __builtin_nontemporal_store(v, p);
+    else
+        *p = v;
+}
+
 // Load one full chunk of 8 elements from a 16-byte aligned address.
 __device__ __forceinline__ void load_chunk(const float* p, float (&f)[kChunk]) {
-    const float4 a = *reinterpret_cast<const float4*>(p);
-    const float4 b = *(reinterpret_cast<const float4*>(p) + 1);
+    const f32x4 a = ld16(reinterpret_cast<const f32x4*>(p));
+    const f32x4 b = ld16(reinterpret_cast<const f32x4*>(p) + 1);
     f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
     f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
 }
 __device__ __forceinline__ void load_chunk(const uint16_t* p, float (&f)[kChunk]) {
-    const uint4 w = *reinterpret_cast<const uint4*>(p);
+    const u32x4 w = ld16(reinterpret_cast<const u32x4*>(p));
     f[0] = bf16_lo(w.x); f[1] = bf16_hi(w.x);
     f[2] = bf16_lo(w.y); f[3] = bf16_hi(w.y);
     f[4] = bf16_lo(w.z); f[5] = bf16_hi(w.z);
@@ -91,16 +115,15 @@ __device__ __forceinline__ float load_one(const uint16_t* p) { return bf16_to_f3
 
 // Store one full chunk of 8 values to a 16-byte aligned address.
 __device__ __forceinline__ void store_chunk(float* p, const float (&f)[kChunk]) {
-    *reinterpret_cast<float4*>(p) = make_float4(f[0], f[1], f[2], f[3]);
-    *(reinterpret_cast<float4*>(p) + 1) = make_float4(f[4], f[5], f[6], f[7]);
+    const f32x4 a = {f[0], f[1], f[2], f[3]};
+    const f32x4 b = {f[4], f[5], f[6], f[7]};
+    st16(reinterpret_cast<f32x4*>(p), a);
+    st16(reinterpret_cast<f32x4*>(p) + 1, b);
 }
 __device__ __forceinline__ void store_chunk(uint16_t* p, const float (&f)[kChunk]) {
-    uint4 w;
-    w.x = pack_bf16x2(f[0], f[1]);
-    w.y = pack_bf16x2(f[2], f[3]);
-    w.z = pack_bf16x2(f[4], f[5]);
-    w.w = pack_bf16x2(f[6], f[7]);
-    *reinterpret_cast<uint4*>(p) = w;
+    const u32x4 w = {pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
+                     pack_bf16x2(f[6], f[7])};
+    st16(reinterpret_cast<u32x4*>(p), w);
 }
 __device__ __forceinline__ void store_one(float* p, float f) { *p = f; }
 __device__ __forceinline__ void store_one(uint16_t* p, float f) { *p = f32_to_bf16(f); }
@@ -110,20 +133,15 @@ __device__ __forceinline__ void store_one(uint16_t* p, float f) { *p = f32_to_bf
 // "Final Logit Softcap", Summary: y = c tanh(x / c), dy/dx = 1 - tanh^2.
 //
 // Fused prologue form.  With r = 1 / (1 + 2^(k x)), k = -2 log2(e) / c:
-//   tanh(x / c) = 2 r - 1   and   1 - tanh^2(x / c) = 4 r (1 - r).
-// Both ends are exact (x = +inf: r = 1, tanh = 1; x = -inf: r = 0,
-// tanh = -1; slope 0).  The absolute error of tanh is a few 1e-8, which is
-// what the softmax sees (it depends on absolute errors of y).
-struct CapVal {
-    float a;  // tanh(x / c)
-    float r;  // 1 / (1 + 2^(k x))
-};
-__device__ __forceinline__ CapVal cap_fast(float x, float k) {
-    const float e = ex2(x * k);
-    const float r = rcp(1.0f + e);
-    return {__builtin_fmaf(2.0f, r, -1.0f), r};
-}
-__device__ __forceinline__ float cap_fast_slope(float r) { return 4.0f * r * (1.0f - r); }
+//   tanh(x / c) = 2 r - 1   and   1 - tanh^2(x / c) = 4 r (1 - r),
+// so y log2(e) = (2 c log2(e)) r - c log2(e).  The row kernels carry r
+// itself as the statistic's input with the scale sc = 2 c log2(e): the
+// constant -c log2(e) is common to every logit of the row and cancels
+// exactly in t = y log2(e) - max.  Both ends are exact (x = +inf: r = 1;
+// x = -inf: r = 0, i.e. y = -c; slope 0 at both).  The absolute error of r
+// is about 1e-7 and the softmax depends only on absolute errors of y.
+__device__ __forceinline__ float cap_r(float x, float k) { return rcp(1.0f + ex2(x * k)); }
+__device__ __forceinline__ float cap_slope_r(float r) { return 4.0f * r * (1.0f - r); }
 
 // Standalone form, accurate in RELATIVE terms (the output y itself is
 // compared at 1e-5 relative).  For |u| < 0.55 an odd polynomial
@@ -146,6 +164,238 @@ __device__ __forceinline__ float tanh_precise(float u, float* slope) {
     const bool small = au < 0.55f;
     *slope = small ? __builtin_fmaf(-ts, ts, 1.0f) : 4.0f * e * r * r;
     return small ? ts : tl;
+}
+
+// ------------------------------------------------------ row streaming
+//
+// A group is U chunks of 8 elements for lane tid: chunk (g0 + u BLOCK + tid).
+// Fast groups (every chunk inside the row, 16-byte aligned rows) are loaded
+// as raw 16-byte vectors and kept packed until they are consumed, so the
+// next group's loads can be in flight while the current one is computed.
+template <typename S, int U>
+struct RawGroup;
+template <int U>
+struct RawGroup<uint16_t, U> {
+    u32x4 v[U];
+};
+template <int U>
+struct RawGroup<float, U> {
+    f32x4 v[U][2];
+};
+
+template <int BLOCK, int U>
+__device__ __forceinline__ void raw_load(const uint16_t* __restrict__ row, int64_t g0,
+                                         RawGroup<uint16_t, U>& r) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+        r.v[u] = ld16(reinterpret_cast<const u32x4*>(
+            row + (g0 + u * BLOCK + (int)threadIdx.x) * kChunk));
+}
+template <int BLOCK, int U>
+__device__ __forceinline__ void raw_load(const float* __restrict__ row, int64_t g0,
+                                         RawGroup<float, U>& r) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const f32x4* p =
+            reinterpret_cast<const f32x4*>(row + (g0 + u * BLOCK + (int)threadIdx.x) * kChunk);
+        r.v[u][0] = ld16(p);
+        r.v[u][1] = ld16(p + 1);
+    }
+}
+template <int U>
+__device__ __forceinline__ void raw_unpack(const RawGroup<uint16_t, U>& r, float (&a)[U][kChunk]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        a[u][0] = bf16_lo(r.v[u].x); a[u][1] = bf16_hi(r.v[u].x);
+        a[u][2] = bf16_lo(r.v[u].y); a[u][3] = bf16_hi(r.v[u].y);
+        a[u][4] = bf16_lo(r.v[u].z); a[u][5] = bf16_hi(r.v[u].z);
+        a[u][6] = bf16_lo(r.v[u].w); a[u][7] = bf16_hi(r.v[u].w);
+    }
+}
+template <int U>
+__device__ __forceinline__ void raw_unpack(const RawGroup<float, U>& r, float (&a)[U][kChunk]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        a[u][0] = r.v[u][0].x; a[u][1] = r.v[u][0].y; a[u][2] = r.v[u][0].z; a[u][3] = r.v[u][0].w;
+        a[u][4] = r.v[u][1].x; a[u][5] = r.v[u][1].y; a[u][6] = r.v[u][1].z; a[u][7] = r.v[u][1].w;
+    }
+}
+// Values of one group that is not a full aligned group (the row's tail, or
+// every group of a row that is not 16-byte aligned).  Chunks that lie wholly
+// inside an aligned row still use one vector load; the remaining elements are
+// loaded from clamped (always valid) addresses without branches, so all loads
+// are in flight together, and slots beyond V become -inf (they contribute
+// exactly 0; consumers clamp t before any 0 * t in tail groups).  With CAP
+// the in-range values are mapped to r while padding stays -inf.
+template <int BLOCK, int U, typename S, bool CAP, bool ALIGNED>
+__device__ __forceinline__ void tail_values(const S* __restrict__ row, int64_t V, int64_t nfull,
+                                            int64_t g0, float k, float (&a)[U][kChunk]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t c = g0 + u * BLOCK + (int)threadIdx.x;
+        if (ALIGNED && c < nfull) {
+            load_chunk(row + c * kChunk, a[u]);
+            if (CAP) {
+#pragma unroll
+                for (int e = 0; e < kChunk; ++e) a[u][e] = cap_r(a[u][e], k);
+            }
+        } else if (c * kChunk >= V) {
+#pragma unroll
+            for (int e = 0; e < kChunk; ++e) a[u][e] = neg_inf();
+        } else {
+            float v[kChunk];
+#pragma unroll
+            for (int e = 0; e < kChunk; ++e) {
+                const int64_t col = c * kChunk + e;
+                v[e] = load_one(row + (col < V ? col : V - 1));
+            }
+#pragma unroll
+            for (int e = 0; e < kChunk; ++e) {
+                const int64_t col = c * kChunk + e;
+                const float w = CAP ? cap_r(v[e], k) : v[e];
+                a[u][e] = col < V ? w : neg_inf();
+            }
+        }
+    }
+}
+// Fast-group counterpart: unpack the raw vectors (and apply the cap).
+template <int U, typename S, bool CAP>
+__device__ __forceinline__ void fast_values(const RawGroup<S, U>& r, float k, float (&a)[U][kChunk]) {
+    raw_unpack(r, a);
+    if (CAP) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int e = 0; e < kChunk; ++e) a[u][e] = cap_r(a[u][e], k);
+    }
+}
+
+// Walk a row group by group, calling f(g0, full, a) with the values of each
+// group in order.  Full aligned groups are loaded as raw 16-byte vectors; with
+// PIPE two register buffers alternate so that the next group's loads are in
+// flight while the current group is consumed.  The order in which f sees the
+// groups, and the values, are the same for every path.
+template <int BLOCK, int U, typename S, bool CAP, bool ALIGNED, bool PIPE, typename F>
+__device__ __forceinline__ void for_each_group(const S* __restrict__ row, int64_t V, float k, F&& f) {
+    const int64_t step = (int64_t)U * BLOCK;
+    const int64_t nchunks = (V + kChunk - 1) / kChunk, nfull = V / kChunk;
+    const int64_t nfg = ALIGNED ? nfull / step : 0;  // full aligned groups
+    int64_t gi = 0;
+    if (PIPE && nfg > 0) {
+        RawGroup<S, U> A, B;
+        raw_load<BLOCK, U>(row, 0, A);
+        for (; gi + 1 < nfg; gi += 2) {
+            raw_load<BLOCK, U>(row, (gi + 1) * step, B);
+            {
+                float a[U][kChunk];
+                fast_values<U, S, CAP>(A, k, a);
+                f(gi * step, true, a);
+            }
+            if (gi + 2 < nfg) raw_load<BLOCK, U>(row, (gi + 2) * step, A);
+            {
+                float a[U][kChunk];
+                fast_values<U, S, CAP>(B, k, a);
+                f((gi + 1) * step, true, a);
+            }
+        }
+        if (gi < nfg) {
+            float a[U][kChunk];
+            fast_values<U, S, CAP>(A, k, a);
+            f(gi * step, true, a);
+            ++gi;
+        }
+    } else {
+        for (; gi < nfg; ++gi) {
+            RawGroup<S, U> A;
+            raw_load<BLOCK, U>(row, gi * step, A);
+            float a[U][kChunk];
+            fast_values<U, S, CAP>(A, k, a);
+            f(gi * step, true, a);
+        }
+    }
+    for (int64_t g0 = gi * step; g0 < nchunks; g0 += step) {
+        float a[U][kChunk];
+        tail_values<BLOCK, U, S, CAP, ALIGNED>(row, V, nfull, g0, k, a);
+        f(g0, false, a);
+    }
+}
+
+// Same walk over two rows in lockstep (KL: policy and reference).
+template <int BLOCK, int U, typename S, bool CAPA, bool CAPB, bool ALIGNED, bool PIPE, typename F>
+__device__ __forceinline__ void for_each_group2(const S* __restrict__ ra, const S* __restrict__ rb,
+                                                int64_t V, float ka, float kb, F&& f) {
+    const int64_t step = (int64_t)U * BLOCK;
+    const int64_t nchunks = (V + kChunk - 1) / kChunk, nfull = V / kChunk;
+    const int64_t nfg = ALIGNED ? nfull / step : 0;
+    int64_t gi = 0;
+    if (PIPE && nfg > 0) {
+        RawGroup<S, U> A0, B0, A1, B1;
+        raw_load<BLOCK, U>(ra, 0, A0);
+        raw_load<BLOCK, U>(rb, 0, B0);
+        for (; gi + 1 < nfg; gi += 2) {
+            raw_load<BLOCK, U>(ra, (gi + 1) * step, A1);
+            raw_load<BLOCK, U>(rb, (gi + 1) * step, B1);
+            {
+                float a[U][kChunk], b[U][kChunk];
+                fast_values<U, S, CAPA>(A0, ka, a);
+                fast_values<U, S, CAPB>(B0, kb, b);
+                f(gi * step, true, a, b);
+            }
+            if (gi + 2 < nfg) {
+                raw_load<BLOCK, U>(ra, (gi + 2) * step, A0);
+                raw_load<BLOCK, U>(rb, (gi + 2) * step, B0);
+            }
+            {
+                float a[U][kChunk], b[U][kChunk];
+                fast_values<U, S, CAPA>(A1, ka, a);
+                fast_values<U, S, CAPB>(B1, kb, b);
+                f((gi + 1) * step, true, a, b);
+            }
+        }
+        if (gi < nfg) {
+            float a[U][kChunk], b[U][kChunk];
+            fast_values<U, S, CAPA>(A0, ka, a);
+            fast_values<U, S, CAPB>(B0, kb, b);
+            f(gi * step, true, a, b);
+            ++gi;
+        }
+    } else {
+        for (; gi < nfg; ++gi) {
+            RawGroup<S, U> A, B;
+            raw_load<BLOCK, U>(ra, gi * step, A);
+            raw_load<BLOCK, U>(rb, gi * step, B);
+            float a[U][kChunk], b[U][kChunk];
+            fast_values<U, S, CAPA>(A, ka, a);
+            fast_values<U, S, CAPB>(B, kb, b);
+            f(gi * step, true, a, b);
+        }
+    }
+    for (int64_t g0 = gi * step; g0 < nchunks; g0 += step) {
+        float a[U][kChunk], b[U][kChunk];
+        tail_values<BLOCK, U, S, CAPA, ALIGNED>(ra, V, nfull, g0, ka, a);
+        tail_values<BLOCK, U, S, CAPB, ALIGNED>(rb, V, nfull, g0, kb, b);
+        f(g0, false, a, b);
+    }
+}
+
+// Store a group of results.  Full aligned groups use 16-byte stores; in
+// other groups, whole in-range chunks of an aligned row still do, and the
+// remaining elements are stored one by one (nothing beyond V is written).
+template <int BLOCK, int U, typename S, bool ALIGNED>
+__device__ __forceinline__ void store_group(S* __restrict__ row, int64_t V, int64_t g0, bool full,
+                                            const float (&v)[U][kChunk]) {
+    const int64_t nfull = V / kChunk;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t c = g0 + u * BLOCK + (int)threadIdx.x;
+        if (ALIGNED && (full || c < nfull)) {
+            store_chunk(row + c * kChunk, v[u]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < kChunk; ++e)
+                if (c * kChunk + e < V) store_one(row + c * kChunk + e, v[u][e]);
+        }
+    }
 }
 
 // ------------------------------------------------------- online statistics

@@ -9,48 +9,21 @@
 //   entropy  H = log S - W / S,
 //   KL(A||B) = W / S_A - log S_A + log S_B,
 // and a support-mismatch flag decided on the logits.  The logprobs head reads
-// the target logit after the row statistics (pull request 495, Behavior
-// changes: targets outside [0, V) give 0).
+// the target logit (prefetched when the row starts) and subtracts the row's
+// logsumexp (pull request 495, Behavior changes: targets outside [0, V)
+// give 0).
+//
+// Streaming: one workgroup per row; lane tid consumes groups of U chunks of 8
+// logits with 16-byte nontemporal loads (for_each_group in rlk_device.h).
 #include "rlk_device.h"
 #include "rlk_launch.h"
 
 namespace rlk {
 
-// Load the U chunks of one group for lane `tid`: a[u][e] = element
-// (g0 + u BLOCK + tid) * 8 + e, softcapped when CAP, -inf beyond V.
-template <int BLOCK, int U, typename S, bool CAP, bool ALIGNED>
-__device__ __forceinline__ void load_group(const S* __restrict__ row, int64_t V, int64_t g0,
-                                           bool full, float k, float (&a)[U][kChunk]) {
-    const int tid = threadIdx.x;
-    if (ALIGNED && full) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) load_chunk(row + (g0 + u * BLOCK + tid) * kChunk, a[u]);
-        if (CAP) {
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-#pragma unroll
-                for (int e = 0; e < kChunk; ++e) a[u][e] = cap_fast(a[u][e], k).a;
-        }
-    } else {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t c0 = (g0 + u * BLOCK + tid) * kChunk;
-#pragma unroll
-            for (int e = 0; e < kChunk; ++e) {
-                const int64_t col = c0 + e;
-                float v = neg_inf();
-                if (col < V) {
-                    v = load_one(row + col);
-                    if (CAP) v = cap_fast(v, k).a;
-                }
-                a[u][e] = v;
-            }
-        }
-    }
-}
-
-// Fold one group into a single-tensor state.
-template <int U, bool WITH_W>
+// Fold one group into a single-tensor state.  CLAMP keeps 0 * (-inf) out of
+// W where -inf can occur: masked logits (never with the softcap) and the
+// padding of a row's tail group.
+template <int U, bool WITH_W, bool CLAMP>
 __device__ __forceinline__ void update1(Stat1& st, const float (&a)[U][kChunk], float sc) {
     float gm = a[0][0];
 #pragma unroll
@@ -73,7 +46,7 @@ __device__ __forceinline__ void update1(Stat1& st, const float (&a)[U][kChunk], 
 #pragma unroll
         for (int e = 0; e < kChunk; ++e) {
             float t = __builtin_fmaf(a[u][e], sc, -st.mL);
-            if (WITH_W) t = fmaxf(t, kClampT);
+            if (CLAMP) t = fmaxf(t, kClampT);
             const float ex = ex2(t);
             st.S += ex;
             if (WITH_W) st.W = __builtin_fmaf(ex, t, st.W);
@@ -142,24 +115,33 @@ __device__ __forceinline__ void update_kl(StatKL& st, const float (&a)[U][kChunk
 
 // Logprobs / entropy forward: one workgroup per row.
 template <int BLOCK, int U, typename T, int HEAD, bool CAP, bool ALIGNED>
-__global__ __launch_bounds__(BLOCK) void fwd1_kernel(FwdParams p) {
+__global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void fwd1_kernel(FwdParams p) {
     using S = typename T::storage;
     constexpr bool WITH_W = HEAD == kHeadEntropy;
+    constexpr bool CLAMP = WITH_W && !CAP;  // full groups; tail groups always clamp
     constexpr int NW = BLOCK / 64;
     __shared__ Stat1 red[NW];
     __shared__ float bc[2];
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-    const int64_t nchunks = (p.V + kChunk - 1) / kChunk, nfull = p.V / kChunk;
     RowStats* stats = static_cast<RowStats*>(p.stats);
     for (int64_t row = blockIdx.x; row < p.N; row += gridDim.x) {
         const S* __restrict__ x = static_cast<const S*>(p.x) + row * p.ldx;
-        Stat1 st = stat1_init();
-        for (int64_t g0 = 0; g0 < nchunks; g0 += (int64_t)U * BLOCK) {
-            float a[U][kChunk];
-            const bool full = g0 + (int64_t)U * BLOCK <= nfull;
-            load_group<BLOCK, U, S, CAP, ALIGNED>(x, p.V, g0, full, p.kx, a);
-            update1<U, WITH_W>(st, a, p.scx);
+        // Prefetch this lane's first target slot and its logit.
+        int64_t t0 = -1;
+        float xt0 = 0.0f;
+        if (HEAD == kHeadLogp && tid < p.k) {
+            t0 = p.targets[row * p.k + tid];
+            if (t0 >= 0 && t0 < p.V) xt0 = load_one(x + t0);
         }
+        Stat1 st = stat1_init();
+        for_each_group<BLOCK, U, S, CAP, ALIGNED, kFwdPipe>(
+            x, p.V, p.kx,
+            [&](int64_t, bool full, const float (&a)[U][kChunk]) {
+                if (full)
+                    update1<U, WITH_W, CLAMP>(st, a, p.scx);
+                else
+                    update1<U, WITH_W, WITH_W>(st, a, p.scx);
+            });
         st = wave_reduce<WITH_W>(st);
         if (lane == 0) red[wid] = st;
         __syncthreads();
@@ -190,11 +172,11 @@ __global__ __launch_bounds__(BLOCK) void fwd1_kernel(FwdParams p) {
         if (HEAD == kHeadLogp) {
             const float mL = bc[0], log2S = bc[1];
             for (int64_t j = tid; j < p.k; j += BLOCK) {
-                const int64_t t = p.targets[row * p.k + j];
+                const int64_t t = j == tid ? t0 : p.targets[row * p.k + j];
                 float o = 0.0f;
                 if (t >= 0 && t < p.V) {
-                    float a = load_one(x + t);
-                    if (CAP) a = cap_fast(a, p.kx).a;
+                    float a = j == tid ? xt0 : load_one(x + t);
+                    if (CAP) a = cap_r(a, p.kx);
                     o = (__builtin_fmaf(a, p.scx, -mL) - log2S) * kLn2;
                 }
                 p.out[row * p.k + j] = o;
@@ -206,24 +188,21 @@ __global__ __launch_bounds__(BLOCK) void fwd1_kernel(FwdParams p) {
 
 // KL forward (either direction): one workgroup per row pair.
 template <int BLOCK, int U, typename T, bool REVERSE, bool CAPA, bool CAPB, bool ALIGNED>
-__global__ __launch_bounds__(BLOCK) void fwdkl_kernel(FwdParams p) {
+__global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void fwdkl_kernel(FwdParams p) {
     using S = typename T::storage;
     constexpr int NW = BLOCK / 64;
     __shared__ StatKL red[NW];
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-    const int64_t nchunks = (p.V + kChunk - 1) / kChunk, nfull = p.V / kChunk;
     RowStats* stats = static_cast<RowStats*>(p.stats);
     for (int64_t row = blockIdx.x; row < p.N; row += gridDim.x) {
         const S* __restrict__ xa = static_cast<const S*>(p.x) + row * p.ldx;
         const S* __restrict__ xb = static_cast<const S*>(p.y) + row * p.ldy;
         StatKL st = statkl_init<REVERSE>();
-        for (int64_t g0 = 0; g0 < nchunks; g0 += (int64_t)U * BLOCK) {
-            float a[U][kChunk], b[U][kChunk];
-            const bool full = g0 + (int64_t)U * BLOCK <= nfull;
-            load_group<BLOCK, U, S, CAPA, ALIGNED>(xa, p.V, g0, full, p.kx, a);
-            load_group<BLOCK, U, S, CAPB, ALIGNED>(xb, p.V, g0, full, p.ky, b);
-            update_kl<U, REVERSE>(st, a, b, p.scx, p.scy);
-        }
+        for_each_group2<BLOCK, U, S, CAPA, CAPB, ALIGNED, kFwdPipe>(
+            xa, xb, p.V, p.kx, p.ky,
+            [&](int64_t, bool, const float (&a)[U][kChunk], const float (&b)[U][kChunk]) {
+                update_kl<U, REVERSE>(st, a, b, p.scx, p.scy);
+            });
         st = wave_reduce_kl<REVERSE>(st);
         if (lane == 0) red[wid] = st;
         __syncthreads();

@@ -10,13 +10,65 @@ namespace rlk {
 // Heads of the fused row kernels.
 enum Head : int { kHeadLogp = 0, kHeadEntropy = 1, kHeadKLReverse = 2, kHeadKLForward = 3 };
 
-// Launch shape of the row kernels: one workgroup of kBlock threads per row
-// (grid-stride over rows), each lane consuming kUnroll chunks of 8 elements
-// per group.  These constants fix the reduction tree, so they are the same
-// for every N.
-constexpr int kBlock = 256;
-constexpr int kUnroll1 = 4;   // single-tensor heads (logp, entropy)
-constexpr int kUnrollKL = 2;  // KL reads two tensors per group
+// Launch shape of the row kernels: one workgroup per row (grid-stride over
+// rows), each lane consuming groups of U chunks of 8 elements.  The forward
+// constants fix the reduction tree, so they are the same for every N (the
+// batch-invariance guarantee).  The backward is elementwise given the row
+// record, so its shape is free; it is tuned for the read+write stream.
+// (Overridable at compile time for launch-shape sweeps.)
+#ifndef RLK_BLOCK
+#define RLK_BLOCK 256
+#endif
+#ifndef RLK_UNROLL1
+#define RLK_UNROLL1 4
+#endif
+#ifndef RLK_UNROLL_KL
+#define RLK_UNROLL_KL 2
+#endif
+#ifndef RLK_BWD_BLOCK
+#define RLK_BWD_BLOCK 1024
+#endif
+#ifndef RLK_BWD_UNROLL1
+#define RLK_BWD_UNROLL1 2
+#endif
+#ifndef RLK_BWD_UNROLL_KL
+#define RLK_BWD_UNROLL_KL 1
+#endif
+#ifndef RLK_BWD_BLOCK_TOPK
+#define RLK_BWD_BLOCK_TOPK 512
+#endif
+#ifndef RLK_BWD_UNROLL_TOPK
+#define RLK_BWD_UNROLL_TOPK 2
+#endif
+#ifndef RLK_BWD_WIDE_TOPK
+#define RLK_BWD_WIDE_TOPK 64
+#endif
+#ifndef RLK_FWD_PIPE
+#define RLK_FWD_PIPE 1
+#endif
+#ifndef RLK_BWD_PIPE
+#define RLK_BWD_PIPE 0
+#endif
+constexpr bool kFwdPipe = RLK_FWD_PIPE;
+constexpr bool kBwdPipe = RLK_BWD_PIPE;
+// Minimum waves per SIMD requested from the register allocator (0: none).
+#ifndef RLK_WAVES_PER_EU
+#define RLK_WAVES_PER_EU 0
+#endif
+#if RLK_WAVES_PER_EU > 0
+#define RLK_OCCUPANCY __attribute__((amdgpu_waves_per_eu(RLK_WAVES_PER_EU)))
+#else
+#define RLK_OCCUPANCY
+#endif
+constexpr int kBlock = RLK_BLOCK;
+constexpr int kUnroll1 = RLK_UNROLL1;    // forward, single-tensor heads
+constexpr int kUnrollKL = RLK_UNROLL_KL;  // forward, KL (two tensors per group)
+constexpr int kBwdBlock = RLK_BWD_BLOCK;
+constexpr int kBwdUnroll1 = RLK_BWD_UNROLL1;
+constexpr int kBwdUnrollKL = RLK_BWD_UNROLL_KL;
+constexpr int kBwdBlockTopk = RLK_BWD_BLOCK_TOPK;    // logp backward with k >= kBwdWideTopk
+constexpr int kBwdUnrollTopk = RLK_BWD_UNROLL_TOPK;
+constexpr int kBwdWideTopk = RLK_BWD_WIDE_TOPK;
 constexpr int kMaxGrid = 1 << 20;
 
 struct FwdParams {
