@@ -44,7 +44,10 @@ __global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void bwd_kernel(BwdParams p) {
     int* tg = smem_topk;
     float* gg = reinterpret_cast<float*>(smem_topk + p.k);
 
-    for (int64_t row = blockIdx.x; row < p.N; row += gridDim.x) {
+    for (int64_t it = blockIdx.x; it < p.N; it += gridDim.x) {
+        // Rows are visited last-first: the end of the forward's stream is the
+        // part still held in the Infinity Cache when the backward follows it.
+        const int64_t row = p.N - 1 - it;
         const S* __restrict__ xa = static_cast<const S*>(p.x) + row * p.ldx;
         const S* __restrict__ xb = KL ? static_cast<const S*>(p.y) + row * p.ldy : nullptr;
         S* __restrict__ gx = static_cast<S*>(p.gx) + row * p.V;
