@@ -24,7 +24,7 @@
  * Conventions common to every entry point:
  *   - Tensor pointers are DEVICE pointers owned by the caller.  The library
  *     allocates, frees and copies nothing and keeps no state between calls.
- *   - Logits are fp32 or bf16 (rlk_dtype).  All arithmetic is fp32; head
+ *   - Logits are fp32, bf16 or fp16 (rlk_dtype).  All arithmetic is fp32; head
  *     outputs are fp32; gradients with respect to the logits are written in
  *     the logits dtype with a single round-to-nearest-even cast.
  *   - A logits matrix is [N, V] row-major with row stride ld >= V elements
@@ -63,12 +63,12 @@ extern "C" {
 /* Largest top-k width accepted by rlk_logp_fwd / rlk_logp_bwd. */
 #define RLK_MAX_TOPK 4096
 
-typedef enum { RLK_F32 = 0, RLK_BF16 = 1 } rlk_dtype;
+typedef enum { RLK_F32 = 0, RLK_BF16 = 1, RLK_F16 = 2 } rlk_dtype;
 
 typedef enum {
     RLK_OK = 0,
     RLK_ERR_ARG = 1,    /* null pointer, bad cap, bad enum value          */
-    RLK_ERR_DTYPE = 2,  /* dtype outside rlk_dtype (fp16, fp64, ints...)  */
+    RLK_ERR_DTYPE = 2,  /* dtype outside rlk_dtype (fp64, ints, ...)      */
     RLK_ERR_SHAPE = 3,  /* N < 0, V < 1, ld < V, k out of range, overflow */
     RLK_ERR_DEVICE = 4, /* pointer not device memory, or on another GPU   */
     RLK_ERR_LAUNCH = 5  /* the HIP runtime refused a launch               */

@@ -9,6 +9,10 @@ Tolerances (fixed for this library; derivations in the design notes):
   * bf16 gradients: |d| <= max(4e-3, one bf16 ulp of ref): a correct fp32
     value rounded once to bf16 is within half an ulp, and above |2| half an
     ulp already exceeds 4e-3;
+  * fp16 logits: head outputs as for fp32 logits (the inputs are exact, the
+    arithmetic is the same fp32); fp16 gradients |d| <= 1e-3 + 1e-3 |ref|
+    (the fp16 row of the same accuracy table; half an fp16 ulp is 4.9e-4
+    relative);
   * exact: the class of every element (NaN / +inf / -inf / finite) must
     match, and structural zeros (ignored targets, rows without a valid
     target, masked columns of entropy and reverse KL) must be exactly 0.
@@ -23,6 +27,7 @@ OUT_F32 = (1e-5, 1e-5)    # (abs, rel) for outputs from fp32 logits
 OUT_BF16 = 2e-3
 GRAD_F32 = (1e-5, 1e-5)
 GRAD_BF16 = 4e-3
+GRAD_F16 = (1e-3, 1e-3)
 
 
 def to64(t: torch.Tensor) -> np.ndarray:
@@ -66,7 +71,7 @@ def assert_out(gpu_t: torch.Tensor, ref: np.ndarray, in_dtype, what="out", exact
         assert (gpu[ez] == 0).all(), f"{what}: structural zeros are not exactly 0"
     fin = np.isfinite(ref)
     err = np.where(fin, np.abs(gpu - ref), 0.0)
-    if in_dtype == torch.float32:
+    if in_dtype in (torch.float32, torch.float16):
         tol = OUT_F32[0] + OUT_F32[1] * np.abs(np.where(fin, ref, 0.0))
     else:
         tol = np.full(err.shape, OUT_BF16)
@@ -85,6 +90,8 @@ def assert_grad(gpu_t: torch.Tensor, ref: np.ndarray, what="grad", exact_zero=No
     err = np.where(fin, np.abs(gpu - ref), 0.0)
     if gpu_t.dtype == torch.float32:
         tol = GRAD_F32[0] + GRAD_F32[1] * np.abs(r0)
+    elif gpu_t.dtype == torch.float16:
+        tol = GRAD_F16[0] + GRAD_F16[1] * np.abs(r0)
     else:
         tol = np.maximum(GRAD_BF16, bf16_ulp(r0))
     _report(err, tol, gpu, ref, what)

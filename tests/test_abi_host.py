@@ -58,7 +58,7 @@ def _logp_fwd(lib, dtype=1, N=4, V=10, ld=10, k=1, cap=0.0, ptrs=True):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(dtype=2), DTYPE), (dict(dtype=-1), DTYPE),
+    (dict(dtype=3), DTYPE), (dict(dtype=-1), DTYPE),
     (dict(N=-1), SHAPE), (dict(V=0), SHAPE), (dict(ld=9), SHAPE), (dict(V=2**31, ld=2**31), SHAPE),
     (dict(k=0), SHAPE), (dict(k=4097), SHAPE), (dict(N=2**40, ld=2**30, V=10), SHAPE),
     (dict(cap=-1.0), ARG), (dict(cap=float("nan")), ARG), (dict(cap=float("inf")), ARG),
@@ -86,6 +86,7 @@ def test_other_entry_points_validate(lib):
     p = ctypes.c_void_p(16)
     assert lib.rlk_softcap_fwd(p, 1, p, 0, 8, F(0.0), None) == ARG        # cap must be > 0
     assert lib.rlk_softcap_fwd(p, 1, p, 3, 8, F(30.0), None) == DTYPE
+    assert lib.rlk_softcap_fwd(p, 7, p, 0, 8, F(30.0), None) == DTYPE
     assert lib.rlk_softcap_bwd(p, 5, p, p, 8, F(30.0), None) == DTYPE
     assert lib.rlk_softcap_bwd(p, 1, p, p, -1, F(30.0), None) == SHAPE
     assert lib.rlk_entropy_fwd(p, 1, 4, 8, 7, F(0), p, p, None) == SHAPE   # ld < V

@@ -92,7 +92,8 @@ def test_batch_invariance(dev, V):
         assert_bitwise(full[k][5:6], single[k], f"single row {k}")
 
 
-@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.float16],
+                         ids=["f32", "bf16", "f16"])
 @pytest.mark.parametrize("V,pad", [(4096, 8), (4099, 5), (151936, 64)])
 def test_padded_stride_reads_nothing_outside_the_row(dev, dtype, V, pad):
     N = 12
@@ -124,17 +125,18 @@ def test_misaligned_base_pointer(dev, dtype):
         assert_bitwise(want[k], got[k], f"misaligned {k}")
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "f16"])
 @pytest.mark.parametrize("cap", [0.0, 20.0])
-def test_bf16_equals_fp32_of_same_values(dev, cap):
+def test_half_dtypes_equal_fp32_of_same_values(dev, dtype, cap):
     N, V = 10, 75968
-    x, ref, t, g_t, g_r = make(N, V, torch.bfloat16, 5, dev)
+    x, ref, t, g_t, g_r = make(N, V, dtype, 5, dev)
     b = run_all(x, ref, t, g_t, g_r, cap)
     f = run_all(x.float(), ref.float(), t, g_t, g_r, cap)
     for k in b:
         if k.endswith("grad"):
-            assert_bitwise(b[k], f[k].to(torch.bfloat16), f"bf16 grad == RNE(fp32 grad) {k}")
+            assert_bitwise(b[k], f[k].to(dtype), f"{dtype} grad == RNE(fp32 grad) {k}")
         else:
-            assert_bitwise(b[k], f[k], f"bf16 vs fp32 output {k}")
+            assert_bitwise(b[k], f[k], f"{dtype} vs fp32 output {k}")
 
 
 def test_outputs_independent_of_stats_buffer_history(dev):

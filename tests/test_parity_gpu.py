@@ -20,7 +20,8 @@ from vocab_log_softmax_amd import rlk
 pytestmark = pytest.mark.gpu
 
 VS = [1, 2, 7, 255, 1031, 2048, 4097, 32000]
-DTYPES = [torch.float32, torch.bfloat16]
+DTYPES = [torch.float32, torch.bfloat16, torch.float16]
+DT_IDS = ["f32", "bf16", "f16"]
 
 
 def gen(seed):
@@ -58,7 +59,7 @@ def _run_logp(dev, orc, x, t, g, cap):
     return out, gx, ref_out, ref_gx
 
 
-@pytest.mark.parametrize("dtype", DTYPES, ids=["f32", "bf16"])
+@pytest.mark.parametrize("dtype", DTYPES, ids=DT_IDS)
 @pytest.mark.parametrize("V", VS)
 @pytest.mark.parametrize("cap", [0.0, 30.0])
 def test_logp_k1(dev, orc, dtype, V, cap):
@@ -102,7 +103,7 @@ def test_logp_target_on_masked_column(dev, orc):
     assert_grad(gx, ref_gx)
 
 
-@pytest.mark.parametrize("dtype", DTYPES, ids=["f32", "bf16"])
+@pytest.mark.parametrize("dtype", DTYPES, ids=DT_IDS)
 @pytest.mark.parametrize("V,k", [(7, 4), (255, 17), (4097, 64), (32768, 256), (2000, 300)])
 @pytest.mark.parametrize("cap", [0.0, 20.0])
 def test_logp_topk(dev, orc, dtype, V, k, cap):
@@ -130,7 +131,7 @@ def test_logp_topk(dev, orc, dtype, V, k, cap):
 
 # ------------------------------------------------------------------- entropy
 
-@pytest.mark.parametrize("dtype", DTYPES, ids=["f32", "bf16"])
+@pytest.mark.parametrize("dtype", DTYPES, ids=DT_IDS)
 @pytest.mark.parametrize("V", VS)
 @pytest.mark.parametrize("cap", [0.0, 30.0])
 def test_entropy(dev, orc, dtype, V, cap):
@@ -181,7 +182,7 @@ def kl_pair(N, V, dtype, seed, mismatch_rows=(), empty_rows=(), both_masked_rows
     return a.to(dtype), b.to(dtype)
 
 
-@pytest.mark.parametrize("dtype", DTYPES, ids=["f32", "bf16"])
+@pytest.mark.parametrize("dtype", DTYPES, ids=DT_IDS)
 @pytest.mark.parametrize("V", [2, 7, 1031, 4097, 32000])
 @pytest.mark.parametrize("direction", [0, 1], ids=["rev", "fwd"])
 @pytest.mark.parametrize("caps", [(0.0, 0.0), (30.0, 20.0)], ids=["nocap", "cap"])
@@ -219,8 +220,8 @@ def test_kl_self_is_zero(dev):
 
 # ------------------------------------------------------------------- softcap
 
-@pytest.mark.parametrize("xdt", DTYPES, ids=["x_f32", "x_bf16"])
-@pytest.mark.parametrize("ydt", DTYPES, ids=["y_f32", "y_bf16"])
+@pytest.mark.parametrize("xdt", DTYPES, ids=["x_" + i for i in DT_IDS])
+@pytest.mark.parametrize("ydt", DTYPES, ids=["y_" + i for i in DT_IDS])
 @pytest.mark.parametrize("n", [1, 7, 8, 1025, 6 * 262144])
 @pytest.mark.parametrize("cap", [20.0, 30.0])
 def test_softcap(dev, orc, xdt, ydt, n, cap):

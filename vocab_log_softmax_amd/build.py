@@ -21,7 +21,9 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "librlk.so")
 
-SOURCES = ["rlk_fwd.hip", "rlk_bwd.hip", "rlk_softcap.hip", "rlk_api.cpp"]
+SOURCES = ["rlk_fwd_f32.hip", "rlk_fwd_bf16.hip", "rlk_fwd_f16.hip",
+           "rlk_bwd_f32.hip", "rlk_bwd_bf16.hip", "rlk_bwd_f16.hip",
+           "rlk_softcap.hip", "rlk_api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

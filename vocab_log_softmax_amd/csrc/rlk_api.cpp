@@ -35,7 +35,7 @@ rlk_status ok() {
     return RLK_OK;
 }
 
-bool dtype_ok(int d) { return d == RLK_F32 || d == RLK_BF16; }
+bool dtype_ok(int d) { return d == RLK_F32 || d == RLK_BF16 || d == RLK_F16; }
 int64_t esize(int d) { return d == RLK_F32 ? 4 : 2; }
 
 // A fused-head cap: 0 = off, otherwise finite and > 0.
@@ -159,7 +159,7 @@ const char* rlk_last_error(void) { return g_err; }
 rlk_status rlk_softcap_fwd(const void* x, rlk_dtype x_dtype, void* y, rlk_dtype y_dtype,
                            int64_t n, float cap, void* stream) {
     if (!dtype_ok(x_dtype) || !dtype_ok(y_dtype))
-        return fail(RLK_ERR_DTYPE, "softcap dtypes must be RLK_F32 or RLK_BF16");
+        return fail(RLK_ERR_DTYPE, "softcap dtypes must be RLK_F32, RLK_BF16 or RLK_F16");
     if (!std::isfinite(cap) || !(cap > 0.0f))
         return fail(RLK_ERR_ARG, "softcap cap must be finite and > 0, got %g", (double)cap);
     if (n < 0) return fail(RLK_ERR_SHAPE, "n must be >= 0, got %lld", (long long)n);
@@ -176,7 +176,7 @@ rlk_status rlk_softcap_fwd(const void* x, rlk_dtype x_dtype, void* y, rlk_dtype 
 
 rlk_status rlk_softcap_bwd(const void* x, rlk_dtype x_dtype, const float* grad_y, void* grad_x,
                            int64_t n, float cap, void* stream) {
-    if (!dtype_ok(x_dtype)) return fail(RLK_ERR_DTYPE, "x dtype must be RLK_F32 or RLK_BF16");
+    if (!dtype_ok(x_dtype)) return fail(RLK_ERR_DTYPE, "x dtype must be RLK_F32, RLK_BF16 or RLK_F16");
     if (!std::isfinite(cap) || !(cap > 0.0f))
         return fail(RLK_ERR_ARG, "softcap cap must be finite and > 0, got %g", (double)cap);
     if (n < 0) return fail(RLK_ERR_SHAPE, "n must be >= 0, got %lld", (long long)n);
@@ -195,7 +195,7 @@ rlk_status rlk_softcap_bwd(const void* x, rlk_dtype x_dtype, const float* grad_y
 
 static rlk_status logp_common(const void* logits, rlk_dtype dtype, int64_t N, int64_t V,
                               int64_t ld, const int64_t* targets, int64_t k, float softcap) {
-    if (!dtype_ok(dtype)) return fail(RLK_ERR_DTYPE, "logits dtype must be RLK_F32 or RLK_BF16");
+    if (!dtype_ok(dtype)) return fail(RLK_ERR_DTYPE, "logits dtype must be RLK_F32, RLK_BF16 or RLK_F16");
     rlk_status s = check_matrix(N, V, ld, esize(dtype), "logits");
     if (s != RLK_OK) return s;
     if (k < 1 || k > RLK_MAX_TOPK)
@@ -271,7 +271,7 @@ rlk_status rlk_logp_bwd(const void* logits, rlk_dtype dtype, int64_t N, int64_t 
 
 rlk_status rlk_entropy_fwd(const void* logits, rlk_dtype dtype, int64_t N, int64_t V, int64_t ld,
                            float softcap, float* entropy, void* stats, void* stream) {
-    if (!dtype_ok(dtype)) return fail(RLK_ERR_DTYPE, "logits dtype must be RLK_F32 or RLK_BF16");
+    if (!dtype_ok(dtype)) return fail(RLK_ERR_DTYPE, "logits dtype must be RLK_F32, RLK_BF16 or RLK_F16");
     rlk_status s = check_matrix(N, V, ld, esize(dtype), "logits");
     if (s != RLK_OK) return s;
     s = check_head_cap(softcap, "softcap");
@@ -301,7 +301,7 @@ rlk_status rlk_entropy_fwd(const void* logits, rlk_dtype dtype, int64_t N, int64
 rlk_status rlk_entropy_bwd(const void* logits, rlk_dtype dtype, int64_t N, int64_t V, int64_t ld,
                            float softcap, const void* stats, const float* grad_entropy,
                            void* grad_logits, void* stream) {
-    if (!dtype_ok(dtype)) return fail(RLK_ERR_DTYPE, "logits dtype must be RLK_F32 or RLK_BF16");
+    if (!dtype_ok(dtype)) return fail(RLK_ERR_DTYPE, "logits dtype must be RLK_F32, RLK_BF16 or RLK_F16");
     rlk_status s = check_matrix(N, V, ld, esize(dtype), "logits");
     if (s != RLK_OK) return s;
     s = check_head_cap(softcap, "softcap");
@@ -335,7 +335,7 @@ rlk_status rlk_entropy_bwd(const void* logits, rlk_dtype dtype, int64_t N, int64
 
 static rlk_status kl_common(rlk_dtype dtype, int64_t N, int64_t V, int64_t ld_policy,
                             int64_t ld_ref, rlk_kl_dir dir, float cp, float cr) {
-    if (!dtype_ok(dtype)) return fail(RLK_ERR_DTYPE, "logits dtype must be RLK_F32 or RLK_BF16");
+    if (!dtype_ok(dtype)) return fail(RLK_ERR_DTYPE, "logits dtype must be RLK_F32, RLK_BF16 or RLK_F16");
     rlk_status s = check_matrix(N, V, ld_policy, esize(dtype), "policy");
     if (s != RLK_OK) return s;
     s = check_matrix(N, V, ld_ref, esize(dtype), "ref");

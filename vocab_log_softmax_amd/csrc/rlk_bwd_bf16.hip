@@ -1,0 +1,12 @@
+// rlk_bwd_bf16.hip -- backward row kernels instantiated for bf16 logits
+// (one translation unit per dtype so the library builds in parallel).
+#include "rlk_bwd_kernels.h"
+
+namespace rlk {
+
+hipError_t launch_bwd_bf16(int head, bool cap_x, bool cap_y, bool aligned,
+                           const BwdParams& p, hipStream_t stream) {
+    return bwd_dispatch_cap<BF16>(head, cap_x, cap_y, aligned, p, stream);
+}
+
+}  // namespace rlk

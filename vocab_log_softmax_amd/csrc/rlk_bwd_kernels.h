@@ -1,4 +1,4 @@
-// rlk_bwd.hip -- fused zero-workspace backward row kernels.
+// rlk_bwd_kernels.h -- fused zero-workspace backward row kernels.
 //
 // "perf(logp): fused zero-workspace backward for the generic CUDA fused logp"
 // (RL-Kernel pull request 495), Summary: the gradient g (onehot - softmax) is
@@ -17,6 +17,8 @@
 //   entropy:  -p_v (log p_v + H);
 //   reverse KL(P||R): p_v (log p_v - log q_v - D);
 //   forward KL(R||P): p_v - q_v.
+#pragma once
+
 #include "rlk_device.h"
 #include "rlk_launch.h"
 
@@ -40,14 +42,20 @@ __global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void bwd_kernel(BwdParams p) {
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int64_t step = (int64_t)U * BLOCK;
     const int64_t nchunks = (p.V + kChunk - 1) / kChunk, nfull = p.V / kChunk;
+    const int64_t ngroups = (nchunks + step - 1) / step;
+    const int64_t gps = (ngroups + p.split - 1) / p.split;  // groups per column segment
     const RowStats* stats = static_cast<const RowStats*>(p.stats);
     int* tg = smem_topk;
     float* gg = reinterpret_cast<float*>(smem_topk + p.k);
 
-    for (int64_t it = blockIdx.x; it < p.N; it += gridDim.x) {
-        // Rows are visited last-first: the end of the forward's stream is the
-        // part still held in the Infinity Cache when the backward follows it.
-        const int64_t row = p.N - 1 - it;
+    for (int64_t it = blockIdx.x; it < p.N * p.split; it += gridDim.x) {
+        // Work item = (row, column segment).  Rows are visited last-first: the
+        // end of the forward's stream is the part still held in the Infinity
+        // Cache when the backward follows it.
+        const int64_t rit = it / p.split, seg = it - rit * p.split;
+        const int64_t row = p.N - 1 - rit;
+        const int64_t gbeg = seg * gps, gend = gbeg + gps < ngroups ? gbeg + gps : ngroups;
+        const int64_t cbeg = gbeg * step * kChunk, cend = gend * step * kChunk;  // columns
         const S* __restrict__ xa = static_cast<const S*>(p.x) + row * p.ldx;
         const S* __restrict__ xb = KL ? static_cast<const S*>(p.y) + row * p.ldy : nullptr;
         S* __restrict__ gx = static_cast<S*>(p.gx) + row * p.V;
@@ -153,7 +161,8 @@ __global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void bwd_kernel(BwdParams p) {
                         float v[U][kChunk];
                         grad_group(a, reinterpret_cast<const float(&)[UB][kChunk]>(b), v);
                         store_group<BLOCK, U, S, ALIGNED>(gx, p.V, g0, full, v);
-                    });
+                    },
+                    gbeg, gend);
             } else {
                 for_each_group<BLOCK, U, S, CAPA, ALIGNED, kBwdPipe>(
                     xa, p.V, p.kx, [&](int64_t g0, bool full, const float (&a)[U][kChunk]) {
@@ -161,7 +170,8 @@ __global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void bwd_kernel(BwdParams p) {
                         const float b[UB][kChunk] = {};
                         grad_group(a, b, v);
                         store_group<BLOCK, U, S, ALIGNED>(gx, p.V, g0, full, v);
-                    });
+                    },
+                    gbeg, gend);
             }
         } else if (mode == kModeMismatch) {
             // Reverse KL with a support mismatch: NaN on the policy's support,
@@ -175,7 +185,8 @@ __global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void bwd_kernel(BwdParams p) {
                         for (int e = 0; e < kChunk; ++e)
                             v[u][e] = (!CAPA && a[u][e] == neg_inf()) ? 0.0f : qnan();
                     store_group<BLOCK, U, S, ALIGNED>(gx, p.V, g0, full, v);
-                });
+                },
+                gbeg, gend);
         } else {
             const float fill = mode == kModeZero ? 0.0f : qnan();
             float v[U][kChunk];
@@ -183,7 +194,7 @@ __global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void bwd_kernel(BwdParams p) {
             for (int u = 0; u < U; ++u)
 #pragma unroll
                 for (int e = 0; e < kChunk; ++e) v[u][e] = fill;
-            for (int64_t g0 = 0; g0 < nchunks; g0 += step)
+            for (int64_t g0 = gbeg * step; g0 < gend * step; g0 += step)
                 store_group<BLOCK, U, S, ALIGNED>(gx, p.V, g0, g0 + step <= nfull, v);
         }
 
@@ -194,7 +205,7 @@ __global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void bwd_kernel(BwdParams p) {
             __syncthreads();
             for (int64_t j = tid; j < p.k; j += BLOCK) {
                 const int t = tg[j];
-                if (t < 0) continue;
+                if (t < 0 || t < cbeg || t >= cend) continue;  // not in this segment
                 bool first = true;
                 float h = 0.0f;
                 for (int64_t jj = 0; jj < p.k; ++jj) {
@@ -225,8 +236,8 @@ __global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void bwd_kernel(BwdParams p) {
 // fix-up follows each row (fewer idle lanes per row, more rows per CU).
 
 template <int BB, int U1, int UKL, typename T, bool CAPX, bool CAPY, bool AL>
-static hipError_t bwd_dispatch_head(int head, const BwdParams& p, hipStream_t s) {
-    const dim3 grid(row_grid(p.N)), block(BB);
+inline hipError_t bwd_dispatch_head(int head, const BwdParams& p, hipStream_t s) {
+    const dim3 grid(row_grid(p.N * p.split)), block(BB);
     switch (head) {
         case kHeadLogp: {
             const size_t lds = static_cast<size_t>(p.k) * (sizeof(int) + sizeof(float));
@@ -253,7 +264,20 @@ static hipError_t bwd_dispatch_head(int head, const BwdParams& p, hipStream_t s)
 }
 
 template <typename T, bool CAPX, bool CAPY>
-static hipError_t bwd_dispatch_al(int head, bool al, const BwdParams& p, hipStream_t s) {
+inline hipError_t bwd_dispatch_al(int head, bool al, const BwdParams& p0, hipStream_t s) {
+    BwdParams p = p0;
+    p.split = 1;
+    if (p.N < kBwdSmallRows) {
+        // Few rows: narrow workgroups, each row cut into column segments.
+        const int64_t step = (int64_t)kBwdUnrollSmall * kBwdBlockSmall;
+        const int64_t ngroups = ((p.V + kChunk - 1) / kChunk + step - 1) / step;
+        int64_t split = (kBwdTargetItems + p.N - 1) / p.N;
+        p.split = split < ngroups ? split : ngroups;
+        return al ? bwd_dispatch_head<kBwdBlockSmall, kBwdUnrollSmall, kBwdUnrollSmall, T, CAPX,
+                                      CAPY, true>(head, p, s)
+                  : bwd_dispatch_head<kBwdBlockSmall, kBwdUnrollSmall, kBwdUnrollSmall, T, CAPX,
+                                      CAPY, false>(head, p, s);
+    }
     const bool wide_topk = head == kHeadLogp && p.k >= kBwdWideTopk;
     if (wide_topk)
         return al ? bwd_dispatch_head<kBwdBlockTopk, kBwdUnrollTopk, kBwdUnrollTopk, T, CAPX, CAPY,
@@ -267,7 +291,7 @@ static hipError_t bwd_dispatch_al(int head, bool al, const BwdParams& p, hipStre
 }
 
 template <typename T>
-static hipError_t bwd_dispatch_cap(int head, bool cx, bool cy, bool al, const BwdParams& p,
+inline hipError_t bwd_dispatch_cap(int head, bool cx, bool cy, bool al, const BwdParams& p,
                                    hipStream_t s) {
     const bool kl = head == kHeadKLReverse || head == kHeadKLForward;
     if (!kl) cy = false;
@@ -275,12 +299,6 @@ static hipError_t bwd_dispatch_cap(int head, bool cx, bool cy, bool al, const Bw
     if (cx) return bwd_dispatch_al<T, true, false>(head, al, p, s);
     if (cy) return bwd_dispatch_al<T, false, true>(head, al, p, s);
     return bwd_dispatch_al<T, false, false>(head, al, p, s);
-}
-
-hipError_t launch_bwd(int head, int dtype, bool cap_x, bool cap_y, bool aligned,
-                      const BwdParams& p, hipStream_t stream) {
-    if (dtype == 0) return bwd_dispatch_cap<F32>(head, cap_x, cap_y, aligned, p, stream);
-    return bwd_dispatch_cap<BF16>(head, cap_x, cap_y, aligned, p, stream);
 }
 
 }  // namespace rlk

@@ -55,6 +55,11 @@ struct BF16 {
     using storage = uint16_t;
     static constexpr int kBytes = 2;
 };
+struct F16 {
+    using storage = _Float16;
+    static constexpr int kBytes = 2;
+};
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -110,8 +115,19 @@ __device__ __forceinline__ void load_chunk(const uint16_t* p, float (&f)[kChunk]
     f[4] = bf16_lo(w.z); f[5] = bf16_hi(w.z);
     f[6] = bf16_lo(w.w); f[7] = bf16_hi(w.w);
 }
+__device__ __forceinline__ void load_chunk(const _Float16* p, float (&f)[kChunk]) {
+    const u32x4 w = ld16(reinterpret_cast<const u32x4*>(p));
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const f16x2_t h = __builtin_bit_cast(f16x2_t, ws[i]);
+        f[2 * i] = static_cast<float>(h.x);
+        f[2 * i + 1] = static_cast<float>(h.y);
+    }
+}
 __device__ __forceinline__ float load_one(const float* p) { return *p; }
 __device__ __forceinline__ float load_one(const uint16_t* p) { return bf16_to_f32(*p); }
+__device__ __forceinline__ float load_one(const _Float16* p) { return static_cast<float>(*p); }
 
 // Store one full chunk of 8 values to a 16-byte aligned address.
 __device__ __forceinline__ void store_chunk(float* p, const float (&f)[kChunk]) {
@@ -125,8 +141,21 @@ __device__ __forceinline__ void store_chunk(uint16_t* p, const float (&f)[kChunk
                      pack_bf16x2(f[6], f[7])};
     st16(reinterpret_cast<u32x4*>(p), w);
 }
+// Round-to-nearest-even fp16 pack (overflow gives +-inf, NaN stays NaN).
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+    f16x2_t v;
+    v.x = static_cast<_Float16>(lo);
+    v.y = static_cast<_Float16>(hi);
+    return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ void store_chunk(_Float16* p, const float (&f)[kChunk]) {
+    const u32x4 w = {pack_f16x2(f[0], f[1]), pack_f16x2(f[2], f[3]), pack_f16x2(f[4], f[5]),
+                     pack_f16x2(f[6], f[7])};
+    st16(reinterpret_cast<u32x4*>(p), w);
+}
 __device__ __forceinline__ void store_one(float* p, float f) { *p = f; }
 __device__ __forceinline__ void store_one(uint16_t* p, float f) { *p = f32_to_bf16(f); }
+__device__ __forceinline__ void store_one(_Float16* p, float f) { *p = static_cast<_Float16>(f); }
 
 // ---------------------------------------------------------------- softcap
 //
@@ -182,10 +211,22 @@ template <int U>
 struct RawGroup<float, U> {
     f32x4 v[U][2];
 };
+template <int U>
+struct RawGroup<_Float16, U> {
+    u32x4 v[U];
+};
 
 template <int BLOCK, int U>
 __device__ __forceinline__ void raw_load(const uint16_t* __restrict__ row, int64_t g0,
                                          RawGroup<uint16_t, U>& r) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+        r.v[u] = ld16(reinterpret_cast<const u32x4*>(
+            row + (g0 + u * BLOCK + (int)threadIdx.x) * kChunk));
+}
+template <int BLOCK, int U>
+__device__ __forceinline__ void raw_load(const _Float16* __restrict__ row, int64_t g0,
+                                         RawGroup<_Float16, U>& r) {
 #pragma unroll
     for (int u = 0; u < U; ++u)
         r.v[u] = ld16(reinterpret_cast<const u32x4*>(
@@ -210,6 +251,19 @@ __device__ __forceinline__ void raw_unpack(const RawGroup<uint16_t, U>& r, float
         a[u][2] = bf16_lo(r.v[u].y); a[u][3] = bf16_hi(r.v[u].y);
         a[u][4] = bf16_lo(r.v[u].z); a[u][5] = bf16_hi(r.v[u].z);
         a[u][6] = bf16_lo(r.v[u].w); a[u][7] = bf16_hi(r.v[u].w);
+    }
+}
+template <int U>
+__device__ __forceinline__ void raw_unpack(const RawGroup<_Float16, U>& r, float (&a)[U][kChunk]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const uint32_t ws[4] = {r.v[u].x, r.v[u].y, r.v[u].z, r.v[u].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const f16x2_t h = __builtin_bit_cast(f16x2_t, ws[i]);
+            a[u][2 * i] = static_cast<float>(h.x);
+            a[u][2 * i + 1] = static_cast<float>(h.y);
+        }
     }
 }
 template <int U>
@@ -275,15 +329,22 @@ __device__ __forceinline__ void fast_values(const RawGroup<S, U>& r, float k, fl
 // PIPE two register buffers alternate so that the next group's loads are in
 // flight while the current group is consumed.  The order in which f sees the
 // groups, and the values, are the same for every path.
+//
+// gbeg / gend restrict the walk to the groups [gbeg, gend) of the row (a
+// column segment); -1 for gend means "to the end of the row".
 template <int BLOCK, int U, typename S, bool CAP, bool ALIGNED, bool PIPE, typename F>
-__device__ __forceinline__ void for_each_group(const S* __restrict__ row, int64_t V, float k, F&& f) {
+__device__ __forceinline__ void for_each_group(const S* __restrict__ row, int64_t V, float k, F&& f,
+                                               int64_t gbeg = 0, int64_t gend = -1) {
     const int64_t step = (int64_t)U * BLOCK;
     const int64_t nchunks = (V + kChunk - 1) / kChunk, nfull = V / kChunk;
-    const int64_t nfg = ALIGNED ? nfull / step : 0;  // full aligned groups
-    int64_t gi = 0;
-    if (PIPE && nfg > 0) {
+    const int64_t ngroups = (nchunks + step - 1) / step;
+    if (gend < 0 || gend > ngroups) gend = ngroups;
+    const int64_t nfg_row = ALIGNED ? nfull / step : 0;  // full aligned groups of the row
+    const int64_t nfg = nfg_row < gend ? nfg_row : gend;
+    int64_t gi = gbeg;
+    if (PIPE && gi < nfg) {
         RawGroup<S, U> A, B;
-        raw_load<BLOCK, U>(row, 0, A);
+        raw_load<BLOCK, U>(row, gi * step, A);
         for (; gi + 1 < nfg; gi += 2) {
             raw_load<BLOCK, U>(row, (gi + 1) * step, B);
             {
@@ -313,25 +374,29 @@ __device__ __forceinline__ void for_each_group(const S* __restrict__ row, int64_
             f(gi * step, true, a);
         }
     }
-    for (int64_t g0 = gi * step; g0 < nchunks; g0 += step) {
+    for (; gi < gend; ++gi) {
         float a[U][kChunk];
-        tail_values<BLOCK, U, S, CAP, ALIGNED>(row, V, nfull, g0, k, a);
-        f(g0, false, a);
+        tail_values<BLOCK, U, S, CAP, ALIGNED>(row, V, nfull, gi * step, k, a);
+        f(gi * step, false, a);
     }
 }
 
 // Same walk over two rows in lockstep (KL: policy and reference).
 template <int BLOCK, int U, typename S, bool CAPA, bool CAPB, bool ALIGNED, bool PIPE, typename F>
 __device__ __forceinline__ void for_each_group2(const S* __restrict__ ra, const S* __restrict__ rb,
-                                                int64_t V, float ka, float kb, F&& f) {
+                                                int64_t V, float ka, float kb, F&& f,
+                                                int64_t gbeg = 0, int64_t gend = -1) {
     const int64_t step = (int64_t)U * BLOCK;
     const int64_t nchunks = (V + kChunk - 1) / kChunk, nfull = V / kChunk;
-    const int64_t nfg = ALIGNED ? nfull / step : 0;
-    int64_t gi = 0;
-    if (PIPE && nfg > 0) {
+    const int64_t ngroups = (nchunks + step - 1) / step;
+    if (gend < 0 || gend > ngroups) gend = ngroups;
+    const int64_t nfg_row = ALIGNED ? nfull / step : 0;
+    const int64_t nfg = nfg_row < gend ? nfg_row : gend;
+    int64_t gi = gbeg;
+    if (PIPE && gi < nfg) {
         RawGroup<S, U> A0, B0, A1, B1;
-        raw_load<BLOCK, U>(ra, 0, A0);
-        raw_load<BLOCK, U>(rb, 0, B0);
+        raw_load<BLOCK, U>(ra, gi * step, A0);
+        raw_load<BLOCK, U>(rb, gi * step, B0);
         for (; gi + 1 < nfg; gi += 2) {
             raw_load<BLOCK, U>(ra, (gi + 1) * step, A1);
             raw_load<BLOCK, U>(rb, (gi + 1) * step, B1);
@@ -370,11 +435,11 @@ __device__ __forceinline__ void for_each_group2(const S* __restrict__ ra, const 
             f(gi * step, true, a, b);
         }
     }
-    for (int64_t g0 = gi * step; g0 < nchunks; g0 += step) {
+    for (; gi < gend; ++gi) {
         float a[U][kChunk], b[U][kChunk];
-        tail_values<BLOCK, U, S, CAPA, ALIGNED>(ra, V, nfull, g0, ka, a);
-        tail_values<BLOCK, U, S, CAPB, ALIGNED>(rb, V, nfull, g0, kb, b);
-        f(g0, false, a, b);
+        tail_values<BLOCK, U, S, CAPA, ALIGNED>(ra, V, nfull, gi * step, ka, a);
+        tail_values<BLOCK, U, S, CAPB, ALIGNED>(rb, V, nfull, gi * step, kb, b);
+        f(gi * step, false, a, b);
     }
 }
 

@@ -1,0 +1,12 @@
+// rlk_fwd_bf16.hip -- forward row kernels instantiated for bf16 logits
+// (one translation unit per dtype so the library builds in parallel).
+#include "rlk_fwd_kernels.h"
+
+namespace rlk {
+
+hipError_t launch_fwd_bf16(int head, bool cap_x, bool cap_y, bool aligned,
+                           const FwdParams& p, hipStream_t stream) {
+    return fwd_dispatch_cap<BF16>(head, cap_x, cap_y, aligned, p, stream);
+}
+
+}  // namespace rlk

@@ -1,4 +1,4 @@
-// rlk_fwd.hip -- forward row kernels: one read of each logit, online
+// rlk_fwd_kernels.h -- forward row kernels: one read of each logit, online
 // statistics, head outputs and the per-row record for the backward.
 //
 // Single-read statistics follow the review comment "Suggested change: read
@@ -15,6 +15,8 @@
 //
 // Streaming: one workgroup per row; lane tid consumes groups of U chunks of 8
 // logits with 16-byte nontemporal loads (for_each_group in rlk_device.h).
+#pragma once
+
 #include "rlk_device.h"
 #include "rlk_launch.h"
 
@@ -235,7 +237,7 @@ __global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void fwdkl_kernel(FwdParams p)
 // ------------------------------------------------------------- dispatch
 
 template <typename T, bool CAPX, bool CAPY, bool AL>
-static hipError_t fwd_dispatch_head(int head, const FwdParams& p, hipStream_t s) {
+inline hipError_t fwd_dispatch_head(int head, const FwdParams& p, hipStream_t s) {
     const dim3 grid(row_grid(p.N)), block(kBlock);
     switch (head) {
         case kHeadLogp:
@@ -261,13 +263,13 @@ static hipError_t fwd_dispatch_head(int head, const FwdParams& p, hipStream_t s)
 }
 
 template <typename T, bool CAPX, bool CAPY>
-static hipError_t fwd_dispatch_al(int head, bool al, const FwdParams& p, hipStream_t s) {
+inline hipError_t fwd_dispatch_al(int head, bool al, const FwdParams& p, hipStream_t s) {
     return al ? fwd_dispatch_head<T, CAPX, CAPY, true>(head, p, s)
               : fwd_dispatch_head<T, CAPX, CAPY, false>(head, p, s);
 }
 
 template <typename T>
-static hipError_t fwd_dispatch_cap(int head, bool cx, bool cy, bool al, const FwdParams& p,
+inline hipError_t fwd_dispatch_cap(int head, bool cx, bool cy, bool al, const FwdParams& p,
                                    hipStream_t s) {
     const bool kl = head == kHeadKLReverse || head == kHeadKLForward;
     if (!kl) cy = false;  // the second cap only exists for KL
@@ -275,12 +277,6 @@ static hipError_t fwd_dispatch_cap(int head, bool cx, bool cy, bool al, const Fw
     if (cx) return fwd_dispatch_al<T, true, false>(head, al, p, s);
     if (cy) return fwd_dispatch_al<T, false, true>(head, al, p, s);
     return fwd_dispatch_al<T, false, false>(head, al, p, s);
-}
-
-hipError_t launch_fwd(int head, int dtype, bool cap_x, bool cap_y, bool aligned,
-                      const FwdParams& p, hipStream_t stream) {
-    if (dtype == 0) return fwd_dispatch_cap<F32>(head, cap_x, cap_y, aligned, p, stream);
-    return fwd_dispatch_cap<BF16>(head, cap_x, cap_y, aligned, p, stream);
 }
 
 }  // namespace rlk

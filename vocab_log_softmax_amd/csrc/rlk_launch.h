@@ -69,6 +69,12 @@ constexpr int kBwdUnrollKL = RLK_BWD_UNROLL_KL;
 constexpr int kBwdBlockTopk = RLK_BWD_BLOCK_TOPK;    // logp backward with k >= kBwdWideTopk
 constexpr int kBwdUnrollTopk = RLK_BWD_UNROLL_TOPK;
 constexpr int kBwdWideTopk = RLK_BWD_WIDE_TOPK;
+// Few rows: a narrow shape whose rows are also split into column segments,
+// so that there are enough workgroups to cover the chip.
+constexpr int kBwdBlockSmall = 256;
+constexpr int kBwdUnrollSmall = 1;
+constexpr int64_t kBwdSmallRows = 512;      // below this many rows
+constexpr int64_t kBwdTargetItems = 2048;   // aim for this many (row, segment) items
 constexpr int kMaxGrid = 1 << 20;
 
 struct FwdParams {
@@ -93,13 +99,36 @@ struct BwdParams {
     const void* stats;
     const float* g;  // upstream gradient: [N, k] (logp) or [N]
     void* gx;        // gradient w.r.t. x, [N, V] contiguous, logits dtype
+    int64_t split;   // column segments per row (one workgroup each), >= 1
 };
 
-// dtype codes follow rlk_dtype (0 fp32, 1 bf16).
-hipError_t launch_fwd(int head, int dtype, bool cap_x, bool cap_y, bool aligned,
-                      const FwdParams& p, hipStream_t stream);
-hipError_t launch_bwd(int head, int dtype, bool cap_x, bool cap_y, bool aligned,
-                      const BwdParams& p, hipStream_t stream);
+// Per-dtype row-kernel launchers (rlk_fwd_<dtype>.hip, rlk_bwd_<dtype>.hip).
+hipError_t launch_fwd_f32(int head, bool cap_x, bool cap_y, bool aligned, const FwdParams& p,
+                          hipStream_t stream);
+hipError_t launch_fwd_bf16(int head, bool cap_x, bool cap_y, bool aligned, const FwdParams& p,
+                           hipStream_t stream);
+hipError_t launch_fwd_f16(int head, bool cap_x, bool cap_y, bool aligned, const FwdParams& p,
+                          hipStream_t stream);
+hipError_t launch_bwd_f32(int head, bool cap_x, bool cap_y, bool aligned, const BwdParams& p,
+                          hipStream_t stream);
+hipError_t launch_bwd_bf16(int head, bool cap_x, bool cap_y, bool aligned, const BwdParams& p,
+                           hipStream_t stream);
+hipError_t launch_bwd_f16(int head, bool cap_x, bool cap_y, bool aligned, const BwdParams& p,
+                          hipStream_t stream);
+
+// dtype codes follow rlk_dtype (0 fp32, 1 bf16, 2 fp16).
+inline hipError_t launch_fwd(int head, int dtype, bool cap_x, bool cap_y, bool aligned,
+                             const FwdParams& p, hipStream_t stream) {
+    if (dtype == 0) return launch_fwd_f32(head, cap_x, cap_y, aligned, p, stream);
+    if (dtype == 1) return launch_fwd_bf16(head, cap_x, cap_y, aligned, p, stream);
+    return launch_fwd_f16(head, cap_x, cap_y, aligned, p, stream);
+}
+inline hipError_t launch_bwd(int head, int dtype, bool cap_x, bool cap_y, bool aligned,
+                             const BwdParams& p, hipStream_t stream) {
+    if (dtype == 0) return launch_bwd_f32(head, cap_x, cap_y, aligned, p, stream);
+    if (dtype == 1) return launch_bwd_bf16(head, cap_x, cap_y, aligned, p, stream);
+    return launch_bwd_f16(head, cap_x, cap_y, aligned, p, stream);
+}
 hipError_t launch_softcap_fwd(const void* x, int x_dtype, void* y, int y_dtype, int64_t n,
                               float cap, bool aligned, hipStream_t stream);
 hipError_t launch_softcap_bwd(const void* x, int x_dtype, const float* gy, void* gx, int64_t n,

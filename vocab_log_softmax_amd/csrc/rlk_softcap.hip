@@ -92,34 +92,38 @@ static hipError_t cap_fwd_al(const void* x, void* y, int64_t n, float c, bool al
     return hipGetLastError();
 }
 
+template <typename TX>
+static hipError_t cap_fwd_y(const void* x, void* y, int y_dtype, int64_t n, float c, bool al,
+                            hipStream_t s) {
+    if (y_dtype == 0) return cap_fwd_al<TX, F32>(x, y, n, c, al, s);
+    if (y_dtype == 1) return cap_fwd_al<TX, BF16>(x, y, n, c, al, s);
+    return cap_fwd_al<TX, F16>(x, y, n, c, al, s);
+}
+
 hipError_t launch_softcap_fwd(const void* x, int x_dtype, void* y, int y_dtype, int64_t n,
                               float cap, bool aligned, hipStream_t stream) {
-    if (x_dtype == 0 && y_dtype == 0) return cap_fwd_al<F32, F32>(x, y, n, cap, aligned, stream);
-    if (x_dtype == 0) return cap_fwd_al<F32, BF16>(x, y, n, cap, aligned, stream);
-    if (y_dtype == 0) return cap_fwd_al<BF16, F32>(x, y, n, cap, aligned, stream);
-    return cap_fwd_al<BF16, BF16>(x, y, n, cap, aligned, stream);
+    if (x_dtype == 0) return cap_fwd_y<F32>(x, y, y_dtype, n, cap, aligned, stream);
+    if (x_dtype == 1) return cap_fwd_y<BF16>(x, y, y_dtype, n, cap, aligned, stream);
+    return cap_fwd_y<F16>(x, y, y_dtype, n, cap, aligned, stream);
+}
+
+template <typename TX>
+static hipError_t cap_bwd_al(const void* x, const float* gy, void* gx, int64_t n, float inv_c,
+                             bool al, hipStream_t s) {
+    const dim3 grid(cap_grid(n)), block(kCapBlock);
+    if (al)
+        hipLaunchKernelGGL((softcap_bwd_kernel<TX, true>), grid, block, 0, s, x, gy, gx, n, inv_c);
+    else
+        hipLaunchKernelGGL((softcap_bwd_kernel<TX, false>), grid, block, 0, s, x, gy, gx, n, inv_c);
+    return hipGetLastError();
 }
 
 hipError_t launch_softcap_bwd(const void* x, int x_dtype, const float* gy, void* gx, int64_t n,
                               float cap, bool aligned, hipStream_t stream) {
     const float inv_c = 1.0f / cap;
-    const dim3 grid(cap_grid(n)), block(kCapBlock);
-    if (x_dtype == 0) {
-        if (aligned)
-            hipLaunchKernelGGL((softcap_bwd_kernel<F32, true>), grid, block, 0, stream, x, gy, gx,
-                               n, inv_c);
-        else
-            hipLaunchKernelGGL((softcap_bwd_kernel<F32, false>), grid, block, 0, stream, x, gy, gx,
-                               n, inv_c);
-    } else {
-        if (aligned)
-            hipLaunchKernelGGL((softcap_bwd_kernel<BF16, true>), grid, block, 0, stream, x, gy,
-                               gx, n, inv_c);
-        else
-            hipLaunchKernelGGL((softcap_bwd_kernel<BF16, false>), grid, block, 0, stream, x, gy,
-                               gx, n, inv_c);
-    }
-    return hipGetLastError();
+    if (x_dtype == 0) return cap_bwd_al<F32>(x, gy, gx, n, inv_c, aligned, stream);
+    if (x_dtype == 1) return cap_bwd_al<BF16>(x, gy, gx, n, inv_c, aligned, stream);
+    return cap_bwd_al<F16>(x, gy, gx, n, inv_c, aligned, stream);
 }
 
 }  // namespace rlk

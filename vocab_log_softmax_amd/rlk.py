@@ -21,7 +21,7 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("RLK_LIB", os.path.join(_PKG, "librlk.so"))
 
-RLK_F32, RLK_BF16 = 0, 1
+RLK_F32, RLK_BF16, RLK_F16 = 0, 1, 2
 RLK_HEAD_LOGP, RLK_HEAD_ENTROPY, RLK_HEAD_KL = 0, 1, 2
 RLK_KL_REVERSE, RLK_KL_FORWARD = 0, 1
 RLK_MAX_TOPK = 4096
@@ -88,7 +88,9 @@ def _dtype_code(t: torch.Tensor, what: str) -> int:
         return RLK_F32
     if t.dtype == torch.bfloat16:
         return RLK_BF16
-    raise TypeError(f"{what} must be float32 or bfloat16, got {t.dtype}")
+    if t.dtype == torch.float16:
+        return RLK_F16
+    raise TypeError(f"{what} must be float32, bfloat16 or float16, got {t.dtype}")
 
 
 def _ptr(t):
