@@ -80,6 +80,22 @@ typedef enum { RLK_HEAD_LOGP = 0, RLK_HEAD_ENTROPY = 1, RLK_HEAD_KL = 2 } rlk_he
  * RLK_KL_FORWARD: KL(ref || policy) = sum q (log q - log p). */
 typedef enum { RLK_KL_REVERSE = 0, RLK_KL_FORWARD = 1 } rlk_kl_dir;
 
+/* Row layout of a two-stride view (the `_strided` entry points).  Row i of N
+ * is (b, t) = (i / rows_per_batch, i % rows_per_batch) and starts at element
+ * b * batch_stride + t * row_stride; the vocabulary dimension is unit-stride.
+ * A [B, T, V] tensor with strides (sB, sT, 1) is {T, sB, sT} with N = B * T;
+ * e.g. logits[:, :-1] of a contiguous [B, T + 1, V] tensor is
+ * {T, (T + 1) * V, V}, read in place ("Add Triton kernels for vocab-parallel
+ * logprobs, entropy and KL", review comment: rows addressed with up to two
+ * strides so a sequence slice is not copied).  A plain [N, V] matrix with row
+ * stride ld is {N, 0, ld}.  rows_per_batch >= 1 and strides >= 0; input rows
+ * may overlap (broadcast views), gradient rows must not. */
+typedef struct {
+    int64_t rows_per_batch;
+    int64_t batch_stride;
+    int64_t row_stride;
+} rlk_rows;
+
 /* ABI version of the loaded library (RLK_ABI_VERSION at build time). */
 int rlk_abi_version(void);
 
@@ -162,6 +178,36 @@ rlk_status rlk_kl_bwd(const void* policy, const void* ref, rlk_dtype dtype, int6
                       int64_t ld_policy, int64_t ld_ref, rlk_kl_dir dir, float softcap_policy,
                       float softcap_ref, const void* stats, const float* grad_kl,
                       void* grad_policy, void* stream);
+
+/* ------------------------------------------------ two-stride row views
+ * The same heads on rows laid out by rlk_rows (inputs read in place, the
+ * gradient written through its own layout, e.g. straight into the slice of a
+ * full [B, T + 1, V] gradient buffer).  Semantics, outputs ([N], [N, k] in
+ * row order i = b * T + t), errors and the stats record are exactly those of
+ * the matching plain call; results are bitwise identical to it. */
+rlk_status rlk_logp_fwd_strided(const void* logits, rlk_dtype dtype, int64_t N, int64_t V,
+                                const rlk_rows* rows, const int64_t* targets, int64_t k,
+                                float softcap, float* logp, void* stats, void* stream);
+rlk_status rlk_logp_bwd_strided(const void* logits, rlk_dtype dtype, int64_t N, int64_t V,
+                                const rlk_rows* rows, const int64_t* targets, int64_t k,
+                                float softcap, const void* stats, const float* grad_logp,
+                                void* grad_logits, const rlk_rows* grad_rows, void* stream);
+rlk_status rlk_entropy_fwd_strided(const void* logits, rlk_dtype dtype, int64_t N, int64_t V,
+                                   const rlk_rows* rows, float softcap, float* entropy,
+                                   void* stats, void* stream);
+rlk_status rlk_entropy_bwd_strided(const void* logits, rlk_dtype dtype, int64_t N, int64_t V,
+                                   const rlk_rows* rows, float softcap, const void* stats,
+                                   const float* grad_entropy, void* grad_logits,
+                                   const rlk_rows* grad_rows, void* stream);
+rlk_status rlk_kl_fwd_strided(const void* policy, const void* ref, rlk_dtype dtype, int64_t N,
+                              int64_t V, const rlk_rows* policy_rows, const rlk_rows* ref_rows,
+                              rlk_kl_dir dir, float softcap_policy, float softcap_ref, float* kl,
+                              void* stats, void* stream);
+rlk_status rlk_kl_bwd_strided(const void* policy, const void* ref, rlk_dtype dtype, int64_t N,
+                              int64_t V, const rlk_rows* policy_rows, const rlk_rows* ref_rows,
+                              rlk_kl_dir dir, float softcap_policy, float softcap_ref,
+                              const void* stats, const float* grad_kl, void* grad_policy,
+                              const rlk_rows* grad_rows, void* stream);
 
 #ifdef __cplusplus
 }

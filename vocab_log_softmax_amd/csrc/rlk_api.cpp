@@ -191,68 +191,95 @@ rlk_status rlk_softcap_bwd(const void* x, rlk_dtype x_dtype, const float* grad_y
                     "softcap_bwd");
 }
 
-// ------------------------------------------------------------ logprobs
+// ------------------------------------------------------------ row layouts
 
-static rlk_status logp_common(const void* logits, rlk_dtype dtype, int64_t N, int64_t V,
-                              int64_t ld, const int64_t* targets, int64_t k, float softcap) {
-    if (!dtype_ok(dtype)) return fail(RLK_ERR_DTYPE, "logits dtype must be RLK_F32, RLK_BF16 or RLK_F16");
-    rlk_status s = check_matrix(N, V, ld, esize(dtype), "logits");
-    if (s != RLK_OK) return s;
-    if (k < 1 || k > RLK_MAX_TOPK)
-        return fail(RLK_ERR_SHAPE, "k must be in [1, %d], got %lld", RLK_MAX_TOPK, (long long)k);
-    if (N > 0 && k > INT64_MAX / N) return fail(RLK_ERR_SHAPE, "N * k overflows");
-    s = check_head_cap(softcap, "softcap");
-    if (s != RLK_OK) return s;
-    (void)logits;
-    (void)targets;
+}  // extern "C"
+
+namespace {
+
+using rlk::RowMap;
+
+RowMap plain_rows(int64_t N, int64_t ld) { return RowMap{N > 0 ? N : 1, 0, ld}; }
+
+// Validate a row layout of N rows of V elements (es bytes each).  `output`:
+// the rows are written, so they must not overlap.
+rlk_status check_rows(const rlk_rows* r, int64_t N, int64_t V, int64_t es, const char* name,
+                      bool output, RowMap* m) {
+    if (!r) return fail(RLK_ERR_ARG, "%s: layout pointer is null", name);
+    const int64_t T = r->rows_per_batch, sb = r->batch_stride, st = r->row_stride;
+    if (T < 1) return fail(RLK_ERR_SHAPE, "%s: rows_per_batch must be >= 1", name);
+    if (sb < 0 || st < 0) return fail(RLK_ERR_SHAPE, "%s: strides must be >= 0", name);
+    const int64_t B = N > 0 ? (N + T - 1) / T : 0;
+    if (N > 0) {
+        // the last element touched: (B-1) sb + (min(N,T)-1) st + V - 1 must fit
+        const int64_t tmax = (N < T ? N : T) - 1;
+        const long double last = (long double)(B - 1) * sb + (long double)tmax * st + V;
+        if (last * es > (long double)INT64_MAX)
+            return fail(RLK_ERR_SHAPE, "%s: layout overflows 64-bit offsets", name);
+    }
+    if (output && N > 1) {
+        const int64_t Tn = N < T ? N : T;
+        const bool rows_ok = Tn == 1 || st >= V;
+        const bool batch_major = B == 1 || sb >= (Tn - 1) * st + V;
+        const bool time_major = Tn == 1 || st >= (B - 1) * sb + V;
+        if (!((rows_ok && batch_major) || (sb >= V && time_major)))
+            return fail(RLK_ERR_SHAPE, "%s: output rows overlap", name);
+    }
+    // (input rows may overlap: a broadcast view is read, never written)
+    *m = RowMap{T, sb, st};
     return RLK_OK;
 }
 
-rlk_status rlk_logp_fwd(const void* logits, rlk_dtype dtype, int64_t N, int64_t V, int64_t ld,
-                        const int64_t* targets, int64_t k, float softcap, float* logp,
-                        void* stats, void* stream) {
-    rlk_status s = logp_common(logits, dtype, N, V, ld, targets, k, softcap);
-    if (s != RLK_OK) return s;
+bool rows_aligned(const void* base, const RowMap& m, int64_t es) {
+    return aligned16(base) && (m.st * es) % 16 == 0 && (m.sb * es) % 16 == 0;
+}
+
+rlk_status logp_fwd_impl(const void* logits, rlk_dtype dtype, int64_t N, int64_t V,
+                         const RowMap& mx, const int64_t* targets, int64_t k, float softcap,
+                         float* logp, void* stats, void* stream) {
     if (N == 0) return ok();
     if (!logits || !targets || !logp || !stats)
         return fail(RLK_ERR_ARG, "logits, targets, logp and stats must be non-null when N > 0");
     DeviceBinding dev;
-    s = dev.bind({{logits, "logits"}, {targets, "targets"}, {logp, "logp"}, {stats, "stats"}});
+    rlk_status s = dev.bind({{logits, "logits"}, {targets, "targets"}, {logp, "logp"},
+                             {stats, "stats"}});
     if (s != RLK_OK) return s;
     rlk::FwdParams p{};
     p.x = logits;
     p.N = N;
     p.V = V;
-    p.ldx = ld;
+    p.mx = mx;
+    p.my = mx;
     p.targets = targets;
     p.k = k;
     p.kx = cap_k(softcap);
     p.scx = cap_sc(softcap);
     p.out = logp;
     p.stats = stats;
-    const bool al = aligned16(logits) && (ld * esize(dtype)) % 16 == 0;
+    const bool al = rows_aligned(logits, mx, esize(dtype));
     return launched(rlk::launch_fwd(rlk::kHeadLogp, dtype, softcap != 0.0f, false, al, p,
                                     static_cast<hipStream_t>(stream)),
                     "logp_fwd");
 }
 
-rlk_status rlk_logp_bwd(const void* logits, rlk_dtype dtype, int64_t N, int64_t V, int64_t ld,
-                        const int64_t* targets, int64_t k, float softcap, const void* stats,
-                        const float* grad_logp, void* grad_logits, void* stream) {
-    rlk_status s = logp_common(logits, dtype, N, V, ld, targets, k, softcap);
-    if (s != RLK_OK) return s;
+rlk_status logp_bwd_impl(const void* logits, rlk_dtype dtype, int64_t N, int64_t V,
+                         const RowMap& mx, const int64_t* targets, int64_t k, float softcap,
+                         const void* stats, const float* grad_logp, void* grad_logits,
+                         const RowMap& mg, void* stream) {
     if (N == 0) return ok();
     if (!logits || !targets || !stats || !grad_logp || !grad_logits)
         return fail(RLK_ERR_ARG, "null pointer with N > 0");
     DeviceBinding dev;
-    s = dev.bind({{logits, "logits"}, {targets, "targets"}, {stats, "stats"},
-                  {grad_logp, "grad_logp"}, {grad_logits, "grad_logits"}});
+    rlk_status s = dev.bind({{logits, "logits"}, {targets, "targets"}, {stats, "stats"},
+                             {grad_logp, "grad_logp"}, {grad_logits, "grad_logits"}});
     if (s != RLK_OK) return s;
     rlk::BwdParams p{};
     p.x = logits;
     p.N = N;
     p.V = V;
-    p.ldx = ld;
+    p.mx = mx;
+    p.my = mx;
+    p.mg = mg;
     p.targets = targets;
     p.k = k;
     p.kx = cap_k(softcap);
@@ -260,162 +287,310 @@ rlk_status rlk_logp_bwd(const void* logits, rlk_dtype dtype, int64_t N, int64_t 
     p.stats = stats;
     p.g = grad_logp;
     p.gx = grad_logits;
-    const bool al = aligned16(logits) && (ld * esize(dtype)) % 16 == 0 && aligned16(grad_logits) &&
-                    (V * esize(dtype)) % 16 == 0;
+    const int64_t es = esize(dtype);
+    const bool al = rows_aligned(logits, mx, es) && rows_aligned(grad_logits, mg, es);
     return launched(rlk::launch_bwd(rlk::kHeadLogp, dtype, softcap != 0.0f, false, al, p,
                                     static_cast<hipStream_t>(stream)),
                     "logp_bwd");
 }
 
-// -------------------------------------------------------------- entropy
-
-rlk_status rlk_entropy_fwd(const void* logits, rlk_dtype dtype, int64_t N, int64_t V, int64_t ld,
-                           float softcap, float* entropy, void* stats, void* stream) {
-    if (!dtype_ok(dtype)) return fail(RLK_ERR_DTYPE, "logits dtype must be RLK_F32, RLK_BF16 or RLK_F16");
-    rlk_status s = check_matrix(N, V, ld, esize(dtype), "logits");
-    if (s != RLK_OK) return s;
-    s = check_head_cap(softcap, "softcap");
-    if (s != RLK_OK) return s;
+rlk_status entropy_fwd_impl(const void* logits, rlk_dtype dtype, int64_t N, int64_t V,
+                            const RowMap& mx, float softcap, float* entropy, void* stats,
+                            void* stream) {
     if (N == 0) return ok();
     if (!logits || !entropy || !stats)
         return fail(RLK_ERR_ARG, "logits, entropy and stats must be non-null when N > 0");
     DeviceBinding dev;
-    s = dev.bind({{logits, "logits"}, {entropy, "entropy"}, {stats, "stats"}});
+    rlk_status s = dev.bind({{logits, "logits"}, {entropy, "entropy"}, {stats, "stats"}});
     if (s != RLK_OK) return s;
     rlk::FwdParams p{};
     p.x = logits;
     p.N = N;
     p.V = V;
-    p.ldx = ld;
+    p.mx = mx;
+    p.my = mx;
     p.k = 1;
     p.kx = cap_k(softcap);
     p.scx = cap_sc(softcap);
     p.out = entropy;
     p.stats = stats;
-    const bool al = aligned16(logits) && (ld * esize(dtype)) % 16 == 0;
+    const bool al = rows_aligned(logits, mx, esize(dtype));
     return launched(rlk::launch_fwd(rlk::kHeadEntropy, dtype, softcap != 0.0f, false, al, p,
                                     static_cast<hipStream_t>(stream)),
                     "entropy_fwd");
 }
 
-rlk_status rlk_entropy_bwd(const void* logits, rlk_dtype dtype, int64_t N, int64_t V, int64_t ld,
-                           float softcap, const void* stats, const float* grad_entropy,
-                           void* grad_logits, void* stream) {
-    if (!dtype_ok(dtype)) return fail(RLK_ERR_DTYPE, "logits dtype must be RLK_F32, RLK_BF16 or RLK_F16");
-    rlk_status s = check_matrix(N, V, ld, esize(dtype), "logits");
-    if (s != RLK_OK) return s;
-    s = check_head_cap(softcap, "softcap");
-    if (s != RLK_OK) return s;
+rlk_status entropy_bwd_impl(const void* logits, rlk_dtype dtype, int64_t N, int64_t V,
+                            const RowMap& mx, float softcap, const void* stats,
+                            const float* grad_entropy, void* grad_logits, const RowMap& mg,
+                            void* stream) {
     if (N == 0) return ok();
     if (!logits || !stats || !grad_entropy || !grad_logits)
         return fail(RLK_ERR_ARG, "null pointer with N > 0");
     DeviceBinding dev;
-    s = dev.bind({{logits, "logits"}, {stats, "stats"}, {grad_entropy, "grad_entropy"},
-                  {grad_logits, "grad_logits"}});
+    rlk_status s = dev.bind({{logits, "logits"}, {stats, "stats"},
+                             {grad_entropy, "grad_entropy"}, {grad_logits, "grad_logits"}});
     if (s != RLK_OK) return s;
     rlk::BwdParams p{};
     p.x = logits;
     p.N = N;
     p.V = V;
-    p.ldx = ld;
+    p.mx = mx;
+    p.my = mx;
+    p.mg = mg;
     p.k = 1;
     p.kx = cap_k(softcap);
     p.scx = cap_sc(softcap);
     p.stats = stats;
     p.g = grad_entropy;
     p.gx = grad_logits;
-    const bool al = aligned16(logits) && (ld * esize(dtype)) % 16 == 0 && aligned16(grad_logits) &&
-                    (V * esize(dtype)) % 16 == 0;
+    const int64_t es = esize(dtype);
+    const bool al = rows_aligned(logits, mx, es) && rows_aligned(grad_logits, mg, es);
     return launched(rlk::launch_bwd(rlk::kHeadEntropy, dtype, softcap != 0.0f, false, al, p,
                                     static_cast<hipStream_t>(stream)),
                     "entropy_bwd");
 }
 
-// ------------------------------------------------------------------- KL
-
-static rlk_status kl_common(rlk_dtype dtype, int64_t N, int64_t V, int64_t ld_policy,
-                            int64_t ld_ref, rlk_kl_dir dir, float cp, float cr) {
-    if (!dtype_ok(dtype)) return fail(RLK_ERR_DTYPE, "logits dtype must be RLK_F32, RLK_BF16 or RLK_F16");
-    rlk_status s = check_matrix(N, V, ld_policy, esize(dtype), "policy");
-    if (s != RLK_OK) return s;
-    s = check_matrix(N, V, ld_ref, esize(dtype), "ref");
-    if (s != RLK_OK) return s;
-    if (dir != RLK_KL_REVERSE && dir != RLK_KL_FORWARD)
-        return fail(RLK_ERR_ARG, "dir must be RLK_KL_REVERSE or RLK_KL_FORWARD, got %d", (int)dir);
-    s = check_head_cap(cp, "softcap_policy");
-    if (s != RLK_OK) return s;
-    return check_head_cap(cr, "softcap_ref");
-}
-
-rlk_status rlk_kl_fwd(const void* policy, const void* ref, rlk_dtype dtype, int64_t N, int64_t V,
-                      int64_t ld_policy, int64_t ld_ref, rlk_kl_dir dir, float softcap_policy,
-                      float softcap_ref, float* kl, void* stats, void* stream) {
-    rlk_status s = kl_common(dtype, N, V, ld_policy, ld_ref, dir, softcap_policy, softcap_ref);
-    if (s != RLK_OK) return s;
+rlk_status kl_fwd_impl(const void* policy, const void* ref, rlk_dtype dtype, int64_t N, int64_t V,
+                       const RowMap& mp, const RowMap& mr, rlk_kl_dir dir, float cp, float cr,
+                       float* kl, void* stats, void* stream) {
     if (N == 0) return ok();
     if (!policy || !ref || !kl || !stats)
         return fail(RLK_ERR_ARG, "policy, ref, kl and stats must be non-null when N > 0");
     DeviceBinding dev;
-    s = dev.bind({{policy, "policy"}, {ref, "ref"}, {kl, "kl"}, {stats, "stats"}});
+    rlk_status s = dev.bind({{policy, "policy"}, {ref, "ref"}, {kl, "kl"}, {stats, "stats"}});
     if (s != RLK_OK) return s;
     rlk::FwdParams p{};
     p.x = policy;
     p.y = ref;
     p.N = N;
     p.V = V;
-    p.ldx = ld_policy;
-    p.ldy = ld_ref;
+    p.mx = mp;
+    p.my = mr;
     p.k = 1;
-    p.kx = cap_k(softcap_policy);
-    p.ky = cap_k(softcap_ref);
-    p.scx = cap_sc(softcap_policy);
-    p.scy = cap_sc(softcap_ref);
+    p.kx = cap_k(cp);
+    p.ky = cap_k(cr);
+    p.scx = cap_sc(cp);
+    p.scy = cap_sc(cr);
     p.out = kl;
     p.stats = stats;
     const int64_t es = esize(dtype);
-    const bool al = aligned16(policy) && aligned16(ref) && (ld_policy * es) % 16 == 0 &&
-                    (ld_ref * es) % 16 == 0;
+    const bool al = rows_aligned(policy, mp, es) && rows_aligned(ref, mr, es);
     const int head = dir == RLK_KL_REVERSE ? rlk::kHeadKLReverse : rlk::kHeadKLForward;
-    return launched(rlk::launch_fwd(head, dtype, softcap_policy != 0.0f, softcap_ref != 0.0f, al,
-                                    p, static_cast<hipStream_t>(stream)),
+    return launched(rlk::launch_fwd(head, dtype, cp != 0.0f, cr != 0.0f, al, p,
+                                    static_cast<hipStream_t>(stream)),
                     "kl_fwd");
 }
 
-rlk_status rlk_kl_bwd(const void* policy, const void* ref, rlk_dtype dtype, int64_t N, int64_t V,
-                      int64_t ld_policy, int64_t ld_ref, rlk_kl_dir dir, float softcap_policy,
-                      float softcap_ref, const void* stats, const float* grad_kl,
-                      void* grad_policy, void* stream) {
-    rlk_status s = kl_common(dtype, N, V, ld_policy, ld_ref, dir, softcap_policy, softcap_ref);
-    if (s != RLK_OK) return s;
+rlk_status kl_bwd_impl(const void* policy, const void* ref, rlk_dtype dtype, int64_t N, int64_t V,
+                       const RowMap& mp, const RowMap& mr, rlk_kl_dir dir, float cp, float cr,
+                       const void* stats, const float* grad_kl, void* grad_policy,
+                       const RowMap& mg, void* stream) {
     if (N == 0) return ok();
     if (!policy || !ref || !stats || !grad_kl || !grad_policy)
         return fail(RLK_ERR_ARG, "null pointer with N > 0");
     DeviceBinding dev;
-    s = dev.bind({{policy, "policy"}, {ref, "ref"}, {stats, "stats"}, {grad_kl, "grad_kl"},
-                  {grad_policy, "grad_policy"}});
+    rlk_status s = dev.bind({{policy, "policy"}, {ref, "ref"}, {stats, "stats"},
+                             {grad_kl, "grad_kl"}, {grad_policy, "grad_policy"}});
     if (s != RLK_OK) return s;
     rlk::BwdParams p{};
     p.x = policy;
     p.y = ref;
     p.N = N;
     p.V = V;
-    p.ldx = ld_policy;
-    p.ldy = ld_ref;
+    p.mx = mp;
+    p.my = mr;
+    p.mg = mg;
     p.k = 1;
-    p.kx = cap_k(softcap_policy);
-    p.ky = cap_k(softcap_ref);
-    p.scx = cap_sc(softcap_policy);
-    p.scy = cap_sc(softcap_ref);
+    p.kx = cap_k(cp);
+    p.ky = cap_k(cr);
+    p.scx = cap_sc(cp);
+    p.scy = cap_sc(cr);
     p.stats = stats;
     p.g = grad_kl;
     p.gx = grad_policy;
     const int64_t es = esize(dtype);
-    const bool al = aligned16(policy) && aligned16(ref) && (ld_policy * es) % 16 == 0 &&
-                    (ld_ref * es) % 16 == 0 && aligned16(grad_policy) && (V * es) % 16 == 0;
+    const bool al = rows_aligned(policy, mp, es) && rows_aligned(ref, mr, es) &&
+                    rows_aligned(grad_policy, mg, es);
     const int head = dir == RLK_KL_REVERSE ? rlk::kHeadKLReverse : rlk::kHeadKLForward;
-    return launched(rlk::launch_bwd(head, dtype, softcap_policy != 0.0f, softcap_ref != 0.0f, al,
-                                    p, static_cast<hipStream_t>(stream)),
+    return launched(rlk::launch_bwd(head, dtype, cp != 0.0f, cr != 0.0f, al, p,
+                                    static_cast<hipStream_t>(stream)),
                     "kl_bwd");
+}
+
+rlk_status check_common(rlk_dtype dtype, int64_t N, int64_t V, float cap, const char* capname) {
+    if (!dtype_ok(dtype))
+        return fail(RLK_ERR_DTYPE, "logits dtype must be RLK_F32, RLK_BF16 or RLK_F16");
+    if (N < 0) return fail(RLK_ERR_SHAPE, "N must be >= 0, got %lld", (long long)N);
+    if (V < 1) return fail(RLK_ERR_SHAPE, "V must be >= 1, got %lld", (long long)V);
+    if (V > INT32_MAX) return fail(RLK_ERR_SHAPE, "V must be < 2^31, got %lld", (long long)V);
+    return check_head_cap(cap, capname);
+}
+
+rlk_status check_k(int64_t N, int64_t k) {
+    if (k < 1 || k > RLK_MAX_TOPK)
+        return fail(RLK_ERR_SHAPE, "k must be in [1, %d], got %lld", RLK_MAX_TOPK, (long long)k);
+    if (N > 0 && k > INT64_MAX / N) return fail(RLK_ERR_SHAPE, "N * k overflows");
+    return RLK_OK;
+}
+
+rlk_status check_dir(rlk_kl_dir dir) {
+    if (dir != RLK_KL_REVERSE && dir != RLK_KL_FORWARD)
+        return fail(RLK_ERR_ARG, "dir must be RLK_KL_REVERSE or RLK_KL_FORWARD, got %d", (int)dir);
+    return RLK_OK;
+}
+
+#define RLK_TRY(expr)                          \
+    do {                                       \
+        const rlk_status s_ = (expr);          \
+        if (s_ != RLK_OK) return s_;           \
+    } while (0)
+
+}  // namespace
+
+extern "C" {
+
+// ------------------------------------------------------------ logprobs
+
+rlk_status rlk_logp_fwd(const void* logits, rlk_dtype dtype, int64_t N, int64_t V, int64_t ld,
+                        const int64_t* targets, int64_t k, float softcap, float* logp,
+                        void* stats, void* stream) {
+    RLK_TRY(check_common(dtype, N, V, softcap, "softcap"));
+    RLK_TRY(check_matrix(N, V, ld, esize(dtype), "logits"));
+    RLK_TRY(check_k(N, k));
+    return logp_fwd_impl(logits, dtype, N, V, plain_rows(N, ld), targets, k, softcap, logp, stats,
+                         stream);
+}
+
+rlk_status rlk_logp_bwd(const void* logits, rlk_dtype dtype, int64_t N, int64_t V, int64_t ld,
+                        const int64_t* targets, int64_t k, float softcap, const void* stats,
+                        const float* grad_logp, void* grad_logits, void* stream) {
+    RLK_TRY(check_common(dtype, N, V, softcap, "softcap"));
+    RLK_TRY(check_matrix(N, V, ld, esize(dtype), "logits"));
+    RLK_TRY(check_k(N, k));
+    return logp_bwd_impl(logits, dtype, N, V, plain_rows(N, ld), targets, k, softcap, stats,
+                         grad_logp, grad_logits, plain_rows(N, V), stream);
+}
+
+rlk_status rlk_logp_fwd_strided(const void* logits, rlk_dtype dtype, int64_t N, int64_t V,
+                                const rlk_rows* rows, const int64_t* targets, int64_t k,
+                                float softcap, float* logp, void* stats, void* stream) {
+    RLK_TRY(check_common(dtype, N, V, softcap, "softcap"));
+    RowMap mx;
+    RLK_TRY(check_rows(rows, N, V, esize(dtype), "logits", false, &mx));
+    RLK_TRY(check_k(N, k));
+    return logp_fwd_impl(logits, dtype, N, V, mx, targets, k, softcap, logp, stats, stream);
+}
+
+rlk_status rlk_logp_bwd_strided(const void* logits, rlk_dtype dtype, int64_t N, int64_t V,
+                                const rlk_rows* rows, const int64_t* targets, int64_t k,
+                                float softcap, const void* stats, const float* grad_logp,
+                                void* grad_logits, const rlk_rows* grad_rows, void* stream) {
+    RLK_TRY(check_common(dtype, N, V, softcap, "softcap"));
+    RowMap mx, mg;
+    RLK_TRY(check_rows(rows, N, V, esize(dtype), "logits", false, &mx));
+    RLK_TRY(check_rows(grad_rows, N, V, esize(dtype), "grad_logits", true, &mg));
+    RLK_TRY(check_k(N, k));
+    return logp_bwd_impl(logits, dtype, N, V, mx, targets, k, softcap, stats, grad_logp,
+                         grad_logits, mg, stream);
+}
+
+// -------------------------------------------------------------- entropy
+
+rlk_status rlk_entropy_fwd(const void* logits, rlk_dtype dtype, int64_t N, int64_t V, int64_t ld,
+                           float softcap, float* entropy, void* stats, void* stream) {
+    RLK_TRY(check_common(dtype, N, V, softcap, "softcap"));
+    RLK_TRY(check_matrix(N, V, ld, esize(dtype), "logits"));
+    return entropy_fwd_impl(logits, dtype, N, V, plain_rows(N, ld), softcap, entropy, stats,
+                            stream);
+}
+
+rlk_status rlk_entropy_bwd(const void* logits, rlk_dtype dtype, int64_t N, int64_t V, int64_t ld,
+                           float softcap, const void* stats, const float* grad_entropy,
+                           void* grad_logits, void* stream) {
+    RLK_TRY(check_common(dtype, N, V, softcap, "softcap"));
+    RLK_TRY(check_matrix(N, V, ld, esize(dtype), "logits"));
+    return entropy_bwd_impl(logits, dtype, N, V, plain_rows(N, ld), softcap, stats, grad_entropy,
+                            grad_logits, plain_rows(N, V), stream);
+}
+
+rlk_status rlk_entropy_fwd_strided(const void* logits, rlk_dtype dtype, int64_t N, int64_t V,
+                                   const rlk_rows* rows, float softcap, float* entropy,
+                                   void* stats, void* stream) {
+    RLK_TRY(check_common(dtype, N, V, softcap, "softcap"));
+    RowMap mx;
+    RLK_TRY(check_rows(rows, N, V, esize(dtype), "logits", false, &mx));
+    return entropy_fwd_impl(logits, dtype, N, V, mx, softcap, entropy, stats, stream);
+}
+
+rlk_status rlk_entropy_bwd_strided(const void* logits, rlk_dtype dtype, int64_t N, int64_t V,
+                                   const rlk_rows* rows, float softcap, const void* stats,
+                                   const float* grad_entropy, void* grad_logits,
+                                   const rlk_rows* grad_rows, void* stream) {
+    RLK_TRY(check_common(dtype, N, V, softcap, "softcap"));
+    RowMap mx, mg;
+    RLK_TRY(check_rows(rows, N, V, esize(dtype), "logits", false, &mx));
+    RLK_TRY(check_rows(grad_rows, N, V, esize(dtype), "grad_logits", true, &mg));
+    return entropy_bwd_impl(logits, dtype, N, V, mx, softcap, stats, grad_entropy, grad_logits,
+                            mg, stream);
+}
+
+// ------------------------------------------------------------------- KL
+
+rlk_status rlk_kl_fwd(const void* policy, const void* ref, rlk_dtype dtype, int64_t N, int64_t V,
+                      int64_t ld_policy, int64_t ld_ref, rlk_kl_dir dir, float softcap_policy,
+                      float softcap_ref, float* kl, void* stats, void* stream) {
+    RLK_TRY(check_common(dtype, N, V, softcap_policy, "softcap_policy"));
+    RLK_TRY(check_head_cap(softcap_ref, "softcap_ref"));
+    RLK_TRY(check_matrix(N, V, ld_policy, esize(dtype), "policy"));
+    RLK_TRY(check_matrix(N, V, ld_ref, esize(dtype), "ref"));
+    RLK_TRY(check_dir(dir));
+    return kl_fwd_impl(policy, ref, dtype, N, V, plain_rows(N, ld_policy), plain_rows(N, ld_ref),
+                       dir, softcap_policy, softcap_ref, kl, stats, stream);
+}
+
+rlk_status rlk_kl_bwd(const void* policy, const void* ref, rlk_dtype dtype, int64_t N, int64_t V,
+                      int64_t ld_policy, int64_t ld_ref, rlk_kl_dir dir, float softcap_policy,
+                      float softcap_ref, const void* stats, const float* grad_kl,
+                      void* grad_policy, void* stream) {
+    RLK_TRY(check_common(dtype, N, V, softcap_policy, "softcap_policy"));
+    RLK_TRY(check_head_cap(softcap_ref, "softcap_ref"));
+    RLK_TRY(check_matrix(N, V, ld_policy, esize(dtype), "policy"));
+    RLK_TRY(check_matrix(N, V, ld_ref, esize(dtype), "ref"));
+    RLK_TRY(check_dir(dir));
+    return kl_bwd_impl(policy, ref, dtype, N, V, plain_rows(N, ld_policy), plain_rows(N, ld_ref),
+                       dir, softcap_policy, softcap_ref, stats, grad_kl, grad_policy,
+                       plain_rows(N, V), stream);
+}
+
+rlk_status rlk_kl_fwd_strided(const void* policy, const void* ref, rlk_dtype dtype, int64_t N,
+                              int64_t V, const rlk_rows* policy_rows, const rlk_rows* ref_rows,
+                              rlk_kl_dir dir, float softcap_policy, float softcap_ref, float* kl,
+                              void* stats, void* stream) {
+    RLK_TRY(check_common(dtype, N, V, softcap_policy, "softcap_policy"));
+    RLK_TRY(check_head_cap(softcap_ref, "softcap_ref"));
+    RowMap mp, mr;
+    RLK_TRY(check_rows(policy_rows, N, V, esize(dtype), "policy", false, &mp));
+    RLK_TRY(check_rows(ref_rows, N, V, esize(dtype), "ref", false, &mr));
+    RLK_TRY(check_dir(dir));
+    return kl_fwd_impl(policy, ref, dtype, N, V, mp, mr, dir, softcap_policy, softcap_ref, kl,
+                       stats, stream);
+}
+
+rlk_status rlk_kl_bwd_strided(const void* policy, const void* ref, rlk_dtype dtype, int64_t N,
+                              int64_t V, const rlk_rows* policy_rows, const rlk_rows* ref_rows,
+                              rlk_kl_dir dir, float softcap_policy, float softcap_ref,
+                              const void* stats, const float* grad_kl, void* grad_policy,
+                              const rlk_rows* grad_rows, void* stream) {
+    RLK_TRY(check_common(dtype, N, V, softcap_policy, "softcap_policy"));
+    RLK_TRY(check_head_cap(softcap_ref, "softcap_ref"));
+    RowMap mp, mr, mg;
+    RLK_TRY(check_rows(policy_rows, N, V, esize(dtype), "policy", false, &mp));
+    RLK_TRY(check_rows(ref_rows, N, V, esize(dtype), "ref", false, &mr));
+    RLK_TRY(check_rows(grad_rows, N, V, esize(dtype), "grad_policy", true, &mg));
+    RLK_TRY(check_dir(dir));
+    return kl_bwd_impl(policy, ref, dtype, N, V, mp, mr, dir, softcap_policy, softcap_ref, stats,
+                       grad_kl, grad_policy, mg, stream);
 }
 
 }  // extern "C"

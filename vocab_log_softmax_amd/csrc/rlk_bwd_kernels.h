@@ -56,9 +56,9 @@ __global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void bwd_kernel(BwdParams p) {
         const int64_t row = p.N - 1 - rit;
         const int64_t gbeg = seg * gps, gend = gbeg + gps < ngroups ? gbeg + gps : ngroups;
         const int64_t cbeg = gbeg * step * kChunk, cend = gend * step * kChunk;  // columns
-        const S* __restrict__ xa = static_cast<const S*>(p.x) + row * p.ldx;
-        const S* __restrict__ xb = KL ? static_cast<const S*>(p.y) + row * p.ldy : nullptr;
-        S* __restrict__ gx = static_cast<S*>(p.gx) + row * p.V;
+        const S* __restrict__ xa = static_cast<const S*>(p.x) + p.mx.offset(row);
+        const S* __restrict__ xb = KL ? static_cast<const S*>(p.y) + p.my.offset(row) : nullptr;
+        S* __restrict__ gx = static_cast<S*>(p.gx) + p.mg.offset(row);
 
         const RowStats rs = stats[row];
 

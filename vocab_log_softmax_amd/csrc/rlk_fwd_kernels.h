@@ -127,7 +127,7 @@ __global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void fwd1_kernel(FwdParams p) 
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     RowStats* stats = static_cast<RowStats*>(p.stats);
     for (int64_t row = blockIdx.x; row < p.N; row += gridDim.x) {
-        const S* __restrict__ x = static_cast<const S*>(p.x) + row * p.ldx;
+        const S* __restrict__ x = static_cast<const S*>(p.x) + p.mx.offset(row);
         // Prefetch this lane's first target slot and its logit.
         int64_t t0 = -1;
         float xt0 = 0.0f;
@@ -197,8 +197,8 @@ __global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void fwdkl_kernel(FwdParams p)
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     RowStats* stats = static_cast<RowStats*>(p.stats);
     for (int64_t row = blockIdx.x; row < p.N; row += gridDim.x) {
-        const S* __restrict__ xa = static_cast<const S*>(p.x) + row * p.ldx;
-        const S* __restrict__ xb = static_cast<const S*>(p.y) + row * p.ldy;
+        const S* __restrict__ xa = static_cast<const S*>(p.x) + p.mx.offset(row);
+        const S* __restrict__ xb = static_cast<const S*>(p.y) + p.my.offset(row);
         StatKL st = statkl_init<REVERSE>();
         for_each_group2<BLOCK, U, S, CAPA, CAPB, ALIGNED, kFwdPipe>(
             xa, xb, p.V, p.kx, p.ky,

@@ -77,10 +77,22 @@ constexpr int64_t kBwdSmallRows = 512;      // below this many rows
 constexpr int64_t kBwdTargetItems = 2048;   // aim for this many (row, segment) items
 constexpr int kMaxGrid = 1 << 20;
 
+// Row i of a (possibly two-stride) view starts at element
+// (i / T) * sb + (i % T) * st: a [B, T, V] view with strides (sb, st, 1).
+// A plain [N, V] matrix with row stride ld is {T = N, sb = 0, st = ld}.
+struct RowMap {
+    int64_t T, sb, st;
+    __host__ __device__ int64_t offset(int64_t i) const {
+        const int64_t b = i / T;
+        return b * sb + (i - b * T) * st;
+    }
+};
+
 struct FwdParams {
     const void* x;   // logits (KL: policy)
     const void* y;   // KL reference (else unused)
-    int64_t N, V, ldx, ldy;
+    int64_t N, V;
+    RowMap mx, my;   // row layouts of x and y
     const int64_t* targets;  // logp: [N, k]
     int64_t k;
     float kx, ky;    // softcap multiplier -2 log2(e) / c (unused when off)
@@ -92,7 +104,8 @@ struct FwdParams {
 struct BwdParams {
     const void* x;
     const void* y;
-    int64_t N, V, ldx, ldy;
+    int64_t N, V;
+    RowMap mx, my, mg;  // row layouts of x, y and of the gradient output
     const int64_t* targets;
     int64_t k;
     float kx, ky, scx, scy;

@@ -30,7 +30,15 @@ STATUS = {0: "RLK_OK", 1: "RLK_ERR_ARG", 2: "RLK_ERR_DTYPE", 3: "RLK_ERR_SHAPE",
 
 EXPORTS = ("rlk_abi_version", "rlk_stats_bytes", "rlk_status_str", "rlk_last_error",
            "rlk_softcap_fwd", "rlk_softcap_bwd", "rlk_logp_fwd", "rlk_logp_bwd",
-           "rlk_entropy_fwd", "rlk_entropy_bwd", "rlk_kl_fwd", "rlk_kl_bwd")
+           "rlk_entropy_fwd", "rlk_entropy_bwd", "rlk_kl_fwd", "rlk_kl_bwd",
+           "rlk_logp_fwd_strided", "rlk_logp_bwd_strided", "rlk_entropy_fwd_strided",
+           "rlk_entropy_bwd_strided", "rlk_kl_fwd_strided", "rlk_kl_bwd_strided")
+
+
+class RlkRows(ctypes.Structure):
+    """ctypes mirror of rlk_rows: row i = (i // T, i % T) at b*batch_stride + t*row_stride."""
+    _fields_ = [("rows_per_batch", ctypes.c_int64), ("batch_stride", ctypes.c_int64),
+                ("row_stride", ctypes.c_int64)]
 
 
 class RLKError(RuntimeError):
@@ -52,6 +60,7 @@ def load_library(path: str = LIB_PATH):
                           "(there is no fallback implementation)")
     lib = ctypes.CDLL(path)
     vp, i64, f32, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int
+    rp = ctypes.POINTER(RlkRows)
     sig = {
         "rlk_abi_version": ([], ci),
         "rlk_stats_bytes": ([ci, i64, i64], ctypes.c_size_t),
@@ -65,6 +74,13 @@ def load_library(path: str = LIB_PATH):
         "rlk_entropy_bwd": ([vp, ci, i64, i64, i64, f32, vp, vp, vp, vp], ci),
         "rlk_kl_fwd": ([vp, vp, ci, i64, i64, i64, i64, ci, f32, f32, vp, vp, vp], ci),
         "rlk_kl_bwd": ([vp, vp, ci, i64, i64, i64, i64, ci, f32, f32, vp, vp, vp, vp], ci),
+        "rlk_logp_fwd_strided": ([vp, ci, i64, i64, rp, vp, i64, f32, vp, vp, vp], ci),
+        "rlk_logp_bwd_strided": ([vp, ci, i64, i64, rp, vp, i64, f32, vp, vp, vp, rp, vp], ci),
+        "rlk_entropy_fwd_strided": ([vp, ci, i64, i64, rp, f32, vp, vp, vp], ci),
+        "rlk_entropy_bwd_strided": ([vp, ci, i64, i64, rp, f32, vp, vp, vp, rp, vp], ci),
+        "rlk_kl_fwd_strided": ([vp, vp, ci, i64, i64, rp, rp, ci, f32, f32, vp, vp, vp], ci),
+        "rlk_kl_bwd_strided": ([vp, vp, ci, i64, i64, rp, rp, ci, f32, f32, vp, vp, vp, rp,
+                                vp], ci),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -110,6 +126,25 @@ def _rows(x: torch.Tensor, what: str) -> torch.Tensor:
     if x.stride(1) != 1 or x.stride(0) < x.shape[1]:
         x = x.contiguous()
     return x
+
+
+def _view3(x: torch.Tensor, what: str) -> torch.Tensor:
+    """[B, T, V] view with a unit-stride vocabulary dimension (copy only if not)."""
+    if x.dim() != 3:
+        raise ValueError(f"{what} must be 3-D [B, T, V], got shape {tuple(x.shape)}")
+    if x.stride(2) != 1 and x.shape[2] > 1:
+        x = x.contiguous()
+    return x
+
+
+def rows_of(x: torch.Tensor) -> RlkRows:
+    """rlk_rows of a [B, T, V] (or [N, V]) view with unit-stride last dimension."""
+    if x.dim() == 2:
+        return RlkRows(max(1, x.shape[0]), 0, _ld(x))
+    B, T, V = x.shape
+    st = x.stride(1) if T > 1 else V
+    sb = x.stride(0) if B > 1 else T * st
+    return RlkRows(max(1, T), sb, st)
 
 
 def _ld(x: torch.Tensor) -> int:
@@ -210,6 +245,73 @@ def rlk_kl_bwd(policy, ref, direction, softcap_policy, softcap_ref, stats, grad_
           _ptr(stats), _ptr(grad_kl), _ptr(grad_policy), _stream(policy))
 
 
+def rlk_logp_fwd_strided(logits, targets, softcap, logp, stats) -> None:
+    B, T, V = logits.shape
+    N, k = B * T, targets.shape[-1]
+    _need(targets, torch.int64, (N, k), "targets")
+    _need(logp, torch.float32, (N, k), "logp")
+    r = rows_of(logits)
+    _call("rlk_logp_fwd_strided", _ptr(logits), _dtype_code(logits, "logits"), N, V,
+          ctypes.byref(r), _ptr(targets), k, float(softcap), _ptr(logp), _ptr(stats),
+          _stream(logits))
+
+
+def rlk_logp_bwd_strided(logits, targets, softcap, stats, grad_logp, grad_logits) -> None:
+    B, T, V = logits.shape
+    N, k = B * T, targets.shape[-1]
+    _need(targets, torch.int64, (N, k), "targets")
+    _need(grad_logp, torch.float32, (N, k), "grad_logp")
+    if grad_logits.dtype != logits.dtype or tuple(grad_logits.shape) != (B, T, V):
+        raise ValueError("grad_logits must be a [B, T, V] view in the logits dtype")
+    r, rg = rows_of(logits), rows_of(grad_logits)
+    _call("rlk_logp_bwd_strided", _ptr(logits), _dtype_code(logits, "logits"), N, V,
+          ctypes.byref(r), _ptr(targets), k, float(softcap), _ptr(stats), _ptr(grad_logp),
+          _ptr(grad_logits), ctypes.byref(rg), _stream(logits))
+
+
+def rlk_entropy_fwd_strided(logits, softcap, entropy, stats) -> None:
+    B, T, V = logits.shape
+    _need(entropy, torch.float32, (B * T,), "entropy")
+    r = rows_of(logits)
+    _call("rlk_entropy_fwd_strided", _ptr(logits), _dtype_code(logits, "logits"), B * T, V,
+          ctypes.byref(r), float(softcap), _ptr(entropy), _ptr(stats), _stream(logits))
+
+
+def rlk_entropy_bwd_strided(logits, softcap, stats, grad_entropy, grad_logits) -> None:
+    B, T, V = logits.shape
+    _need(grad_entropy, torch.float32, (B * T,), "grad_entropy")
+    if grad_logits.dtype != logits.dtype or tuple(grad_logits.shape) != (B, T, V):
+        raise ValueError("grad_logits must be a [B, T, V] view in the logits dtype")
+    r, rg = rows_of(logits), rows_of(grad_logits)
+    _call("rlk_entropy_bwd_strided", _ptr(logits), _dtype_code(logits, "logits"), B * T, V,
+          ctypes.byref(r), float(softcap), _ptr(stats), _ptr(grad_entropy), _ptr(grad_logits),
+          ctypes.byref(rg), _stream(logits))
+
+
+def rlk_kl_fwd_strided(policy, ref, direction, softcap_policy, softcap_ref, kl, stats) -> None:
+    B, T, V = policy.shape
+    if tuple(ref.shape) != (B, T, V) or ref.dtype != policy.dtype:
+        raise ValueError("policy and ref must have the same shape and dtype")
+    _need(kl, torch.float32, (B * T,), "kl")
+    rp, rr = rows_of(policy), rows_of(ref)
+    _call("rlk_kl_fwd_strided", _ptr(policy), _ptr(ref), _dtype_code(policy, "policy"), B * T, V,
+          ctypes.byref(rp), ctypes.byref(rr), int(direction), float(softcap_policy),
+          float(softcap_ref), _ptr(kl), _ptr(stats), _stream(policy))
+
+
+def rlk_kl_bwd_strided(policy, ref, direction, softcap_policy, softcap_ref, stats, grad_kl,
+                       grad_policy) -> None:
+    B, T, V = policy.shape
+    _need(grad_kl, torch.float32, (B * T,), "grad_kl")
+    if grad_policy.dtype != policy.dtype or tuple(grad_policy.shape) != (B, T, V):
+        raise ValueError("grad_policy must be a [B, T, V] view in the logits dtype")
+    rp, rr, rg = rows_of(policy), rows_of(ref), rows_of(grad_policy)
+    _call("rlk_kl_bwd_strided", _ptr(policy), _ptr(ref), _dtype_code(policy, "policy"), B * T, V,
+          ctypes.byref(rp), ctypes.byref(rr), int(direction), float(softcap_policy),
+          float(softcap_ref), _ptr(stats), _ptr(grad_kl), _ptr(grad_policy), ctypes.byref(rg),
+          _stream(policy))
+
+
 # ------------------------------------------------ allocating convenience layer
 
 def new_stats(head: int, N: int, V: int, device) -> torch.Tensor:
@@ -221,7 +323,19 @@ def _targets2d(targets: torch.Tensor, N: int) -> torch.Tensor:
     return t.contiguous() if t.dtype == torch.int64 else t.to(torch.int64).contiguous()
 
 
+# The allocating wrappers accept [N, V] matrices and [B, T, V] views (read in
+# place, e.g. logits[:, :-1]); outputs are [N] / [N, k] (or [B, T] / [B, T, k])
+# and gradients come back contiguous in the input's shape.
+
 def logp_fwd(logits, targets, softcap=0.0):
+    if logits.dim() == 3:
+        logits = _view3(logits, "logits")
+        B, T, V = logits.shape
+        t = _targets2d(targets, B * T)
+        out = torch.empty(t.shape, dtype=torch.float32, device=logits.device)
+        stats = new_stats(RLK_HEAD_LOGP, B * T, V, logits.device)
+        rlk_logp_fwd_strided(logits, t, softcap, out, stats)
+        return out.reshape(targets.shape), stats
     logits = _rows(logits, "logits")
     N, V = logits.shape
     t = _targets2d(targets, N)
@@ -231,7 +345,17 @@ def logp_fwd(logits, targets, softcap=0.0):
     return out.reshape(targets.shape), stats
 
 
-def logp_bwd(logits, targets, grad_logp, stats, softcap=0.0):
+def logp_bwd(logits, targets, grad_logp, stats, softcap=0.0, out=None):
+    """Gradient w.r.t. the logits; ``out`` may be a [B, T, V] view to write into."""
+    if logits.dim() == 3:
+        logits = _view3(logits, "logits")
+        B, T, V = logits.shape
+        t = _targets2d(targets, B * T)
+        g = grad_logp.reshape(t.shape).to(torch.float32).contiguous()
+        gx = out if out is not None else torch.empty((B, T, V), dtype=logits.dtype,
+                                                     device=logits.device)
+        rlk_logp_bwd_strided(logits, t, softcap, stats, g, gx)
+        return gx
     logits = _rows(logits, "logits")
     N, V = logits.shape
     t = _targets2d(targets, N)
@@ -242,6 +366,13 @@ def logp_bwd(logits, targets, grad_logp, stats, softcap=0.0):
 
 
 def entropy_fwd(logits, softcap=0.0):
+    if logits.dim() == 3:
+        logits = _view3(logits, "logits")
+        B, T, V = logits.shape
+        out = torch.empty(B * T, dtype=torch.float32, device=logits.device)
+        stats = new_stats(RLK_HEAD_ENTROPY, B * T, V, logits.device)
+        rlk_entropy_fwd_strided(logits, softcap, out, stats)
+        return out.reshape(B, T), stats
     logits = _rows(logits, "logits")
     N, V = logits.shape
     out = torch.empty(N, dtype=torch.float32, device=logits.device)
@@ -250,7 +381,15 @@ def entropy_fwd(logits, softcap=0.0):
     return out, stats
 
 
-def entropy_bwd(logits, grad_entropy, stats, softcap=0.0):
+def entropy_bwd(logits, grad_entropy, stats, softcap=0.0, out=None):
+    if logits.dim() == 3:
+        logits = _view3(logits, "logits")
+        B, T, V = logits.shape
+        gx = out if out is not None else torch.empty((B, T, V), dtype=logits.dtype,
+                                                     device=logits.device)
+        rlk_entropy_bwd_strided(logits, softcap, stats,
+                                grad_entropy.reshape(-1).to(torch.float32).contiguous(), gx)
+        return gx
     logits = _rows(logits, "logits")
     N, V = logits.shape
     gx = torch.empty((N, V), dtype=logits.dtype, device=logits.device)
@@ -259,6 +398,13 @@ def entropy_bwd(logits, grad_entropy, stats, softcap=0.0):
 
 
 def kl_fwd(policy, ref, direction=RLK_KL_REVERSE, softcap_policy=0.0, softcap_ref=0.0):
+    if policy.dim() == 3:
+        policy, ref = _view3(policy, "policy"), _view3(ref, "ref")
+        B, T, V = policy.shape
+        out = torch.empty(B * T, dtype=torch.float32, device=policy.device)
+        stats = new_stats(RLK_HEAD_KL, B * T, V, policy.device)
+        rlk_kl_fwd_strided(policy, ref, direction, softcap_policy, softcap_ref, out, stats)
+        return out.reshape(B, T), stats
     policy, ref = _rows(policy, "policy"), _rows(ref, "ref")
     N, V = policy.shape
     out = torch.empty(N, dtype=torch.float32, device=policy.device)
@@ -268,7 +414,15 @@ def kl_fwd(policy, ref, direction=RLK_KL_REVERSE, softcap_policy=0.0, softcap_re
 
 
 def kl_bwd(policy, ref, grad_kl, stats, direction=RLK_KL_REVERSE, softcap_policy=0.0,
-           softcap_ref=0.0):
+           softcap_ref=0.0, out=None):
+    if policy.dim() == 3:
+        policy, ref = _view3(policy, "policy"), _view3(ref, "ref")
+        B, T, V = policy.shape
+        gx = out if out is not None else torch.empty((B, T, V), dtype=policy.dtype,
+                                                     device=policy.device)
+        rlk_kl_bwd_strided(policy, ref, direction, softcap_policy, softcap_ref, stats,
+                           grad_kl.reshape(-1).to(torch.float32).contiguous(), gx)
+        return gx
     policy, ref = _rows(policy, "policy"), _rows(ref, "ref")
     N, V = policy.shape
     gx = torch.empty((N, V), dtype=policy.dtype, device=policy.device)
