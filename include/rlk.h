@@ -209,6 +209,57 @@ rlk_status rlk_kl_bwd_strided(const void* policy, const void* ref, rlk_dtype dty
                               const void* stats, const float* grad_kl, void* grad_policy,
                               const rlk_rows* grad_rows, void* stream);
 
+/* ------------------------------------------------- vocabulary shards
+ * The single-GPU half of vocabulary parallelism ("Add Triton kernels for
+ * vocab-parallel logprobs, entropy and KL", Changes and review comment:
+ * local statistics from one read, rescaled to the global maximum and summed;
+ * the mismatch flag travels with the maximum).  A shard holds the columns
+ * [v0, v0 + V_shard) of rows of width V_total.
+ *   1. each shard: rlk_*_fwd_partial -> one 32-byte record per row
+ *      (rlk_partial_bytes), and for logprobs the statistic input of every
+ *      target it owns ([N, k] floats, unowned slots 0);
+ *   2. gather the P records (and target values) in rank order into
+ *      [P, N] (and [P, N, k]) device buffers -- the only cross-rank step;
+ *   3. rlk_combine folds them in rank order with the merges of the row
+ *      kernels and writes the heads and the row record, identically on every
+ *      rank that combines the same gathered data;
+ *   4. backward per shard: rlk_logp_bwd_shard, or the plain
+ *      rlk_entropy_bwd / rlk_kl_bwd on the shard's columns with the combined
+ *      record.  A one-shard combine gives bitwise the plain forward. */
+#define RLK_MAX_SHARDS 64
+
+/* Bytes of N partial records (32 per row). */
+size_t rlk_partial_bytes(int64_t N);
+
+rlk_status rlk_logp_fwd_partial(const void* logits, rlk_dtype dtype, int64_t N, int64_t V_shard,
+                                int64_t ld, int64_t v0, int64_t V_total, const int64_t* targets,
+                                int64_t k, float softcap, void* partial, float* target_vals,
+                                void* stream);
+rlk_status rlk_entropy_fwd_partial(const void* logits, rlk_dtype dtype, int64_t N,
+                                   int64_t V_shard, int64_t ld, float softcap, void* partial,
+                                   void* stream);
+rlk_status rlk_kl_fwd_partial(const void* policy, const void* ref, rlk_dtype dtype, int64_t N,
+                              int64_t V_shard, int64_t ld_policy, int64_t ld_ref, rlk_kl_dir dir,
+                              float softcap_policy, float softcap_ref, void* partial,
+                              void* stream);
+
+/* Fold P shard records [P, N] (rank order; bounds = host array of P + 1
+ * increasing columns, bounds[0] = 0, bounds[P] = V_total) and write the
+ * head outputs (logp [N, k], entropy [N] or KL [N]) and the row record
+ * `stats` (rlk_stats_bytes).  Logprobs also needs targets [N, k],
+ * target_vals [P, N, k] and the softcap; `dir` is read for KL only. */
+rlk_status rlk_combine(rlk_head head, rlk_kl_dir dir, int64_t P, const int64_t* bounds, int64_t N,
+                       const void* partials, const int64_t* targets, int64_t k,
+                       const float* target_vals, float softcap, float* out, void* stats,
+                       void* stream);
+
+/* Logprobs backward of one shard with the combined record; targets are
+ * global column ids; grad_logits is [N, V_shard] contiguous. */
+rlk_status rlk_logp_bwd_shard(const void* logits, rlk_dtype dtype, int64_t N, int64_t V_shard,
+                              int64_t ld, int64_t v0, int64_t V_total, const int64_t* targets,
+                              int64_t k, float softcap, const void* stats,
+                              const float* grad_logp, void* grad_logits, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

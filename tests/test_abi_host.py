@@ -137,3 +137,37 @@ def test_strided_layout_validation(lib):
     assert st == DEVICE
     assert lib.rlk_kl_fwd_strided(None, None, 1, 0, 10, None, None, 0, F(0), F(0), None, None,
                                   None) == ARG  # layout pointers are required even for N = 0
+
+
+def test_shard_entry_points_validate(lib):
+    p = ctypes.c_void_p(16)
+    I64 = ctypes.c_int64
+    assert lib.rlk_partial_bytes(5) == 160 and lib.rlk_partial_bytes(0) == 0
+    # shard [v0, v0 + V_shard) must lie inside [0, V_total)
+    assert lib.rlk_logp_fwd_partial(p, 1, 4, 8, 8, 10, 16, p, 1, F(0), p, p, None) == SHAPE
+    assert lib.rlk_logp_fwd_partial(p, 1, 4, 8, 8, -1, 16, p, 1, F(0), p, p, None) == SHAPE
+    assert lib.rlk_logp_fwd_partial(p, 1, 4, 8, 6, 0, 16, p, 1, F(0), p, p, None) == SHAPE
+    assert lib.rlk_logp_fwd_partial(p, 1, 4, 8, 8, 0, 16, p, 0, F(0), p, p, None) == SHAPE
+    assert lib.rlk_logp_fwd_partial(p, 1, 4, 8, 8, 0, 16, p, 1, F(0), p, None, None) == ARG
+    assert lib.rlk_logp_fwd_partial(p, 1, 0, 8, 8, 0, 16, p, 1, F(0), p, p, None) == OK
+    assert lib.rlk_entropy_fwd_partial(p, 1, 4, -1, 8, F(0), p, None) == SHAPE
+    assert lib.rlk_entropy_fwd_partial(p, 1, 4, 8, 8, F(0), None, None) == ARG
+    assert lib.rlk_kl_fwd_partial(p, p, 1, 4, 8, 8, 8, 3, F(0), F(0), p, None) == ARG
+    assert lib.rlk_logp_bwd_shard(p, 1, 4, 8, 8, 12, 16, p, 1, F(0), p, p, p, None) == SHAPE
+    assert lib.rlk_logp_bwd_shard(p, 1, 4, 0, 0, 16, 16, p, 1, F(0), p, p, p, None) == OK
+    # combine: head, shard count, bounds
+    b = (I64 * 3)(0, 5, 9)
+    assert lib.rlk_combine(7, 0, 2, b, 4, p, p, 1, p, F(0), p, p, None) == ARG
+    assert lib.rlk_combine(2, 5, 2, b, 4, p, p, 1, p, F(0), p, p, None) == ARG
+    assert lib.rlk_combine(1, 0, 0, b, 4, p, p, 1, p, F(0), p, p, None) == SHAPE
+    assert lib.rlk_combine(1, 0, 65, b, 4, p, p, 1, p, F(0), p, p, None) == SHAPE
+    assert lib.rlk_combine(1, 0, 2, None, 4, p, p, 1, p, F(0), p, p, None) == ARG
+    assert lib.rlk_combine(1, 0, 2, (I64 * 3)(1, 5, 9), 4, p, p, 1, p, F(0), p, p,
+                           None) == SHAPE
+    assert lib.rlk_combine(1, 0, 2, (I64 * 3)(0, 5, 4), 4, p, p, 1, p, F(0), p, p,
+                           None) == SHAPE
+    assert lib.rlk_combine(1, 0, 2, (I64 * 3)(0, 0, 0), 4, p, p, 1, p, F(0), p, p,
+                           None) == SHAPE
+    assert lib.rlk_combine(0, 0, 2, b, 4, p, None, 1, p, F(0), p, p, None) == ARG
+    assert lib.rlk_combine(0, 0, 2, b, 4, p, p, 1, p, F(-1), p, p, None) == ARG
+    assert lib.rlk_combine(1, 0, 2, b, 0, None, None, 1, None, F(0), None, None, None) == OK

@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(PKG, "librlk.so")
 
 SOURCES = ["rlk_fwd_f32.hip", "rlk_fwd_bf16.hip", "rlk_fwd_f16.hip",
            "rlk_bwd_f32.hip", "rlk_bwd_bf16.hip", "rlk_bwd_f16.hip",
-           "rlk_softcap.hip", "rlk_api.cpp"]
+           "rlk_softcap.hip", "rlk_combine.hip", "rlk_api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -248,6 +248,7 @@ rlk_status logp_fwd_impl(const void* logits, rlk_dtype dtype, int64_t N, int64_t
     p.x = logits;
     p.N = N;
     p.V = V;
+    p.vtotal = V;
     p.mx = mx;
     p.my = mx;
     p.targets = targets;
@@ -277,6 +278,7 @@ rlk_status logp_bwd_impl(const void* logits, rlk_dtype dtype, int64_t N, int64_t
     p.x = logits;
     p.N = N;
     p.V = V;
+    p.vtotal = V;
     p.mx = mx;
     p.my = mx;
     p.mg = mg;
@@ -307,6 +309,7 @@ rlk_status entropy_fwd_impl(const void* logits, rlk_dtype dtype, int64_t N, int6
     p.x = logits;
     p.N = N;
     p.V = V;
+    p.vtotal = V;
     p.mx = mx;
     p.my = mx;
     p.k = 1;
@@ -335,6 +338,7 @@ rlk_status entropy_bwd_impl(const void* logits, rlk_dtype dtype, int64_t N, int6
     p.x = logits;
     p.N = N;
     p.V = V;
+    p.vtotal = V;
     p.mx = mx;
     p.my = mx;
     p.mg = mg;
@@ -365,6 +369,7 @@ rlk_status kl_fwd_impl(const void* policy, const void* ref, rlk_dtype dtype, int
     p.y = ref;
     p.N = N;
     p.V = V;
+    p.vtotal = V;
     p.mx = mp;
     p.my = mr;
     p.k = 1;
@@ -398,6 +403,7 @@ rlk_status kl_bwd_impl(const void* policy, const void* ref, rlk_dtype dtype, int
     p.y = ref;
     p.N = N;
     p.V = V;
+    p.vtotal = V;
     p.mx = mp;
     p.my = mr;
     p.mg = mg;
@@ -437,6 +443,23 @@ rlk_status check_k(int64_t N, int64_t k) {
 rlk_status check_dir(rlk_kl_dir dir) {
     if (dir != RLK_KL_REVERSE && dir != RLK_KL_FORWARD)
         return fail(RLK_ERR_ARG, "dir must be RLK_KL_REVERSE or RLK_KL_FORWARD, got %d", (int)dir);
+    return RLK_OK;
+}
+
+// A vocabulary shard: columns [v0, v0 + V_shard) of rows of width V_total,
+// stored with row stride ld.  An empty shard (V_shard = 0) is allowed.
+rlk_status check_shard(int64_t N, int64_t V_shard, int64_t ld, int64_t v0, int64_t V_total,
+                       int64_t es, const char* name) {
+    if (N < 0) return fail(RLK_ERR_SHAPE, "N must be >= 0, got %lld", (long long)N);
+    if (V_shard < 0) return fail(RLK_ERR_SHAPE, "%s: V_shard must be >= 0", name);
+    if (v0 < 0 || v0 + V_shard > V_total)
+        return fail(RLK_ERR_SHAPE, "%s: shard [%lld, %lld) is outside [0, %lld)", name,
+                    (long long)v0, (long long)(v0 + V_shard), (long long)V_total);
+    if (V_shard > 0 && ld < V_shard)
+        return fail(RLK_ERR_SHAPE, "%s: row stride %lld is smaller than V_shard = %lld", name,
+                    (long long)ld, (long long)V_shard);
+    if (N > 0 && V_shard > 0 && ld > INT64_MAX / es / N)
+        return fail(RLK_ERR_SHAPE, "%s: N * ld overflows 64-bit offsets", name);
     return RLK_OK;
 }
 
@@ -591,6 +614,190 @@ rlk_status rlk_kl_bwd_strided(const void* policy, const void* ref, rlk_dtype dty
     RLK_TRY(check_dir(dir));
     return kl_bwd_impl(policy, ref, dtype, N, V, mp, mr, dir, softcap_policy, softcap_ref, stats,
                        grad_kl, grad_policy, mg, stream);
+}
+
+// ------------------------------------------------- vocabulary shards
+
+size_t rlk_partial_bytes(int64_t N) { return N > 0 ? static_cast<size_t>(N) * 32u : 0u; }
+
+rlk_status rlk_logp_fwd_partial(const void* logits, rlk_dtype dtype, int64_t N, int64_t V_shard,
+                                int64_t ld, int64_t v0, int64_t V_total, const int64_t* targets,
+                                int64_t k, float softcap, void* partial, float* target_vals,
+                                void* stream) {
+    RLK_TRY(check_common(dtype, N, V_total, softcap, "softcap"));
+    RLK_TRY(check_shard(N, V_shard, ld, v0, V_total, esize(dtype), "logits"));
+    RLK_TRY(check_k(N, k));
+    if (N == 0) return ok();
+    if ((!logits && V_shard > 0) || !targets || !partial || !target_vals)
+        return fail(RLK_ERR_ARG, "null pointer with N > 0");
+    DeviceBinding dev;
+    RLK_TRY(dev.bind({{logits, "logits"}, {targets, "targets"}, {partial, "partial"},
+                      {target_vals, "target_vals"}}));
+    rlk::FwdParams p{};
+    p.x = logits;
+    p.N = N;
+    p.V = V_shard;
+    p.mx = plain_rows(N, ld);
+    p.my = p.mx;
+    p.targets = targets;
+    p.k = k;
+    p.kx = cap_k(softcap);
+    p.scx = cap_sc(softcap);
+    p.v0 = v0;
+    p.vtotal = V_total;
+    p.part = partial;
+    p.tvals = target_vals;
+    const bool al = rows_aligned(logits, p.mx, esize(dtype));
+    return launched(rlk::launch_fwd(rlk::kHeadLogp, dtype, softcap != 0.0f, false, al, p,
+                                    static_cast<hipStream_t>(stream)),
+                    "logp_fwd_partial");
+}
+
+rlk_status rlk_entropy_fwd_partial(const void* logits, rlk_dtype dtype, int64_t N,
+                                   int64_t V_shard, int64_t ld, float softcap, void* partial,
+                                   void* stream) {
+    RLK_TRY(check_common(dtype, N, V_shard > 0 ? V_shard : 1, softcap, "softcap"));
+    RLK_TRY(check_shard(N, V_shard, ld, 0, V_shard, esize(dtype), "logits"));
+    if (N == 0) return ok();
+    if ((!logits && V_shard > 0) || !partial) return fail(RLK_ERR_ARG, "null pointer with N > 0");
+    DeviceBinding dev;
+    RLK_TRY(dev.bind({{logits, "logits"}, {partial, "partial"}}));
+    rlk::FwdParams p{};
+    p.x = logits;
+    p.N = N;
+    p.V = V_shard;
+    p.vtotal = V_shard;
+    p.mx = plain_rows(N, ld);
+    p.my = p.mx;
+    p.k = 1;
+    p.kx = cap_k(softcap);
+    p.scx = cap_sc(softcap);
+    p.part = partial;
+    const bool al = rows_aligned(logits, p.mx, esize(dtype));
+    return launched(rlk::launch_fwd(rlk::kHeadEntropy, dtype, softcap != 0.0f, false, al, p,
+                                    static_cast<hipStream_t>(stream)),
+                    "entropy_fwd_partial");
+}
+
+rlk_status rlk_kl_fwd_partial(const void* policy, const void* ref, rlk_dtype dtype, int64_t N,
+                              int64_t V_shard, int64_t ld_policy, int64_t ld_ref, rlk_kl_dir dir,
+                              float softcap_policy, float softcap_ref, void* partial,
+                              void* stream) {
+    RLK_TRY(check_common(dtype, N, V_shard > 0 ? V_shard : 1, softcap_policy, "softcap_policy"));
+    RLK_TRY(check_head_cap(softcap_ref, "softcap_ref"));
+    RLK_TRY(check_shard(N, V_shard, ld_policy, 0, V_shard, esize(dtype), "policy"));
+    RLK_TRY(check_shard(N, V_shard, ld_ref, 0, V_shard, esize(dtype), "ref"));
+    RLK_TRY(check_dir(dir));
+    if (N == 0) return ok();
+    if (((!policy || !ref) && V_shard > 0) || !partial)
+        return fail(RLK_ERR_ARG, "null pointer with N > 0");
+    DeviceBinding dev;
+    RLK_TRY(dev.bind({{policy, "policy"}, {ref, "ref"}, {partial, "partial"}}));
+    rlk::FwdParams p{};
+    p.x = policy;
+    p.y = ref;
+    p.N = N;
+    p.V = V_shard;
+    p.vtotal = V_shard;
+    p.mx = plain_rows(N, ld_policy);
+    p.my = plain_rows(N, ld_ref);
+    p.k = 1;
+    p.kx = cap_k(softcap_policy);
+    p.ky = cap_k(softcap_ref);
+    p.scx = cap_sc(softcap_policy);
+    p.scy = cap_sc(softcap_ref);
+    p.part = partial;
+    const int64_t es = esize(dtype);
+    const bool al = rows_aligned(policy, p.mx, es) && rows_aligned(ref, p.my, es);
+    const int head = dir == RLK_KL_REVERSE ? rlk::kHeadKLReverse : rlk::kHeadKLForward;
+    return launched(rlk::launch_fwd(head, dtype, softcap_policy != 0.0f, softcap_ref != 0.0f, al,
+                                    p, static_cast<hipStream_t>(stream)),
+                    "kl_fwd_partial");
+}
+
+rlk_status rlk_combine(rlk_head head, rlk_kl_dir dir, int64_t P, const int64_t* bounds, int64_t N,
+                       const void* partials, const int64_t* targets, int64_t k,
+                       const float* target_vals, float softcap, float* out, void* stats,
+                       void* stream) {
+    if (head != RLK_HEAD_LOGP && head != RLK_HEAD_ENTROPY && head != RLK_HEAD_KL)
+        return fail(RLK_ERR_ARG, "unknown head %d", (int)head);
+    if (head == RLK_HEAD_KL) RLK_TRY(check_dir(dir));
+    if (P < 1 || P > RLK_MAX_SHARDS)
+        return fail(RLK_ERR_SHAPE, "P must be in [1, %d], got %lld", RLK_MAX_SHARDS, (long long)P);
+    if (!bounds) return fail(RLK_ERR_ARG, "bounds (host array of P + 1 columns) is null");
+    if (bounds[0] != 0) return fail(RLK_ERR_SHAPE, "bounds[0] must be 0");
+    for (int64_t s = 0; s < P; ++s)
+        if (bounds[s + 1] < bounds[s]) return fail(RLK_ERR_SHAPE, "bounds must not decrease");
+    const int64_t V_total = bounds[P];
+    if (V_total < 1 || V_total > INT32_MAX)
+        return fail(RLK_ERR_SHAPE, "the vocabulary width bounds[P] must be in [1, 2^31)");
+    if (N < 0) return fail(RLK_ERR_SHAPE, "N must be >= 0");
+    if (head == RLK_HEAD_LOGP) {
+        RLK_TRY(check_k(N, k));
+        RLK_TRY(check_head_cap(softcap, "softcap"));
+    }
+    if (N > 0 && P > INT64_MAX / N) return fail(RLK_ERR_SHAPE, "P * N overflows");
+    if (N == 0) return ok();
+    if (!partials || !out || !stats) return fail(RLK_ERR_ARG, "null pointer with N > 0");
+    if (head == RLK_HEAD_LOGP && (!targets || !target_vals))
+        return fail(RLK_ERR_ARG, "logprobs combine needs targets and target_vals");
+    DeviceBinding dev;
+    RLK_TRY(dev.bind({{partials, "partials"}, {out, "out"}, {stats, "stats"},
+                      {head == RLK_HEAD_LOGP ? targets : nullptr, "targets"},
+                      {head == RLK_HEAD_LOGP ? target_vals : nullptr, "target_vals"}}));
+    rlk::CombineParams q{};
+    q.P = static_cast<int>(P);
+    q.N = N;
+    q.k = head == RLK_HEAD_LOGP ? k : 1;
+    q.vtotal = V_total;
+    for (int64_t s = 0; s <= P; ++s) q.bounds[s] = bounds[s];
+    q.part = partials;
+    q.targets = targets;
+    q.tvals = target_vals;
+    q.sc = cap_sc(softcap);
+    q.out = out;
+    q.stats = stats;
+    const int h = head == RLK_HEAD_LOGP      ? rlk::kHeadLogp
+                  : head == RLK_HEAD_ENTROPY ? rlk::kHeadEntropy
+                  : dir == RLK_KL_REVERSE    ? rlk::kHeadKLReverse
+                                             : rlk::kHeadKLForward;
+    return launched(rlk::launch_combine(h, q, static_cast<hipStream_t>(stream)), "combine");
+}
+
+rlk_status rlk_logp_bwd_shard(const void* logits, rlk_dtype dtype, int64_t N, int64_t V_shard,
+                              int64_t ld, int64_t v0, int64_t V_total, const int64_t* targets,
+                              int64_t k, float softcap, const void* stats,
+                              const float* grad_logp, void* grad_logits, void* stream) {
+    RLK_TRY(check_common(dtype, N, V_total, softcap, "softcap"));
+    RLK_TRY(check_shard(N, V_shard, ld, v0, V_total, esize(dtype), "logits"));
+    RLK_TRY(check_k(N, k));
+    if (N == 0 || V_shard == 0) return ok();
+    if (!logits || !targets || !stats || !grad_logp || !grad_logits)
+        return fail(RLK_ERR_ARG, "null pointer with N > 0");
+    DeviceBinding dev;
+    RLK_TRY(dev.bind({{logits, "logits"}, {targets, "targets"}, {stats, "stats"},
+                      {grad_logp, "grad_logp"}, {grad_logits, "grad_logits"}}));
+    rlk::BwdParams p{};
+    p.x = logits;
+    p.N = N;
+    p.V = V_shard;
+    p.v0 = v0;
+    p.vtotal = V_total;
+    p.mx = plain_rows(N, ld);
+    p.my = p.mx;
+    p.mg = plain_rows(N, V_shard);
+    p.targets = targets;
+    p.k = k;
+    p.kx = cap_k(softcap);
+    p.scx = cap_sc(softcap);
+    p.stats = stats;
+    p.g = grad_logp;
+    p.gx = grad_logits;
+    const int64_t es = esize(dtype);
+    const bool al = rows_aligned(logits, p.mx, es) && rows_aligned(grad_logits, p.mg, es);
+    return launched(rlk::launch_bwd(rlk::kHeadLogp, dtype, softcap != 0.0f, false, al, p,
+                                    static_cast<hipStream_t>(stream)),
+                    "logp_bwd_shard");
 }
 
 }  // extern "C"

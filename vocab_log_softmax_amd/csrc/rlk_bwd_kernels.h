@@ -71,10 +71,13 @@ __global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void bwd_kernel(BwdParams p) {
             float part = 0.0f, cnt = 0.0f;
             if (tid < kGLanes) {
                 for (int64_t j = tid; j < p.k; j += kGLanes) {
+                    // valid over the whole row; local to this vocabulary shard
+                    // (plain call: the same) -> its column, else -1 / -2
                     const int64_t t = p.targets[row * p.k + j];
-                    const bool valid = t >= 0 && t < p.V;
+                    const bool valid = t >= 0 && t < p.vtotal;
+                    const bool local = t >= p.v0 && t < p.v0 + p.V;
                     const float g = p.g[row * p.k + j];
-                    tg[j] = valid ? static_cast<int>(t) : -1;
+                    tg[j] = local ? static_cast<int>(t - p.v0) : (valid ? -2 : -1);
                     gg[j] = g;
                     if (valid) {
                         part += g;

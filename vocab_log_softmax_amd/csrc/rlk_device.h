@@ -597,4 +597,68 @@ struct alignas(16) RowStats {
 };
 constexpr uint32_t kFlagEmptyA = 1u, kFlagEmptyB = 2u, kFlagMismatch = 4u;
 
+// Row state of one vocabulary shard (32 bytes per row), exported before the
+// heads are finalized so that P shards can be folded in rank order with the
+// same merges as the in-kernel tree (the cross-shard step of "Add Triton
+// kernels for vocab-parallel logprobs, entropy and KL", Changes: local
+// statistics rescaled to the global maximum).
+struct alignas(16) PartialRec {
+    float ma, mLa, Sa, W, mb, mLb, Sb, flag;
+};
+
+__device__ __forceinline__ PartialRec to_partial(const Stat1& s) {
+    return {s.m, s.mL, s.S, s.W, 0.0f, 0.0f, 0.0f, 0.0f};
+}
+__device__ __forceinline__ PartialRec to_partial(const StatKL& s) {
+    return {s.ma, s.mLa, s.Sa, s.W, s.mb, s.mLb, s.Sb, s.flag};
+}
+__device__ __forceinline__ Stat1 stat1_of(const PartialRec& r) { return {r.ma, r.mLa, r.Sa, r.W}; }
+__device__ __forceinline__ StatKL statkl_of(const PartialRec& r) {
+    return {r.ma, r.mLa, r.Sa, r.mb, r.mLb, r.Sb, r.W, r.flag};
+}
+
+// Heads and row record from a row's final single-tensor state:
+// logsumexp = ln2 (mL + log2 S), entropy H = ln2 (log2 S - W / S); an empty
+// row (every logit -inf) has log2 S = -inf and H = NaN.
+template <bool WITH_W>
+__device__ __forceinline__ RowStats finalize1(const Stat1& r) {
+    const bool empty = r.m == neg_inf();
+    const float log2S = log2f(r.S);  // -inf for an empty row
+    RowStats rs;
+    rs.mLa = r.mL;
+    rs.log2Sa = log2S;
+    rs.mLb = 0.0f;
+    rs.log2Sb = 0.0f;
+    rs.flags = empty ? kFlagEmptyA : 0u;
+    rs.value = WITH_W ? (empty ? qnan() : kLn2 * (log2S - r.W / r.S)) : 0.0f;
+    rs.pad0 = rs.pad1 = 0.0f;
+    return rs;
+}
+
+// KL(A||B) = ln2 (W / S_A - log2 S_A + log2 S_B) (reverse: A = policy), NaN
+// if either row is empty, +inf on a support mismatch.
+template <bool REVERSE>
+__device__ __forceinline__ RowStats finalize_kl(const StatKL& r) {
+    const bool empty_a = r.ma == neg_inf(), empty_b = r.mb == neg_inf();
+    const bool mismatch = REVERSE ? r.flag == pos_inf() : r.flag == neg_inf();
+    const float log2Sa = log2f(r.Sa), log2Sb = log2f(r.Sb);
+    const float D = REVERSE ? kLn2 * (r.W / r.Sa - log2Sa + log2Sb)
+                            : kLn2 * (r.W / r.Sb - log2Sb + log2Sa);
+    RowStats rs;
+    rs.mLa = r.mLa;
+    rs.log2Sa = log2Sa;
+    rs.mLb = r.mLb;
+    rs.log2Sb = log2Sb;
+    rs.value = (empty_a || empty_b) ? qnan() : (mismatch ? pos_inf() : D);
+    rs.flags = (empty_a ? kFlagEmptyA : 0u) | (empty_b ? kFlagEmptyB : 0u) |
+               (mismatch ? kFlagMismatch : 0u);
+    rs.pad0 = rs.pad1 = 0.0f;
+    return rs;
+}
+
+// log p of a target from its statistic input a and the row record.
+__device__ __forceinline__ float target_logp(float a, float sc, const RowStats& rs) {
+    return (__builtin_fmaf(a, sc, -rs.mLa) - rs.log2Sa) * kLn2;
+}
+
 }  // namespace rlk

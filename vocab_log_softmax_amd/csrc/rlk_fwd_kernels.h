@@ -128,12 +128,13 @@ __global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void fwd1_kernel(FwdParams p) 
     RowStats* stats = static_cast<RowStats*>(p.stats);
     for (int64_t row = blockIdx.x; row < p.N; row += gridDim.x) {
         const S* __restrict__ x = static_cast<const S*>(p.x) + p.mx.offset(row);
-        // Prefetch this lane's first target slot and its logit.
+        // Prefetch this lane's first target slot and its logit (if this
+        // shard owns the column).
         int64_t t0 = -1;
         float xt0 = 0.0f;
         if (HEAD == kHeadLogp && tid < p.k) {
             t0 = p.targets[row * p.k + tid];
-            if (t0 >= 0 && t0 < p.V) xt0 = load_one(x + t0);
+            if (t0 >= p.v0 && t0 < p.v0 + p.V) xt0 = load_one(x + (t0 - p.v0));
         }
         Stat1 st = stat1_init();
         for_each_group<BLOCK, U, S, CAP, ALIGNED, kFwdPipe>(
@@ -151,37 +152,33 @@ __global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void fwd1_kernel(FwdParams p) 
             Stat1 r = red[0];
 #pragma unroll
             for (int w = 1; w < NW; ++w) r = stat1_merge<WITH_W>(r, red[w]);
-            const bool empty = r.m == neg_inf();
-            const float log2S = log2f(r.S);  // -inf for an empty row
-            RowStats rs;
-            rs.mLa = r.mL;
-            rs.log2Sa = log2S;
-            rs.mLb = 0.0f;
-            rs.log2Sb = 0.0f;
-            rs.flags = empty ? kFlagEmptyA : 0u;
-            rs.value = 0.0f;
-            rs.pad0 = rs.pad1 = 0.0f;
-            if (HEAD == kHeadEntropy) {
-                const float H = empty ? qnan() : kLn2 * (log2S - r.W / r.S);
-                rs.value = H;
-                p.out[row] = H;
+            if (p.part) {
+                static_cast<PartialRec*>(p.part)[row] = to_partial(r);
+            } else {
+                const RowStats rs = finalize1<WITH_W>(r);
+                if (HEAD == kHeadEntropy) p.out[row] = rs.value;
+                stats[row] = rs;
+                bc[0] = rs.mLa;
+                bc[1] = rs.log2Sa;
             }
-            stats[row] = rs;
-            bc[0] = r.mL;
-            bc[1] = log2S;
         }
         __syncthreads();
         if (HEAD == kHeadLogp) {
-            const float mL = bc[0], log2S = bc[1];
+            RowStats rs;
+            rs.mLa = bc[0];
+            rs.log2Sa = bc[1];
             for (int64_t j = tid; j < p.k; j += BLOCK) {
                 const int64_t t = j == tid ? t0 : p.targets[row * p.k + j];
-                float o = 0.0f;
-                if (t >= 0 && t < p.V) {
-                    float a = j == tid ? xt0 : load_one(x + t);
+                const bool local = t >= p.v0 && t < p.v0 + p.V;
+                float a = 0.0f;
+                if (local) {
+                    a = j == tid ? xt0 : load_one(x + (t - p.v0));
                     if (CAP) a = cap_r(a, p.kx);
-                    o = (__builtin_fmaf(a, p.scx, -mL) - log2S) * kLn2;
                 }
-                p.out[row * p.k + j] = o;
+                if (p.part)
+                    p.tvals[row * p.k + j] = a;  // statistic input of an owned target
+                else
+                    p.out[row * p.k + j] = (t >= 0 && t < p.vtotal) ? target_logp(a, p.scx, rs) : 0.0f;
             }
         }
         __syncthreads();
@@ -212,23 +209,13 @@ __global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void fwdkl_kernel(FwdParams p)
             StatKL r = red[0];
 #pragma unroll
             for (int w = 1; w < NW; ++w) r = statkl_merge<REVERSE>(r, red[w]);
-            const bool empty_a = r.ma == neg_inf(), empty_b = r.mb == neg_inf();
-            const bool mismatch = REVERSE ? r.flag == pos_inf() : r.flag == neg_inf();
-            const float log2Sa = log2f(r.Sa), log2Sb = log2f(r.Sb);
-            const float D = REVERSE ? kLn2 * (r.W / r.Sa - log2Sa + log2Sb)
-                                    : kLn2 * (r.W / r.Sb - log2Sb + log2Sa);
-            const float out = (empty_a || empty_b) ? qnan() : (mismatch ? pos_inf() : D);
-            RowStats rs;
-            rs.mLa = r.mLa;
-            rs.log2Sa = log2Sa;
-            rs.mLb = r.mLb;
-            rs.log2Sb = log2Sb;
-            rs.value = out;
-            rs.flags = (empty_a ? kFlagEmptyA : 0u) | (empty_b ? kFlagEmptyB : 0u) |
-                       (mismatch ? kFlagMismatch : 0u);
-            rs.pad0 = rs.pad1 = 0.0f;
-            stats[row] = rs;
-            p.out[row] = out;
+            if (p.part) {
+                static_cast<PartialRec*>(p.part)[row] = to_partial(r);
+            } else {
+                const RowStats rs = finalize_kl<REVERSE>(r);
+                stats[row] = rs;
+                p.out[row] = rs.value;
+            }
         }
         __syncthreads();
     }

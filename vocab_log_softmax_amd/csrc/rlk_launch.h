@@ -99,6 +99,13 @@ struct FwdParams {
     float scx, scy;  // log2(e), or c log2(e) when the softcap is on
     float* out;      // logp [N, k], entropy [N] or KL [N]
     void* stats;     // RowStats [N]
+    // Vocabulary shard: the columns of x are [v0, v0 + V) of a row of width
+    // vtotal (plain call: v0 = 0, vtotal = V).  With `part` set, the kernel
+    // writes the shard's PartialRec [N] (and, for logprobs, the statistic
+    // input of every target it owns into tvals [N, k]) instead of the heads.
+    int64_t v0, vtotal;
+    void* part;
+    float* tvals;
 };
 
 struct BwdParams {
@@ -113,7 +120,24 @@ struct BwdParams {
     const float* g;  // upstream gradient: [N, k] (logp) or [N]
     void* gx;        // gradient w.r.t. x, [N, V] contiguous, logits dtype
     int64_t split;   // column segments per row (one workgroup each), >= 1
+    int64_t v0, vtotal;  // vocabulary shard of x (plain call: 0, V)
 };
+
+constexpr int kMaxShards = 64;
+
+struct CombineParams {
+    int P;
+    int64_t N, k, vtotal;
+    int64_t bounds[kMaxShards + 1];  // shard s owns columns [bounds[s], bounds[s+1])
+    const void* part;                // PartialRec [P, N]
+    const int64_t* targets;          // logp: [N, k]
+    const float* tvals;              // logp: [P, N, k]
+    float sc;                        // statistic scale of the (capped) logits
+    float* out;
+    void* stats;
+};
+
+hipError_t launch_combine(int head, const CombineParams& q, hipStream_t stream);
 
 // Per-dtype row-kernel launchers (rlk_fwd_<dtype>.hip, rlk_bwd_<dtype>.hip).
 hipError_t launch_fwd_f32(int head, bool cap_x, bool cap_y, bool aligned, const FwdParams& p,

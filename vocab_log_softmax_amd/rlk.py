@@ -25,6 +25,7 @@ RLK_F32, RLK_BF16, RLK_F16 = 0, 1, 2
 RLK_HEAD_LOGP, RLK_HEAD_ENTROPY, RLK_HEAD_KL = 0, 1, 2
 RLK_KL_REVERSE, RLK_KL_FORWARD = 0, 1
 RLK_MAX_TOPK = 4096
+RLK_MAX_SHARDS = 64
 STATUS = {0: "RLK_OK", 1: "RLK_ERR_ARG", 2: "RLK_ERR_DTYPE", 3: "RLK_ERR_SHAPE",
           4: "RLK_ERR_DEVICE", 5: "RLK_ERR_LAUNCH"}
 
@@ -32,7 +33,9 @@ EXPORTS = ("rlk_abi_version", "rlk_stats_bytes", "rlk_status_str", "rlk_last_err
            "rlk_softcap_fwd", "rlk_softcap_bwd", "rlk_logp_fwd", "rlk_logp_bwd",
            "rlk_entropy_fwd", "rlk_entropy_bwd", "rlk_kl_fwd", "rlk_kl_bwd",
            "rlk_logp_fwd_strided", "rlk_logp_bwd_strided", "rlk_entropy_fwd_strided",
-           "rlk_entropy_bwd_strided", "rlk_kl_fwd_strided", "rlk_kl_bwd_strided")
+           "rlk_entropy_bwd_strided", "rlk_kl_fwd_strided", "rlk_kl_bwd_strided",
+           "rlk_partial_bytes", "rlk_logp_fwd_partial", "rlk_entropy_fwd_partial",
+           "rlk_kl_fwd_partial", "rlk_combine", "rlk_logp_bwd_shard")
 
 
 class RlkRows(ctypes.Structure):
@@ -81,6 +84,15 @@ def load_library(path: str = LIB_PATH):
         "rlk_kl_fwd_strided": ([vp, vp, ci, i64, i64, rp, rp, ci, f32, f32, vp, vp, vp], ci),
         "rlk_kl_bwd_strided": ([vp, vp, ci, i64, i64, rp, rp, ci, f32, f32, vp, vp, vp, rp,
                                 vp], ci),
+        "rlk_partial_bytes": ([i64], ctypes.c_size_t),
+        "rlk_logp_fwd_partial": ([vp, ci, i64, i64, i64, i64, i64, vp, i64, f32, vp, vp, vp],
+                                 ci),
+        "rlk_entropy_fwd_partial": ([vp, ci, i64, i64, i64, f32, vp, vp], ci),
+        "rlk_kl_fwd_partial": ([vp, vp, ci, i64, i64, i64, i64, ci, f32, f32, vp, vp], ci),
+        "rlk_combine": ([ci, ci, i64, ctypes.POINTER(i64), i64, vp, vp, i64, vp, f32, vp, vp,
+                         vp], ci),
+        "rlk_logp_bwd_shard": ([vp, ci, i64, i64, i64, i64, i64, vp, i64, f32, vp, vp, vp, vp],
+                               ci),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -310,6 +322,85 @@ def rlk_kl_bwd_strided(policy, ref, direction, softcap_policy, softcap_ref, stat
           ctypes.byref(rp), ctypes.byref(rr), int(direction), float(softcap_policy),
           float(softcap_ref), _ptr(stats), _ptr(grad_kl), _ptr(grad_policy), ctypes.byref(rg),
           _stream(policy))
+
+
+# ------------------------------------------------------- vocabulary shards
+# A shard is the [N, V_shard] block of columns [v0, v0 + V_shard) of rows of
+# width V_total (a 2-D view with unit column stride; V_shard may be 0).
+
+def _shard(x: torch.Tensor, what: str):
+    if x.dim() != 2:
+        raise ValueError(f"{what} must be 2-D [N, V_shard], got shape {tuple(x.shape)}")
+    N, Vs = x.shape
+    if Vs > 0 and (x.stride(1) != 1 or (N > 1 and x.stride(0) < Vs)):
+        raise ValueError(f"{what} must have unit column stride and row stride >= V_shard")
+    ld = _ld(x) if Vs > 0 else 0
+    return N, Vs, ld
+
+
+def rlk_partial_bytes(N: int) -> int:
+    return load_library().rlk_partial_bytes(N)
+
+
+def rlk_logp_fwd_partial(logits, v0, V_total, targets, softcap, partial, target_vals) -> None:
+    N, Vs, ld = _shard(logits, "logits")
+    k = targets.shape[1]
+    _need(targets, torch.int64, (N, k), "targets")
+    _need(target_vals, torch.float32, (N, k), "target_vals")
+    _call("rlk_logp_fwd_partial", _ptr(logits) if Vs else None, _dtype_code(logits, "logits"),
+          N, Vs, ld, int(v0), int(V_total), _ptr(targets), k, float(softcap), _ptr(partial),
+          _ptr(target_vals), _stream(targets))
+
+
+def rlk_entropy_fwd_partial(logits, softcap, partial) -> None:
+    N, Vs, ld = _shard(logits, "logits")
+    _call("rlk_entropy_fwd_partial", _ptr(logits) if Vs else None,
+          _dtype_code(logits, "logits"), N, Vs, ld, float(softcap), _ptr(partial),
+          _stream(partial))
+
+
+def rlk_kl_fwd_partial(policy, ref, direction, softcap_policy, softcap_ref, partial) -> None:
+    N, Vs, ldp = _shard(policy, "policy")
+    if tuple(ref.shape) != (N, Vs) or ref.dtype != policy.dtype:
+        raise ValueError("policy and ref shards must have the same shape and dtype")
+    _, _, ldr = _shard(ref, "ref")
+    _call("rlk_kl_fwd_partial", _ptr(policy) if Vs else None, _ptr(ref) if Vs else None,
+          _dtype_code(policy, "policy"), N, Vs, ldp, ldr, int(direction),
+          float(softcap_policy), float(softcap_ref), _ptr(partial), _stream(partial))
+
+
+def rlk_combine(head, direction, bounds, partials, targets, target_vals, softcap, out,
+                stats) -> None:
+    """Fold gathered shard records partials [P, N * 32 bytes] in rank order."""
+    P = len(bounds) - 1
+    b = (ctypes.c_int64 * (P + 1))(*[int(v) for v in bounds])
+    N = out.shape[0]
+    k = targets.shape[1] if targets is not None else 1
+    if head == RLK_HEAD_LOGP:
+        _need(targets, torch.int64, (N, k), "targets")
+        _need(target_vals, torch.float32, (P, N, k), "target_vals")
+        _need(out, torch.float32, (N, k), "out")
+    else:
+        _need(out, torch.float32, (N,), "out")
+    _call("rlk_combine", int(head), int(direction), P, b, N, _ptr(partials), _ptr(targets), k,
+          _ptr(target_vals), float(softcap), _ptr(out), _ptr(stats), _stream(out))
+
+
+def rlk_logp_bwd_shard(logits, v0, V_total, targets, softcap, stats, grad_logp,
+                       grad_logits) -> None:
+    N, Vs, ld = _shard(logits, "logits")
+    k = targets.shape[1]
+    _need(targets, torch.int64, (N, k), "targets")
+    _need(grad_logp, torch.float32, (N, k), "grad_logp")
+    _need(grad_logits, logits.dtype, (N, Vs), "grad_logits")
+    _call("rlk_logp_bwd_shard", _ptr(logits) if Vs else None, _dtype_code(logits, "logits"), N,
+          Vs, ld, int(v0), int(V_total), _ptr(targets), k, float(softcap), _ptr(stats),
+          _ptr(grad_logp), _ptr(grad_logits), _stream(targets))
+
+
+def new_partials(P: int, N: int, device) -> torch.Tensor:
+    """Uninitialised buffer for P shard records of N rows ([P, N * 32] bytes)."""
+    return torch.empty((P, max(1, rlk_partial_bytes(N))), dtype=torch.uint8, device=device)
 
 
 # ------------------------------------------------ allocating convenience layer
