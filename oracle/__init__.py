@@ -70,6 +70,8 @@ def _load(path: str = LIB_PATH):
     lib.orc_kl_fwd.restype = ctypes.c_int
     lib.orc_kl_bwd.argtypes = [d, d, i64, i64, ctypes.c_int, dbl, dbl, d, d]
     lib.orc_kl_bwd.restype = ctypes.c_int
+    lib.orc_kl_bwd_ref.argtypes = [d, d, i64, i64, ctypes.c_int, dbl, dbl, d, d]
+    lib.orc_kl_bwd_ref.restype = ctypes.c_int
     return lib
 
 
@@ -178,6 +180,17 @@ class Oracle:
         self._check(self.lib.orc_kl_bwd(pp, pr, N, V, int(direction), float(cap_pol),
                                         float(cap_ref), pg, self._d(gx)[1]))
         return gx
+
+    def kl_bwd_ref(self, pol, ref, grad_out, direction=KL_REVERSE, cap_pol=0.0, cap_ref=0.0):
+        """Gradient of the KL with respect to the reference logits."""
+        pol, pp = self._d(pol)
+        ref, pr = self._d(ref)
+        N, V = pol.shape
+        g, pg = self._d(np.asarray(grad_out, dtype=np.float64).reshape(N))
+        gr = np.empty((N, V), dtype=np.float64)
+        self._check(self.lib.orc_kl_bwd_ref(pp, pr, N, V, int(direction), float(cap_pol),
+                                            float(cap_ref), pg, self._d(gr)[1]))
+        return gr
 
 
 _default = None

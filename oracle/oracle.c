@@ -39,6 +39,9 @@
  *     column is finite in A and -inf in B, even where p_A underflows [VP];
  *   - on a reverse-KL mismatch row the gradient is NaN on the policy's
  *     support and 0 elsewhere; forward KL keeps its finite gradient g(p - q);
+ *   - the gradient with respect to the reference mirrors this: reverse KL
+ *     keeps its finite g(q - p), forward KL gives NaN on the reference's
+ *     support of a mismatch row and 0 elsewhere;
  *   - duplicate top-k ids each receive the same output; their upstream
  *     gradients add (ascending slot order) [VP];
  *   - softcap off is cap == 0; with a cap, -inf maps to -cap.
@@ -360,6 +363,57 @@ int orc_kl_bwd(const double* pol, const double* ref, int64_t N, int64_t V, int d
             }
         } else {
             for (int64_t v = 0; v < V; ++v) gr[v] = g[i] * (P.p[v] - R.p[v]) * P.s[v];
+        }
+        buf_free(&P);
+        buf_free(&R);
+    }
+    return bad;
+}
+
+/* Gradient with respect to the reference logits (a reference that is not
+ * detached).  With log q_u = z_u - logsumexp(z) for the (capped) reference
+ * logits z, d log q_u / d z_v = [u == v] - q_v, hence
+ *   reverse: d/dz_v KL(P||R) = -sum_u p_u ([u == v] - q_v) = q_v - p_v,
+ *            finite on every row where both distributions exist (a support
+ *            mismatch included: no infinite term enters it);
+ *   forward: d/dz_v KL(R||P) = q_v (log q_v - log p_v - D), 0 off the
+ *            reference's support, and on a mismatch row (D = +inf) NaN on
+ *            the reference's support -- the mirror images of the two policy
+ *            gradients above.
+ * Both times g and the reference's softcap slope; an empty row in either
+ * tensor gives NaN everywhere. */
+int orc_kl_bwd_ref(const double* pol, const double* ref, int64_t N, int64_t V, int dir,
+                   double cap_pol, double cap_ref, const double* g, double* gr_out) {
+    int bad = 0;
+#pragma omp parallel for schedule(static) num_threads(g_threads) reduction(| : bad)
+    for (int64_t i = 0; i < N; ++i) {
+        double* gr = gr_out + i * V;
+        row_buf P, R;
+        int okp = buf_alloc(&P, V), okr = buf_alloc(&R, V);
+        if (!okp || !okr) {
+            bad |= 1;
+            buf_free(&P);
+            buf_free(&R);
+            continue;
+        }
+        row_prologue(pol + i * V, V, cap_pol, P.y, P.s);
+        row_prologue(ref + i * V, V, cap_ref, R.y, R.s);
+        int ep = row_log_softmax(P.y, V, P.logp, P.p);
+        int er = row_log_softmax(R.y, V, R.logp, R.p);
+        if (ep || er) {
+            for (int64_t v = 0; v < V; ++v) gr[v] = NAN;
+        } else if (dir == ORC_KL_REVERSE) {
+            for (int64_t v = 0; v < V; ++v) gr[v] = g[i] * (R.p[v] - P.p[v]) * R.s[v];
+        } else {
+            double D = row_kl(&R, &P, V);
+            for (int64_t v = 0; v < V; ++v) {
+                if (R.logp[v] == -INFINITY)
+                    gr[v] = 0.0;
+                else if (D == INFINITY)
+                    gr[v] = NAN;
+                else
+                    gr[v] = g[i] * R.p[v] * ((R.logp[v] - P.logp[v]) - D) * R.s[v];
+            }
         }
         buf_free(&P);
         buf_free(&R);

@@ -465,4 +465,75 @@ def pin_kl_masked_policy(orc):
     close(orc.kl_fwd(a, b, 0), rev.numpy(), 1e-11, 1e-13, "masked-policy reverse KL")
 
 
+# -- gradient with respect to the reference (not detached) -------------------
+
+def pin_kl_ref_autograd(orc):
+    r = rng(22)
+    for cap_p, cap_r in ((0.0, 0.0), (30.0, 20.0)):
+        a = r.normal(0, 3, (5, 64))
+        b = a + r.normal(0, 0.5, (5, 64))
+        g = r.normal(0, 1, 5)
+        for d in (0, 1):
+            bt = torch.from_numpy(b).requires_grad_(True)
+            lpa = torch.log_softmax(_cap_t(torch.from_numpy(a), cap_p), -1)
+            lpb = torch.log_softmax(_cap_t(bt, cap_r), -1)
+            if d == 0:
+                kl = (lpa.exp() * (lpa - lpb)).sum(-1)
+            else:
+                kl = (lpb.exp() * (lpb - lpa)).sum(-1)
+            (kl * torch.from_numpy(g)).sum().backward()
+            close(orc.kl_bwd_ref(a, b, g, d, cap_p, cap_r), bt.grad.numpy(), 1e-10, 1e-13,
+                  f"KL dir={d} reference grad vs autograd")
+
+
+def pin_kl_ref_finite_difference(orc):
+    r = rng(23)
+    a = r.normal(0, 2, (3, 25))
+    b = a + r.normal(0, 0.7, (3, 25))
+    g = r.normal(0, 1, 3)
+    for d in (0, 1):
+        f = lambda z: float((orc.kl_fwd(a, z, d, 0.0, 20.0) * g).sum())  # noqa: E731
+        _fd_check(f, b, orc.kl_bwd_ref(a, b, g, d, 0.0, 20.0), what=f"KL ref fd dir={d}")
+
+
+def pin_kl_ref_equals_policy_grad_of_swapped_roles(orc):
+    # KL(P||R) is the forward KL of the pair (policy R, reference P), and the
+    # other way round, so the reference gradient of one direction is the
+    # policy gradient of the other with the two tensors (and caps) swapped.
+    r = rng(24)
+    a = _masked_rows(r, 4, 40, 3.0)
+    b = np.where(np.isfinite(a), a + r.normal(0, 0.5, a.shape), -np.inf)
+    g = r.normal(0, 1, 4)
+    for cp, cr in ((0.0, 0.0), (20.0, 30.0)):
+        for d in (0, 1):
+            close(orc.kl_bwd_ref(a, b, g, d, cp, cr), orc.kl_bwd(b, a, g, 1 - d, cr, cp),
+                  1e-15, 0, f"swap dir={d} caps={cp, cr}")
+
+
+def pin_kl_ref_special_rows(orc):
+    V = 8
+    a = np.zeros((5, V))
+    b = np.zeros((5, V))
+    b[0, 6:] = -np.inf          # reverse mismatch: reference masks policy columns
+    a[1, 5:] = -np.inf          # forward mismatch: policy masks reference columns
+    a[2] = -np.inf              # empty policy row
+    b[3] = -np.inf              # empty reference row
+    g = np.ones(5)
+    rv = orc.kl_bwd_ref(a, b, g, 0)
+    # q - p: reference-masked columns get exactly -p = -1/8, the rest 1/6 - 1/8
+    close(rv[0, 6:], np.full(2, -1 / 8), 1e-15, 0, "reverse KL ref grad on masked ref")
+    close(rv[0, :6], np.full(6, 1 / 6 - 1 / 8), 1e-15, 1e-16, "reverse KL ref grad on support")
+    close(rv[1, 5:], np.full(3, 1 / 8), 1e-15, 0, "reverse KL ref grad, policy-masked")
+    assert np.isnan(rv[2:4]).all() and (rv[4] == 0).all()
+    fw = orc.kl_bwd_ref(a, b, g, 1)
+    assert np.isinf(orc.kl_fwd(a, b, 1)[1])
+    assert np.isnan(fw[1]).all()                     # reference supports every column
+    assert np.isfinite(fw[0]).all() and (fw[0, 6:] == 0).all()
+    assert np.isnan(fw[2:4]).all() and (fw[4] == 0).all()
+    b2 = b.copy()
+    b2[1, 7] = -np.inf                               # masked reference column on a mismatch row
+    fw2 = orc.kl_bwd_ref(a, b2, g, 1)
+    assert fw2[1, 7] == 0 and np.isnan(fw2[1, :7]).all()
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

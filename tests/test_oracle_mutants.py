@@ -55,6 +55,19 @@ MUTANTS = {
                                    "        int ep = row_log_softmax(P.y, V, P.logp, P.p);\n"
                                    "        int er = row_log_softmax(R.y, V, R.logp, R.p);\n"
                                    "        if (ep || er)\n            out[i] = NAN;"),
+    "ref_grad_reverse_sign": ("g[i] * (R.p[v] - P.p[v]) * R.s[v]",
+                              "g[i] * (P.p[v] - R.p[v]) * R.s[v]"),
+    "ref_grad_reverse_slope_of_policy": ("g[i] * (R.p[v] - P.p[v]) * R.s[v]",
+                                         "g[i] * (R.p[v] - P.p[v]) * P.s[v]"),
+    "ref_grad_forward_D_dropped": ("((R.logp[v] - P.logp[v]) - D)", "((R.logp[v] - P.logp[v]))"),
+    "ref_grad_forward_weights_from_policy": ("g[i] * R.p[v] * ((R.logp",
+                                             "g[i] * P.p[v] * ((R.logp"),
+    "ref_grad_forward_uses_reverse_D": ("double D = row_kl(&R, &P, V);",
+                                        "double D = row_kl(&P, &R, V);"),
+    "ref_grad_forward_mismatch_nan_dropped": (
+        "else if (D == INFINITY)\n                    gr[v] = NAN;\n"
+        "                else\n                    gr[v] = g[i] * R.p[v]",
+        "else\n                    gr[v] = g[i] * R.p[v]"),
 }
 
 
