@@ -209,6 +209,44 @@ rlk_status rlk_kl_bwd_strided(const void* policy, const void* ref, rlk_dtype dty
                               const void* stats, const float* grad_kl, void* grad_policy,
                               const rlk_rows* grad_rows, void* stream);
 
+/* ------------------------------------------------- KL: both directions,
+ * reference gradient.  "Add Triton kernels for vocab-parallel logprobs,
+ * entropy and KL", Changes: both KL directions are offered and the reference
+ * is detached there; a caller that trains both distributions needs the
+ * gradient with respect to the reference too.
+ *
+ * rlk_kl_fwd_both: reverse KL(P||R) and forward KL(R||P) from one read of
+ * the pair; each output and row record is bit-identical to the one
+ * rlk_kl_fwd writes for that direction, so either record feeds rlk_kl_bwd /
+ * rlk_kl_bwd_ref of its direction. */
+rlk_status rlk_kl_fwd_both(const void* policy, const void* ref, rlk_dtype dtype, int64_t N,
+                           int64_t V, int64_t ld_policy, int64_t ld_ref, float softcap_policy,
+                           float softcap_ref, float* kl_reverse, void* stats_reverse,
+                           float* kl_forward, void* stats_forward, void* stream);
+rlk_status rlk_kl_fwd_both_strided(const void* policy, const void* ref, rlk_dtype dtype,
+                                   int64_t N, int64_t V, const rlk_rows* policy_rows,
+                                   const rlk_rows* ref_rows, float softcap_policy,
+                                   float softcap_ref, float* kl_reverse, void* stats_reverse,
+                                   float* kl_forward, void* stats_forward, void* stream);
+
+/* Gradient with respect to the reference logits (ref's layout, dtype, cap),
+ * from the record of the same direction's forward:
+ *   reverse KL(P||R): g (q - p) * dr/dref on every row where both inputs
+ *     exist (a support-mismatch row included: no infinite term enters it);
+ *   forward KL(R||P): g q (log q - log p - D) * dr/dref, 0 on the
+ *     reference's masked columns, NaN on its support of a mismatch row.
+ * Rows where either input is all -inf: NaN.  grad_ref is [N, V] contiguous
+ * (strided: its own rlk_rows). */
+rlk_status rlk_kl_bwd_ref(const void* policy, const void* ref, rlk_dtype dtype, int64_t N,
+                          int64_t V, int64_t ld_policy, int64_t ld_ref, rlk_kl_dir dir,
+                          float softcap_policy, float softcap_ref, const void* stats,
+                          const float* grad_kl, void* grad_ref, void* stream);
+rlk_status rlk_kl_bwd_ref_strided(const void* policy, const void* ref, rlk_dtype dtype, int64_t N,
+                                  int64_t V, const rlk_rows* policy_rows,
+                                  const rlk_rows* ref_rows, rlk_kl_dir dir, float softcap_policy,
+                                  float softcap_ref, const void* stats, const float* grad_kl,
+                                  void* grad_ref, const rlk_rows* grad_rows, void* stream);
+
 /* ------------------------------------------------- vocabulary shards
  * The single-GPU half of vocabulary parallelism ("Add Triton kernels for
  * vocab-parallel logprobs, entropy and KL", Changes and review comment:

@@ -171,3 +171,23 @@ def test_shard_entry_points_validate(lib):
     assert lib.rlk_combine(0, 0, 2, b, 4, p, None, 1, p, F(0), p, p, None) == ARG
     assert lib.rlk_combine(0, 0, 2, b, 4, p, p, 1, p, F(-1), p, p, None) == ARG
     assert lib.rlk_combine(1, 0, 2, b, 0, None, None, 1, None, F(0), None, None, None) == OK
+
+
+def test_kl_both_and_reference_gradient_validate(lib):
+    p = ctypes.c_void_p(16)
+    # both directions: the forward-KL outputs are required
+    assert lib.rlk_kl_fwd_both(p, p, 1, 4, 8, 8, 8, F(0), F(0), p, p, None, p, None) == ARG
+    assert lib.rlk_kl_fwd_both(p, p, 1, 4, 8, 8, 8, F(0), F(0), p, p, p, None, None) == ARG
+    assert lib.rlk_kl_fwd_both(p, p, 1, 4, 8, 7, 8, F(0), F(0), p, p, p, p, None) == SHAPE
+    assert lib.rlk_kl_fwd_both(p, p, 3, 4, 8, 8, 8, F(0), F(0), p, p, p, p, None) == DTYPE
+    assert lib.rlk_kl_fwd_both(p, p, 1, 0, 8, 8, 8, F(0), F(0), None, None, None, None,
+                               None) == OK
+    # reference gradient
+    assert lib.rlk_kl_bwd_ref(p, p, 1, 4, 8, 8, 8, 2, F(0), F(0), p, p, p, None) == ARG
+    assert lib.rlk_kl_bwd_ref(p, p, 1, 4, 8, 8, 6, 0, F(0), F(0), p, p, p, None) == SHAPE
+    assert lib.rlk_kl_bwd_ref(p, p, 1, 4, 8, 8, 8, 0, F(0), F(-2), p, p, p, None) == ARG
+    assert lib.rlk_kl_bwd_ref(p, p, 1, 4, 8, 8, 8, 0, F(0), F(0), p, p, None, None) == ARG
+    R = rlk.RlkRows
+    assert lib.rlk_kl_bwd_ref_strided(p, p, 1, 8, 10, ctypes.byref(R(4, 40, 10)),
+                                      ctypes.byref(R(4, 40, 10)), 0, F(0), F(0), p, p, p,
+                                      ctypes.byref(R(4, 20, 5)), None) == SHAPE

@@ -355,14 +355,18 @@ rlk_status entropy_bwd_impl(const void* logits, rlk_dtype dtype, int64_t N, int6
                     "entropy_bwd");
 }
 
+// One KL direction (kl2 == nullptr), or both from one read of the pair:
+// reverse KL to (kl, stats) and forward KL to (kl2, stats2).
 rlk_status kl_fwd_impl(const void* policy, const void* ref, rlk_dtype dtype, int64_t N, int64_t V,
                        const RowMap& mp, const RowMap& mr, rlk_kl_dir dir, float cp, float cr,
-                       float* kl, void* stats, void* stream) {
+                       float* kl, void* stats, float* kl2, void* stats2, void* stream) {
+    const bool both = kl2 != nullptr || stats2 != nullptr;
     if (N == 0) return ok();
-    if (!policy || !ref || !kl || !stats)
-        return fail(RLK_ERR_ARG, "policy, ref, kl and stats must be non-null when N > 0");
+    if (!policy || !ref || !kl || !stats || (both && (!kl2 || !stats2)))
+        return fail(RLK_ERR_ARG, "policy, ref, outputs and row records must be non-null when N > 0");
     DeviceBinding dev;
-    rlk_status s = dev.bind({{policy, "policy"}, {ref, "ref"}, {kl, "kl"}, {stats, "stats"}});
+    rlk_status s = dev.bind({{policy, "policy"}, {ref, "ref"}, {kl, "kl"}, {stats, "stats"},
+                             {kl2, "kl_forward"}, {stats2, "stats_forward"}});
     if (s != RLK_OK) return s;
     rlk::FwdParams p{};
     p.x = policy;
@@ -379,49 +383,62 @@ rlk_status kl_fwd_impl(const void* policy, const void* ref, rlk_dtype dtype, int
     p.scy = cap_sc(cr);
     p.out = kl;
     p.stats = stats;
+    p.out2 = kl2;
+    p.stats2 = stats2;
     const int64_t es = esize(dtype);
     const bool al = rows_aligned(policy, mp, es) && rows_aligned(ref, mr, es);
-    const int head = dir == RLK_KL_REVERSE ? rlk::kHeadKLReverse : rlk::kHeadKLForward;
+    const int head = both                    ? rlk::kHeadKLBoth
+                     : dir == RLK_KL_REVERSE ? rlk::kHeadKLReverse
+                                             : rlk::kHeadKLForward;
     return launched(rlk::launch_fwd(head, dtype, cp != 0.0f, cr != 0.0f, al, p,
                                     static_cast<hipStream_t>(stream)),
-                    "kl_fwd");
+                    both ? "kl_fwd_both" : "kl_fwd");
 }
 
+// Gradient of the KL w.r.t. the policy, or (wrt_ref) w.r.t. the reference.
+// The reference gradient of one direction is the policy gradient of the other
+// direction with the two tensors swapped (KL(P||R) is the forward KL of the
+// pair policy R, reference P), so it runs the same kernels with the operands,
+// the caps and the two sides of the row record exchanged.
 rlk_status kl_bwd_impl(const void* policy, const void* ref, rlk_dtype dtype, int64_t N, int64_t V,
                        const RowMap& mp, const RowMap& mr, rlk_kl_dir dir, float cp, float cr,
-                       const void* stats, const float* grad_kl, void* grad_policy,
-                       const RowMap& mg, void* stream) {
+                       const void* stats, const float* grad_kl, void* grad_out,
+                       const RowMap& mg, bool wrt_ref, void* stream) {
     if (N == 0) return ok();
-    if (!policy || !ref || !stats || !grad_kl || !grad_policy)
+    if (!policy || !ref || !stats || !grad_kl || !grad_out)
         return fail(RLK_ERR_ARG, "null pointer with N > 0");
+    const char* gname = wrt_ref ? "grad_ref" : "grad_policy";
     DeviceBinding dev;
     rlk_status s = dev.bind({{policy, "policy"}, {ref, "ref"}, {stats, "stats"},
-                             {grad_kl, "grad_kl"}, {grad_policy, "grad_policy"}});
+                             {grad_kl, "grad_kl"}, {grad_out, gname}});
     if (s != RLK_OK) return s;
     rlk::BwdParams p{};
-    p.x = policy;
-    p.y = ref;
+    p.x = wrt_ref ? ref : policy;
+    p.y = wrt_ref ? policy : ref;
     p.N = N;
     p.V = V;
     p.vtotal = V;
-    p.mx = mp;
-    p.my = mr;
+    p.mx = wrt_ref ? mr : mp;
+    p.my = wrt_ref ? mp : mr;
     p.mg = mg;
     p.k = 1;
-    p.kx = cap_k(cp);
-    p.ky = cap_k(cr);
-    p.scx = cap_sc(cp);
-    p.scy = cap_sc(cr);
+    const float cx = wrt_ref ? cr : cp, cy = wrt_ref ? cp : cr;
+    p.kx = cap_k(cx);
+    p.ky = cap_k(cy);
+    p.scx = cap_sc(cx);
+    p.scy = cap_sc(cy);
     p.stats = stats;
+    p.swap = wrt_ref ? 1 : 0;
     p.g = grad_kl;
-    p.gx = grad_policy;
+    p.gx = grad_out;
     const int64_t es = esize(dtype);
     const bool al = rows_aligned(policy, mp, es) && rows_aligned(ref, mr, es) &&
-                    rows_aligned(grad_policy, mg, es);
-    const int head = dir == RLK_KL_REVERSE ? rlk::kHeadKLReverse : rlk::kHeadKLForward;
-    return launched(rlk::launch_bwd(head, dtype, cp != 0.0f, cr != 0.0f, al, p,
+                    rows_aligned(grad_out, mg, es);
+    const bool reverse = (dir == RLK_KL_REVERSE) != wrt_ref;
+    const int head = reverse ? rlk::kHeadKLReverse : rlk::kHeadKLForward;
+    return launched(rlk::launch_bwd(head, dtype, cx != 0.0f, cy != 0.0f, al, p,
                                     static_cast<hipStream_t>(stream)),
-                    "kl_bwd");
+                    wrt_ref ? "kl_bwd_ref" : "kl_bwd");
 }
 
 rlk_status check_common(rlk_dtype dtype, int64_t N, int64_t V, float cap, const char* capname) {
@@ -569,7 +586,22 @@ rlk_status rlk_kl_fwd(const void* policy, const void* ref, rlk_dtype dtype, int6
     RLK_TRY(check_matrix(N, V, ld_ref, esize(dtype), "ref"));
     RLK_TRY(check_dir(dir));
     return kl_fwd_impl(policy, ref, dtype, N, V, plain_rows(N, ld_policy), plain_rows(N, ld_ref),
-                       dir, softcap_policy, softcap_ref, kl, stats, stream);
+                       dir, softcap_policy, softcap_ref, kl, stats, nullptr, nullptr, stream);
+}
+
+rlk_status rlk_kl_fwd_both(const void* policy, const void* ref, rlk_dtype dtype, int64_t N,
+                           int64_t V, int64_t ld_policy, int64_t ld_ref, float softcap_policy,
+                           float softcap_ref, float* kl_reverse, void* stats_reverse,
+                           float* kl_forward, void* stats_forward, void* stream) {
+    RLK_TRY(check_common(dtype, N, V, softcap_policy, "softcap_policy"));
+    RLK_TRY(check_head_cap(softcap_ref, "softcap_ref"));
+    RLK_TRY(check_matrix(N, V, ld_policy, esize(dtype), "policy"));
+    RLK_TRY(check_matrix(N, V, ld_ref, esize(dtype), "ref"));
+    if (N > 0 && (!kl_forward || !stats_forward))
+        return fail(RLK_ERR_ARG, "kl_forward and stats_forward must be non-null when N > 0");
+    return kl_fwd_impl(policy, ref, dtype, N, V, plain_rows(N, ld_policy), plain_rows(N, ld_ref),
+                       RLK_KL_REVERSE, softcap_policy, softcap_ref, kl_reverse, stats_reverse,
+                       kl_forward, stats_forward, stream);
 }
 
 rlk_status rlk_kl_bwd(const void* policy, const void* ref, rlk_dtype dtype, int64_t N, int64_t V,
@@ -583,7 +615,7 @@ rlk_status rlk_kl_bwd(const void* policy, const void* ref, rlk_dtype dtype, int6
     RLK_TRY(check_dir(dir));
     return kl_bwd_impl(policy, ref, dtype, N, V, plain_rows(N, ld_policy), plain_rows(N, ld_ref),
                        dir, softcap_policy, softcap_ref, stats, grad_kl, grad_policy,
-                       plain_rows(N, V), stream);
+                       plain_rows(N, V), false, stream);
 }
 
 rlk_status rlk_kl_fwd_strided(const void* policy, const void* ref, rlk_dtype dtype, int64_t N,
@@ -597,7 +629,23 @@ rlk_status rlk_kl_fwd_strided(const void* policy, const void* ref, rlk_dtype dty
     RLK_TRY(check_rows(ref_rows, N, V, esize(dtype), "ref", false, &mr));
     RLK_TRY(check_dir(dir));
     return kl_fwd_impl(policy, ref, dtype, N, V, mp, mr, dir, softcap_policy, softcap_ref, kl,
-                       stats, stream);
+                       stats, nullptr, nullptr, stream);
+}
+
+rlk_status rlk_kl_fwd_both_strided(const void* policy, const void* ref, rlk_dtype dtype,
+                                   int64_t N, int64_t V, const rlk_rows* policy_rows,
+                                   const rlk_rows* ref_rows, float softcap_policy,
+                                   float softcap_ref, float* kl_reverse, void* stats_reverse,
+                                   float* kl_forward, void* stats_forward, void* stream) {
+    RLK_TRY(check_common(dtype, N, V, softcap_policy, "softcap_policy"));
+    RLK_TRY(check_head_cap(softcap_ref, "softcap_ref"));
+    RowMap mp, mr;
+    RLK_TRY(check_rows(policy_rows, N, V, esize(dtype), "policy", false, &mp));
+    RLK_TRY(check_rows(ref_rows, N, V, esize(dtype), "ref", false, &mr));
+    if (N > 0 && (!kl_forward || !stats_forward))
+        return fail(RLK_ERR_ARG, "kl_forward and stats_forward must be non-null when N > 0");
+    return kl_fwd_impl(policy, ref, dtype, N, V, mp, mr, RLK_KL_REVERSE, softcap_policy,
+                       softcap_ref, kl_reverse, stats_reverse, kl_forward, stats_forward, stream);
 }
 
 rlk_status rlk_kl_bwd_strided(const void* policy, const void* ref, rlk_dtype dtype, int64_t N,
@@ -613,7 +661,37 @@ rlk_status rlk_kl_bwd_strided(const void* policy, const void* ref, rlk_dtype dty
     RLK_TRY(check_rows(grad_rows, N, V, esize(dtype), "grad_policy", true, &mg));
     RLK_TRY(check_dir(dir));
     return kl_bwd_impl(policy, ref, dtype, N, V, mp, mr, dir, softcap_policy, softcap_ref, stats,
-                       grad_kl, grad_policy, mg, stream);
+                       grad_kl, grad_policy, mg, false, stream);
+}
+
+rlk_status rlk_kl_bwd_ref(const void* policy, const void* ref, rlk_dtype dtype, int64_t N,
+                          int64_t V, int64_t ld_policy, int64_t ld_ref, rlk_kl_dir dir,
+                          float softcap_policy, float softcap_ref, const void* stats,
+                          const float* grad_kl, void* grad_ref, void* stream) {
+    RLK_TRY(check_common(dtype, N, V, softcap_policy, "softcap_policy"));
+    RLK_TRY(check_head_cap(softcap_ref, "softcap_ref"));
+    RLK_TRY(check_matrix(N, V, ld_policy, esize(dtype), "policy"));
+    RLK_TRY(check_matrix(N, V, ld_ref, esize(dtype), "ref"));
+    RLK_TRY(check_dir(dir));
+    return kl_bwd_impl(policy, ref, dtype, N, V, plain_rows(N, ld_policy), plain_rows(N, ld_ref),
+                       dir, softcap_policy, softcap_ref, stats, grad_kl, grad_ref,
+                       plain_rows(N, V), true, stream);
+}
+
+rlk_status rlk_kl_bwd_ref_strided(const void* policy, const void* ref, rlk_dtype dtype, int64_t N,
+                                  int64_t V, const rlk_rows* policy_rows,
+                                  const rlk_rows* ref_rows, rlk_kl_dir dir, float softcap_policy,
+                                  float softcap_ref, const void* stats, const float* grad_kl,
+                                  void* grad_ref, const rlk_rows* grad_rows, void* stream) {
+    RLK_TRY(check_common(dtype, N, V, softcap_policy, "softcap_policy"));
+    RLK_TRY(check_head_cap(softcap_ref, "softcap_ref"));
+    RowMap mp, mr, mg;
+    RLK_TRY(check_rows(policy_rows, N, V, esize(dtype), "policy", false, &mp));
+    RLK_TRY(check_rows(ref_rows, N, V, esize(dtype), "ref", false, &mr));
+    RLK_TRY(check_rows(grad_rows, N, V, esize(dtype), "grad_ref", true, &mg));
+    RLK_TRY(check_dir(dir));
+    return kl_bwd_impl(policy, ref, dtype, N, V, mp, mr, dir, softcap_policy, softcap_ref, stats,
+                       grad_kl, grad_ref, mg, true, stream);
 }
 
 // ------------------------------------------------- vocabulary shards

@@ -16,7 +16,10 @@
 //             logprobs, entropy and KL", Changes);
 //   entropy:  -p_v (log p_v + H);
 //   reverse KL(P||R): p_v (log p_v - log q_v - D);
-//   forward KL(R||P): p_v - q_v.
+//   forward KL(R||P): p_v - q_v;
+// and w.r.t. the reference, with the operands and the record's sides
+// exchanged (KL(P||R) is the forward KL of the pair policy R, reference P):
+//   reverse KL(P||R): q_v - p_v;  forward KL(R||P): q_v (log q_v - log p_v - D).
 #pragma once
 
 #include "rlk_device.h"
@@ -60,7 +63,14 @@ __global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void bwd_kernel(BwdParams p) {
         const S* __restrict__ xb = KL ? static_cast<const S*>(p.y) + p.my.offset(row) : nullptr;
         S* __restrict__ gx = static_cast<S*>(p.gx) + p.mg.offset(row);
 
-        const RowStats rs = stats[row];
+        RowStats rs = stats[row];
+        if (KL && p.swap) {  // differentiate w.r.t. the record's b side
+            const float m = rs.mLa, l = rs.log2Sa;
+            rs.mLa = rs.mLb;
+            rs.log2Sa = rs.log2Sb;
+            rs.mLb = m;
+            rs.log2Sb = l;
+        }
 
         int mode = kModeNormal;
         float G = 0.0f;

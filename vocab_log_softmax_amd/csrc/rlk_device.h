@@ -540,6 +540,28 @@ __device__ __forceinline__ StatKL statkl_merge(const StatKL& A, const StatKL& B)
     return o;
 }
 
+// Both KL directions of one row pair at once: the shared sums and maxima,
+// W of each direction and both mismatch flags.  The two directions' views are
+// exactly the single-direction states (same operations in the same order).
+struct StatKL2 {
+    float ma, mLa, Sa, mb, mLb, Sb, Wr, Wf, fmax, fmin;
+};
+
+__device__ __forceinline__ StatKL2 statkl2_init() {
+    return {neg_inf(), 0.0f, 0.0f, neg_inf(), 0.0f, 0.0f, 0.0f, 0.0f, neg_inf(), pos_inf()};
+}
+__device__ __forceinline__ StatKL kl_view_rev(const StatKL2& s) {
+    return {s.ma, s.mLa, s.Sa, s.mb, s.mLb, s.Sb, s.Wr, s.fmax};
+}
+__device__ __forceinline__ StatKL kl_view_fwd(const StatKL2& s) {
+    return {s.ma, s.mLa, s.Sa, s.mb, s.mLb, s.Sb, s.Wf, s.fmin};
+}
+__device__ __forceinline__ StatKL2 statkl2_merge(const StatKL2& A, const StatKL2& B) {
+    const StatKL r = statkl_merge<true>(kl_view_rev(A), kl_view_rev(B));
+    const StatKL f = statkl_merge<false>(kl_view_fwd(A), kl_view_fwd(B));
+    return {r.ma, r.mLa, r.Sa, r.mb, r.mLb, r.Sb, r.W, f.W, r.flag, f.flag};
+}
+
 // ---------------------------------------------------- wave64 shuffles
 
 __device__ __forceinline__ float shfl_xor(float v, int mask) {
@@ -574,6 +596,25 @@ __device__ __forceinline__ StatKL wave_reduce_kl(StatKL s) {
         o.W = shfl_xor(s.W, off);
         o.flag = shfl_xor(s.flag, off);
         s = statkl_merge<REVERSE>(s, o);
+    }
+    return s;
+}
+
+__device__ __forceinline__ StatKL2 wave_reduce_kl2(StatKL2 s) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        StatKL2 o;
+        o.ma = shfl_xor(s.ma, off);
+        o.mLa = shfl_xor(s.mLa, off);
+        o.Sa = shfl_xor(s.Sa, off);
+        o.mb = shfl_xor(s.mb, off);
+        o.mLb = shfl_xor(s.mLb, off);
+        o.Sb = shfl_xor(s.Sb, off);
+        o.Wr = shfl_xor(s.Wr, off);
+        o.Wf = shfl_xor(s.Wf, off);
+        o.fmax = shfl_xor(s.fmax, off);
+        o.fmin = shfl_xor(s.fmin, off);
+        s = statkl2_merge(s, o);
     }
     return s;
 }

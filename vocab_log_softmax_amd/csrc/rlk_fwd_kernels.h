@@ -115,6 +115,60 @@ __device__ __forceinline__ void update_kl(StatKL& st, const float (&a)[U][kChunk
         }
 }
 
+// Fold one group into the two-direction KL state: each direction's W and
+// flag see the very operations of update_kl<U, true> / update_kl<U, false>.
+template <int U>
+__device__ __forceinline__ void update_kl2(StatKL2& st, const float (&a)[U][kChunk],
+                                           const float (&b)[U][kChunk], float sca, float scb) {
+    float gma = a[0][0], gmb = b[0][0];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int e = 0; e < kChunk; ++e) {
+            gma = fmaxf(gma, a[u][e]);
+            gmb = fmaxf(gmb, b[u][e]);
+        }
+    if (gma > st.ma) {
+        const float mLn = gma * sca;
+        if (st.ma != neg_inf()) {
+            const float d = st.mLa - mLn;
+            const float s = ex2(d);
+            st.Wr = s * __builtin_fmaf(d, st.Sa, st.Wr);
+            st.Wf = __builtin_fmaf(-d, st.Sb, st.Wf);
+            st.Sa *= s;
+        }
+        st.ma = gma;
+        st.mLa = mLn;
+    }
+    if (gmb > st.mb) {
+        const float mLn = gmb * scb;
+        if (st.mb != neg_inf()) {
+            const float d = st.mLb - mLn;
+            const float s = ex2(d);
+            st.Wr = __builtin_fmaf(-d, st.Sa, st.Wr);
+            st.Wf = s * __builtin_fmaf(d, st.Sb, st.Wf);
+            st.Sb *= s;
+        }
+        st.mb = gmb;
+        st.mLb = mLn;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int e = 0; e < kChunk; ++e) {
+            const float ta = __builtin_fmaf(a[u][e], sca, -st.mLa);
+            const float tb = __builtin_fmaf(b[u][e], scb, -st.mLb);
+            const float ea = ex2(ta), eb = ex2(tb);
+            st.Sa += ea;
+            st.Sb += eb;
+            const float d = ta - tb;
+            st.fmax = fmaxf(st.fmax, d);
+            st.Wr = __builtin_fmaf(ea, fmaxf(d, kClampT), st.Wr);
+            st.fmin = fminf(st.fmin, d);
+            st.Wf = __builtin_fmaf(eb, fmaxf(-d, kClampT), st.Wf);
+        }
+}
+
 // Logprobs / entropy forward: one workgroup per row.
 template <int BLOCK, int U, typename T, int HEAD, bool CAP, bool ALIGNED>
 __global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void fwd1_kernel(FwdParams p) {
@@ -221,6 +275,43 @@ __global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void fwdkl_kernel(FwdParams p)
     }
 }
 
+// Both KL directions from one read of the pair: reverse KL to out / stats,
+// forward KL to out2 / stats2, each bit-identical to its one-direction call.
+template <int BLOCK, int U, typename T, bool CAPA, bool CAPB, bool ALIGNED>
+__global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void fwdkl2_kernel(FwdParams p) {
+    using S = typename T::storage;
+    constexpr int NW = BLOCK / 64;
+    __shared__ StatKL2 red[NW];
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    RowStats* stats = static_cast<RowStats*>(p.stats);
+    RowStats* stats2 = static_cast<RowStats*>(p.stats2);
+    for (int64_t row = blockIdx.x; row < p.N; row += gridDim.x) {
+        const S* __restrict__ xa = static_cast<const S*>(p.x) + p.mx.offset(row);
+        const S* __restrict__ xb = static_cast<const S*>(p.y) + p.my.offset(row);
+        StatKL2 st = statkl2_init();
+        for_each_group2<BLOCK, U, S, CAPA, CAPB, ALIGNED, kFwdPipe>(
+            xa, xb, p.V, p.kx, p.ky,
+            [&](int64_t, bool, const float (&a)[U][kChunk], const float (&b)[U][kChunk]) {
+                update_kl2<U>(st, a, b, p.scx, p.scy);
+            });
+        st = wave_reduce_kl2(st);
+        if (lane == 0) red[wid] = st;
+        __syncthreads();
+        if (tid == 0) {
+            StatKL2 r = red[0];
+#pragma unroll
+            for (int w = 1; w < NW; ++w) r = statkl2_merge(r, red[w]);
+            const RowStats rr = finalize_kl<true>(kl_view_rev(r));
+            const RowStats rf = finalize_kl<false>(kl_view_fwd(r));
+            stats[row] = rr;
+            p.out[row] = rr.value;
+            stats2[row] = rf;
+            p.out2[row] = rf.value;
+        }
+        __syncthreads();
+    }
+}
+
 // ------------------------------------------------------------- dispatch
 
 template <typename T, bool CAPX, bool CAPY, bool AL>
@@ -243,6 +334,10 @@ inline hipError_t fwd_dispatch_head(int head, const FwdParams& p, hipStream_t s)
             hipLaunchKernelGGL((fwdkl_kernel<kBlock, kUnrollKL, T, false, CAPX, CAPY, AL>), grid,
                                block, 0, s, p);
             break;
+        case kHeadKLBoth:
+            hipLaunchKernelGGL((fwdkl2_kernel<kBlock, kUnrollKL, T, CAPX, CAPY, AL>), grid, block,
+                               0, s, p);
+            break;
         default:
             return hipErrorInvalidValue;
     }
@@ -258,7 +353,7 @@ inline hipError_t fwd_dispatch_al(int head, bool al, const FwdParams& p, hipStre
 template <typename T>
 inline hipError_t fwd_dispatch_cap(int head, bool cx, bool cy, bool al, const FwdParams& p,
                                    hipStream_t s) {
-    const bool kl = head == kHeadKLReverse || head == kHeadKLForward;
+    const bool kl = head == kHeadKLReverse || head == kHeadKLForward || head == kHeadKLBoth;
     if (!kl) cy = false;  // the second cap only exists for KL
     if (cx && cy) return fwd_dispatch_al<T, true, true>(head, al, p, s);
     if (cx) return fwd_dispatch_al<T, true, false>(head, al, p, s);

@@ -8,7 +8,14 @@
 namespace rlk {
 
 // Heads of the fused row kernels.
-enum Head : int { kHeadLogp = 0, kHeadEntropy = 1, kHeadKLReverse = 2, kHeadKLForward = 3 };
+// kHeadKLBoth: forward only, both KL directions from one read of the pair.
+enum Head : int {
+    kHeadLogp = 0,
+    kHeadEntropy = 1,
+    kHeadKLReverse = 2,
+    kHeadKLForward = 3,
+    kHeadKLBoth = 4
+};
 
 // Launch shape of the row kernels: one workgroup per row (grid-stride over
 // rows), each lane consuming groups of U chunks of 8 elements.  The forward
@@ -106,6 +113,10 @@ struct FwdParams {
     int64_t v0, vtotal;
     void* part;
     float* tvals;
+    // kHeadKLBoth: the forward-KL output and row record (out / stats hold
+    // the reverse KL).
+    float* out2;
+    void* stats2;
 };
 
 struct BwdParams {
@@ -121,6 +132,7 @@ struct BwdParams {
     void* gx;        // gradient w.r.t. x, [N, V] contiguous, logits dtype
     int64_t split;   // column segments per row (one workgroup each), >= 1
     int64_t v0, vtotal;  // vocabulary shard of x (plain call: 0, V)
+    int swap;            // KL: x is the record's b side (reference gradient)
 };
 
 constexpr int kMaxShards = 64;

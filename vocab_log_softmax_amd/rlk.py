@@ -35,7 +35,8 @@ EXPORTS = ("rlk_abi_version", "rlk_stats_bytes", "rlk_status_str", "rlk_last_err
            "rlk_logp_fwd_strided", "rlk_logp_bwd_strided", "rlk_entropy_fwd_strided",
            "rlk_entropy_bwd_strided", "rlk_kl_fwd_strided", "rlk_kl_bwd_strided",
            "rlk_partial_bytes", "rlk_logp_fwd_partial", "rlk_entropy_fwd_partial",
-           "rlk_kl_fwd_partial", "rlk_combine", "rlk_logp_bwd_shard")
+           "rlk_kl_fwd_partial", "rlk_combine", "rlk_logp_bwd_shard", "rlk_kl_fwd_both",
+           "rlk_kl_fwd_both_strided", "rlk_kl_bwd_ref", "rlk_kl_bwd_ref_strided")
 
 
 class RlkRows(ctypes.Structure):
@@ -93,6 +94,12 @@ def load_library(path: str = LIB_PATH):
                          vp], ci),
         "rlk_logp_bwd_shard": ([vp, ci, i64, i64, i64, i64, i64, vp, i64, f32, vp, vp, vp, vp],
                                ci),
+        "rlk_kl_fwd_both": ([vp, vp, ci, i64, i64, i64, i64, f32, f32, vp, vp, vp, vp, vp], ci),
+        "rlk_kl_fwd_both_strided": ([vp, vp, ci, i64, i64, rp, rp, f32, f32, vp, vp, vp, vp, vp],
+                                    ci),
+        "rlk_kl_bwd_ref": ([vp, vp, ci, i64, i64, i64, i64, ci, f32, f32, vp, vp, vp, vp], ci),
+        "rlk_kl_bwd_ref_strided": ([vp, vp, ci, i64, i64, rp, rp, ci, f32, f32, vp, vp, vp, rp,
+                                    vp], ci),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -255,6 +262,54 @@ def rlk_kl_bwd(policy, ref, direction, softcap_policy, softcap_ref, stats, grad_
     _call("rlk_kl_bwd", _ptr(policy), _ptr(ref), _dtype_code(policy, "policy"), N, V,
           _ld(policy), _ld(ref), int(direction), float(softcap_policy), float(softcap_ref),
           _ptr(stats), _ptr(grad_kl), _ptr(grad_policy), _stream(policy))
+
+
+def rlk_kl_fwd_both(policy, ref, softcap_policy, softcap_ref, kl_rev, stats_rev, kl_fwd,
+                    stats_fwd) -> None:
+    N, V = policy.shape
+    if tuple(ref.shape) != (N, V) or ref.dtype != policy.dtype:
+        raise ValueError("policy and ref must have the same shape and dtype")
+    _need(kl_rev, torch.float32, (N,), "kl_rev")
+    _need(kl_fwd, torch.float32, (N,), "kl_fwd")
+    _call("rlk_kl_fwd_both", _ptr(policy), _ptr(ref), _dtype_code(policy, "policy"), N, V,
+          _ld(policy), _ld(ref), float(softcap_policy), float(softcap_ref), _ptr(kl_rev),
+          _ptr(stats_rev), _ptr(kl_fwd), _ptr(stats_fwd), _stream(policy))
+
+
+def rlk_kl_bwd_ref(policy, ref, direction, softcap_policy, softcap_ref, stats, grad_kl,
+                   grad_ref) -> None:
+    N, V = policy.shape
+    _need(grad_kl, torch.float32, (N,), "grad_kl")
+    _need(grad_ref, ref.dtype, (N, V), "grad_ref")
+    _call("rlk_kl_bwd_ref", _ptr(policy), _ptr(ref), _dtype_code(policy, "policy"), N, V,
+          _ld(policy), _ld(ref), int(direction), float(softcap_policy), float(softcap_ref),
+          _ptr(stats), _ptr(grad_kl), _ptr(grad_ref), _stream(policy))
+
+
+def rlk_kl_fwd_both_strided(policy, ref, softcap_policy, softcap_ref, kl_rev, stats_rev, kl_fwd,
+                            stats_fwd) -> None:
+    B, T, V = policy.shape
+    N = B * T
+    _need(kl_rev, torch.float32, (N,), "kl_rev")
+    _need(kl_fwd, torch.float32, (N,), "kl_fwd")
+    rp, rr = rows_of(policy), rows_of(ref)
+    _call("rlk_kl_fwd_both_strided", _ptr(policy), _ptr(ref), _dtype_code(policy, "policy"), N,
+          V, ctypes.byref(rp), ctypes.byref(rr), float(softcap_policy), float(softcap_ref),
+          _ptr(kl_rev), _ptr(stats_rev), _ptr(kl_fwd), _ptr(stats_fwd), _stream(policy))
+
+
+def rlk_kl_bwd_ref_strided(policy, ref, direction, softcap_policy, softcap_ref, stats, grad_kl,
+                           grad_ref) -> None:
+    B, T, V = policy.shape
+    N = B * T
+    _need(grad_kl, torch.float32, (N,), "grad_kl")
+    if grad_ref.dtype != ref.dtype or tuple(grad_ref.shape) != (B, T, V):
+        raise ValueError("grad_ref must be a [B, T, V] view in the logits dtype")
+    rp, rr, rg = rows_of(policy), rows_of(ref), rows_of(grad_ref)
+    _call("rlk_kl_bwd_ref_strided", _ptr(policy), _ptr(ref), _dtype_code(policy, "policy"), N,
+          V, ctypes.byref(rp), ctypes.byref(rr), int(direction), float(softcap_policy),
+          float(softcap_ref), _ptr(stats), _ptr(grad_kl), _ptr(grad_ref), ctypes.byref(rg),
+          _stream(policy))
 
 
 def rlk_logp_fwd_strided(logits, targets, softcap, logp, stats) -> None:
@@ -522,6 +577,44 @@ def kl_bwd(policy, ref, grad_kl, stats, direction=RLK_KL_REVERSE, softcap_policy
     return gx
 
 
+def kl_fwd_both(policy, ref, softcap_policy=0.0, softcap_ref=0.0):
+    """Reverse and forward KL from one read: (kl_rev, stats_rev, kl_fwd, stats_fwd)."""
+    three = policy.dim() == 3
+    if three:
+        policy, ref = _view3(policy, "policy"), _view3(ref, "ref")
+        B, T, V = policy.shape
+        N = B * T
+    else:
+        policy, ref = _rows(policy, "policy"), _rows(ref, "ref")
+        N, V = policy.shape
+    outs = [torch.empty(N, dtype=torch.float32, device=policy.device) for _ in range(2)]
+    sts = [new_stats(RLK_HEAD_KL, N, V, policy.device) for _ in range(2)]
+    fn = rlk_kl_fwd_both_strided if three else rlk_kl_fwd_both
+    fn(policy, ref, softcap_policy, softcap_ref, outs[0], sts[0], outs[1], sts[1])
+    if three:
+        outs = [o.reshape(B, T) for o in outs]
+    return outs[0], sts[0], outs[1], sts[1]
+
+
+def kl_bwd_ref(policy, ref, grad_kl, stats, direction=RLK_KL_REVERSE, softcap_policy=0.0,
+               softcap_ref=0.0, out=None):
+    """Gradient of the KL with respect to the reference logits."""
+    if policy.dim() == 3:
+        policy, ref = _view3(policy, "policy"), _view3(ref, "ref")
+        B, T, V = policy.shape
+        gr = out if out is not None else torch.empty((B, T, V), dtype=ref.dtype,
+                                                     device=ref.device)
+        rlk_kl_bwd_ref_strided(policy, ref, direction, softcap_policy, softcap_ref, stats,
+                               grad_kl.reshape(-1).to(torch.float32).contiguous(), gr)
+        return gr
+    policy, ref = _rows(policy, "policy"), _rows(ref, "ref")
+    N, V = policy.shape
+    gr = torch.empty((N, V), dtype=ref.dtype, device=ref.device)
+    rlk_kl_bwd_ref(policy, ref, direction, softcap_policy, softcap_ref, stats,
+                   grad_kl.to(torch.float32).contiguous(), gr)
+    return gr
+
+
 def softcap_fwd(x, cap=30.0, out_dtype=torch.float32):
     x = x.contiguous()
     y = torch.empty(x.shape, dtype=out_dtype, device=x.device)
@@ -579,7 +672,10 @@ class _KL(torch.autograd.Function):
     def backward(ctx, g):
         policy, ref, stats = ctx.saved_tensors
         direction, cp, cr = ctx.args
-        return kl_bwd(policy, ref, g, stats, direction, cp, cr), None, None, None, None
+        gp = kl_bwd(policy, ref, g, stats, direction, cp, cr) if ctx.needs_input_grad[0] else None
+        gr = (kl_bwd_ref(policy, ref, g, stats, direction, cp, cr) if ctx.needs_input_grad[1]
+              else None)
+        return gp, gr, None, None, None
 
 
 class _Softcap(torch.autograd.Function):
@@ -604,9 +700,12 @@ def entropy(logits, softcap=0.0):
     return _Entropy.apply(logits, softcap)
 
 
-def kl_divergence(policy, ref, direction=RLK_KL_REVERSE, softcap_policy=0.0, softcap_ref=0.0):
-    """KL per row; the gradient flows to ``policy`` only (``ref`` is detached)."""
-    return _KL.apply(policy, ref.detach(), direction, softcap_policy, softcap_ref)
+def kl_divergence(policy, ref, direction=RLK_KL_REVERSE, softcap_policy=0.0, softcap_ref=0.0,
+                  detach_ref=True):
+    """KL per row; the gradient flows to ``policy`` and, with ``detach_ref=False``,
+    to ``ref`` as well."""
+    return _KL.apply(policy, ref.detach() if detach_ref else ref, direction, softcap_policy,
+                     softcap_ref)
 
 
 def softcap(x, cap=30.0):
