@@ -18,6 +18,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -57,6 +58,38 @@ def traffic_from_profiles(workload: str, kernel: str):
     if not (m_hash and m_rd and m_wr) or m_hash.group(1) != kernel_source_hash():
         return None
     return float(m_rd.group(1)) + float(m_wr.group(1))
+
+
+class HipEvents:
+    """Raw hipEvent_t timers, recorded on a raw stream handle.
+
+    torch.cuda.Event.record costs a few microseconds of host time per call,
+    which would dominate a launch-bound workload's step; hipEventRecord on
+    the HIP runtime torch already loaded costs a fraction of that.
+    """
+
+    def __init__(self, n: int, torch):
+        lib_dir = os.path.join(os.path.dirname(torch.__file__), "lib")
+        path = os.path.join(lib_dir, "libamdhip64.so")
+        # same soname as the runtime torch loaded -> the same instance
+        self.hip = ctypes.CDLL(path if os.path.exists(path) else "libamdhip64.so.7")
+        self.ev = [ctypes.c_void_p() for _ in range(n)]
+        for e in self.ev:
+            if self.hip.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+
+    def record(self, i: int, stream) -> None:
+        self.hip.hipEventRecord(self.ev[i], stream)
+
+    def elapsed_ms(self, i: int, j: int) -> float:
+        ms = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(ms), self.ev[i], self.ev[j]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def close(self) -> None:
+        for e in self.ev:
+            self.hip.hipEventDestroy(e)
 
 
 def side_bytes(w, N):
@@ -177,19 +210,23 @@ def main() -> int:
         bwd()
     torch.cuda.synchronize()
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # HIP events on the stream the kernels run on, three per step: before the
+    # forward, between forward and backward, after the backward.
+    ev = HipEvents(3 * args.steps, torch)
+    raw = ctypes.c_void_p(stream.cuda_stream)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for e in ev:
-        e[0].record(stream)
+    for i in range(args.steps):
+        ev.record(3 * i, raw)
         fwd()
-        e[1].record(stream)
+        ev.record(3 * i + 1, raw)
         bwd()
-        e[2].record(stream)
+        ev.record(3 * i + 2, raw)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / len(ev)
-    bwd_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / len(ev)
+    fwd_ms = sum(ev.elapsed_ms(3 * i, 3 * i + 1) for i in range(args.steps)) / args.steps
+    bwd_ms = sum(ev.elapsed_ms(3 * i + 1, 3 * i + 2) for i in range(args.steps)) / args.steps
+    ev.close()
     ms_per_step = wall * 1e3 / args.steps
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
 
