@@ -92,6 +92,52 @@ class HipEvents:
             self.hip.hipEventDestroy(e)
 
 
+def measure_ceilings(w, dev, torch) -> dict:
+    """Practical HBM ceilings at the workload's tensor size (libceiling.so).
+
+    Read-only, write-only and copy streams of 16-byte nontemporal accesses,
+    grid-stride and row by row (one workgroup per row of V logits, as the
+    library's kernels stream); median of 15 timed launches after 3 warm-up
+    launches, HIP events on the current stream.
+    """
+    from vocab_log_softmax_amd import build as B
+
+    if not os.path.exists(B.CEILING_LIB):
+        raise SystemExit(f"{B.CEILING_LIB} is missing: run __graft_entry__.build()")
+    lib = ctypes.CDLL(B.CEILING_LIB)
+    lib.ceiling_run.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    lib.ceiling_run.restype = ctypes.c_int
+    row_bytes = w.V * w.esize
+    bytes_ = w.N * row_bytes
+    src = torch.ones(bytes_ // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    raw = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    ev = HipEvents(2 * 15, torch)
+    out = {"bytes_per_tensor": bytes_, "row_bytes": row_bytes}
+    kinds = {"read_grid_stride": (0, 1), "write_grid_stride": (1, 1), "copy_grid_stride": (2, 2),
+             "read_rows": (3, 1), "copy_rows": (4, 2)}
+    for name, (kind, passes) in kinds.items():
+        def run():
+            rc = lib.ceiling_run(kind, src.data_ptr(), dst.data_ptr(), bytes_, row_bytes,
+                                 sink.data_ptr(), raw)
+            if rc != 0:
+                raise RuntimeError(f"ceiling_run({name}) failed: {rc}")
+        for _ in range(3):
+            run()
+        for i in range(15):
+            ev.record(2 * i, raw)
+            run()
+            ev.record(2 * i + 1, raw)
+        torch.cuda.synchronize()
+        ts = sorted(ev.elapsed_ms(2 * i, 2 * i + 1) for i in range(15))
+        ms = ts[len(ts) // 2]
+        out[name] = {"ms": round(ms, 4), "GB/s": round(passes * bytes_ / (ms * 1e-3) / 1e9, 1)}
+    ev.close()
+    return {"ceilings": out, "workload": w.name}
+
+
 def side_bytes(w, N):
     """Per-step bytes of the per-row side arrays (targets, grads, outputs, stats)."""
     k = w.k
@@ -138,6 +184,8 @@ def main() -> int:
     ap.add_argument("--oracle-rows", type=int, default=4096,
                     help="rows of the workload timed on the CPU oracle")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="only measure the read / write / copy ceilings at the workload's size")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain device copy of a known size (counter calibration)")
     args = ap.parse_args()
@@ -169,6 +217,9 @@ def main() -> int:
         print(json.dumps({"copy_probe_bytes_each_way": src.numel(), "launches": 3}))
         return 0
     w = workloads.WORKLOADS[args.workload]
+    if args.ceilings:
+        print(json.dumps(measure_ceilings(w, dev, torch)))
+        return 0
     d = workloads.make_inputs(args.workload, dev)
     x = d["logits"]
     N, V = x.shape
@@ -205,27 +256,41 @@ def main() -> int:
     bwd_bytes = (n_in + 1) * N * V * es + sb      # read again, write the gradient once
     step_bytes = fwd_bytes + bwd_bytes
 
+    torch.cuda.synchronize()
+    tw = time.perf_counter()
     for _ in range(args.warmup):
         fwd()
         bwd()
     torch.cuda.synchronize()
+    warm_ms = (time.perf_counter() - tw) * 1e3 / max(1, args.warmup)
 
-    # HIP events on the stream the kernels run on, three per step: before the
-    # forward, between forward and backward, after the backward.
-    ev = HipEvents(3 * args.steps, torch)
+    # HIP events on the stream the kernels run on, three per sampled step:
+    # before the forward, between forward and backward, after the backward.
+    # Every step is sampled unless a step is so short (launch-bound) that the
+    # event markers themselves would show in its wall time; then every
+    # tenth step is.
+    stride = 1 if warm_ms > 0.2 else 10
+    sampled = list(range(0, args.steps, stride))
+    ev = HipEvents(3 * len(sampled), torch)
     raw = ctypes.c_void_p(stream.cuda_stream)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    j = 0
     for i in range(args.steps):
-        ev.record(3 * i, raw)
-        fwd()
-        ev.record(3 * i + 1, raw)
-        bwd()
-        ev.record(3 * i + 2, raw)
+        if i % stride == 0:
+            ev.record(3 * j, raw)
+            fwd()
+            ev.record(3 * j + 1, raw)
+            bwd()
+            ev.record(3 * j + 2, raw)
+            j += 1
+        else:
+            fwd()
+            bwd()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    fwd_ms = sum(ev.elapsed_ms(3 * i, 3 * i + 1) for i in range(args.steps)) / args.steps
-    bwd_ms = sum(ev.elapsed_ms(3 * i + 1, 3 * i + 2) for i in range(args.steps)) / args.steps
+    fwd_ms = sum(ev.elapsed_ms(3 * j, 3 * j + 1) for j in range(len(sampled))) / len(sampled)
+    bwd_ms = sum(ev.elapsed_ms(3 * j + 1, 3 * j + 2) for j in range(len(sampled))) / len(sampled)
     ev.close()
     ms_per_step = wall * 1e3 / args.steps
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
@@ -243,6 +308,7 @@ def main() -> int:
         "traffic": traffic,
         "algorithmic_bytes_per_launch": bwd_bytes,
         "avg_launch_ms": round(bwd_ms, 4),
+        "event_timed_steps": len(sampled),
         "second_kernel": {"kernel": f"{fwd_name} ({w.head} forward)", "avg_launch_ms":
                           round(fwd_ms, 4), "achieved": round(fwd_gbs, 1),
                           "frac": round(fwd_gbs / HBM_PEAK_GBS, 4),

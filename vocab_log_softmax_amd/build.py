@@ -20,6 +20,9 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "librlk.so")
+# Bandwidth probes for the benchmark's ceiling report (not part of the ABI).
+CEILING_SRC = os.path.join(PKG, "ceiling", "ceiling.hip")
+CEILING_LIB = os.path.join(PKG, "ceiling", "libceiling.so")
 
 SOURCES = ["rlk_fwd_f32.hip", "rlk_fwd_bf16.hip", "rlk_fwd_f16.hip",
            "rlk_bwd_f32.hip", "rlk_bwd_bf16.hip", "rlk_bwd_f16.hip",
@@ -39,7 +42,7 @@ def _compile(src: str, build_dir: str = BUILD_DIR, defines=()) -> str:
     cmd = [HIPCC, *FLAGS, *[f"-D{d}" for d in defines]]
     if src.endswith(".cpp"):
         cmd += ["-x", "hip"]
-    cmd += ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd += ["-c", src if os.path.isabs(src) else os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     err = "\n".join(line for line in r.stderr.splitlines() if noise not in line)
@@ -70,5 +73,21 @@ def build(verbose: bool = True, out_path: str = LIB_PATH, defines=(), build_dir=
     return out_path
 
 
+def build_ceiling(verbose: bool = True) -> str:
+    """Compile the bandwidth probes into libceiling.so (benchmark only)."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    obj = _compile(CEILING_SRC, BUILD_DIR)
+    tmp = CEILING_LIB + ".tmp"
+    r = subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", obj, "-o", tmp],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stderr}")
+    os.replace(tmp, CEILING_LIB)
+    if verbose:
+        print(f"built {CEILING_LIB}")
+    return CEILING_LIB
+
+
 if __name__ == "__main__":
     build()
+    build_ceiling()

@@ -1,0 +1,134 @@
+// ceiling.hip -- bandwidth probes that give the practical HBM ceilings the
+// row kernels are compared with: read-only, write-only and copy streams of
+// 16-byte nontemporal accesses, in two patterns:
+//   * grid-stride: thread i touches 16-byte words i, i + T, i + 2T, ...
+//     (T = grid x block), the usual streaming probe;
+//   * rows: one workgroup per row of `row_bytes`, lanes striding the row as
+//     the library's kernels do (reads: 256 threads, 4 words per lane in
+//     flight; copies: 1024 threads, 8 words per lane in flight).
+// Measurement infrastructure only (built as libceiling.so, loaded by the
+// benchmark); every access is bounds-checked against the buffer or the row.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(1024) void read_gs(const u32x4* __restrict__ a, int64_t n16,
+                                                uint32_t* __restrict__ sink) {
+    uint32_t acc = 0;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) {
+        const u32x4 v = __builtin_nontemporal_load(a + i);
+        acc ^= v.x ^ v.y ^ v.z ^ v.w;
+    }
+    if (acc == 0x9e3779b9u) sink[0] = acc;  // keeps the loads; practically never stores
+}
+
+__global__ __launch_bounds__(1024) void write_gs(u32x4* __restrict__ b, int64_t n16) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    const u32x4 v = {threadIdx.x, 1u, 2u, 3u};
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride)
+        __builtin_nontemporal_store(v, b + i);
+}
+
+__global__ __launch_bounds__(1024) void copy_gs(const u32x4* __restrict__ a,
+                                                u32x4* __restrict__ b, int64_t n16) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride)
+        __builtin_nontemporal_store(__builtin_nontemporal_load(a + i), b + i);
+}
+
+template <int BS, int U>
+__global__ __launch_bounds__(BS) void read_rows(const u32x4* __restrict__ a, int64_t rows,
+                                                int64_t row16, uint32_t* __restrict__ sink) {
+    uint32_t acc = 0;
+    for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+        const u32x4* ra = a + r * row16;
+        for (int64_t c0 = threadIdx.x; c0 < row16; c0 += (int64_t)U * BS) {
+            u32x4 v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t c = c0 + (int64_t)u * BS;
+                v[u] = c < row16 ? __builtin_nontemporal_load(ra + c) : u32x4{0u, 0u, 0u, 0u};
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+        }
+    }
+    if (acc == 0x9e3779b9u) sink[0] = acc;
+}
+
+template <int BS, int U>
+__global__ __launch_bounds__(BS) void copy_rows(const u32x4* __restrict__ a,
+                                                u32x4* __restrict__ b, int64_t rows,
+                                                int64_t row16) {
+    for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+        const u32x4* ra = a + r * row16;
+        u32x4* rb = b + r * row16;
+        for (int64_t c0 = threadIdx.x; c0 < row16; c0 += (int64_t)U * BS) {
+            u32x4 v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t c = c0 + (int64_t)u * BS;
+                if (c < row16) v[u] = __builtin_nontemporal_load(ra + c);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t c = c0 + (int64_t)u * BS;
+                if (c < row16) __builtin_nontemporal_store(v[u], rb + c);
+            }
+        }
+    }
+}
+
+int grid_of(int64_t n) { return static_cast<int>(n < 1 ? 1 : (n < (1 << 20) ? n : (1 << 20))); }
+
+}  // namespace
+
+extern "C" {
+
+// kind: 0 read grid-stride, 1 write grid-stride, 2 copy grid-stride,
+//       3 read rows, 4 copy rows.  bytes and row_bytes are multiples of 16;
+// src / dst hold `bytes` (dst unused by reads); sink holds 4 bytes.
+// Returns 0 on success, 1 on bad arguments, 2 if the launch failed.
+int ceiling_run(int kind, const void* src, void* dst, int64_t bytes, int64_t row_bytes,
+                void* sink, void* stream) {
+    if (bytes <= 0 || bytes % 16 != 0) return 1;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const int64_t n16 = bytes / 16;
+    const auto* a = static_cast<const u32x4*>(src);
+    auto* b = static_cast<u32x4*>(dst);
+    auto* k = static_cast<uint32_t*>(sink);
+    const int gs_block = 1024;
+    const int gs_grid = grid_of((n16 + gs_block - 1) / gs_block / 2);  // ~2 words per thread
+    switch (kind) {
+        case 0:
+            hipLaunchKernelGGL(read_gs, dim3(gs_grid), dim3(gs_block), 0, s, a, n16, k);
+            break;
+        case 1:
+            hipLaunchKernelGGL(write_gs, dim3(gs_grid), dim3(gs_block), 0, s, b, n16);
+            break;
+        case 2:
+            hipLaunchKernelGGL(copy_gs, dim3(gs_grid), dim3(gs_block), 0, s, a, b, n16);
+            break;
+        case 3:
+        case 4: {
+            if (row_bytes <= 0 || row_bytes % 16 != 0 || bytes % row_bytes != 0) return 1;
+            const int64_t rows = bytes / row_bytes, row16 = row_bytes / 16;
+            if (kind == 3)
+                hipLaunchKernelGGL((read_rows<256, 4>), dim3(grid_of(rows)), dim3(256), 0, s, a,
+                                   rows, row16, k);
+            else
+                hipLaunchKernelGGL((copy_rows<1024, 8>), dim3(grid_of(rows)), dim3(1024), 0, s, a,
+                                   b, rows, row16);
+            break;
+        }
+        default:
+            return 1;
+    }
+    return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+}  // extern "C"

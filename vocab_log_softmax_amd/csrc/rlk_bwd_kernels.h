@@ -33,6 +33,73 @@ constexpr int kGLanes = 256;
 // Row modes.
 enum : int { kModeNormal = 0, kModeZero = 1, kModeNaN = 2, kModeMismatch = 3 };
 
+// The record with its a and b sides exchanged (gradient w.r.t. the KL
+// reference: the operands are exchanged too).
+__device__ __forceinline__ void swap_sides(RowStats& rs) {
+    const float m = rs.mLa, l = rs.log2Sa;
+    rs.mLa = rs.mLb;
+    rs.log2Sa = rs.log2Sb;
+    rs.mLb = m;
+    rs.log2Sb = l;
+}
+
+// Per-row coefficients of grad_elem (the slope 4 r (1 - r) has its 4 folded
+// in): logp A = -G; entropy A = -g ln2, B = -g H; reverse KL A = g ln2,
+// B = -g D; forward KL A = g.
+template <int HEAD, bool CAPA>
+__device__ __forceinline__ void row_coeffs(const RowStats& rs, float G, float g_row, float& A,
+                                           float& B) {
+    A = 0.0f;
+    B = 0.0f;
+    if (HEAD == kHeadLogp) {
+        A = CAPA ? -4.0f * G : -G;
+    } else if (HEAD == kHeadEntropy) {
+        A = (CAPA ? -4.0f : -1.0f) * g_row * kLn2;
+        B = (CAPA ? -4.0f : -1.0f) * g_row * rs.value;
+    } else if (HEAD == kHeadKLReverse) {
+        A = (CAPA ? 4.0f : 1.0f) * g_row * kLn2;
+        B = (CAPA ? -4.0f : -1.0f) * g_row * rs.value;
+    } else {
+        A = CAPA ? 4.0f * g_row : g_row;
+    }
+}
+
+// Gradient of one element from its statistic inputs (a; b for KL) and the
+// row's record and coefficients; p comes from the forward's own FMA.
+template <int HEAD, bool CAPA>
+__device__ __forceinline__ float grad_elem(float a, float b, const RowStats& rs, float A, float B,
+                                           float scx, float scy) {
+    const float ta = __builtin_fmaf(a, scx, -rs.mLa) - rs.log2Sa;
+    float o;
+    if (HEAD == kHeadLogp) {
+        o = A * ex2(ta);
+    } else if (HEAD == kHeadEntropy) {
+        const float tc = CAPA ? ta : fmaxf(ta, kClampT);
+        o = ex2(tc) * __builtin_fmaf(A, tc, B);
+    } else {
+        const float tb = __builtin_fmaf(b, scy, -rs.mLb) - rs.log2Sb;
+        if (HEAD == kHeadKLReverse) {
+            const float l = CAPA ? ta - tb : fmaxf(ta - tb, kClampT);
+            o = ex2(ta) * __builtin_fmaf(A, l, B);
+        } else {
+            o = A * (ex2(ta) - ex2(tb));
+        }
+    }
+    // slope / 4 = r (1 - r) = r - r^2 in one FMA (the 4 is in A, B)
+    if (CAPA) o *= __builtin_fmaf(-a, a, a);
+    return o;
+}
+
+// Logprobs gradient at a target column: h - p G (h: the column's summed
+// upstream gradients), times the cap's slope.
+template <bool CAPA>
+__device__ __forceinline__ float target_grad(float a, const RowStats& rs, float G, float h,
+                                             float scx) {
+    const float pt = ex2(__builtin_fmaf(a, scx, -rs.mLa) - rs.log2Sa);
+    const float v = __builtin_fmaf(-pt, G, h);
+    return CAPA ? v * cap_slope_r(a) : v;
+}
+
 template <int BLOCK, int U, typename T, int HEAD, bool CAPA, bool CAPB, bool ALIGNED>
 __global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void bwd_kernel(BwdParams p) {
     using S = typename T::storage;
@@ -64,13 +131,7 @@ __global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void bwd_kernel(BwdParams p) {
         S* __restrict__ gx = static_cast<S*>(p.gx) + p.mg.offset(row);
 
         RowStats rs = stats[row];
-        if (KL && p.swap) {  // differentiate w.r.t. the record's b side
-            const float m = rs.mLa, l = rs.log2Sa;
-            rs.mLa = rs.mLb;
-            rs.log2Sa = rs.log2Sb;
-            rs.mLb = m;
-            rs.log2Sb = l;
-        }
+        if (KL && p.swap) swap_sides(rs);  // differentiate w.r.t. the record's b side
 
         int mode = kModeNormal;
         float G = 0.0f;
@@ -122,20 +183,9 @@ __global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void bwd_kernel(BwdParams p) {
                 mode = kModeMismatch;
         }
 
-        // Per-row coefficients (the slope 4 r (1 - r) has its 4 folded in).
         const float g_row = (HEAD == kHeadLogp) ? 0.0f : p.g[row];
-        float A = 0.0f, B = 0.0f;
-        if (HEAD == kHeadLogp) {
-            A = CAPA ? -4.0f * G : -G;
-        } else if (HEAD == kHeadEntropy) {
-            A = (CAPA ? -4.0f : -1.0f) * g_row * kLn2;
-            B = (CAPA ? -4.0f : -1.0f) * g_row * rs.value;
-        } else if (HEAD == kHeadKLReverse) {
-            A = (CAPA ? 4.0f : 1.0f) * g_row * kLn2;
-            B = (CAPA ? -4.0f : -1.0f) * g_row * rs.value;
-        } else {
-            A = CAPA ? 4.0f * g_row : g_row;
-        }
+        float A, B;
+        row_coeffs<HEAD, CAPA>(rs, G, g_row, A, B);
 
         // Gradient of one group from its logit values.
         auto grad_group = [&](const float (&a)[U][kChunk], const float (&b)[UB][kChunk],
@@ -143,26 +193,9 @@ __global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void bwd_kernel(BwdParams p) {
 #pragma unroll
             for (int u = 0; u < U; ++u)
 #pragma unroll
-                for (int e = 0; e < kChunk; ++e) {
-                    const float ta = __builtin_fmaf(a[u][e], p.scx, -rs.mLa) - rs.log2Sa;
-                    float o;
-                    if (HEAD == kHeadLogp) {
-                        o = A * ex2(ta);
-                    } else if (HEAD == kHeadEntropy) {
-                        const float tc = CAPA ? ta : fmaxf(ta, kClampT);
-                        o = ex2(tc) * __builtin_fmaf(A, tc, B);
-                    } else {
-                        const float tb = __builtin_fmaf(b[KL ? u : 0][e], p.scy, -rs.mLb) - rs.log2Sb;
-                        if (HEAD == kHeadKLReverse) {
-                            const float l = CAPA ? ta - tb : fmaxf(ta - tb, kClampT);
-                            o = ex2(ta) * __builtin_fmaf(A, l, B);
-                        } else {
-                            o = A * (ex2(ta) - ex2(tb));
-                        }
-                    }
-                    if (CAPA) o *= a[u][e] * (1.0f - a[u][e]);  // slope / 4 (4 is in A, B)
-                    v[u][e] = o;
-                }
+                for (int e = 0; e < kChunk; ++e)
+                    v[u][e] = grad_elem<HEAD, CAPA>(a[u][e], b[KL ? u : 0][e], rs, A, B, p.scx,
+                                                    p.scy);
         };
 
         if (mode == kModeNormal) {
@@ -228,16 +261,131 @@ __global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void bwd_kernel(BwdParams p) {
                     }
                 }
                 if (!first) continue;
-                float a = load_one(xa + t), slope = 1.0f;
-                if (CAPA) {
-                    a = cap_r(a, p.kx);
-                    slope = cap_slope_r(a);
-                }
-                const float pt = ex2(__builtin_fmaf(a, p.scx, -rs.mLa) - rs.log2Sa);
-                store_one(gx + t, __builtin_fmaf(-pt, G, h) * slope);
+                float a = load_one(xa + t);
+                if (CAPA) a = cap_r(a, p.kx);
+                store_one(gx + t, target_grad<CAPA>(a, rs, G, h, p.scx));
             }
         }
         __syncthreads();
+    }
+}
+
+// Logprobs calls with at most this many slots per row take the piece kernel.
+constexpr int kPieceMaxK = 4;
+
+// One-shot pieces: every workgroup computes the gradient of one chunk per
+// lane (BLOCK x 8 consecutive columns) of one row and exits.  Its loads are
+// issued before anything else, there is no barrier, no LDS and no loop, and
+// a workgroup's stores never hold up the next load: on this part such a
+// stream of short workgroups moves noticeably more bytes per second than
+// row-long loops.  Logprobs slots (k <= kPieceMaxK) are read by every lane:
+// G is summed in the association of the row kernel's tree, and target
+// columns take target_grad, so both kernels give the same bits.
+template <int BLOCK, typename T, int HEAD, bool CAPA, bool CAPB, bool ALIGNED>
+__global__ __launch_bounds__(BLOCK) void bwd_piece_kernel(BwdParams p, int64_t rbase) {
+    using S = typename T::storage;
+    constexpr bool KL = HEAD == kHeadKLReverse || HEAD == kHeadKLForward;
+    const int64_t nfull = p.V / kChunk;
+    const RowStats* stats = static_cast<const RowStats*>(p.stats);
+    {
+        // grid (pieces of a row, rows): consecutive workgroups take consecutive
+        // pieces of a row, so the chip sweeps the matrix front to back; rows
+        // run last-first (see bwd_kernel).
+        const int64_t row = p.N - 1 - (rbase + static_cast<int64_t>(blockIdx.y));
+        const int64_t g0 = static_cast<int64_t>(blockIdx.x) * BLOCK;  // first chunk of the piece
+        const int64_t c = g0 + (int)threadIdx.x;                       // this lane's chunk
+        const S* __restrict__ xa = static_cast<const S*>(p.x) + p.mx.offset(row);
+        S* __restrict__ gx = static_cast<S*>(p.gx) + p.mg.offset(row);
+
+        float a[1][kChunk], b[1][kChunk];
+        tail_values<BLOCK, 1, S, CAPA, ALIGNED>(xa, p.V, nfull, g0, p.kx, a);
+        if (KL) {
+            const S* __restrict__ xb = static_cast<const S*>(p.y) + p.my.offset(row);
+            tail_values<BLOCK, 1, S, CAPB, ALIGNED>(xb, p.V, nfull, g0, p.ky, b);
+        }
+
+        RowStats rs = stats[row];
+        if (KL && p.swap) swap_sides(rs);
+
+        int mode = kModeNormal;
+        float G = 0.0f;
+        int64_t tl[kPieceMaxK];  // local column of each slot, -1 if none
+        float gs[kPieceMaxK];
+        if (HEAD == kHeadLogp) {
+            float sv[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // valid slots' g, zeros beyond k
+            int nvalid = 0;
+#pragma unroll
+            for (int j = 0; j < kPieceMaxK; ++j) {
+                tl[j] = -1;
+                gs[j] = 0.0f;
+                if (j < p.k) {
+                    const int64_t t = p.targets[row * p.k + j];
+                    const float g = p.g[row * p.k + j];
+                    const bool valid = t >= 0 && t < p.vtotal;
+                    tl[j] = (t >= p.v0 && t < p.v0 + p.V) ? t - p.v0 : -1;
+                    gs[j] = g;
+                    if (valid) {
+                        sv[j] = g;
+                        ++nvalid;
+                    }
+                }
+            }
+            // the row kernel's wave64 butterfly over lanes 0..3 holding the slots
+            G = (sv[0] + sv[2]) + (sv[1] + sv[3]);
+            if (nvalid == 0)
+                mode = kModeZero;
+            else if (rs.flags & kFlagEmptyA)
+                mode = kModeNaN;
+        } else if (HEAD == kHeadEntropy) {
+            if (rs.flags & kFlagEmptyA) mode = kModeNaN;
+        } else {
+            if (rs.flags & (kFlagEmptyA | kFlagEmptyB))
+                mode = kModeNaN;
+            else if (HEAD == kHeadKLReverse && (rs.flags & kFlagMismatch))
+                mode = kModeMismatch;
+        }
+
+        float v[1][kChunk];
+        if (mode == kModeNormal) {
+            const float g_row = (HEAD == kHeadLogp) ? 0.0f : p.g[row];
+            float A, B;
+            row_coeffs<HEAD, CAPA>(rs, G, g_row, A, B);
+#pragma unroll
+            for (int e = 0; e < kChunk; ++e)
+                v[0][e] = grad_elem<HEAD, CAPA>(a[0][e], KL ? b[0][e] : 0.0f, rs, A, B, p.scx,
+                                                p.scy);
+            if (HEAD == kHeadLogp) {
+                // one-hot terms: a slot whose column falls in this lane's chunk
+                const int64_t col0 = c * kChunk;
+                bool any = false;
+#pragma unroll
+                for (int j = 0; j < kPieceMaxK; ++j)
+                    any |= tl[j] >= col0 && tl[j] < col0 + kChunk;
+                if (any) {
+#pragma unroll
+                    for (int e = 0; e < kChunk; ++e) {
+                        float h = 0.0f;
+                        bool hit = false;
+#pragma unroll
+                        for (int j = 0; j < kPieceMaxK; ++j)
+                            if (tl[j] == col0 + e) {
+                                h += gs[j];
+                                hit = true;
+                            }
+                        if (hit) v[0][e] = target_grad<CAPA>(a[0][e], rs, G, h, p.scx);
+                    }
+                }
+            }
+        } else if (mode == kModeMismatch) {
+#pragma unroll
+            for (int e = 0; e < kChunk; ++e)
+                v[0][e] = (!CAPA && a[0][e] == neg_inf()) ? 0.0f : qnan();
+        } else {
+            const float fill = mode == kModeZero ? 0.0f : qnan();
+#pragma unroll
+            for (int e = 0; e < kChunk; ++e) v[0][e] = fill;
+        }
+        store_group<BLOCK, 1, S, ALIGNED>(gx, p.V, g0, g0 + BLOCK <= nfull, v);
     }
 }
 
@@ -245,8 +393,9 @@ __global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void bwd_kernel(BwdParams p) {
 //
 // The backward is elementwise given the row record (and G has a fixed tree),
 // so its launch shape does not change any result and is chosen per call:
-// 1024-thread workgroups for the plain streaming rows, 512 when a wide top-k
-// fix-up follows each row (fewer idle lanes per row, more rows per CU).
+// one-shot 256-thread pieces for entropy, KL and logprobs with k <= 4; for
+// wider top-k the row kernel, 512-thread workgroups (fewer idle lanes during
+// each row's fix-up), rows cut into column segments when there are few.
 
 template <int BB, int U1, int UKL, typename T, bool CAPX, bool CAPY, bool AL>
 inline hipError_t bwd_dispatch_head(int head, const BwdParams& p, hipStream_t s) {
@@ -276,10 +425,48 @@ inline hipError_t bwd_dispatch_head(int head, const BwdParams& p, hipStream_t s)
     return hipGetLastError();
 }
 
+// Rows per piece launch (the grid's second dimension is limited to 65536).
+constexpr int64_t kPieceRowsPerLaunch = 65536;
+
+template <typename T, int HEAD, bool CAPX, bool CAPY, bool AL>
+inline hipError_t bwd_piece_launch(const BwdParams& p, int64_t pieces, hipStream_t s) {
+    for (int64_t r0 = 0; r0 < p.N; r0 += kPieceRowsPerLaunch) {
+        const int64_t rows = p.N - r0 < kPieceRowsPerLaunch ? p.N - r0 : kPieceRowsPerLaunch;
+        const dim3 grid(static_cast<unsigned>(pieces), static_cast<unsigned>(rows));
+        hipLaunchKernelGGL((bwd_piece_kernel<kBwdPieceBlock, T, HEAD, CAPX, CAPY, AL>), grid,
+                           dim3(kBwdPieceBlock), 0, s, p, r0);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+template <typename T, bool CAPX, bool CAPY, bool AL>
+inline hipError_t bwd_piece_dispatch(int head, const BwdParams& p, int64_t pieces,
+                                     hipStream_t s) {
+    switch (head) {
+        case kHeadLogp:
+            return bwd_piece_launch<T, kHeadLogp, CAPX, false, AL>(p, pieces, s);
+        case kHeadEntropy:
+            return bwd_piece_launch<T, kHeadEntropy, CAPX, false, AL>(p, pieces, s);
+        case kHeadKLReverse:
+            return bwd_piece_launch<T, kHeadKLReverse, CAPX, CAPY, AL>(p, pieces, s);
+        case kHeadKLForward:
+            return bwd_piece_launch<T, kHeadKLForward, CAPX, CAPY, AL>(p, pieces, s);
+        default:
+            return hipErrorInvalidValue;
+    }
+}
+
 template <typename T, bool CAPX, bool CAPY>
 inline hipError_t bwd_dispatch_al(int head, bool al, const BwdParams& p0, hipStream_t s) {
     BwdParams p = p0;
     p.split = 1;
+    const int64_t pieces =
+        ((p.V + kChunk - 1) / kChunk + kBwdPieceBlock - 1) / kBwdPieceBlock;
+    if (kBwdPieces && (head != kHeadLogp || p.k <= kPieceMaxK) && pieces <= kMaxGrid)
+        return al ? bwd_piece_dispatch<T, CAPX, CAPY, true>(head, p, pieces, s)
+                  : bwd_piece_dispatch<T, CAPX, CAPY, false>(head, p, pieces, s);
     if (p.N < kBwdSmallRows) {
         // Few rows: narrow workgroups, each row cut into column segments.
         const int64_t step = (int64_t)kBwdUnrollSmall * kBwdBlockSmall;

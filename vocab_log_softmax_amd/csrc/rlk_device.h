@@ -170,7 +170,7 @@ __device__ __forceinline__ void store_one(_Float16* p, float f) { *p = static_ca
 // x = -inf: r = 0, i.e. y = -c; slope 0 at both).  The absolute error of r
 // is about 1e-7 and the softmax depends only on absolute errors of y.
 __device__ __forceinline__ float cap_r(float x, float k) { return rcp(1.0f + ex2(x * k)); }
-__device__ __forceinline__ float cap_slope_r(float r) { return 4.0f * r * (1.0f - r); }
+__device__ __forceinline__ float cap_slope_r(float r) { return 4.0f * __builtin_fmaf(-r, r, r); }
 
 // Standalone form, accurate in RELATIVE terms (the output y itself is
 // compared at 1e-5 relative).  For |u| < 0.55 an odd polynomial

@@ -50,6 +50,14 @@ enum Head : int {
 #ifndef RLK_BWD_WIDE_TOPK
 #define RLK_BWD_WIDE_TOPK 64
 #endif
+// Backward in one-shot pieces (every workgroup handles BLOCK chunks of one
+// row and exits) for every head except logprobs with more than a few slots.
+#ifndef RLK_BWD_PIECES
+#define RLK_BWD_PIECES 1
+#endif
+#ifndef RLK_BWD_PIECE_BLOCK
+#define RLK_BWD_PIECE_BLOCK 256
+#endif
 #ifndef RLK_FWD_PIPE
 #define RLK_FWD_PIPE 1
 #endif
@@ -58,6 +66,8 @@ enum Head : int {
 #endif
 constexpr bool kFwdPipe = RLK_FWD_PIPE;
 constexpr bool kBwdPipe = RLK_BWD_PIPE;
+constexpr bool kBwdPieces = RLK_BWD_PIECES;
+constexpr int kBwdPieceBlock = RLK_BWD_PIECE_BLOCK;
 // Minimum waves per SIMD requested from the register allocator (0: none).
 #ifndef RLK_WAVES_PER_EU
 #define RLK_WAVES_PER_EU 0
@@ -82,7 +92,9 @@ constexpr int kBwdBlockSmall = 256;
 constexpr int kBwdUnrollSmall = 1;
 constexpr int64_t kBwdSmallRows = 512;      // below this many rows
 constexpr int64_t kBwdTargetItems = 2048;   // aim for this many (row, segment) items
-constexpr int kMaxGrid = 1 << 20;
+// Largest grid in workgroups: a dispatch counts work-items in 32 bits, and
+// blocks are at most 1024 threads.
+constexpr int kMaxGrid = (1 << 22) - 1;
 
 // Row i of a (possibly two-stride) view starts at element
 // (i / T) * sb + (i % T) * st: a [B, T, V] view with strides (sb, st, 1).
@@ -90,6 +102,11 @@ constexpr int kMaxGrid = 1 << 20;
 struct RowMap {
     int64_t T, sb, st;
     __host__ __device__ int64_t offset(int64_t i) const {
+        if (i < T) return i * st;  // first (or only) batch: no division
+        if (((i | T) >> 32) == 0) {  // 32-bit division when both fit
+            const int64_t b = static_cast<uint32_t>(i) / static_cast<uint32_t>(T);
+            return b * sb + (i - b * T) * st;
+        }
         const int64_t b = i / T;
         return b * sb + (i - b * T) * st;
     }
