@@ -181,7 +181,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c2_logp_bf16")
-    ap.add_argument("--oracle-rows", type=int, default=4096,
+    ap.add_argument("--oracle-rows", type=int, default=8192,
                     help="rows of the workload timed on the CPU oracle")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--ceilings", action="store_true",
@@ -233,7 +233,9 @@ def main() -> int:
         gx = torch.empty_like(x)
         fwd = lambda: rlk.rlk_logp_fwd(x, tg, w.cap, out, st)          # noqa: E731
         bwd = lambda: rlk.rlk_logp_bwd(x, tg, w.cap, st, g, gx)        # noqa: E731
-        n_in, fwd_name, bwd_name = 1, "fwd1_kernel", "bwd_kernel"
+        # k <= 4 slots: one-shot pieces; wider top-k: the row kernel
+        n_in, fwd_name, bwd_name = 1, "fwd1_kernel", ("bwd_piece_kernel" if w.k <= 4
+                                                      else "bwd_kernel")
     elif w.head == "entropy":
         g = d["grad"]
         out = torch.empty(N, dtype=torch.float32, device=dev)
@@ -241,7 +243,7 @@ def main() -> int:
         gx = torch.empty_like(x)
         fwd = lambda: rlk.rlk_entropy_fwd(x, w.cap, out, st)           # noqa: E731
         bwd = lambda: rlk.rlk_entropy_bwd(x, w.cap, st, g, gx)         # noqa: E731
-        n_in, fwd_name, bwd_name = 1, "fwd1_kernel", "bwd_kernel"
+        n_in, fwd_name, bwd_name = 1, "fwd1_kernel", "bwd_piece_kernel"
     else:
         ref, g = d["ref"], d["grad"]
         out = torch.empty(N, dtype=torch.float32, device=dev)
@@ -249,7 +251,7 @@ def main() -> int:
         gx = torch.empty_like(x)
         fwd = lambda: rlk.rlk_kl_fwd(x, ref, 0, 0.0, 0.0, out, st)     # noqa: E731
         bwd = lambda: rlk.rlk_kl_bwd(x, ref, 0, 0.0, 0.0, st, g, gx)   # noqa: E731
-        n_in, fwd_name, bwd_name = 2, "fwdkl_kernel", "bwd_kernel"
+        n_in, fwd_name, bwd_name = 2, "fwdkl_kernel", "bwd_piece_kernel"
 
     sf, sb = side_bytes(w, N)
     fwd_bytes = n_in * N * V * es + sf            # read every input logit once
