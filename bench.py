@@ -251,7 +251,7 @@ def main() -> int:
         bwd = lambda: rlk.rlk_logp_bwd(x, tg, w.cap, st, g, gx)        # noqa: E731
         # k <= 4 slots: one-shot pieces; wider top-k: the row kernel
         n_in, fwd_name, bwd_name = 1, "fwd1_kernel", ("bwd_piece_kernel" if w.k <= 4
-                                                      else "bwd_kernel")
+                                                      else "bwd_topk_kernel")
     elif w.head == "entropy":
         g = d["grad"]
         out = torch.empty(N, dtype=torch.float32, device=dev)

@@ -151,3 +151,27 @@ def test_outputs_independent_of_stats_buffer_history(dev):
     torch.cuda.synchronize()
     assert_bitwise(lp, out2, "logp")
     assert_bitwise(g1, g2, "grad")
+
+
+@pytest.mark.parametrize("N", [37, 700])
+@pytest.mark.parametrize("cap", [0.0, 20.0])
+def test_piece_and_topk_backward_kernels_agree(dev, N, cap):
+    # k <= 4 runs the one-shot piece kernel, k = 5 the top-k row kernel
+    # (few rows: column segments); a fifth slot that is ignored changes
+    # neither G nor any one-hot sum, so both must give the same bits.
+    V = 9001
+    x = (torch.randn(N, V, generator=_gen(11)) * 3).to(torch.bfloat16).to(dev)
+    t4 = torch.randint(0, V, (N, 4), generator=_gen(12))
+    t4[::7, 2] = t4[::7, 0]          # duplicates
+    t4[::5, 1] = -100                # ignored
+    t5 = torch.cat([t4, torch.full((N, 1), -100, dtype=torch.int64)], 1)
+    g4 = torch.randn(N, 4, generator=_gen(13))
+    g5 = torch.cat([g4, torch.randn(N, 1, generator=_gen(14))], 1)
+    t4, t5, g4, g5 = t4.to(dev), t5.to(dev), g4.to(dev), g5.to(dev)
+    lp4, st4 = rlk.logp_fwd(x, t4, cap)
+    lp5, st5 = rlk.logp_fwd(x, t5, cap)
+    gx4 = rlk.logp_bwd(x, t4, g4, st4, cap)
+    gx5 = rlk.logp_bwd(x, t5, g5, st5, cap)
+    torch.cuda.synchronize()
+    assert_bitwise(lp4, lp5[:, :4], "forward outputs")
+    assert_bitwise(gx4, gx5, "gradients of the two backward kernels")

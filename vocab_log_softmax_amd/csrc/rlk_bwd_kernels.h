@@ -100,13 +100,17 @@ __device__ __forceinline__ float target_grad(float a, const RowStats& rs, float 
     return CAPA ? v * cap_slope_r(a) : v;
 }
 
-template <int BLOCK, int U, typename T, int HEAD, bool CAPA, bool CAPB, bool ALIGNED>
-__global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void bwd_kernel(BwdParams p) {
+// Logprobs with wide top-k: one workgroup per (row, column segment), visited
+// last-first (the end of the forward's stream is what the Infinity Cache
+// still holds).  The k slots are staged in LDS and G is summed in a tree
+// fixed by kGLanes (slot j by lane j mod kGLanes, in order), not by BLOCK;
+// after the bulk pass a barrier orders the target columns' one-hot rewrites
+// after the bulk stores of the same addresses.
+template <int BLOCK, int U, typename T, bool CAPA, bool ALIGNED>
+__global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void bwd_topk_kernel(BwdParams p) {
     using S = typename T::storage;
-    constexpr bool KL = HEAD == kHeadKLReverse || HEAD == kHeadKLForward;
-    constexpr int UB = KL ? U : 1;  // reference group (KL only)
     static_assert(BLOCK >= kGLanes, "the G tree needs kGLanes threads");
-    extern __shared__ int smem_topk[];  // logp: int32 target (-1: ignored) [k], fp32 g [k]
+    extern __shared__ int smem_topk[];  // int32 local target (-1 ignored, -2 other shard) [k], fp32 g [k]
     __shared__ float red_g[kGLanes / 64];
     __shared__ float red_n[kGLanes / 64];
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -119,139 +123,68 @@ __global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void bwd_kernel(BwdParams p) {
     float* gg = reinterpret_cast<float*>(smem_topk + p.k);
 
     for (int64_t it = blockIdx.x; it < p.N * p.split; it += gridDim.x) {
-        // Work item = (row, column segment).  Rows are visited last-first: the
-        // end of the forward's stream is the part still held in the Infinity
-        // Cache when the backward follows it.
         const int64_t rit = it / p.split, seg = it - rit * p.split;
         const int64_t row = p.N - 1 - rit;
         const int64_t gbeg = seg * gps, gend = gbeg + gps < ngroups ? gbeg + gps : ngroups;
         const int64_t cbeg = gbeg * step * kChunk, cend = gend * step * kChunk;  // columns
         const S* __restrict__ xa = static_cast<const S*>(p.x) + p.mx.offset(row);
-        const S* __restrict__ xb = KL ? static_cast<const S*>(p.y) + p.my.offset(row) : nullptr;
         S* __restrict__ gx = static_cast<S*>(p.gx) + p.mg.offset(row);
+        const RowStats rs = stats[row];
 
-        RowStats rs = stats[row];
-        if (KL && p.swap) swap_sides(rs);  // differentiate w.r.t. the record's b side
-
-        int mode = kModeNormal;
-        float G = 0.0f;
-        if (HEAD == kHeadLogp) {
-            // Stage the slots and sum G over the valid ones.  The tree is fixed
-            // by kGLanes (slot j is summed by lane j mod kGLanes, in order),
-            // not by BLOCK, so G has the same bits for every launch shape.
-            float part = 0.0f, cnt = 0.0f;
-            if (tid < kGLanes) {
-                for (int64_t j = tid; j < p.k; j += kGLanes) {
-                    // valid over the whole row; local to this vocabulary shard
-                    // (plain call: the same) -> its column, else -1 / -2
-                    const int64_t t = p.targets[row * p.k + j];
-                    const bool valid = t >= 0 && t < p.vtotal;
-                    const bool local = t >= p.v0 && t < p.v0 + p.V;
-                    const float g = p.g[row * p.k + j];
-                    tg[j] = local ? static_cast<int>(t - p.v0) : (valid ? -2 : -1);
-                    gg[j] = g;
-                    if (valid) {
-                        part += g;
-                        cnt += 1.0f;
-                    }
+        // Stage the slots (valid over the whole row; local to this vocabulary
+        // shard -- plain call: the same -- as its column, else -1 / -2).
+        float part = 0.0f, cnt = 0.0f;
+        if (tid < kGLanes) {
+            for (int64_t j = tid; j < p.k; j += kGLanes) {
+                const int64_t t = p.targets[row * p.k + j];
+                const bool valid = t >= 0 && t < p.vtotal;
+                const bool local = t >= p.v0 && t < p.v0 + p.V;
+                const float g = p.g[row * p.k + j];
+                tg[j] = local ? static_cast<int>(t - p.v0) : (valid ? -2 : -1);
+                gg[j] = g;
+                if (valid) {
+                    part += g;
+                    cnt += 1.0f;
                 }
             }
-            part = wave_sum(part);
-            cnt = wave_sum(cnt);
-            if (lane == 0 && wid < kGLanes / 64) {
-                red_g[wid] = part;
-                red_n[wid] = cnt;
-            }
-            __syncthreads();
-            float n = red_n[0];
-            G = red_g[0];
-#pragma unroll
-            for (int w = 1; w < kGLanes / 64; ++w) {
-                G += red_g[w];
-                n += red_n[w];
-            }
-            if (n == 0.0f)
-                mode = kModeZero;
-            else if (rs.flags & kFlagEmptyA)
-                mode = kModeNaN;
-        } else if (HEAD == kHeadEntropy) {
-            if (rs.flags & kFlagEmptyA) mode = kModeNaN;
-        } else {
-            if (rs.flags & (kFlagEmptyA | kFlagEmptyB))
-                mode = kModeNaN;
-            else if (HEAD == kHeadKLReverse && (rs.flags & kFlagMismatch))
-                mode = kModeMismatch;
         }
-
-        const float g_row = (HEAD == kHeadLogp) ? 0.0f : p.g[row];
-        float A, B;
-        row_coeffs<HEAD, CAPA>(rs, G, g_row, A, B);
-
-        // Gradient of one group from its logit values.
-        auto grad_group = [&](const float (&a)[U][kChunk], const float (&b)[UB][kChunk],
-                              float (&v)[U][kChunk]) {
+        part = wave_sum(part);
+        cnt = wave_sum(cnt);
+        if (lane == 0 && wid < kGLanes / 64) {
+            red_g[wid] = part;
+            red_n[wid] = cnt;
+        }
+        __syncthreads();
+        float n = red_n[0], G = red_g[0];
 #pragma unroll
-            for (int u = 0; u < U; ++u)
-#pragma unroll
-                for (int e = 0; e < kChunk; ++e)
-                    v[u][e] = grad_elem<HEAD, CAPA>(a[u][e], b[KL ? u : 0][e], rs, A, B, p.scx,
-                                                    p.scy);
-        };
+        for (int w = 1; w < kGLanes / 64; ++w) {
+            G += red_g[w];
+            n += red_n[w];
+        }
+        const int mode = n == 0.0f ? kModeZero : ((rs.flags & kFlagEmptyA) ? kModeNaN : kModeNormal);
 
         if (mode == kModeNormal) {
-            if (KL) {
-                for_each_group2<BLOCK, U, S, CAPA, CAPB, ALIGNED, kBwdPipe>(
-                    xa, xb, p.V, p.kx, p.ky,
-                    [&](int64_t g0, bool full, const float (&a)[U][kChunk],
-                        const float (&b)[U][kChunk]) {
-                        float v[U][kChunk];
-                        grad_group(a, reinterpret_cast<const float(&)[UB][kChunk]>(b), v);
-                        store_group<BLOCK, U, S, ALIGNED>(gx, p.V, g0, full, v);
-                    },
-                    gbeg, gend);
-            } else {
-                for_each_group<BLOCK, U, S, CAPA, ALIGNED, kBwdPipe>(
-                    xa, p.V, p.kx, [&](int64_t g0, bool full, const float (&a)[U][kChunk]) {
-                        float v[U][kChunk];
-                        const float b[UB][kChunk] = {};
-                        grad_group(a, b, v);
-                        store_group<BLOCK, U, S, ALIGNED>(gx, p.V, g0, full, v);
-                    },
-                    gbeg, gend);
-            }
-        } else if (mode == kModeMismatch) {
-            // Reverse KL with a support mismatch: NaN on the policy's support,
-            // 0 on its masked columns.
-            for_each_group<BLOCK, U, S, false, ALIGNED, kBwdPipe>(
-                xa, p.V, 0.0f, [&](int64_t g0, bool full, const float (&a)[U][kChunk]) {
+            float A, B;
+            row_coeffs<kHeadLogp, CAPA>(rs, G, 0.0f, A, B);
+            for_each_group<BLOCK, U, S, CAPA, ALIGNED, kBwdPipe>(
+                xa, p.V, p.kx,
+                [&](int64_t g0, bool full, const float (&a)[U][kChunk]) {
                     float v[U][kChunk];
 #pragma unroll
                     for (int u = 0; u < U; ++u)
 #pragma unroll
                         for (int e = 0; e < kChunk; ++e)
-                            v[u][e] = (!CAPA && a[u][e] == neg_inf()) ? 0.0f : qnan();
+                            v[u][e] = grad_elem<kHeadLogp, CAPA>(a[u][e], 0.0f, rs, A, B, p.scx,
+                                                                 p.scy);
                     store_group<BLOCK, U, S, ALIGNED>(gx, p.V, g0, full, v);
                 },
                 gbeg, gend);
-        } else {
-            const float fill = mode == kModeZero ? 0.0f : qnan();
-            float v[U][kChunk];
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-#pragma unroll
-                for (int e = 0; e < kChunk; ++e) v[u][e] = fill;
-            for (int64_t g0 = gbeg * step; g0 < gend * step; g0 += step)
-                store_group<BLOCK, U, S, ALIGNED>(gx, p.V, g0, g0 + step <= nfull, v);
-        }
-
-        if (HEAD == kHeadLogp && mode == kModeNormal) {
-            // Target columns: rewrite the bulk value with its one-hot term.
-            // The barrier orders these stores after this workgroup's bulk
-            // stores of the same addresses.
+            // Target columns of this segment: the bulk value becomes the
+            // one-hot term (first slot of each column sums its duplicates).
             __syncthreads();
             for (int64_t j = tid; j < p.k; j += BLOCK) {
                 const int t = tg[j];
-                if (t < 0 || t < cbeg || t >= cend) continue;  // not in this segment
+                if (t < 0 || t < cbeg || t >= cend) continue;
                 bool first = true;
                 float h = 0.0f;
                 for (int64_t jj = 0; jj < p.k; ++jj) {
@@ -265,12 +198,22 @@ __global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void bwd_kernel(BwdParams p) {
                 if (CAPA) a = cap_r(a, p.kx);
                 store_one(gx + t, target_grad<CAPA>(a, rs, G, h, p.scx));
             }
+        } else {
+            const float fill = mode == kModeZero ? 0.0f : qnan();
+            float v[U][kChunk];
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int e = 0; e < kChunk; ++e) v[u][e] = fill;
+            for (int64_t g0 = gbeg * step; g0 < gend * step; g0 += step)
+                store_group<BLOCK, U, S, ALIGNED>(gx, p.V, g0, g0 + step <= nfull, v);
         }
         __syncthreads();
     }
 }
 
-// Logprobs calls with at most this many slots per row take the piece kernel.
+// Logprobs calls with at most this many slots per row take the piece kernel
+// (wider ones bwd_topk_kernel).
 constexpr int kPieceMaxK = 4;
 
 // One-shot pieces: every workgroup computes the gradient of one chunk per
@@ -290,7 +233,7 @@ __global__ __launch_bounds__(BLOCK) void bwd_piece_kernel(BwdParams p, int64_t r
     {
         // grid (pieces of a row, rows): consecutive workgroups take consecutive
         // pieces of a row, so the chip sweeps the matrix front to back; rows
-        // run last-first (see bwd_kernel).
+        // run last-first (see bwd_topk_kernel).
         const int64_t row = p.N - 1 - (rbase + static_cast<int64_t>(blockIdx.y));
         const int64_t g0 = static_cast<int64_t>(blockIdx.x) * BLOCK;  // first chunk of the piece
         const int64_t c = g0 + (int)threadIdx.x;                       // this lane's chunk
@@ -394,42 +337,16 @@ __global__ __launch_bounds__(BLOCK) void bwd_piece_kernel(BwdParams p, int64_t r
 // The backward is elementwise given the row record (and G has a fixed tree),
 // so its launch shape does not change any result and is chosen per call:
 // one-shot 256-thread pieces for entropy, KL and logprobs with k <= 4; for
-// wider top-k the row kernel, 512-thread workgroups (fewer idle lanes during
-// each row's fix-up), rows cut into column segments when there are few.
-
-template <int BB, int U1, int UKL, typename T, bool CAPX, bool CAPY, bool AL>
-inline hipError_t bwd_dispatch_head(int head, const BwdParams& p, hipStream_t s) {
-    const dim3 grid(row_grid(p.N * p.split)), block(BB);
-    switch (head) {
-        case kHeadLogp: {
-            const size_t lds = static_cast<size_t>(p.k) * (sizeof(int) + sizeof(float));
-            hipLaunchKernelGGL((bwd_kernel<BB, U1, T, kHeadLogp, CAPX, false, AL>), grid, block,
-                               lds, s, p);
-            break;
-        }
-        case kHeadEntropy:
-            hipLaunchKernelGGL((bwd_kernel<BB, U1, T, kHeadEntropy, CAPX, false, AL>), grid, block,
-                               0, s, p);
-            break;
-        case kHeadKLReverse:
-            hipLaunchKernelGGL((bwd_kernel<BB, UKL, T, kHeadKLReverse, CAPX, CAPY, AL>), grid,
-                               block, 0, s, p);
-            break;
-        case kHeadKLForward:
-            hipLaunchKernelGGL((bwd_kernel<BB, UKL, T, kHeadKLForward, CAPX, CAPY, AL>), grid,
-                               block, 0, s, p);
-            break;
-        default:
-            return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
-}
+// wider top-k bwd_topk_kernel with 512-thread workgroups (fewer idle lanes
+// during each row's fix-up), or, for fewer than kBwdSmallRows rows, 256-thread
+// workgroups with the rows cut into column segments.
 
 // Rows per piece launch (the grid's second dimension is limited to 65536).
 constexpr int64_t kPieceRowsPerLaunch = 65536;
 
 template <typename T, int HEAD, bool CAPX, bool CAPY, bool AL>
-inline hipError_t bwd_piece_launch(const BwdParams& p, int64_t pieces, hipStream_t s) {
+inline hipError_t bwd_piece_launch(const BwdParams& p, hipStream_t s) {
+    const int64_t pieces = ((p.V + kChunk - 1) / kChunk + kBwdPieceBlock - 1) / kBwdPieceBlock;
     for (int64_t r0 = 0; r0 < p.N; r0 += kPieceRowsPerLaunch) {
         const int64_t rows = p.N - r0 < kPieceRowsPerLaunch ? p.N - r0 : kPieceRowsPerLaunch;
         const dim3 grid(static_cast<unsigned>(pieces), static_cast<unsigned>(rows));
@@ -441,53 +358,40 @@ inline hipError_t bwd_piece_launch(const BwdParams& p, int64_t pieces, hipStream
     return hipSuccess;
 }
 
+template <int BB, int U, typename T, bool CAPX, bool AL>
+inline hipError_t bwd_topk_launch(const BwdParams& p, hipStream_t s) {
+    const size_t lds = static_cast<size_t>(p.k) * (sizeof(int) + sizeof(float));
+    hipLaunchKernelGGL((bwd_topk_kernel<BB, U, T, CAPX, AL>), dim3(row_grid(p.N * p.split)),
+                       dim3(BB), lds, s, p);
+    return hipGetLastError();
+}
+
 template <typename T, bool CAPX, bool CAPY, bool AL>
-inline hipError_t bwd_piece_dispatch(int head, const BwdParams& p, int64_t pieces,
-                                     hipStream_t s) {
+inline hipError_t bwd_dispatch_al(int head, const BwdParams& p0, hipStream_t s) {
     switch (head) {
-        case kHeadLogp:
-            return bwd_piece_launch<T, kHeadLogp, CAPX, false, AL>(p, pieces, s);
         case kHeadEntropy:
-            return bwd_piece_launch<T, kHeadEntropy, CAPX, false, AL>(p, pieces, s);
+            return bwd_piece_launch<T, kHeadEntropy, CAPX, false, AL>(p0, s);
         case kHeadKLReverse:
-            return bwd_piece_launch<T, kHeadKLReverse, CAPX, CAPY, AL>(p, pieces, s);
+            return bwd_piece_launch<T, kHeadKLReverse, CAPX, CAPY, AL>(p0, s);
         case kHeadKLForward:
-            return bwd_piece_launch<T, kHeadKLForward, CAPX, CAPY, AL>(p, pieces, s);
+            return bwd_piece_launch<T, kHeadKLForward, CAPX, CAPY, AL>(p0, s);
+        case kHeadLogp:
+            break;
         default:
             return hipErrorInvalidValue;
     }
-}
-
-template <typename T, bool CAPX, bool CAPY>
-inline hipError_t bwd_dispatch_al(int head, bool al, const BwdParams& p0, hipStream_t s) {
+    if (p0.k <= kPieceMaxK) return bwd_piece_launch<T, kHeadLogp, CAPX, false, AL>(p0, s);
     BwdParams p = p0;
-    p.split = 1;
-    const int64_t pieces =
-        ((p.V + kChunk - 1) / kChunk + kBwdPieceBlock - 1) / kBwdPieceBlock;
-    if (kBwdPieces && (head != kHeadLogp || p.k <= kPieceMaxK) && pieces <= kMaxGrid)
-        return al ? bwd_piece_dispatch<T, CAPX, CAPY, true>(head, p, pieces, s)
-                  : bwd_piece_dispatch<T, CAPX, CAPY, false>(head, p, pieces, s);
     if (p.N < kBwdSmallRows) {
         // Few rows: narrow workgroups, each row cut into column segments.
         const int64_t step = (int64_t)kBwdUnrollSmall * kBwdBlockSmall;
         const int64_t ngroups = ((p.V + kChunk - 1) / kChunk + step - 1) / step;
-        int64_t split = (kBwdTargetItems + p.N - 1) / p.N;
-        p.split = split < ngroups ? split : ngroups;
-        return al ? bwd_dispatch_head<kBwdBlockSmall, kBwdUnrollSmall, kBwdUnrollSmall, T, CAPX,
-                                      CAPY, true>(head, p, s)
-                  : bwd_dispatch_head<kBwdBlockSmall, kBwdUnrollSmall, kBwdUnrollSmall, T, CAPX,
-                                      CAPY, false>(head, p, s);
+        const int64_t split = (kBwdTargetItems + p.N - 1) / p.N;
+        p.split = split < ngroups ? split : (ngroups > 0 ? ngroups : 1);
+        return bwd_topk_launch<kBwdBlockSmall, kBwdUnrollSmall, T, CAPX, AL>(p, s);
     }
-    const bool wide_topk = head == kHeadLogp && p.k >= kBwdWideTopk;
-    if (wide_topk)
-        return al ? bwd_dispatch_head<kBwdBlockTopk, kBwdUnrollTopk, kBwdUnrollTopk, T, CAPX, CAPY,
-                                      true>(head, p, s)
-                  : bwd_dispatch_head<kBwdBlockTopk, kBwdUnrollTopk, kBwdUnrollTopk, T, CAPX, CAPY,
-                                      false>(head, p, s);
-    return al ? bwd_dispatch_head<kBwdBlock, kBwdUnroll1, kBwdUnrollKL, T, CAPX, CAPY, true>(head, p,
-                                                                                            s)
-              : bwd_dispatch_head<kBwdBlock, kBwdUnroll1, kBwdUnrollKL, T, CAPX, CAPY, false>(head,
-                                                                                             p, s);
+    p.split = 1;
+    return bwd_topk_launch<kBwdBlockTopk, kBwdUnrollTopk, T, CAPX, AL>(p, s);
 }
 
 template <typename T>
@@ -495,10 +399,14 @@ inline hipError_t bwd_dispatch_cap(int head, bool cx, bool cy, bool al, const Bw
                                    hipStream_t s) {
     const bool kl = head == kHeadKLReverse || head == kHeadKLForward;
     if (!kl) cy = false;
-    if (cx && cy) return bwd_dispatch_al<T, true, true>(head, al, p, s);
-    if (cx) return bwd_dispatch_al<T, true, false>(head, al, p, s);
-    if (cy) return bwd_dispatch_al<T, false, true>(head, al, p, s);
-    return bwd_dispatch_al<T, false, false>(head, al, p, s);
+    if (cx && cy) return al ? bwd_dispatch_al<T, true, true, true>(head, p, s)
+                            : bwd_dispatch_al<T, true, true, false>(head, p, s);
+    if (cx) return al ? bwd_dispatch_al<T, true, false, true>(head, p, s)
+                      : bwd_dispatch_al<T, true, false, false>(head, p, s);
+    if (cy) return al ? bwd_dispatch_al<T, false, true, true>(head, p, s)
+                      : bwd_dispatch_al<T, false, true, false>(head, p, s);
+    return al ? bwd_dispatch_al<T, false, false, true>(head, p, s)
+              : bwd_dispatch_al<T, false, false, false>(head, p, s);
 }
 
 }  // namespace rlk

@@ -17,8 +17,8 @@ enum Head : int {
     kHeadKLBoth = 4
 };
 
-// Launch shape of the row kernels: one workgroup per row (grid-stride over
-// rows), each lane consuming groups of U chunks of 8 elements.  The forward
+// Launch shape of the forward row kernels: one workgroup per row (grid-stride
+// over rows), each lane consuming groups of U chunks of 8 elements.  These
 // constants fix the reduction tree, so they are the same for every N (the
 // batch-invariance guarantee).  The backward is elementwise given the row
 // record, so its shape is free; it is tuned for the read+write stream.
@@ -32,29 +32,15 @@ enum Head : int {
 #ifndef RLK_UNROLL_KL
 #define RLK_UNROLL_KL 2
 #endif
-#ifndef RLK_BWD_BLOCK
-#define RLK_BWD_BLOCK 1024
-#endif
-#ifndef RLK_BWD_UNROLL1
-#define RLK_BWD_UNROLL1 2
-#endif
-#ifndef RLK_BWD_UNROLL_KL
-#define RLK_BWD_UNROLL_KL 1
-#endif
 #ifndef RLK_BWD_BLOCK_TOPK
 #define RLK_BWD_BLOCK_TOPK 512
 #endif
 #ifndef RLK_BWD_UNROLL_TOPK
 #define RLK_BWD_UNROLL_TOPK 2
 #endif
-#ifndef RLK_BWD_WIDE_TOPK
-#define RLK_BWD_WIDE_TOPK 64
-#endif
 // Backward in one-shot pieces (every workgroup handles BLOCK chunks of one
-// row and exits) for every head except logprobs with more than a few slots.
-#ifndef RLK_BWD_PIECES
-#define RLK_BWD_PIECES 1
-#endif
+// row and exits) for every head except logprobs with more than a few slots,
+// whose row kernel takes the _TOPK shape.
 #ifndef RLK_BWD_PIECE_BLOCK
 #define RLK_BWD_PIECE_BLOCK 256
 #endif
@@ -66,7 +52,6 @@ enum Head : int {
 #endif
 constexpr bool kFwdPipe = RLK_FWD_PIPE;
 constexpr bool kBwdPipe = RLK_BWD_PIPE;
-constexpr bool kBwdPieces = RLK_BWD_PIECES;
 constexpr int kBwdPieceBlock = RLK_BWD_PIECE_BLOCK;
 // Minimum waves per SIMD requested from the register allocator (0: none).
 #ifndef RLK_WAVES_PER_EU
@@ -80,12 +65,8 @@ constexpr int kBwdPieceBlock = RLK_BWD_PIECE_BLOCK;
 constexpr int kBlock = RLK_BLOCK;
 constexpr int kUnroll1 = RLK_UNROLL1;    // forward, single-tensor heads
 constexpr int kUnrollKL = RLK_UNROLL_KL;  // forward, KL (two tensors per group)
-constexpr int kBwdBlock = RLK_BWD_BLOCK;
-constexpr int kBwdUnroll1 = RLK_BWD_UNROLL1;
-constexpr int kBwdUnrollKL = RLK_BWD_UNROLL_KL;
-constexpr int kBwdBlockTopk = RLK_BWD_BLOCK_TOPK;    // logp backward with k >= kBwdWideTopk
+constexpr int kBwdBlockTopk = RLK_BWD_BLOCK_TOPK;  // logprobs backward with wide top-k
 constexpr int kBwdUnrollTopk = RLK_BWD_UNROLL_TOPK;
-constexpr int kBwdWideTopk = RLK_BWD_WIDE_TOPK;
 // Few rows: a narrow shape whose rows are also split into column segments,
 // so that there are enough workgroups to cover the chip.
 constexpr int kBwdBlockSmall = 256;
