@@ -43,33 +43,51 @@ __device__ __forceinline__ void swap_sides(RowStats& rs) {
     rs.log2Sb = l;
 }
 
-// Per-row coefficients of grad_elem (the slope 4 r (1 - r) has its 4 folded
-// in): logp A = -G; entropy A = -g ln2, B = -g H; reverse KL A = g ln2,
-// B = -g D; forward KL A = g.
+// Per-row coefficients of grad_elem.  With t = y log2 e - mL (the exponent
+// of the forward's FMA), p = 2^t / S, so the row's 1 / S = 2^-log2 S (as the
+// record holds it) and the log2 S shift of log p are folded into the
+// coefficients once per row instead of subtracted per element:
+//   logp        A = -G / S                          o = A 2^t
+//   entropy     A = -g ln2 / S, B = -g (H - ln2 log2 S) / S
+//                                                   o = 2^t (A t + B)
+//   reverse KL  A = g ln2 / S_a, B = -g (D + ln2 (log2 S_a - log2 S_b)) / S_a
+//                                                   o = 2^ta (A (ta - tb) + B)
+//   forward KL  A = g / S_a, B = g / S_b             o = A 2^ta - B 2^tb
+// (the slope 4 r (1 - r) of the cap has its 4 folded in as well).
 template <int HEAD, bool CAPA>
 __device__ __forceinline__ void row_coeffs(const RowStats& rs, float G, float g_row, float& A,
                                            float& B) {
-    A = 0.0f;
-    B = 0.0f;
+    float a0 = 0.0f, b0 = 0.0f;
     if (HEAD == kHeadLogp) {
-        A = CAPA ? -4.0f * G : -G;
+        a0 = CAPA ? -4.0f * G : -G;
     } else if (HEAD == kHeadEntropy) {
-        A = (CAPA ? -4.0f : -1.0f) * g_row * kLn2;
-        B = (CAPA ? -4.0f : -1.0f) * g_row * rs.value;
+        a0 = (CAPA ? -4.0f : -1.0f) * g_row * kLn2;
+        b0 = (CAPA ? -4.0f : -1.0f) * g_row * rs.value;
     } else if (HEAD == kHeadKLReverse) {
-        A = (CAPA ? 4.0f : 1.0f) * g_row * kLn2;
-        B = (CAPA ? -4.0f : -1.0f) * g_row * rs.value;
+        a0 = (CAPA ? 4.0f : 1.0f) * g_row * kLn2;
+        b0 = (CAPA ? -4.0f : -1.0f) * g_row * rs.value;
     } else {
-        A = CAPA ? 4.0f * g_row : g_row;
+        a0 = CAPA ? 4.0f * g_row : g_row;
     }
+    const float inv_sa = ex2(-rs.log2Sa);
+    A = a0 * inv_sa;
+    if (HEAD == kHeadLogp)
+        B = 0.0f;
+    else if (HEAD == kHeadEntropy)
+        B = __builtin_fmaf(-a0, rs.log2Sa, b0) * inv_sa;
+    else if (HEAD == kHeadKLReverse)
+        B = __builtin_fmaf(-a0, rs.log2Sa - rs.log2Sb, b0) * inv_sa;
+    else
+        B = a0 * ex2(-rs.log2Sb);
 }
 
 // Gradient of one element from its statistic inputs (a; b for KL) and the
-// row's record and coefficients; p comes from the forward's own FMA.
+// row's record and coefficients; the exponent t comes from the forward's own
+// FMA.
 template <int HEAD, bool CAPA>
 __device__ __forceinline__ float grad_elem(float a, float b, const RowStats& rs, float A, float B,
                                            float scx, float scy) {
-    const float ta = __builtin_fmaf(a, scx, -rs.mLa) - rs.log2Sa;
+    const float ta = __builtin_fmaf(a, scx, -rs.mLa);
     float o;
     if (HEAD == kHeadLogp) {
         o = A * ex2(ta);
@@ -77,12 +95,15 @@ __device__ __forceinline__ float grad_elem(float a, float b, const RowStats& rs,
         const float tc = CAPA ? ta : fmaxf(ta, kClampT);
         o = ex2(tc) * __builtin_fmaf(A, tc, B);
     } else {
-        const float tb = __builtin_fmaf(b, scy, -rs.mLb) - rs.log2Sb;
+        const float tb = __builtin_fmaf(b, scy, -rs.mLb);
         if (HEAD == kHeadKLReverse) {
             const float l = CAPA ? ta - tb : fmaxf(ta - tb, kClampT);
             o = ex2(ta) * __builtin_fmaf(A, l, B);
         } else {
-            o = A * (ex2(ta) - ex2(tb));
+            // two rounded products and their difference, never contracted to
+            // an FMA: equal distributions give exactly 0
+#pragma clang fp contract(off)
+            o = A * ex2(ta) - B * ex2(tb);
         }
     }
     // slope / 4 = r (1 - r) = r - r^2 in one FMA (the 4 is in A, B)
