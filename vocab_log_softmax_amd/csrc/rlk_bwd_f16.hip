@@ -1,4 +1,4 @@
-// rlk_bwd_f16.hip -- backward row kernels instantiated for f16 logits
+// rlk_bwd_f16.hip -- backward kernels instantiated for f16 logits
 // (one translation unit per dtype so the library builds in parallel).
 #include "rlk_bwd_kernels.h"
 

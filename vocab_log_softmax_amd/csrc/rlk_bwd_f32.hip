@@ -1,4 +1,4 @@
-// rlk_bwd_f32.hip -- backward row kernels instantiated for f32 logits
+// rlk_bwd_f32.hip -- backward kernels instantiated for f32 logits
 // (one translation unit per dtype so the library builds in parallel).
 #include "rlk_bwd_kernels.h"
 

@@ -1,4 +1,4 @@
-// rlk_bwd_kernels.h -- fused zero-workspace backward row kernels.
+// rlk_bwd_kernels.h -- fused zero-workspace backward kernels.
 //
 // "perf(logp): fused zero-workspace backward for the generic CUDA fused logp"
 // (RL-Kernel pull request 495), Summary: the gradient g (onehot - softmax) is
@@ -6,8 +6,8 @@
 // whose targets are all outside [0, V) get an exactly zero gradient (Behavior
 // changes).  Here the softmax is not recomputed from two more passes: the
 // forward saved (max log2 e, log2 S) per row, so each logit is read once and
-// each gradient written once, and p comes from the very same FMA as in the
-// forward (bitwise-consistent with the forward output).
+// each gradient written once, and p takes its exponent from the very same
+// FMA as the forward.
 //
 // Heads (all times the upstream g of the row and, with a softcap, the
 // derivative 1 - tanh^2 of "Final Logit Softcap", Summary):
@@ -243,7 +243,7 @@ constexpr int kPieceMaxK = 4;
 // a workgroup's stores never hold up the next load: on this part such a
 // stream of short workgroups moves noticeably more bytes per second than
 // row-long loops.  Logprobs slots (k <= kPieceMaxK) are read by every lane:
-// G is summed in the association of the row kernel's tree, and target
+// G is summed in the association of bwd_topk_kernel's tree, and target
 // columns take target_grad, so both kernels give the same bits.
 template <int BLOCK, typename T, int HEAD, bool CAPA, bool CAPB, bool ALIGNED>
 __global__ __launch_bounds__(BLOCK) void bwd_piece_kernel(BwdParams p, int64_t rbase) {
@@ -294,7 +294,7 @@ __global__ __launch_bounds__(BLOCK) void bwd_piece_kernel(BwdParams p, int64_t r
                     }
                 }
             }
-            // the row kernel's wave64 butterfly over lanes 0..3 holding the slots
+            // bwd_topk_kernel's wave64 butterfly over lanes 0..3 holding the slots
             G = (sv[0] + sv[2]) + (sv[1] + sv[3]);
             if (nvalid == 0)
                 mode = kModeZero;
