@@ -150,7 +150,8 @@ def side_bytes(w, N):
     return fwd, bwd
 
 
-def run_oracle_sample(w, d, max_rows: int, threads: int, min_seconds: float = 1.0):
+def run_oracle_sample(w, d, max_rows: int, threads: int, min_seconds: float = 1.0,
+                      direction: int = 0):
     """Time the fp64 oracle's fwd+bwd on the first max_rows rows (host cores).
 
     A sample that takes less than min_seconds is repeated (up to 1000 times)
@@ -174,8 +175,8 @@ def run_oracle_sample(w, d, max_rows: int, threads: int, min_seconds: float = 1.
             orc.entropy_fwd(x, w.cap)
             orc.entropy_bwd(x, g, w.cap)
         else:
-            orc.kl_fwd(x, r, 0, 0.0, 0.0)
-            orc.kl_bwd(x, r, g, 0, 0.0, 0.0)
+            orc.kl_fwd(x, r, direction, 0.0, 0.0)
+            orc.kl_bwd(x, r, g, direction, 0.0, 0.0)
 
     passes = 0
     t0 = time.perf_counter()
@@ -197,6 +198,11 @@ def main() -> int:
     ap.add_argument("--oracle-rows", type=int, default=8192,
                     help="rows of the workload timed on the CPU oracle")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--rows", type=int, default=None,
+                    help="override the workload's row count N (same recipe, e.g. 32768 rows "
+                         "of c2_logp_bf16 for the pages' B200 comparison)")
+    ap.add_argument("--direction", type=int, default=0, choices=(0, 1),
+                    help="KL workloads: 0 reverse KL(policy||ref), 1 forward KL(ref||policy)")
     ap.add_argument("--cold", action="store_true",
                     help="write a 1 GiB buffer before every step (flushes the 256 MB Infinity "
                          "Cache and the L2s) and time the two kernels with events only")
@@ -236,7 +242,7 @@ def main() -> int:
     if args.ceilings:
         print(json.dumps(measure_ceilings(w, dev, torch)))
         return 0
-    d = workloads.make_inputs(args.workload, dev)
+    d = workloads.make_inputs(args.workload, dev, N=args.rows)
     x = d["logits"]
     N, V = x.shape
     es = x.element_size()
@@ -265,8 +271,9 @@ def main() -> int:
         out = torch.empty(N, dtype=torch.float32, device=dev)
         st = rlk.new_stats(rlk.RLK_HEAD_KL, N, V, dev)
         gx = torch.empty_like(x)
-        fwd = lambda: rlk.rlk_kl_fwd(x, ref, 0, 0.0, 0.0, out, st)     # noqa: E731
-        bwd = lambda: rlk.rlk_kl_bwd(x, ref, 0, 0.0, 0.0, st, g, gx)   # noqa: E731
+        kd = args.direction
+        fwd = lambda: rlk.rlk_kl_fwd(x, ref, kd, 0.0, 0.0, out, st)     # noqa: E731
+        bwd = lambda: rlk.rlk_kl_bwd(x, ref, kd, 0.0, 0.0, st, g, gx)   # noqa: E731
         n_in, fwd_name, bwd_name = 2, "fwdkl_kernel", "bwd_piece_kernel"
 
     sf, sb = side_bytes(w, N)
@@ -341,7 +348,8 @@ def main() -> int:
     cpu = None
     if not args.no_cpu_baseline:
         threads = min(len(os.sched_getaffinity(0)), 16)
-        n, dt, passes = run_oracle_sample(w, d, args.oracle_rows, threads)
+        n, dt, passes = run_oracle_sample(w, d, args.oracle_rows, threads,
+                                          direction=args.direction)
         sample_bytes = step_bytes * n / N
         cpu = {"value": round(sample_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
                "kind": "oracle",
@@ -365,9 +373,12 @@ def main() -> int:
         "timing": ("cold: 1 GiB written before every step, step = forward + backward event time"
                    if args.cold else "warm: back-to-back steps, wall clock"),
         "config": {
-            "workload": f"{args.workload}: {w.head} fwd+bwd, "
+            "workload": f"{args.workload}" + (f" (N overridden to {N})" if args.rows else "")
+                        + f": {w.head} fwd+bwd, "
                         f"{'bf16' if es == 2 else 'fp32'} logits [{N}, {V}]"
                         + (f", k={w.k}" if w.head == "logp" else "")
+                        + ((", forward KL(ref||policy)" if args.direction else
+                            ", reverse KL(policy||ref)") if w.head == "kl" else "")
                         + (f", softcap {w.cap:g}" if w.cap else ""),
             "N": N, "V": V, "logits_dtype": "bf16" if es == 2 else "fp32",
             "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
