@@ -138,6 +138,37 @@ def measure_ceilings(w, dev, torch) -> dict:
     return {"ceilings": out, "workload": w.name}
 
 
+def time_softcap(name: str, dev, torch, reps: int = 50) -> dict:
+    """The standalone softcap forward (y fp32) and backward on the workload's
+    softcap tensor: mean kernel time over `reps` launches, HIP events."""
+    from vocab_log_softmax_amd import rlk, workloads
+
+    w = workloads.WORKLOADS[name]
+    x, gy = workloads.make_softcap_inputs(name, dev)
+    y = torch.empty(x.shape, dtype=torch.float32, device=dev)
+    gx = torch.empty_like(x)
+    n, es = x.numel(), x.element_size()
+    raw = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    out = {"shape": list(x.shape), "dtype": str(x.dtype).replace("torch.", ""), "cap": w.cap}
+    for what, fn, nbytes in (("fwd", lambda: rlk.rlk_softcap_fwd(x, y, w.cap), n * (es + 4)),
+                             ("bwd", lambda: rlk.rlk_softcap_bwd(x, gy, gx, w.cap),
+                              n * (es + 4 + es))):
+        for _ in range(5):
+            fn()
+        ev = HipEvents(2, torch)
+        torch.cuda.synchronize()
+        ev.record(0, raw)
+        for _ in range(reps):
+            fn()
+        ev.record(1, raw)
+        torch.cuda.synchronize()
+        ms = ev.elapsed_ms(0, 1) / reps
+        ev.close()
+        out[what] = {"us": round(ms * 1e3, 2), "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                     "bytes": nbytes}
+    return out
+
+
 def side_bytes(w, N):
     """Per-step bytes of the per-row side arrays (targets, grads, outputs, stats)."""
     k = w.k
@@ -386,6 +417,8 @@ def main() -> int:
         },
         "roofline": roofline,
         "cpu_baseline": cpu,
+        **({"softcap_standalone": time_softcap(args.workload, dev, torch)}
+           if "softcap_shape" in w.extra else {}),
     }
     print(json.dumps(result), flush=True)
     return 0
