@@ -64,7 +64,7 @@ def assert_bitwise(a, b, what):
 
 
 @pytest.mark.parametrize("V", [1031, 32000, 151936])
-@pytest.mark.parametrize("cap", [0.0, 30.0])
+@pytest.mark.parametrize("cap", [0.0, 30.0, 50.0])
 def test_repeat_is_bitwise(dev, V, cap):
     args = make(16, V, torch.bfloat16, V, dev)
     a = run_all(*args, cap)
@@ -126,7 +126,7 @@ def test_misaligned_base_pointer(dev, dtype):
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "f16"])
-@pytest.mark.parametrize("cap", [0.0, 20.0])
+@pytest.mark.parametrize("cap", [0.0, 20.0, 60.0])
 def test_half_dtypes_equal_fp32_of_same_values(dev, dtype, cap):
     N, V = 10, 75968
     x, ref, t, g_t, g_r = make(N, V, dtype, 5, dev)
@@ -154,7 +154,7 @@ def test_outputs_independent_of_stats_buffer_history(dev):
 
 
 @pytest.mark.parametrize("N", [37, 700])
-@pytest.mark.parametrize("cap", [0.0, 20.0])
+@pytest.mark.parametrize("cap", [0.0, 20.0, 60.0])
 def test_piece_and_topk_backward_kernels_agree(dev, N, cap):
     # k <= 4 runs the one-shot piece kernel, k = 5 the top-k row kernel
     # (few rows: column segments); a fifth slot that is ignored changes

@@ -42,8 +42,8 @@ def pair(N, V, dtype, seed, caps):
 @pytest.mark.parametrize("dtype", DTYPES, ids=DT_IDS)
 @pytest.mark.parametrize("V", [2, 7, 1031, 4097, 32000])
 @pytest.mark.parametrize("direction", [0, 1], ids=["rev", "fwd"])
-@pytest.mark.parametrize("caps", [(0.0, 0.0), (30.0, 20.0), (0.0, 25.0)],
-                         ids=["nocap", "cap", "refcap"])
+@pytest.mark.parametrize("caps", [(0.0, 0.0), (30.0, 20.0), (0.0, 25.0), (50.0, 20.0)],
+                         ids=["nocap", "cap", "refcap", "online_fixed"])
 def test_kl_reference_gradient(dev, orc, dtype, V, direction, caps):
     N = 12
     cp, cr = caps
@@ -66,7 +66,8 @@ def test_kl_reference_gradient(dev, orc, dtype, V, direction, caps):
 
 @pytest.mark.parametrize("dtype", DTYPES, ids=DT_IDS)
 @pytest.mark.parametrize("V", [7, 4099, 75968])
-@pytest.mark.parametrize("caps", [(0.0, 0.0), (30.0, 20.0)], ids=["nocap", "cap"])
+@pytest.mark.parametrize("caps", [(0.0, 0.0), (30.0, 20.0), (20.0, 50.0)],
+                         ids=["nocap", "cap", "fixed_online"])
 def test_both_directions_forward_is_bitwise_single(dev, orc, dtype, V, caps):
     N = 12
     cp, cr = caps
@@ -103,7 +104,8 @@ def swap_record(st):
 
 
 @pytest.mark.parametrize("dtype", DTYPES, ids=DT_IDS)
-@pytest.mark.parametrize("caps", [(0.0, 0.0), (30.0, 20.0)], ids=["nocap", "cap"])
+@pytest.mark.parametrize("caps", [(0.0, 0.0), (30.0, 20.0), (50.0, 20.0)],
+                         ids=["nocap", "cap", "online_fixed"])
 def test_reference_gradient_is_policy_gradient_of_swapped_pair(dev, dtype, caps):
     # KL(P||R) is the forward KL of the pair (policy R, reference P): with the
     # record's sides exchanged, the policy gradient of the swapped pair is the

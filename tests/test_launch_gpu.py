@@ -51,7 +51,7 @@ def test_more_rows_than_one_launch(dev, orc, head):
     assert_grad(gx, ref_gx, f"{head} grad")
 
 
-@pytest.mark.parametrize("cap", [0.0, 30.0])
+@pytest.mark.parametrize("cap", [0.0, 30.0, 50.0])
 def test_graph_capture_replays_equal_eager(dev, cap):
     N, V, k = 96, 50_000, 3
     x = (torch.randn(N, V, generator=_gen(5)) * 4).to(torch.bfloat16).to(dev)

@@ -59,9 +59,11 @@ def _run_logp(dev, orc, x, t, g, cap):
     return out, gx, ref_out, ref_gx
 
 
+# Caps 20 and 30 take the fixed-reference form of the fused cap, 50 and 60
+# (2 c log2 e above 120) the running-max form.
 @pytest.mark.parametrize("dtype", DTYPES, ids=DT_IDS)
 @pytest.mark.parametrize("V", VS)
-@pytest.mark.parametrize("cap", [0.0, 30.0])
+@pytest.mark.parametrize("cap", [0.0, 30.0, 50.0])
 def test_logp_k1(dev, orc, dtype, V, cap):
     N = 12
     x = logits_rows(N, V, 3.0 if not cap else 15.0, dtype, V,
@@ -105,7 +107,7 @@ def test_logp_target_on_masked_column(dev, orc):
 
 @pytest.mark.parametrize("dtype", DTYPES, ids=DT_IDS)
 @pytest.mark.parametrize("V,k", [(7, 4), (255, 17), (4097, 64), (32768, 256), (2000, 300)])
-@pytest.mark.parametrize("cap", [0.0, 20.0])
+@pytest.mark.parametrize("cap", [0.0, 20.0, 60.0])
 def test_logp_topk(dev, orc, dtype, V, k, cap):
     N = 9
     x = logits_rows(N, V, 10.0 if cap else 3.0, dtype, V + k)
@@ -133,7 +135,7 @@ def test_logp_topk(dev, orc, dtype, V, k, cap):
 
 @pytest.mark.parametrize("dtype", DTYPES, ids=DT_IDS)
 @pytest.mark.parametrize("V", VS)
-@pytest.mark.parametrize("cap", [0.0, 30.0])
+@pytest.mark.parametrize("cap", [0.0, 30.0, 50.0])
 def test_entropy(dev, orc, dtype, V, cap):
     N = 10
     x = logits_rows(N, V, 15.0 if cap else 3.0, dtype, 100 + V,
@@ -149,6 +151,49 @@ def test_entropy(dev, orc, dtype, V, cap):
     assert_out(H, orc.entropy_fwd(x64, cap), dtype, "entropy")
     masked = np.isneginf(x64) & ~np.isneginf(x64).all(1, keepdims=True) if not cap else None
     assert_grad(gx, orc.entropy_bwd(x64, to64(g), cap), "entropy grad", exact_zero=masked)
+
+
+@pytest.mark.parametrize("cap", [41.5, 41.7], ids=["fixed_edge", "online_edge"])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+def test_cap_mode_edge_rows(dev, orc, cap, dtype):
+    """Both sides of the cap-form threshold (2 c log2 e = 120 lies between the
+    two caps) on rows at the ends of the cap: every logit far below (all
+    shifted exponents near -2 c log2 e, the smallest row sums of the fixed
+    form), -inf and +inf columns (slope exactly 0), all at +1000, mixed."""
+    N, V = 8, 4097
+    x = torch.randn(N, V, generator=gen(11)) * 15.0
+    x[0] = -1e4
+    x[1] = float("-inf")
+    x[2, :5] = float("inf")
+    x[2, 5:10] = float("-inf")
+    x[3] += 1000.0
+    x[4, ::2] = -1e4
+    x[5, :V // 2] = float("-inf")
+    x = x.to(dtype)
+    inf_cols = np.isinf(to64(x))
+    xd = x.to(dev)
+    t = torch.randint(0, V, (N, 1), generator=gen(12))
+    t[2, 0] = 1                                   # a +inf column
+    t[5, 0] = 0                                   # a -inf column
+    g = torch.randn(N, 1, generator=gen(13))
+    out, gx, ref_out, ref_gx = _run_logp(dev, orc, x, t, g, cap)
+    assert_out(out, ref_out, dtype, "logp")
+    assert_grad(gx, ref_gx, "logp grad", exact_zero=inf_cols)
+    gr = torch.randn(N, generator=gen(14))
+    H, st = rlk.entropy_fwd(xd, cap)
+    gH = rlk.entropy_bwd(xd, gr.to(dev), st, cap)
+    y = (x.double() + torch.randn(N, V, generator=gen(15)) * 0.5).to(dtype)
+    y[1] = -1e4
+    for d in (0, 1):
+        D, sk = rlk.kl_fwd(xd, y.to(dev), d, cap, cap)
+        gD = rlk.kl_bwd(xd, y.to(dev), gr.to(dev), sk, d, cap, cap)
+        torch.cuda.synchronize()
+        assert_out(D, orc.kl_fwd(to64(x), to64(y), d, cap, cap), dtype, f"kl {d}")
+        assert_grad(gD, orc.kl_bwd(to64(x), to64(y), to64(gr), d, cap, cap), f"kl {d} grad",
+                    exact_zero=inf_cols)
+    torch.cuda.synchronize()
+    assert_out(H, orc.entropy_fwd(to64(x), cap), dtype, "entropy")
+    assert_grad(gH, orc.entropy_bwd(to64(x), to64(gr), cap), "entropy grad", exact_zero=inf_cols)
 
 
 def test_entropy_saturated_cap_rows(dev, orc):
@@ -185,7 +230,8 @@ def kl_pair(N, V, dtype, seed, mismatch_rows=(), empty_rows=(), both_masked_rows
 @pytest.mark.parametrize("dtype", DTYPES, ids=DT_IDS)
 @pytest.mark.parametrize("V", [2, 7, 1031, 4097, 32000])
 @pytest.mark.parametrize("direction", [0, 1], ids=["rev", "fwd"])
-@pytest.mark.parametrize("caps", [(0.0, 0.0), (30.0, 20.0)], ids=["nocap", "cap"])
+@pytest.mark.parametrize("caps", [(0.0, 0.0), (30.0, 20.0), (50.0, 20.0), (0.0, 45.0), (41.5, 0.0)],
+                         ids=["nocap", "cap", "online_fixed", "none_online", "fixed_none"])
 def test_kl(dev, orc, dtype, V, direction, caps):
     N = 12
     cp, cr = caps

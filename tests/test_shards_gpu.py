@@ -99,7 +99,7 @@ def _bits(t):
 @pytest.mark.parametrize("dtype", DTYPES, ids=DT_IDS)
 @pytest.mark.parametrize("V", [7, 1031, 32000])
 @pytest.mark.parametrize("k", [1, 40])
-@pytest.mark.parametrize("cap", [0.0, 30.0])
+@pytest.mark.parametrize("cap", [0.0, 30.0, 50.0])
 def test_logp_shards(dev, orc, dtype, V, k, cap):
     N = 10
     for bounds in splits(V):
@@ -133,7 +133,7 @@ def test_logp_shards(dev, orc, dtype, V, k, cap):
 
 @pytest.mark.parametrize("dtype", DTYPES, ids=DT_IDS)
 @pytest.mark.parametrize("V", [7, 1031, 32000])
-@pytest.mark.parametrize("cap", [0.0, 30.0])
+@pytest.mark.parametrize("cap", [0.0, 30.0, 50.0])
 def test_entropy_shards(dev, orc, dtype, V, cap):
     N = 10
     for bounds in splits(V):
@@ -183,7 +183,7 @@ def test_kl_shards(dev, orc, dtype, V, direction, caps):
 # ------------------------------------------------- one shard == plain forward
 
 @pytest.mark.parametrize("dtype", DTYPES, ids=DT_IDS)
-@pytest.mark.parametrize("cap", [0.0, 20.0])
+@pytest.mark.parametrize("cap", [0.0, 20.0, 60.0])
 def test_single_shard_combine_is_bitwise_plain(dev, dtype, cap):
     N, V, k = 9, 4099, 5
     x = logits_rows(N, V, 6.0, dtype, 3).to(dev)

@@ -56,7 +56,7 @@ def make_seq(B, T1, V, dtype, seed, dev):
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32, torch.float16],
                          ids=["bf16", "f32", "f16"])
 @pytest.mark.parametrize("V", [4096, 32000, 4099])
-@pytest.mark.parametrize("cap", [0.0, 30.0])
+@pytest.mark.parametrize("cap", [0.0, 30.0, 50.0])
 def test_sequence_slice_in_place(dev, dtype, V, cap):
     B, T1, k = 3, 9, 2
     T = T1 - 1

@@ -60,12 +60,27 @@ rlk_status check_matrix(int64_t N, int64_t V, int64_t ld, int64_t es, const char
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Softcap constants of the row kernels: k = -2 log2(e) / c gives
-// r = 1 / (1 + 2^(k x)), and the statistic input is x log2(e) (cap off) or
-// r with scale 2 c log2(e) (cap on; see rlk_device.h).
-float cap_k(float c) { return c != 0.0f ? -2.0f * 1.44269504088896340736f / c : 0.0f; }
+// Softcap constants of the row kernels (rlk::CapMode): k = -2 log2(e) / c
+// gives r = 1 / (1 + 2^(k x)); the statistic input is x with scale log2(e)
+// (cap off), r with scale 2 c log2(e) (online form) or t = (y - c) log2(e)
+// itself with scale 1 (fixed form, caps with 2 c log2(e) <=
+// kCapFixedMaxScale), whose kernels also take 1 / (2 c log2(e)).  A forward
+// call, its backward and the shard combine all derive the mode from the same c.
+constexpr double kLog2eD = 1.44269504088896340736;
+int cap_mode(float c) {
+    if (c == 0.0f) return rlk::kCapNone;
+    return 2.0 * c * kLog2eD <= rlk::kCapFixedMaxScale ? rlk::kCapFixed : rlk::kCapOnline;
+}
+float cap_k(float c) { return c != 0.0f ? static_cast<float>(-2.0 * kLog2eD / c) : 0.0f; }
 float cap_sc(float c) {
-    return c != 0.0f ? 2.0f * c * 1.44269504088896340736f : 1.44269504088896340736f;
+    switch (cap_mode(c)) {
+        case rlk::kCapFixed: return 1.0f;
+        case rlk::kCapOnline: return static_cast<float>(2.0 * c * kLog2eD);
+        default: return static_cast<float>(kLog2eD);
+    }
+}
+float cap_isc(float c) {
+    return cap_mode(c) == rlk::kCapFixed ? static_cast<float>(1.0 / (2.0 * c * kLog2eD)) : 0.0f;
 }
 
 // Device that owns `ptr` (device or managed memory only).
@@ -255,10 +270,11 @@ rlk_status logp_fwd_impl(const void* logits, rlk_dtype dtype, int64_t N, int64_t
     p.k = k;
     p.kx = cap_k(softcap);
     p.scx = cap_sc(softcap);
+    p.ix = cap_isc(softcap);
     p.out = logp;
     p.stats = stats;
     const bool al = rows_aligned(logits, mx, esize(dtype));
-    return launched(rlk::launch_fwd(rlk::kHeadLogp, dtype, softcap != 0.0f, false, al, p,
+    return launched(rlk::launch_fwd(rlk::kHeadLogp, dtype, cap_mode(softcap), rlk::kCapNone, al, p,
                                     static_cast<hipStream_t>(stream)),
                     "logp_fwd");
 }
@@ -286,12 +302,13 @@ rlk_status logp_bwd_impl(const void* logits, rlk_dtype dtype, int64_t N, int64_t
     p.k = k;
     p.kx = cap_k(softcap);
     p.scx = cap_sc(softcap);
+    p.ix = cap_isc(softcap);
     p.stats = stats;
     p.g = grad_logp;
     p.gx = grad_logits;
     const int64_t es = esize(dtype);
     const bool al = rows_aligned(logits, mx, es) && rows_aligned(grad_logits, mg, es);
-    return launched(rlk::launch_bwd(rlk::kHeadLogp, dtype, softcap != 0.0f, false, al, p,
+    return launched(rlk::launch_bwd(rlk::kHeadLogp, dtype, cap_mode(softcap), rlk::kCapNone, al, p,
                                     static_cast<hipStream_t>(stream)),
                     "logp_bwd");
 }
@@ -315,10 +332,11 @@ rlk_status entropy_fwd_impl(const void* logits, rlk_dtype dtype, int64_t N, int6
     p.k = 1;
     p.kx = cap_k(softcap);
     p.scx = cap_sc(softcap);
+    p.ix = cap_isc(softcap);
     p.out = entropy;
     p.stats = stats;
     const bool al = rows_aligned(logits, mx, esize(dtype));
-    return launched(rlk::launch_fwd(rlk::kHeadEntropy, dtype, softcap != 0.0f, false, al, p,
+    return launched(rlk::launch_fwd(rlk::kHeadEntropy, dtype, cap_mode(softcap), rlk::kCapNone, al, p,
                                     static_cast<hipStream_t>(stream)),
                     "entropy_fwd");
 }
@@ -345,12 +363,13 @@ rlk_status entropy_bwd_impl(const void* logits, rlk_dtype dtype, int64_t N, int6
     p.k = 1;
     p.kx = cap_k(softcap);
     p.scx = cap_sc(softcap);
+    p.ix = cap_isc(softcap);
     p.stats = stats;
     p.g = grad_entropy;
     p.gx = grad_logits;
     const int64_t es = esize(dtype);
     const bool al = rows_aligned(logits, mx, es) && rows_aligned(grad_logits, mg, es);
-    return launched(rlk::launch_bwd(rlk::kHeadEntropy, dtype, softcap != 0.0f, false, al, p,
+    return launched(rlk::launch_bwd(rlk::kHeadEntropy, dtype, cap_mode(softcap), rlk::kCapNone, al, p,
                                     static_cast<hipStream_t>(stream)),
                     "entropy_bwd");
 }
@@ -380,7 +399,9 @@ rlk_status kl_fwd_impl(const void* policy, const void* ref, rlk_dtype dtype, int
     p.kx = cap_k(cp);
     p.ky = cap_k(cr);
     p.scx = cap_sc(cp);
+    p.ix = cap_isc(cp);
     p.scy = cap_sc(cr);
+    p.iy = cap_isc(cr);
     p.out = kl;
     p.stats = stats;
     p.out2 = kl2;
@@ -390,7 +411,7 @@ rlk_status kl_fwd_impl(const void* policy, const void* ref, rlk_dtype dtype, int
     const int head = both                    ? rlk::kHeadKLBoth
                      : dir == RLK_KL_REVERSE ? rlk::kHeadKLReverse
                                              : rlk::kHeadKLForward;
-    return launched(rlk::launch_fwd(head, dtype, cp != 0.0f, cr != 0.0f, al, p,
+    return launched(rlk::launch_fwd(head, dtype, cap_mode(cp), cap_mode(cr), al, p,
                                     static_cast<hipStream_t>(stream)),
                     both ? "kl_fwd_both" : "kl_fwd");
 }
@@ -426,7 +447,9 @@ rlk_status kl_bwd_impl(const void* policy, const void* ref, rlk_dtype dtype, int
     p.kx = cap_k(cx);
     p.ky = cap_k(cy);
     p.scx = cap_sc(cx);
+    p.ix = cap_isc(cx);
     p.scy = cap_sc(cy);
+    p.iy = cap_isc(cy);
     p.stats = stats;
     p.swap = wrt_ref ? 1 : 0;
     p.g = grad_kl;
@@ -436,7 +459,7 @@ rlk_status kl_bwd_impl(const void* policy, const void* ref, rlk_dtype dtype, int
                     rows_aligned(grad_out, mg, es);
     const bool reverse = (dir == RLK_KL_REVERSE) != wrt_ref;
     const int head = reverse ? rlk::kHeadKLReverse : rlk::kHeadKLForward;
-    return launched(rlk::launch_bwd(head, dtype, cx != 0.0f, cy != 0.0f, al, p,
+    return launched(rlk::launch_bwd(head, dtype, cap_mode(cx), cap_mode(cy), al, p,
                                     static_cast<hipStream_t>(stream)),
                     wrt_ref ? "kl_bwd_ref" : "kl_bwd");
 }
@@ -721,12 +744,13 @@ rlk_status rlk_logp_fwd_partial(const void* logits, rlk_dtype dtype, int64_t N, 
     p.k = k;
     p.kx = cap_k(softcap);
     p.scx = cap_sc(softcap);
+    p.ix = cap_isc(softcap);
     p.v0 = v0;
     p.vtotal = V_total;
     p.part = partial;
     p.tvals = target_vals;
     const bool al = rows_aligned(logits, p.mx, esize(dtype));
-    return launched(rlk::launch_fwd(rlk::kHeadLogp, dtype, softcap != 0.0f, false, al, p,
+    return launched(rlk::launch_fwd(rlk::kHeadLogp, dtype, cap_mode(softcap), rlk::kCapNone, al, p,
                                     static_cast<hipStream_t>(stream)),
                     "logp_fwd_partial");
 }
@@ -750,9 +774,10 @@ rlk_status rlk_entropy_fwd_partial(const void* logits, rlk_dtype dtype, int64_t 
     p.k = 1;
     p.kx = cap_k(softcap);
     p.scx = cap_sc(softcap);
+    p.ix = cap_isc(softcap);
     p.part = partial;
     const bool al = rows_aligned(logits, p.mx, esize(dtype));
-    return launched(rlk::launch_fwd(rlk::kHeadEntropy, dtype, softcap != 0.0f, false, al, p,
+    return launched(rlk::launch_fwd(rlk::kHeadEntropy, dtype, cap_mode(softcap), rlk::kCapNone, al, p,
                                     static_cast<hipStream_t>(stream)),
                     "entropy_fwd_partial");
 }
@@ -783,12 +808,14 @@ rlk_status rlk_kl_fwd_partial(const void* policy, const void* ref, rlk_dtype dty
     p.kx = cap_k(softcap_policy);
     p.ky = cap_k(softcap_ref);
     p.scx = cap_sc(softcap_policy);
+    p.ix = cap_isc(softcap_policy);
     p.scy = cap_sc(softcap_ref);
+    p.iy = cap_isc(softcap_ref);
     p.part = partial;
     const int64_t es = esize(dtype);
     const bool al = rows_aligned(policy, p.mx, es) && rows_aligned(ref, p.my, es);
     const int head = dir == RLK_KL_REVERSE ? rlk::kHeadKLReverse : rlk::kHeadKLForward;
-    return launched(rlk::launch_fwd(head, dtype, softcap_policy != 0.0f, softcap_ref != 0.0f, al,
+    return launched(rlk::launch_fwd(head, dtype, cap_mode(softcap_policy), cap_mode(softcap_ref), al,
                                     p, static_cast<hipStream_t>(stream)),
                     "kl_fwd_partial");
 }
@@ -868,12 +895,13 @@ rlk_status rlk_logp_bwd_shard(const void* logits, rlk_dtype dtype, int64_t N, in
     p.k = k;
     p.kx = cap_k(softcap);
     p.scx = cap_sc(softcap);
+    p.ix = cap_isc(softcap);
     p.stats = stats;
     p.g = grad_logp;
     p.gx = grad_logits;
     const int64_t es = esize(dtype);
     const bool al = rows_aligned(logits, p.mx, es) && rows_aligned(grad_logits, p.mg, es);
-    return launched(rlk::launch_bwd(rlk::kHeadLogp, dtype, softcap != 0.0f, false, al, p,
+    return launched(rlk::launch_bwd(rlk::kHeadLogp, dtype, cap_mode(softcap), rlk::kCapNone, al, p,
                                     static_cast<hipStream_t>(stream)),
                     "logp_bwd_shard");
 }

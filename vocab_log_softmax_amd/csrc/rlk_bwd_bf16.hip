@@ -4,7 +4,7 @@
 
 namespace rlk {
 
-hipError_t launch_bwd_bf16(int head, bool cap_x, bool cap_y, bool aligned,
+hipError_t launch_bwd_bf16(int head, int cap_x, int cap_y, bool aligned,
                            const BwdParams& p, hipStream_t stream) {
     return bwd_dispatch_cap<BF16>(head, cap_x, cap_y, aligned, p, stream);
 }

@@ -54,20 +54,21 @@ __device__ __forceinline__ void swap_sides(RowStats& rs) {
 //                                                   o = 2^ta (A (ta - tb) + B)
 //   forward KL  A = g / S_a, B = g / S_b             o = A 2^ta - B 2^tb
 // (the slope 4 r (1 - r) of the cap has its 4 folded in as well).
-template <int HEAD, bool CAPA>
+template <int HEAD, int CAPA>
 __device__ __forceinline__ void row_coeffs(const RowStats& rs, float G, float g_row, float& A,
                                            float& B) {
+    constexpr bool C = CAPA != kCapNone;
     float a0 = 0.0f, b0 = 0.0f;
     if (HEAD == kHeadLogp) {
-        a0 = CAPA ? -4.0f * G : -G;
+        a0 = C ? -4.0f * G : -G;
     } else if (HEAD == kHeadEntropy) {
-        a0 = (CAPA ? -4.0f : -1.0f) * g_row * kLn2;
-        b0 = (CAPA ? -4.0f : -1.0f) * g_row * rs.value;
+        a0 = (C ? -4.0f : -1.0f) * g_row * kLn2;
+        b0 = (C ? -4.0f : -1.0f) * g_row * rs.value;
     } else if (HEAD == kHeadKLReverse) {
-        a0 = (CAPA ? 4.0f : 1.0f) * g_row * kLn2;
-        b0 = (CAPA ? -4.0f : -1.0f) * g_row * rs.value;
+        a0 = (C ? 4.0f : 1.0f) * g_row * kLn2;
+        b0 = (C ? -4.0f : -1.0f) * g_row * rs.value;
     } else {
-        a0 = CAPA ? 4.0f * g_row : g_row;
+        a0 = C ? 4.0f * g_row : g_row;
     }
     const float inv_sa = ex2(-rs.log2Sa);
     A = a0 * inv_sa;
@@ -81,23 +82,40 @@ __device__ __forceinline__ void row_coeffs(const RowStats& rs, float G, float g_
         B = a0 * ex2(-rs.log2Sb);
 }
 
-// Gradient of one element from its statistic inputs (a; b for KL) and the
-// row's record and coefficients; the exponent t comes from the forward's own
-// FMA.
-template <int HEAD, bool CAPA>
-__device__ __forceinline__ float grad_elem(float a, float b, const RowStats& rs, float A, float B,
-                                           float scx, float scy) {
+// With a fixed-form cap, S can be as small as 2^-kCapFixedMaxScale and 1 / S
+// would overflow the row coefficients: that side's log2 S moves into its
+// exponent reference instead (mL is 0 there), so every exponent of it is
+// log2 p <= 0 and its 1 / S factor is 1.
+template <int CAPA, int CAPB, bool KL>
+__device__ __forceinline__ void fixed_refs(RowStats& rs) {
+    if (CAPA == kCapFixed) {
+        rs.mLa += rs.log2Sa;
+        rs.log2Sa = 0.0f;
+    }
+    if (KL && CAPB == kCapFixed) {
+        rs.mLb += rs.log2Sb;
+        rs.log2Sb = 0.0f;
+    }
+}
+
+// Gradient of one element from its statistic inputs (a; b for KL), the
+// quarter slope s4 of the cap (cap_value_slope) and the row's record and
+// coefficients; the exponent t comes from the forward's own FMA.
+template <int HEAD, int CAPA>
+__device__ __forceinline__ float grad_elem(float a, float s4, float b, const RowStats& rs, float A,
+                                           float B, float scx, float scy) {
+    constexpr bool C = CAPA != kCapNone;
     const float ta = __builtin_fmaf(a, scx, -rs.mLa);
     float o;
     if (HEAD == kHeadLogp) {
         o = A * ex2(ta);
     } else if (HEAD == kHeadEntropy) {
-        const float tc = CAPA ? ta : fmaxf(ta, kClampT);
+        const float tc = C ? ta : fmaxf(ta, kClampT);
         o = ex2(tc) * __builtin_fmaf(A, tc, B);
     } else {
         const float tb = __builtin_fmaf(b, scy, -rs.mLb);
         if (HEAD == kHeadKLReverse) {
-            const float l = CAPA ? ta - tb : fmaxf(ta - tb, kClampT);
+            const float l = C ? ta - tb : fmaxf(ta - tb, kClampT);
             o = ex2(ta) * __builtin_fmaf(A, l, B);
         } else {
             // two rounded products and their difference, never contracted to
@@ -106,19 +124,18 @@ __device__ __forceinline__ float grad_elem(float a, float b, const RowStats& rs,
             o = A * ex2(ta) - B * ex2(tb);
         }
     }
-    // slope / 4 = r (1 - r) = r - r^2 in one FMA (the 4 is in A, B)
-    if (CAPA) o *= __builtin_fmaf(-a, a, a);
+    if (C) o *= s4;  // the slope's 4 is in A, B
     return o;
 }
 
 // Logprobs gradient at a target column: h - p G (h: the column's summed
-// upstream gradients), times the cap's slope.
-template <bool CAPA>
-__device__ __forceinline__ float target_grad(float a, const RowStats& rs, float G, float h,
-                                             float scx) {
+// upstream gradients), times the cap's slope 4 s4.
+template <int CAPA>
+__device__ __forceinline__ float target_grad(float a, float s4, const RowStats& rs, float G,
+                                             float h, float scx) {
     const float pt = ex2(__builtin_fmaf(a, scx, -rs.mLa) - rs.log2Sa);
     const float v = __builtin_fmaf(-pt, G, h);
-    return CAPA ? v * cap_slope_r(a) : v;
+    return CAPA != kCapNone ? v * (4.0f * s4) : v;
 }
 
 // Logprobs with wide top-k: one workgroup per (row, column segment), visited
@@ -127,7 +144,7 @@ __device__ __forceinline__ float target_grad(float a, const RowStats& rs, float 
 // fixed by kGLanes (slot j by lane j mod kGLanes, in order), not by BLOCK;
 // after the bulk pass a barrier orders the target columns' one-hot rewrites
 // after the bulk stores of the same addresses.
-template <int BLOCK, int U, typename T, bool CAPA, bool ALIGNED>
+template <int BLOCK, int U, typename T, int CAPA, bool ALIGNED>
 __global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void bwd_topk_kernel(BwdParams p) {
     using S = typename T::storage;
     static_assert(BLOCK >= kGLanes, "the G tree needs kGLanes threads");
@@ -142,6 +159,7 @@ __global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void bwd_topk_kernel(BwdParams
     const RowStats* stats = static_cast<const RowStats*>(p.stats);
     int* tg = smem_topk;
     float* gg = reinterpret_cast<float*>(smem_topk + p.k);
+    const CapArgs ca{p.kx, p.ix};
 
     for (int64_t it = blockIdx.x; it < p.N * p.split; it += gridDim.x) {
         const int64_t rit = it / p.split, seg = it - rit * p.split;
@@ -150,7 +168,8 @@ __global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void bwd_topk_kernel(BwdParams
         const int64_t cbeg = gbeg * step * kChunk, cend = gend * step * kChunk;  // columns
         const S* __restrict__ xa = static_cast<const S*>(p.x) + p.mx.offset(row);
         S* __restrict__ gx = static_cast<S*>(p.gx) + p.mg.offset(row);
-        const RowStats rs = stats[row];
+        RowStats rs = stats[row];
+        fixed_refs<CAPA, kCapNone, false>(rs);
 
         // Stage the slots (valid over the whole row; local to this vocabulary
         // shard -- plain call: the same -- as its column, else -1 / -2).
@@ -187,16 +206,19 @@ __global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void bwd_topk_kernel(BwdParams
         if (mode == kModeNormal) {
             float A, B;
             row_coeffs<kHeadLogp, CAPA>(rs, G, 0.0f, A, B);
-            for_each_group<BLOCK, U, S, CAPA, ALIGNED, kBwdPipe>(
-                xa, p.V, p.kx,
-                [&](int64_t g0, bool full, const float (&a)[U][kChunk]) {
+            for_each_group<BLOCK, U, S, kCapNone, ALIGNED, kBwdPipe>(
+                xa, p.V, CapArgs{},
+                [&](int64_t g0, bool full, const float (&x)[U][kChunk]) {
                     float v[U][kChunk];
 #pragma unroll
                     for (int u = 0; u < U; ++u)
 #pragma unroll
-                        for (int e = 0; e < kChunk; ++e)
-                            v[u][e] = grad_elem<kHeadLogp, CAPA>(a[u][e], 0.0f, rs, A, B, p.scx,
+                        for (int e = 0; e < kChunk; ++e) {
+                            float s4;
+                            const float a = cap_value_slope<CAPA>(x[u][e], ca, s4);
+                            v[u][e] = grad_elem<kHeadLogp, CAPA>(a, s4, 0.0f, rs, A, B, p.scx,
                                                                  p.scy);
+                        }
                     store_group<BLOCK, U, S, ALIGNED>(gx, p.V, g0, full, v);
                 },
                 gbeg, gend);
@@ -215,9 +237,9 @@ __global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void bwd_topk_kernel(BwdParams
                     }
                 }
                 if (!first) continue;
-                float a = load_one(xa + t);
-                if (CAPA) a = cap_r(a, p.kx);
-                store_one(gx + t, target_grad<CAPA>(a, rs, G, h, p.scx));
+                float s4;
+                const float a = cap_value_slope<CAPA>(load_one(xa + t), ca, s4);
+                store_one(gx + t, target_grad<CAPA>(a, s4, rs, G, h, p.scx));
             }
         } else {
             const float fill = mode == kModeZero ? 0.0f : qnan();
@@ -245,7 +267,7 @@ constexpr int kPieceMaxK = 4;
 // row-long loops.  Logprobs slots (k <= kPieceMaxK) are read by every lane:
 // G is summed in the association of bwd_topk_kernel's tree, and target
 // columns take target_grad, so both kernels give the same bits.
-template <int BLOCK, typename T, int HEAD, bool CAPA, bool CAPB, bool ALIGNED>
+template <int BLOCK, typename T, int HEAD, int CAPA, int CAPB, bool ALIGNED>
 __global__ __launch_bounds__(BLOCK) void bwd_piece_kernel(BwdParams p, int64_t rbase) {
     using S = typename T::storage;
     constexpr bool KL = HEAD == kHeadKLReverse || HEAD == kHeadKLForward;
@@ -261,15 +283,19 @@ __global__ __launch_bounds__(BLOCK) void bwd_piece_kernel(BwdParams p, int64_t r
         const S* __restrict__ xa = static_cast<const S*>(p.x) + p.mx.offset(row);
         S* __restrict__ gx = static_cast<S*>(p.gx) + p.mg.offset(row);
 
-        float a[1][kChunk], b[1][kChunk];
-        tail_values<BLOCK, 1, S, CAPA, ALIGNED>(xa, p.V, nfull, g0, p.kx, a);
+        // raw logits of x (the cap and its slope are taken per element),
+        // statistic inputs of y
+        float x[1][kChunk], b[1][kChunk];
+        tail_values<BLOCK, 1, S, kCapNone, ALIGNED>(xa, p.V, nfull, g0, CapArgs{}, x);
         if (KL) {
             const S* __restrict__ xb = static_cast<const S*>(p.y) + p.my.offset(row);
-            tail_values<BLOCK, 1, S, CAPB, ALIGNED>(xb, p.V, nfull, g0, p.ky, b);
+            tail_values<BLOCK, 1, S, CAPB, ALIGNED>(xb, p.V, nfull, g0, CapArgs{p.ky, p.iy}, b);
         }
+        const CapArgs ca{p.kx, p.ix};
 
         RowStats rs = stats[row];
         if (KL && p.swap) swap_sides(rs);
+        fixed_refs<CAPA, CAPB, KL>(rs);
 
         int mode = kModeNormal;
         float G = 0.0f;
@@ -314,10 +340,13 @@ __global__ __launch_bounds__(BLOCK) void bwd_piece_kernel(BwdParams p, int64_t r
             const float g_row = (HEAD == kHeadLogp) ? 0.0f : p.g[row];
             float A, B;
             row_coeffs<HEAD, CAPA>(rs, G, g_row, A, B);
+            float a[kChunk], s4[kChunk];
 #pragma unroll
-            for (int e = 0; e < kChunk; ++e)
-                v[0][e] = grad_elem<HEAD, CAPA>(a[0][e], KL ? b[0][e] : 0.0f, rs, A, B, p.scx,
-                                                p.scy);
+            for (int e = 0; e < kChunk; ++e) {
+                a[e] = cap_value_slope<CAPA>(x[0][e], ca, s4[e]);
+                v[0][e] = grad_elem<HEAD, CAPA>(a[e], s4[e], KL ? b[0][e] : 0.0f, rs, A, B,
+                                                p.scx, p.scy);
+            }
             if (HEAD == kHeadLogp) {
                 // one-hot terms: a slot whose column falls in this lane's chunk
                 const int64_t col0 = c * kChunk;
@@ -336,14 +365,14 @@ __global__ __launch_bounds__(BLOCK) void bwd_piece_kernel(BwdParams p, int64_t r
                                 h += gs[j];
                                 hit = true;
                             }
-                        if (hit) v[0][e] = target_grad<CAPA>(a[0][e], rs, G, h, p.scx);
+                        if (hit) v[0][e] = target_grad<CAPA>(a[e], s4[e], rs, G, h, p.scx);
                     }
                 }
             }
         } else if (mode == kModeMismatch) {
 #pragma unroll
             for (int e = 0; e < kChunk; ++e)
-                v[0][e] = (!CAPA && a[0][e] == neg_inf()) ? 0.0f : qnan();
+                v[0][e] = (CAPA == kCapNone && x[0][e] == neg_inf()) ? 0.0f : qnan();
         } else {
             const float fill = mode == kModeZero ? 0.0f : qnan();
 #pragma unroll
@@ -365,7 +394,7 @@ __global__ __launch_bounds__(BLOCK) void bwd_piece_kernel(BwdParams p, int64_t r
 // Rows per piece launch (the grid's second dimension is limited to 65536).
 constexpr int64_t kPieceRowsPerLaunch = 65536;
 
-template <typename T, int HEAD, bool CAPX, bool CAPY, bool AL>
+template <typename T, int HEAD, int CAPX, int CAPY, bool AL>
 inline hipError_t bwd_piece_launch(const BwdParams& p, hipStream_t s) {
     const int64_t pieces = ((p.V + kChunk - 1) / kChunk + kBwdPieceBlock - 1) / kBwdPieceBlock;
     for (int64_t r0 = 0; r0 < p.N; r0 += kPieceRowsPerLaunch) {
@@ -379,7 +408,7 @@ inline hipError_t bwd_piece_launch(const BwdParams& p, hipStream_t s) {
     return hipSuccess;
 }
 
-template <int BB, int U, typename T, bool CAPX, bool AL>
+template <int BB, int U, typename T, int CAPX, bool AL>
 inline hipError_t bwd_topk_launch(const BwdParams& p, hipStream_t s) {
     const size_t lds = static_cast<size_t>(p.k) * (sizeof(int) + sizeof(float));
     hipLaunchKernelGGL((bwd_topk_kernel<BB, U, T, CAPX, AL>), dim3(row_grid(p.N * p.split)),
@@ -387,11 +416,11 @@ inline hipError_t bwd_topk_launch(const BwdParams& p, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <typename T, bool CAPX, bool CAPY, bool AL>
+template <typename T, int CAPX, int CAPY, bool AL>
 inline hipError_t bwd_dispatch_al(int head, const BwdParams& p0, hipStream_t s) {
     switch (head) {
         case kHeadEntropy:
-            return bwd_piece_launch<T, kHeadEntropy, CAPX, false, AL>(p0, s);
+            return bwd_piece_launch<T, kHeadEntropy, CAPX, kCapNone, AL>(p0, s);
         case kHeadKLReverse:
             return bwd_piece_launch<T, kHeadKLReverse, CAPX, CAPY, AL>(p0, s);
         case kHeadKLForward:
@@ -401,7 +430,7 @@ inline hipError_t bwd_dispatch_al(int head, const BwdParams& p0, hipStream_t s) 
         default:
             return hipErrorInvalidValue;
     }
-    if (p0.k <= kPieceMaxK) return bwd_piece_launch<T, kHeadLogp, CAPX, false, AL>(p0, s);
+    if (p0.k <= kPieceMaxK) return bwd_piece_launch<T, kHeadLogp, CAPX, kCapNone, AL>(p0, s);
     BwdParams p = p0;
     if (p.N < kBwdSmallRows) {
         // Few rows: narrow workgroups, each row cut into column segments.
@@ -415,19 +444,27 @@ inline hipError_t bwd_dispatch_al(int head, const BwdParams& p0, hipStream_t s) 
     return bwd_topk_launch<kBwdBlockTopk, kBwdUnrollTopk, T, CAPX, AL>(p, s);
 }
 
+template <typename T, int CAPX, int CAPY>
+inline hipError_t bwd_dispatch_a(int head, bool al, const BwdParams& p, hipStream_t s) {
+    return al ? bwd_dispatch_al<T, CAPX, CAPY, true>(head, p, s)
+              : bwd_dispatch_al<T, CAPX, CAPY, false>(head, p, s);
+}
+
+template <typename T, int CAPX>
+inline hipError_t bwd_dispatch_cy(int head, int cy, bool al, const BwdParams& p, hipStream_t s) {
+    if (cy == kCapOnline) return bwd_dispatch_a<T, CAPX, kCapOnline>(head, al, p, s);
+    if (cy == kCapFixed) return bwd_dispatch_a<T, CAPX, kCapFixed>(head, al, p, s);
+    return bwd_dispatch_a<T, CAPX, kCapNone>(head, al, p, s);
+}
+
 template <typename T>
-inline hipError_t bwd_dispatch_cap(int head, bool cx, bool cy, bool al, const BwdParams& p,
+inline hipError_t bwd_dispatch_cap(int head, int cx, int cy, bool al, const BwdParams& p,
                                    hipStream_t s) {
     const bool kl = head == kHeadKLReverse || head == kHeadKLForward;
-    if (!kl) cy = false;
-    if (cx && cy) return al ? bwd_dispatch_al<T, true, true, true>(head, p, s)
-                            : bwd_dispatch_al<T, true, true, false>(head, p, s);
-    if (cx) return al ? bwd_dispatch_al<T, true, false, true>(head, p, s)
-                      : bwd_dispatch_al<T, true, false, false>(head, p, s);
-    if (cy) return al ? bwd_dispatch_al<T, false, true, true>(head, p, s)
-                      : bwd_dispatch_al<T, false, true, false>(head, p, s);
-    return al ? bwd_dispatch_al<T, false, false, true>(head, p, s)
-              : bwd_dispatch_al<T, false, false, false>(head, p, s);
+    if (!kl) cy = kCapNone;
+    if (cx == kCapOnline) return bwd_dispatch_cy<T, kCapOnline>(head, cy, al, p, s);
+    if (cx == kCapFixed) return bwd_dispatch_cy<T, kCapFixed>(head, cy, al, p, s);
+    return bwd_dispatch_cy<T, kCapNone>(head, cy, al, p, s);
 }
 
 }  // namespace rlk

@@ -14,19 +14,23 @@
 // Online statistics in base 2 (the single-read scheme of the review comment
 // on "Add Triton kernels for vocab-parallel logprobs, entropy and KL",
 // DeepSpeed pull request 8838, re-derived here with exp2):
-//   a_v  = x_v, or tanh(x_v / c) when the softcap is on (then y = c a);
-//   sc   = log2(e), or c log2(e);  so y_v log2(e) = a_v sc;
+//   a_v  = the statistic input of logit x_v: x_v itself, or with the softcap
+//          one of the two forms of cap_value below;
+//   sc   = its scale, so that y_v log2(e) = a_v sc + (a constant of the row);
 //   mL   = m sc with m the running maximum of a (a rounded constant that is
-//          used consistently everywhere, so its rounding cancels);
+//          used consistently everywhere, so its rounding cancels), or the
+//          fixed reference 0 of the fixed cap form;
 //   t_v  = a_v sc - mL (one FMA), S = sum 2^t_v, W = sum 2^t_v t_v.
 //   When the maximum grows by d = mL_old - mL_new (< 0):
 //          S <- 2^d S,  W <- 2^d (W + d S).
-//   Then logsumexp(y) = ln2 (mL + log2 S) and the entropy is
+//   Then log p_v = ln2 (t_v - log2 S) and the entropy is
 //          H = ln2 (log2 S - W / S).
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include "rlk_launch.h"
 
 namespace rlk {
 
@@ -163,14 +167,51 @@ __device__ __forceinline__ void store_one(_Float16* p, float f) { *p = static_ca
 //
 // Fused prologue form.  With r = 1 / (1 + 2^(k x)), k = -2 log2(e) / c:
 //   tanh(x / c) = 2 r - 1   and   1 - tanh^2(x / c) = 4 r (1 - r),
-// so y log2(e) = (2 c log2(e)) r - c log2(e).  The row kernels carry r
-// itself as the statistic's input with the scale sc = 2 c log2(e): the
-// constant -c log2(e) is common to every logit of the row and cancels
-// exactly in t = y log2(e) - max.  Both ends are exact (x = +inf: r = 1;
-// x = -inf: r = 0, i.e. y = -c; slope 0 at both).  The absolute error of r
-// is about 1e-7 and the softmax depends only on absolute errors of y.
-__device__ __forceinline__ float cap_r(float x, float k) { return rcp(1.0f + ex2(x * k)); }
-__device__ __forceinline__ float cap_slope_r(float r) { return 4.0f * __builtin_fmaf(-r, r, r); }
+// so y log2(e) = sc r - c log2(e) with sc = 2 c log2(e).  Two forms of the
+// statistic input (CapMode in rlk_launch.h):
+//   online: a = r with the scale sc; the constant -c log2(e) is common to
+//           every logit of the row and cancels exactly in t = y log2(e) - max;
+//   fixed:  a = t = (y - c) log2(e) = sc (r - 1) = -sc / (1 + 2^(-k x))
+//           itself (scale 1, reference 0), one FMA and a reciprocal away
+//           from the exponential: -1 / (1/sc + 2^(-k x) / sc).
+// Both ends are exact (x = +inf: r = 1, t = 0; x = -inf: r = 0, i.e.
+// y = -c; slope 0 at both).  The absolute error of a is about 1e-7 (online)
+// or 1e-7 sc (fixed); the softmax depends only on absolute errors of y.
+struct CapArgs {
+    float k;    // -2 log2(e) / c
+    float isc;  // fixed form: 1 / sc
+};
+
+template <int CAP>
+__device__ __forceinline__ float cap_value(float x, CapArgs c) {
+    if (CAP == kCapOnline) return rcp(1.0f + ex2(x * c.k));
+    if (CAP == kCapFixed) return -rcp(__builtin_fmaf(ex2(-(x * c.k)), c.isc, c.isc));
+    return x;
+}
+
+// Statistic input and a quarter of the slope, r (1 - r) = (1 - tanh^2) / 4.
+// Fixed form: with q = 2^(-k x) and w = sc / (1 + q) (so a = -w), 1 - r =
+// w / sc and r = q (1 - r) -- the latter is inf * 0 only at x = +inf, where
+// the minimum with 1 gives r = 1 (a NaN x stays NaN through 1 - r).  Neither
+// factor is a difference, so the slope keeps its relative accuracy in both
+// tails, and it is exactly 0 at x = -inf (q = 0) and x = +inf (1 - r = 0).
+template <int CAP>
+__device__ __forceinline__ float cap_value_slope(float x, CapArgs c, float& s4) {
+    if (CAP == kCapOnline) {
+        const float r = rcp(1.0f + ex2(x * c.k));
+        s4 = __builtin_fmaf(-r, r, r);
+        return r;
+    }
+    if (CAP == kCapFixed) {
+        const float q = ex2(-(x * c.k));
+        const float w = rcp(__builtin_fmaf(q, c.isc, c.isc));
+        const float u = w * c.isc;
+        s4 = fminf(q * u, 1.0f) * u;
+        return -w;
+    }
+    s4 = 1.0f;
+    return x;
+}
 
 // Standalone form, accurate in RELATIVE terms (the output y itself is
 // compared at 1e-5 relative).  For |u| < 0.55 an odd polynomial
@@ -279,19 +320,20 @@ __device__ __forceinline__ void raw_unpack(const RawGroup<float, U>& r, float (&
 // inside an aligned row still use one vector load; the remaining elements are
 // loaded from clamped (always valid) addresses without branches, so all loads
 // are in flight together, and slots beyond V become -inf (they contribute
-// exactly 0; consumers clamp t before any 0 * t in tail groups).  With CAP
-// the in-range values are mapped to r while padding stays -inf.
-template <int BLOCK, int U, typename S, bool CAP, bool ALIGNED>
+// exactly 0; consumers clamp t before any 0 * t in tail groups).  With a
+// cap the in-range values are mapped to their statistic input (cap_value)
+// while padding stays -inf.
+template <int BLOCK, int U, typename S, int CAP, bool ALIGNED>
 __device__ __forceinline__ void tail_values(const S* __restrict__ row, int64_t V, int64_t nfull,
-                                            int64_t g0, float k, float (&a)[U][kChunk]) {
+                                            int64_t g0, CapArgs ca, float (&a)[U][kChunk]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int64_t c = g0 + u * BLOCK + (int)threadIdx.x;
         if (ALIGNED && c < nfull) {
             load_chunk(row + c * kChunk, a[u]);
-            if (CAP) {
+            if (CAP != kCapNone) {
 #pragma unroll
-                for (int e = 0; e < kChunk; ++e) a[u][e] = cap_r(a[u][e], k);
+                for (int e = 0; e < kChunk; ++e) a[u][e] = cap_value<CAP>(a[u][e], ca);
             }
         } else if (c * kChunk >= V) {
 #pragma unroll
@@ -306,21 +348,22 @@ __device__ __forceinline__ void tail_values(const S* __restrict__ row, int64_t V
 #pragma unroll
             for (int e = 0; e < kChunk; ++e) {
                 const int64_t col = c * kChunk + e;
-                const float w = CAP ? cap_r(v[e], k) : v[e];
+                const float w = cap_value<CAP>(v[e], ca);
                 a[u][e] = col < V ? w : neg_inf();
             }
         }
     }
 }
 // Fast-group counterpart: unpack the raw vectors (and apply the cap).
-template <int U, typename S, bool CAP>
-__device__ __forceinline__ void fast_values(const RawGroup<S, U>& r, float k, float (&a)[U][kChunk]) {
+template <int U, typename S, int CAP>
+__device__ __forceinline__ void fast_values(const RawGroup<S, U>& r, CapArgs ca,
+                                            float (&a)[U][kChunk]) {
     raw_unpack(r, a);
-    if (CAP) {
+    if (CAP != kCapNone) {
 #pragma unroll
         for (int u = 0; u < U; ++u)
 #pragma unroll
-            for (int e = 0; e < kChunk; ++e) a[u][e] = cap_r(a[u][e], k);
+            for (int e = 0; e < kChunk; ++e) a[u][e] = cap_value<CAP>(a[u][e], ca);
     }
 }
 
@@ -332,8 +375,8 @@ __device__ __forceinline__ void fast_values(const RawGroup<S, U>& r, float k, fl
 //
 // gbeg / gend restrict the walk to the groups [gbeg, gend) of the row (a
 // column segment); -1 for gend means "to the end of the row".
-template <int BLOCK, int U, typename S, bool CAP, bool ALIGNED, bool PIPE, typename F>
-__device__ __forceinline__ void for_each_group(const S* __restrict__ row, int64_t V, float k, F&& f,
+template <int BLOCK, int U, typename S, int CAP, bool ALIGNED, bool PIPE, typename F>
+__device__ __forceinline__ void for_each_group(const S* __restrict__ row, int64_t V, CapArgs k, F&& f,
                                                int64_t gbeg = 0, int64_t gend = -1) {
     const int64_t step = (int64_t)U * BLOCK;
     const int64_t nchunks = (V + kChunk - 1) / kChunk, nfull = V / kChunk;
@@ -382,9 +425,9 @@ __device__ __forceinline__ void for_each_group(const S* __restrict__ row, int64_
 }
 
 // Same walk over two rows in lockstep (KL: policy and reference).
-template <int BLOCK, int U, typename S, bool CAPA, bool CAPB, bool ALIGNED, bool PIPE, typename F>
+template <int BLOCK, int U, typename S, int CAPA, int CAPB, bool ALIGNED, bool PIPE, typename F>
 __device__ __forceinline__ void for_each_group2(const S* __restrict__ ra, const S* __restrict__ rb,
-                                                int64_t V, float ka, float kb, F&& f,
+                                                int64_t V, CapArgs ka, CapArgs kb, F&& f,
                                                 int64_t gbeg = 0, int64_t gend = -1) {
     const int64_t step = (int64_t)U * BLOCK;
     const int64_t nchunks = (V + kChunk - 1) / kChunk, nfull = V / kChunk;
@@ -472,7 +515,12 @@ struct Stat1 {
     float m, mL, S, W;
 };
 
-__device__ __forceinline__ Stat1 stat1_init() { return {neg_inf(), 0.0f, 0.0f, 0.0f}; }
+// FIXED (kCapFixed): the reference is the bound 0 of every t from the start
+// (m = mL = 0) and never moves.
+template <bool FIXED = false>
+__device__ __forceinline__ Stat1 stat1_init() {
+    return {FIXED ? 0.0f : neg_inf(), 0.0f, 0.0f, 0.0f};
+}
 
 // Merge two partial states (exact up to rounding; empty parts drop out).
 template <bool WITH_W>
@@ -499,9 +547,10 @@ struct StatKL {
     float ma, mLa, Sa, mb, mLb, Sb, W, flag;
 };
 
-template <bool REVERSE>
+template <bool REVERSE, bool FIXA = false, bool FIXB = false>
 __device__ __forceinline__ StatKL statkl_init() {
-    return {neg_inf(), 0.0f, 0.0f, neg_inf(), 0.0f, 0.0f, 0.0f, REVERSE ? neg_inf() : pos_inf()};
+    return {FIXA ? 0.0f : neg_inf(), 0.0f, 0.0f, FIXB ? 0.0f : neg_inf(), 0.0f, 0.0f, 0.0f,
+            REVERSE ? neg_inf() : pos_inf()};
 }
 
 template <bool REVERSE>
@@ -547,8 +596,10 @@ struct StatKL2 {
     float ma, mLa, Sa, mb, mLb, Sb, Wr, Wf, fmax, fmin;
 };
 
+template <bool FIXA = false, bool FIXB = false>
 __device__ __forceinline__ StatKL2 statkl2_init() {
-    return {neg_inf(), 0.0f, 0.0f, neg_inf(), 0.0f, 0.0f, 0.0f, 0.0f, neg_inf(), pos_inf()};
+    return {FIXA ? 0.0f : neg_inf(), 0.0f, 0.0f, FIXB ? 0.0f : neg_inf(), 0.0f, 0.0f, 0.0f, 0.0f,
+            neg_inf(), pos_inf()};
 }
 __device__ __forceinline__ StatKL kl_view_rev(const StatKL2& s) {
     return {s.ma, s.mLa, s.Sa, s.mb, s.mLb, s.Sb, s.Wr, s.fmax};

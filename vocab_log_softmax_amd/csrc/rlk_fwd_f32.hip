@@ -4,7 +4,7 @@
 
 namespace rlk {
 
-hipError_t launch_fwd_f32(int head, bool cap_x, bool cap_y, bool aligned,
+hipError_t launch_fwd_f32(int head, int cap_x, int cap_y, bool aligned,
                            const FwdParams& p, hipStream_t stream) {
     return fwd_dispatch_cap<F32>(head, cap_x, cap_y, aligned, p, stream);
 }

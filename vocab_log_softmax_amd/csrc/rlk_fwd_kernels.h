@@ -24,15 +24,16 @@ namespace rlk {
 
 // Fold one group into a single-tensor state.  CLAMP keeps 0 * (-inf) out of
 // W where -inf can occur: masked logits (never with the softcap) and the
-// padding of a row's tail group.
-template <int U, bool WITH_W, bool CLAMP>
+// padding of a row's tail group.  FIXED: a is already t (fixed cap form), the
+// reference never moves.
+template <int U, bool WITH_W, bool CLAMP, bool FIXED = false>
 __device__ __forceinline__ void update1(Stat1& st, const float (&a)[U][kChunk], float sc) {
     float gm = a[0][0];
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
         for (int e = 0; e < kChunk; ++e) gm = fmaxf(gm, a[u][e]);
-    if (gm > st.m) {
+    if (!FIXED && gm > st.m) {
         const float mLn = gm * sc;
         if (st.m != neg_inf()) {
             const float d = st.mL - mLn;
@@ -47,7 +48,7 @@ __device__ __forceinline__ void update1(Stat1& st, const float (&a)[U][kChunk], 
     for (int u = 0; u < U; ++u)
 #pragma unroll
         for (int e = 0; e < kChunk; ++e) {
-            float t = __builtin_fmaf(a[u][e], sc, -st.mL);
+            float t = FIXED ? a[u][e] : __builtin_fmaf(a[u][e], sc, -st.mL);
             if (CLAMP) t = fmaxf(t, kClampT);
             const float ex = ex2(t);
             st.S += ex;
@@ -55,8 +56,9 @@ __device__ __forceinline__ void update1(Stat1& st, const float (&a)[U][kChunk], 
         }
 }
 
-// Fold one group into a KL state (a: policy, b: reference).
-template <int U, bool REVERSE>
+// Fold one group into a KL state (a: policy, b: reference).  FIXA / FIXB:
+// that side's values are already t (fixed cap form).
+template <int U, bool REVERSE, bool FIXA = false, bool FIXB = false>
 __device__ __forceinline__ void update_kl(StatKL& st, const float (&a)[U][kChunk],
                                           const float (&b)[U][kChunk], float sca, float scb) {
     float gma = a[0][0], gmb = b[0][0];
@@ -67,7 +69,7 @@ __device__ __forceinline__ void update_kl(StatKL& st, const float (&a)[U][kChunk
             gma = fmaxf(gma, a[u][e]);
             gmb = fmaxf(gmb, b[u][e]);
         }
-    if (gma > st.ma) {
+    if (!FIXA && gma > st.ma) {
         const float mLn = gma * sca;
         if (st.ma != neg_inf()) {
             const float d = st.mLa - mLn;
@@ -81,7 +83,7 @@ __device__ __forceinline__ void update_kl(StatKL& st, const float (&a)[U][kChunk
         st.ma = gma;
         st.mLa = mLn;
     }
-    if (gmb > st.mb) {
+    if (!FIXB && gmb > st.mb) {
         const float mLn = gmb * scb;
         if (st.mb != neg_inf()) {
             const float d = st.mLb - mLn;
@@ -99,8 +101,8 @@ __device__ __forceinline__ void update_kl(StatKL& st, const float (&a)[U][kChunk
     for (int u = 0; u < U; ++u)
 #pragma unroll
         for (int e = 0; e < kChunk; ++e) {
-            const float ta = __builtin_fmaf(a[u][e], sca, -st.mLa);
-            const float tb = __builtin_fmaf(b[u][e], scb, -st.mLb);
+            const float ta = FIXA ? a[u][e] : __builtin_fmaf(a[u][e], sca, -st.mLa);
+            const float tb = FIXB ? b[u][e] : __builtin_fmaf(b[u][e], scb, -st.mLb);
             const float ea = ex2(ta), eb = ex2(tb);
             st.Sa += ea;
             st.Sb += eb;
@@ -117,7 +119,7 @@ __device__ __forceinline__ void update_kl(StatKL& st, const float (&a)[U][kChunk
 
 // Fold one group into the two-direction KL state: each direction's W and
 // flag see the very operations of update_kl<U, true> / update_kl<U, false>.
-template <int U>
+template <int U, bool FIXA = false, bool FIXB = false>
 __device__ __forceinline__ void update_kl2(StatKL2& st, const float (&a)[U][kChunk],
                                            const float (&b)[U][kChunk], float sca, float scb) {
     float gma = a[0][0], gmb = b[0][0];
@@ -128,7 +130,7 @@ __device__ __forceinline__ void update_kl2(StatKL2& st, const float (&a)[U][kChu
             gma = fmaxf(gma, a[u][e]);
             gmb = fmaxf(gmb, b[u][e]);
         }
-    if (gma > st.ma) {
+    if (!FIXA && gma > st.ma) {
         const float mLn = gma * sca;
         if (st.ma != neg_inf()) {
             const float d = st.mLa - mLn;
@@ -140,7 +142,7 @@ __device__ __forceinline__ void update_kl2(StatKL2& st, const float (&a)[U][kChu
         st.ma = gma;
         st.mLa = mLn;
     }
-    if (gmb > st.mb) {
+    if (!FIXB && gmb > st.mb) {
         const float mLn = gmb * scb;
         if (st.mb != neg_inf()) {
             const float d = st.mLb - mLn;
@@ -156,8 +158,8 @@ __device__ __forceinline__ void update_kl2(StatKL2& st, const float (&a)[U][kChu
     for (int u = 0; u < U; ++u)
 #pragma unroll
         for (int e = 0; e < kChunk; ++e) {
-            const float ta = __builtin_fmaf(a[u][e], sca, -st.mLa);
-            const float tb = __builtin_fmaf(b[u][e], scb, -st.mLb);
+            const float ta = FIXA ? a[u][e] : __builtin_fmaf(a[u][e], sca, -st.mLa);
+            const float tb = FIXB ? b[u][e] : __builtin_fmaf(b[u][e], scb, -st.mLb);
             const float ea = ex2(ta), eb = ex2(tb);
             st.Sa += ea;
             st.Sb += eb;
@@ -170,11 +172,13 @@ __device__ __forceinline__ void update_kl2(StatKL2& st, const float (&a)[U][kChu
 }
 
 // Logprobs / entropy forward: one workgroup per row.
-template <int BLOCK, int U, typename T, int HEAD, bool CAP, bool ALIGNED>
+template <int BLOCK, int U, typename T, int HEAD, int CAP, bool ALIGNED>
 __global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void fwd1_kernel(FwdParams p) {
     using S = typename T::storage;
     constexpr bool WITH_W = HEAD == kHeadEntropy;
-    constexpr bool CLAMP = WITH_W && !CAP;  // full groups; tail groups always clamp
+    constexpr bool FIX = CAP == kCapFixed;
+    constexpr bool CLAMP = WITH_W && CAP == kCapNone;  // full groups; tail groups always clamp
+    const CapArgs ca{p.kx, p.ix};
     constexpr int NW = BLOCK / 64;
     __shared__ Stat1 red[NW];
     __shared__ float bc[2];
@@ -190,14 +194,14 @@ __global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void fwd1_kernel(FwdParams p) 
             t0 = p.targets[row * p.k + tid];
             if (t0 >= p.v0 && t0 < p.v0 + p.V) xt0 = load_one(x + (t0 - p.v0));
         }
-        Stat1 st = stat1_init();
+        Stat1 st = stat1_init<FIX>();
         for_each_group<BLOCK, U, S, CAP, ALIGNED, kFwdPipe>(
-            x, p.V, p.kx,
+            x, p.V, ca,
             [&](int64_t, bool full, const float (&a)[U][kChunk]) {
                 if (full)
-                    update1<U, WITH_W, CLAMP>(st, a, p.scx);
+                    update1<U, WITH_W, CLAMP, FIX>(st, a, p.scx);
                 else
-                    update1<U, WITH_W, WITH_W>(st, a, p.scx);
+                    update1<U, WITH_W, WITH_W, FIX>(st, a, p.scx);
             });
         st = wave_reduce<WITH_W>(st);
         if (lane == 0) red[wid] = st;
@@ -226,8 +230,7 @@ __global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void fwd1_kernel(FwdParams p) 
                 const bool local = t >= p.v0 && t < p.v0 + p.V;
                 float a = 0.0f;
                 if (local) {
-                    a = j == tid ? xt0 : load_one(x + (t - p.v0));
-                    if (CAP) a = cap_r(a, p.kx);
+                    a = cap_value<CAP>(j == tid ? xt0 : load_one(x + (t - p.v0)), ca);
                 }
                 if (p.part)
                     p.tvals[row * p.k + j] = a;  // statistic input of an owned target
@@ -240,8 +243,9 @@ __global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void fwd1_kernel(FwdParams p) 
 }
 
 // KL forward (either direction): one workgroup per row pair.
-template <int BLOCK, int U, typename T, bool REVERSE, bool CAPA, bool CAPB, bool ALIGNED>
+template <int BLOCK, int U, typename T, bool REVERSE, int CAPA, int CAPB, bool ALIGNED>
 __global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void fwdkl_kernel(FwdParams p) {
+    constexpr bool FIXA = CAPA == kCapFixed, FIXB = CAPB == kCapFixed;
     using S = typename T::storage;
     constexpr int NW = BLOCK / 64;
     __shared__ StatKL red[NW];
@@ -250,11 +254,11 @@ __global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void fwdkl_kernel(FwdParams p)
     for (int64_t row = blockIdx.x; row < p.N; row += gridDim.x) {
         const S* __restrict__ xa = static_cast<const S*>(p.x) + p.mx.offset(row);
         const S* __restrict__ xb = static_cast<const S*>(p.y) + p.my.offset(row);
-        StatKL st = statkl_init<REVERSE>();
+        StatKL st = statkl_init<REVERSE, FIXA, FIXB>();
         for_each_group2<BLOCK, U, S, CAPA, CAPB, ALIGNED, kFwdPipe>(
-            xa, xb, p.V, p.kx, p.ky,
+            xa, xb, p.V, CapArgs{p.kx, p.ix}, CapArgs{p.ky, p.iy},
             [&](int64_t, bool, const float (&a)[U][kChunk], const float (&b)[U][kChunk]) {
-                update_kl<U, REVERSE>(st, a, b, p.scx, p.scy);
+                update_kl<U, REVERSE, FIXA, FIXB>(st, a, b, p.scx, p.scy);
             });
         st = wave_reduce_kl<REVERSE>(st);
         if (lane == 0) red[wid] = st;
@@ -277,8 +281,9 @@ __global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void fwdkl_kernel(FwdParams p)
 
 // Both KL directions from one read of the pair: reverse KL to out / stats,
 // forward KL to out2 / stats2, each bit-identical to its one-direction call.
-template <int BLOCK, int U, typename T, bool CAPA, bool CAPB, bool ALIGNED>
+template <int BLOCK, int U, typename T, int CAPA, int CAPB, bool ALIGNED>
 __global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void fwdkl2_kernel(FwdParams p) {
+    constexpr bool FIXA = CAPA == kCapFixed, FIXB = CAPB == kCapFixed;
     using S = typename T::storage;
     constexpr int NW = BLOCK / 64;
     __shared__ StatKL2 red[NW];
@@ -288,11 +293,11 @@ __global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void fwdkl2_kernel(FwdParams p
     for (int64_t row = blockIdx.x; row < p.N; row += gridDim.x) {
         const S* __restrict__ xa = static_cast<const S*>(p.x) + p.mx.offset(row);
         const S* __restrict__ xb = static_cast<const S*>(p.y) + p.my.offset(row);
-        StatKL2 st = statkl2_init();
+        StatKL2 st = statkl2_init<FIXA, FIXB>();
         for_each_group2<BLOCK, U, S, CAPA, CAPB, ALIGNED, kFwdPipe>(
-            xa, xb, p.V, p.kx, p.ky,
+            xa, xb, p.V, CapArgs{p.kx, p.ix}, CapArgs{p.ky, p.iy},
             [&](int64_t, bool, const float (&a)[U][kChunk], const float (&b)[U][kChunk]) {
-                update_kl2<U>(st, a, b, p.scx, p.scy);
+                update_kl2<U, FIXA, FIXB>(st, a, b, p.scx, p.scy);
             });
         st = wave_reduce_kl2(st);
         if (lane == 0) red[wid] = st;
@@ -314,7 +319,7 @@ __global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void fwdkl2_kernel(FwdParams p
 
 // ------------------------------------------------------------- dispatch
 
-template <typename T, bool CAPX, bool CAPY, bool AL>
+template <typename T, int CAPX, int CAPY, bool AL>
 inline hipError_t fwd_dispatch_head(int head, const FwdParams& p, hipStream_t s) {
     const dim3 grid(row_grid(p.N)), block(kBlock);
     switch (head) {
@@ -344,21 +349,27 @@ inline hipError_t fwd_dispatch_head(int head, const FwdParams& p, hipStream_t s)
     return hipGetLastError();
 }
 
-template <typename T, bool CAPX, bool CAPY>
+template <typename T, int CAPX, int CAPY>
 inline hipError_t fwd_dispatch_al(int head, bool al, const FwdParams& p, hipStream_t s) {
     return al ? fwd_dispatch_head<T, CAPX, CAPY, true>(head, p, s)
               : fwd_dispatch_head<T, CAPX, CAPY, false>(head, p, s);
 }
 
+template <typename T, int CAPX>
+inline hipError_t fwd_dispatch_cy(int head, int cy, bool al, const FwdParams& p, hipStream_t s) {
+    if (cy == kCapOnline) return fwd_dispatch_al<T, CAPX, kCapOnline>(head, al, p, s);
+    if (cy == kCapFixed) return fwd_dispatch_al<T, CAPX, kCapFixed>(head, al, p, s);
+    return fwd_dispatch_al<T, CAPX, kCapNone>(head, al, p, s);
+}
+
 template <typename T>
-inline hipError_t fwd_dispatch_cap(int head, bool cx, bool cy, bool al, const FwdParams& p,
+inline hipError_t fwd_dispatch_cap(int head, int cx, int cy, bool al, const FwdParams& p,
                                    hipStream_t s) {
     const bool kl = head == kHeadKLReverse || head == kHeadKLForward || head == kHeadKLBoth;
-    if (!kl) cy = false;  // the second cap only exists for KL
-    if (cx && cy) return fwd_dispatch_al<T, true, true>(head, al, p, s);
-    if (cx) return fwd_dispatch_al<T, true, false>(head, al, p, s);
-    if (cy) return fwd_dispatch_al<T, false, true>(head, al, p, s);
-    return fwd_dispatch_al<T, false, false>(head, al, p, s);
+    if (!kl) cy = kCapNone;  // the second cap only exists for KL
+    if (cx == kCapOnline) return fwd_dispatch_cy<T, kCapOnline>(head, cy, al, p, s);
+    if (cx == kCapFixed) return fwd_dispatch_cy<T, kCapFixed>(head, cy, al, p, s);
+    return fwd_dispatch_cy<T, kCapNone>(head, cy, al, p, s);
 }
 
 }  // namespace rlk

@@ -17,6 +17,18 @@ enum Head : int {
     kHeadKLBoth = 4
 };
 
+// Softcap modes of one logits tensor (host-chosen from the cap c, the same
+// for a forward call, its backward and the shard combine):
+//   kCapNone   no cap; statistic input a = x, scale log2(e);
+//   kCapOnline a = r = 1 / (1 + 2^(k x)), scale 2 c log2(e), running max;
+//   kCapFixed  a = t = (y - c) log2(e) = -1 / (1/sc + 2^(-k x)/sc) in one FMA
+//              and a reciprocal, scale 1, reference 0 (no running max).
+// t of the fixed mode lies in [-2 c log2(e), 0], so for caps with
+// 2 c log2(e) <= kCapFixedMaxScale every 2^t is a normal float and the sums
+// need no rescaling; larger caps take the online mode.
+enum CapMode : int { kCapNone = 0, kCapOnline = 1, kCapFixed = 2 };
+constexpr float kCapFixedMaxScale = 120.0f;
+
 // Launch shape of the forward row kernels: one workgroup per row (grid-stride
 // over rows), each lane consuming groups of U chunks of 8 elements.  These
 // constants fix the reduction tree, so they are the same for every N (the
@@ -101,7 +113,8 @@ struct FwdParams {
     const int64_t* targets;  // logp: [N, k]
     int64_t k;
     float kx, ky;    // softcap multiplier -2 log2(e) / c (unused when off)
-    float scx, scy;  // log2(e), or c log2(e) when the softcap is on
+    float scx, scy;  // statistic scale: log2(e), 2 c log2(e) (online cap) or 1 (fixed cap)
+    float ix, iy;    // fixed cap: 1 / (2 c log2(e)) (else unused)
     float* out;      // logp [N, k], entropy [N] or KL [N]
     void* stats;     // RowStats [N]
     // Vocabulary shard: the columns of x are [v0, v0 + V) of a row of width
@@ -124,7 +137,7 @@ struct BwdParams {
     RowMap mx, my, mg;  // row layouts of x, y and of the gradient output
     const int64_t* targets;
     int64_t k;
-    float kx, ky, scx, scy;
+    float kx, ky, scx, scy, ix, iy;
     const void* stats;
     const float* g;  // upstream gradient: [N, k] (logp) or [N]
     void* gx;        // gradient w.r.t. x, [N, V] contiguous, logits dtype
@@ -142,7 +155,7 @@ struct CombineParams {
     const void* part;                // PartialRec [P, N]
     const int64_t* targets;          // logp: [N, k]
     const float* tvals;              // logp: [P, N, k]
-    float sc;                        // statistic scale of the (capped) logits
+    float sc;                        // statistic scale of the logits (as FwdParams::scx)
     float* out;
     void* stats;
 };
@@ -150,27 +163,28 @@ struct CombineParams {
 hipError_t launch_combine(int head, const CombineParams& q, hipStream_t stream);
 
 // Per-dtype row-kernel launchers (rlk_fwd_<dtype>.hip, rlk_bwd_<dtype>.hip).
-hipError_t launch_fwd_f32(int head, bool cap_x, bool cap_y, bool aligned, const FwdParams& p,
+// cap_x / cap_y: CapMode of each tensor.
+hipError_t launch_fwd_f32(int head, int cap_x, int cap_y, bool aligned, const FwdParams& p,
                           hipStream_t stream);
-hipError_t launch_fwd_bf16(int head, bool cap_x, bool cap_y, bool aligned, const FwdParams& p,
+hipError_t launch_fwd_bf16(int head, int cap_x, int cap_y, bool aligned, const FwdParams& p,
                            hipStream_t stream);
-hipError_t launch_fwd_f16(int head, bool cap_x, bool cap_y, bool aligned, const FwdParams& p,
+hipError_t launch_fwd_f16(int head, int cap_x, int cap_y, bool aligned, const FwdParams& p,
                           hipStream_t stream);
-hipError_t launch_bwd_f32(int head, bool cap_x, bool cap_y, bool aligned, const BwdParams& p,
+hipError_t launch_bwd_f32(int head, int cap_x, int cap_y, bool aligned, const BwdParams& p,
                           hipStream_t stream);
-hipError_t launch_bwd_bf16(int head, bool cap_x, bool cap_y, bool aligned, const BwdParams& p,
+hipError_t launch_bwd_bf16(int head, int cap_x, int cap_y, bool aligned, const BwdParams& p,
                            hipStream_t stream);
-hipError_t launch_bwd_f16(int head, bool cap_x, bool cap_y, bool aligned, const BwdParams& p,
+hipError_t launch_bwd_f16(int head, int cap_x, int cap_y, bool aligned, const BwdParams& p,
                           hipStream_t stream);
 
 // dtype codes follow rlk_dtype (0 fp32, 1 bf16, 2 fp16).
-inline hipError_t launch_fwd(int head, int dtype, bool cap_x, bool cap_y, bool aligned,
+inline hipError_t launch_fwd(int head, int dtype, int cap_x, int cap_y, bool aligned,
                              const FwdParams& p, hipStream_t stream) {
     if (dtype == 0) return launch_fwd_f32(head, cap_x, cap_y, aligned, p, stream);
     if (dtype == 1) return launch_fwd_bf16(head, cap_x, cap_y, aligned, p, stream);
     return launch_fwd_f16(head, cap_x, cap_y, aligned, p, stream);
 }
-inline hipError_t launch_bwd(int head, int dtype, bool cap_x, bool cap_y, bool aligned,
+inline hipError_t launch_bwd(int head, int dtype, int cap_x, int cap_y, bool aligned,
                              const BwdParams& p, hipStream_t stream) {
     if (dtype == 0) return launch_bwd_f32(head, cap_x, cap_y, aligned, p, stream);
     if (dtype == 1) return launch_bwd_bf16(head, cap_x, cap_y, aligned, p, stream);
