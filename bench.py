@@ -286,9 +286,10 @@ def main() -> int:
         gx = torch.empty_like(x)
         fwd = lambda: rlk.rlk_logp_fwd(x, tg, w.cap, out, st)          # noqa: E731
         bwd = lambda: rlk.rlk_logp_bwd(x, tg, w.cap, st, g, gx)        # noqa: E731
-        # k <= 4 slots: one-shot pieces; wider top-k: the row kernel
-        n_in, fwd_name, bwd_name = 1, "fwd1_kernel", ("bwd_piece_kernel" if w.k <= 4
-                                                      else "bwd_topk_kernel")
+        # k <= 4 slots: one-shot pieces; up to 256: wide pieces; wider: the row kernel
+        n_in, fwd_name = 1, "fwd1_kernel"
+        bwd_name = ("bwd_piece_kernel" if w.k <= 4 else
+                    "bwd_wide_kernel" if w.k <= 256 else "bwd_topk_kernel")
     elif w.head == "entropy":
         g = d["grad"]
         out = torch.empty(N, dtype=torch.float32, device=dev)

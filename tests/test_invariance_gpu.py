@@ -155,10 +155,10 @@ def test_outputs_independent_of_stats_buffer_history(dev):
 
 @pytest.mark.parametrize("N", [37, 700])
 @pytest.mark.parametrize("cap", [0.0, 20.0, 60.0])
-def test_piece_and_topk_backward_kernels_agree(dev, N, cap):
-    # k <= 4 runs the one-shot piece kernel, k = 5 the top-k row kernel
-    # (few rows: column segments); a fifth slot that is ignored changes
-    # neither G nor any one-hot sum, so both must give the same bits.
+def test_piece_and_wide_backward_kernels_agree(dev, N, cap):
+    # k <= 4 runs the one-shot piece kernel, k = 5 the wide top-k piece
+    # kernel; a fifth slot that is ignored changes neither G nor any one-hot
+    # sum, so both must give the same bits.
     V = 9001
     x = (torch.randn(N, V, generator=_gen(11)) * 3).to(torch.bfloat16).to(dev)
     t4 = torch.randint(0, V, (N, 4), generator=_gen(12))
@@ -175,3 +175,34 @@ def test_piece_and_topk_backward_kernels_agree(dev, N, cap):
     torch.cuda.synchronize()
     assert_bitwise(lp4, lp5[:, :4], "forward outputs")
     assert_bitwise(gx4, gx5, "gradients of the two backward kernels")
+
+
+@pytest.mark.parametrize("N", [37, 700])
+@pytest.mark.parametrize("cap", [0.0, 20.0, 60.0])
+def test_wide_and_topk_backward_kernels_agree(dev, N, cap):
+    # k = 256 runs the wide top-k piece kernel, k = 257 the top-k row kernel
+    # (37 rows: column segments; 700 rows: one workgroup per row); the extra
+    # slot is ignored, so both must give the same bits.  Rows with heavy
+    # duplication, an all-ignored row and (without the cap) an empty row.
+    V = 20011
+    x = (torch.randn(N, V, generator=_gen(21)) * 4).to(torch.bfloat16)
+    if not cap:
+        x[3] = float("-inf")
+    t = torch.randint(0, V, (N, 256), generator=_gen(22))
+    t[:, 100:140] = t[:, 60:100]      # duplicates within the row
+    t[::3, 7] = t[::3, 0]
+    t[1, :] = torch.randint(0, 40, (256,), generator=_gen(23))  # few columns, many repeats
+    t[2, :] = -100                    # no valid slot
+    t[::5, 200:210] = -100
+    t[4, 255] = V + 3                 # out of range
+    g = torch.randn(N, 256, generator=_gen(24))
+    t7 = torch.cat([t, torch.full((N, 1), -100, dtype=torch.int64)], 1)
+    g7 = torch.cat([g, torch.randn(N, 1, generator=_gen(25))], 1)
+    x, t, t7, g, g7 = x.to(dev), t.to(dev), t7.to(dev), g.to(dev), g7.to(dev)
+    lp, st = rlk.logp_fwd(x, t, cap)
+    lp7, st7 = rlk.logp_fwd(x, t7, cap)
+    gx = rlk.logp_bwd(x, t, g, st, cap)
+    gx7 = rlk.logp_bwd(x, t7, g7, st7, cap)
+    torch.cuda.synchronize()
+    assert_bitwise(lp, lp7[:, :256], "forward outputs")
+    assert_bitwise(gx, gx7, "gradients of the two backward kernels")

@@ -259,97 +259,102 @@ __global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void bwd_topk_kernel(BwdParams
 // (wider ones bwd_topk_kernel).
 constexpr int kPieceMaxK = 4;
 
-// One-shot pieces: every workgroup computes the gradient of one chunk per
-// lane (BLOCK x 8 consecutive columns) of one row and exits.  Its loads are
-// issued before anything else, there is no barrier, no LDS and no loop, and
-// a workgroup's stores never hold up the next load: on this part such a
-// stream of short workgroups moves noticeably more bytes per second than
-// row-long loops.  Logprobs slots (k <= kPieceMaxK) are read by every lane:
-// G is summed in the association of bwd_topk_kernel's tree, and target
-// columns take target_grad, so both kernels give the same bits.
-template <int BLOCK, typename T, int HEAD, int CAPA, int CAPB, bool ALIGNED>
-__global__ __launch_bounds__(BLOCK) void bwd_piece_kernel(BwdParams p, int64_t rbase) {
+// One-shot pieces: every workgroup computes the gradient of U chunks per lane
+// (BLOCK x U x 8 columns) of one row and exits.  Its loads are issued before
+// anything else, there is no barrier, no LDS and no loop, and a workgroup's
+// stores never hold up the next load: on this part such a stream of short
+// workgroups moves noticeably more bytes per second than row-long loops.
+// Full pieces (every chunk inside an aligned row) load raw 16-byte vectors
+// with no branch between them.  Logprobs slots (k <= kPieceMaxK) are read by
+// every lane: G is summed in the association of bwd_topk_kernel's tree, and
+// target columns take target_grad, so all backward kernels give the same bits.
+template <int BLOCK, int U, typename T, int HEAD, int CAPA, int CAPB, bool ALIGNED, bool FULL>
+__device__ __forceinline__ void piece(const BwdParams& p, int64_t row, int64_t g0) {
     using S = typename T::storage;
     constexpr bool KL = HEAD == kHeadKLReverse || HEAD == kHeadKLForward;
     const int64_t nfull = p.V / kChunk;
     const RowStats* stats = static_cast<const RowStats*>(p.stats);
-    {
-        // grid (pieces of a row, rows): consecutive workgroups take consecutive
-        // pieces of a row, so the chip sweeps the matrix front to back; rows
-        // run last-first (see bwd_topk_kernel).
-        const int64_t row = p.N - 1 - (rbase + static_cast<int64_t>(blockIdx.y));
-        const int64_t g0 = static_cast<int64_t>(blockIdx.x) * BLOCK;  // first chunk of the piece
-        const int64_t c = g0 + (int)threadIdx.x;                       // this lane's chunk
-        const S* __restrict__ xa = static_cast<const S*>(p.x) + p.mx.offset(row);
-        S* __restrict__ gx = static_cast<S*>(p.gx) + p.mg.offset(row);
+    const S* __restrict__ xa = static_cast<const S*>(p.x) + p.mx.offset(row);
+    S* __restrict__ gx = static_cast<S*>(p.gx) + p.mg.offset(row);
 
-        // raw logits of x (the cap and its slope are taken per element),
-        // statistic inputs of y
-        float x[1][kChunk], b[1][kChunk];
-        tail_values<BLOCK, 1, S, kCapNone, ALIGNED>(xa, p.V, nfull, g0, CapArgs{}, x);
-        if (KL) {
-            const S* __restrict__ xb = static_cast<const S*>(p.y) + p.my.offset(row);
-            tail_values<BLOCK, 1, S, CAPB, ALIGNED>(xb, p.V, nfull, g0, CapArgs{p.ky, p.iy}, b);
-        }
-        const CapArgs ca{p.kx, p.ix};
+    // raw logits of x (the cap and its slope are taken per element),
+    // statistic inputs of y
+    float x[U][kChunk], b[U][kChunk];
+    RawGroup<S, U> rx, ry;
+    const CapArgs cb{p.ky, p.iy};
+    const S* __restrict__ xb = KL ? static_cast<const S*>(p.y) + p.my.offset(row) : nullptr;
+    if (FULL) {
+        raw_load<BLOCK, U>(xa, g0, rx);
+        if (KL) raw_load<BLOCK, U>(xb, g0, ry);
+    } else {
+        tail_values<BLOCK, U, S, kCapNone, ALIGNED>(xa, p.V, nfull, g0, CapArgs{}, x);
+        if (KL) tail_values<BLOCK, U, S, CAPB, ALIGNED>(xb, p.V, nfull, g0, cb, b);
+    }
+    const CapArgs ca{p.kx, p.ix};
 
-        RowStats rs = stats[row];
-        if (KL && p.swap) swap_sides(rs);
-        fixed_refs<CAPA, CAPB, KL>(rs);
+    RowStats rs = stats[row];
+    if (KL && p.swap) swap_sides(rs);
+    fixed_refs<CAPA, CAPB, KL>(rs);
 
-        int mode = kModeNormal;
-        float G = 0.0f;
-        int64_t tl[kPieceMaxK];  // local column of each slot, -1 if none
-        float gs[kPieceMaxK];
-        if (HEAD == kHeadLogp) {
-            float sv[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // valid slots' g, zeros beyond k
-            int nvalid = 0;
+    int mode = kModeNormal;
+    float G = 0.0f;
+    int64_t tl[kPieceMaxK];  // local column of each slot, -1 if none
+    float gs[kPieceMaxK];
+    if (HEAD == kHeadLogp) {
+        float sv[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // valid slots' g, zeros beyond k
+        int nvalid = 0;
 #pragma unroll
-            for (int j = 0; j < kPieceMaxK; ++j) {
-                tl[j] = -1;
-                gs[j] = 0.0f;
-                if (j < p.k) {
-                    const int64_t t = p.targets[row * p.k + j];
-                    const float g = p.g[row * p.k + j];
-                    const bool valid = t >= 0 && t < p.vtotal;
-                    tl[j] = (t >= p.v0 && t < p.v0 + p.V) ? t - p.v0 : -1;
-                    gs[j] = g;
-                    if (valid) {
-                        sv[j] = g;
-                        ++nvalid;
-                    }
+        for (int j = 0; j < kPieceMaxK; ++j) {
+            tl[j] = -1;
+            gs[j] = 0.0f;
+            if (j < p.k) {
+                const int64_t t = p.targets[row * p.k + j];
+                const float g = p.g[row * p.k + j];
+                const bool valid = t >= 0 && t < p.vtotal;
+                tl[j] = (t >= p.v0 && t < p.v0 + p.V) ? t - p.v0 : -1;
+                gs[j] = g;
+                if (valid) {
+                    sv[j] = g;
+                    ++nvalid;
                 }
             }
-            // bwd_topk_kernel's wave64 butterfly over lanes 0..3 holding the slots
-            G = (sv[0] + sv[2]) + (sv[1] + sv[3]);
-            if (nvalid == 0)
-                mode = kModeZero;
-            else if (rs.flags & kFlagEmptyA)
-                mode = kModeNaN;
-        } else if (HEAD == kHeadEntropy) {
-            if (rs.flags & kFlagEmptyA) mode = kModeNaN;
-        } else {
-            if (rs.flags & (kFlagEmptyA | kFlagEmptyB))
-                mode = kModeNaN;
-            else if (HEAD == kHeadKLReverse && (rs.flags & kFlagMismatch))
-                mode = kModeMismatch;
         }
+        // bwd_topk_kernel's wave64 butterfly over lanes 0..3 holding the slots
+        G = (sv[0] + sv[2]) + (sv[1] + sv[3]);
+        if (nvalid == 0)
+            mode = kModeZero;
+        else if (rs.flags & kFlagEmptyA)
+            mode = kModeNaN;
+    } else if (HEAD == kHeadEntropy) {
+        if (rs.flags & kFlagEmptyA) mode = kModeNaN;
+    } else {
+        if (rs.flags & (kFlagEmptyA | kFlagEmptyB))
+            mode = kModeNaN;
+        else if (HEAD == kHeadKLReverse && (rs.flags & kFlagMismatch))
+            mode = kModeMismatch;
+    }
+    if (FULL) {
+        raw_unpack(rx, x);
+        if (KL) fast_values<U, S, CAPB>(ry, cb, b);
+    }
 
-        float v[1][kChunk];
-        if (mode == kModeNormal) {
-            const float g_row = (HEAD == kHeadLogp) ? 0.0f : p.g[row];
-            float A, B;
-            row_coeffs<HEAD, CAPA>(rs, G, g_row, A, B);
+    float v[U][kChunk];
+    if (mode == kModeNormal) {
+        const float g_row = (HEAD == kHeadLogp) ? 0.0f : p.g[row];
+        float A, B;
+        row_coeffs<HEAD, CAPA>(rs, G, g_row, A, B);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
             float a[kChunk], s4[kChunk];
 #pragma unroll
             for (int e = 0; e < kChunk; ++e) {
-                a[e] = cap_value_slope<CAPA>(x[0][e], ca, s4[e]);
-                v[0][e] = grad_elem<HEAD, CAPA>(a[e], s4[e], KL ? b[0][e] : 0.0f, rs, A, B,
+                a[e] = cap_value_slope<CAPA>(x[u][e], ca, s4[e]);
+                v[u][e] = grad_elem<HEAD, CAPA>(a[e], s4[e], KL ? b[u][e] : 0.0f, rs, A, B,
                                                 p.scx, p.scy);
             }
             if (HEAD == kHeadLogp) {
                 // one-hot terms: a slot whose column falls in this lane's chunk
-                const int64_t col0 = c * kChunk;
+                const int64_t col0 = (g0 + u * BLOCK + (int)threadIdx.x) * kChunk;
                 bool any = false;
 #pragma unroll
                 for (int j = 0; j < kPieceMaxK; ++j)
@@ -365,21 +370,178 @@ __global__ __launch_bounds__(BLOCK) void bwd_piece_kernel(BwdParams p, int64_t r
                                 h += gs[j];
                                 hit = true;
                             }
-                        if (hit) v[0][e] = target_grad<CAPA>(a[e], s4[e], rs, G, h, p.scx);
+                        if (hit) v[u][e] = target_grad<CAPA>(a[e], s4[e], rs, G, h, p.scx);
                     }
                 }
             }
-        } else if (mode == kModeMismatch) {
+        }
+    } else if (mode == kModeMismatch) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
 #pragma unroll
             for (int e = 0; e < kChunk; ++e)
-                v[0][e] = (CAPA == kCapNone && x[0][e] == neg_inf()) ? 0.0f : qnan();
-        } else {
-            const float fill = mode == kModeZero ? 0.0f : qnan();
+                v[u][e] = (CAPA == kCapNone && x[u][e] == neg_inf()) ? 0.0f : qnan();
+    } else {
+        const float fill = mode == kModeZero ? 0.0f : qnan();
 #pragma unroll
-            for (int e = 0; e < kChunk; ++e) v[0][e] = fill;
-        }
-        store_group<BLOCK, 1, S, ALIGNED>(gx, p.V, g0, g0 + BLOCK <= nfull, v);
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int e = 0; e < kChunk; ++e) v[u][e] = fill;
     }
+    store_group<BLOCK, U, S, ALIGNED>(gx, p.V, g0, FULL, v);
+}
+
+// grid (pieces of a row, rows): consecutive workgroups take consecutive
+// pieces of a row, so the chip sweeps the matrix front to back; rows run
+// last-first (see bwd_topk_kernel).
+template <int BLOCK, int U, typename T, int HEAD, int CAPA, int CAPB, bool ALIGNED>
+__global__ __launch_bounds__(BLOCK) void bwd_piece_kernel(BwdParams p, int64_t rbase) {
+    const int64_t row = p.N - 1 - (rbase + static_cast<int64_t>(blockIdx.y));
+    const int64_t g0 = static_cast<int64_t>(blockIdx.x) * (BLOCK * U);  // first chunk
+    if (ALIGNED && g0 + BLOCK * U <= p.V / kChunk)
+        piece<BLOCK, U, T, HEAD, CAPA, CAPB, ALIGNED, true>(p, row, g0);
+    else
+        piece<BLOCK, U, T, HEAD, CAPA, CAPB, ALIGNED, false>(p, row, g0);
+}
+
+// Logprobs with kPieceMaxK < k <= kGLanes: one-shot pieces of kGLanes lanes
+// x U chunks (2048 U columns) of one row.  Each lane reads one slot: G and the
+// valid count take bwd_topk_kernel's tree (slot j in lane j, wave butterfly,
+// the four waves in order), so both kernels give the same bits.  The slots
+// whose column falls in the piece are compacted into LDS in slot order
+// (ballot ranks, per-wave offsets) and marked in a bitmap of one byte per
+// chunk; a lane whose chunk has a marked column sums that column's slots from
+// the list in slot order (bwd_topk_kernel's one-hot sum) and writes the
+// target gradient in place of the bulk value.  Every column is computed once
+// and stored once, the data loads are issued first, and the piece exits after
+// its stores: the slot work (k 12-byte records, mostly from L2) is spread
+// over 4 KB U of logits.
+// FULL: every chunk of the piece lies inside an aligned row, so its loads are
+// raw 16-byte vectors issued back to back without branches (tail_values'
+// per-chunk branches would make the compiler wait for each load in turn).
+template <int U, typename T, int CAPA, bool ALIGNED, bool FULL>
+__device__ __forceinline__ void wide_piece(const BwdParams& p, int64_t row, int64_t g0) {
+    using S = typename T::storage;
+    constexpr int BLOCK = kGLanes, NW = kGLanes / 64;
+    constexpr int PC = BLOCK * U;  // chunks per piece
+    __shared__ uint32_t bits[PC / 4];
+    __shared__ int2 list[kGLanes];  // (column in the piece, g as bits), slot order
+    __shared__ float red_g[NW], red_n[NW];
+    __shared__ int red_c[NW];
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int64_t nfull = p.V / kChunk;
+    const RowStats* stats = static_cast<const RowStats*>(p.stats);
+    const S* __restrict__ xa = static_cast<const S*>(p.x) + p.mx.offset(row);
+    S* __restrict__ gx = static_cast<S*>(p.gx) + p.mg.offset(row);
+
+    // The slot loads go first (mostly L2 hits): loads complete in order, so
+    // G, the list and both barriers then overlap the logits' HBM latency.
+    int64_t t = -1;
+    float gj = 0.0f;
+    if (tid < p.k) {
+        t = p.targets[row * p.k + tid];
+        gj = p.g[row * p.k + tid];
+    }
+    RawGroup<S, U> raw;
+    float x[U][kChunk];
+    if (FULL)
+        raw_load<BLOCK, U>(xa, g0, raw);
+    else
+        tail_values<BLOCK, U, S, kCapNone, ALIGNED>(xa, p.V, nfull, g0, CapArgs{}, x);
+    RowStats rs = stats[row];
+    fixed_refs<CAPA, kCapNone, false>(rs);
+
+    float part = 0.0f, cnt = 0.0f;
+    bool mine = false;  // slot tid names a column of this piece
+    int pcol = 0;
+    if (tid < p.k) {
+        if (t >= 0 && t < p.vtotal) {
+            part += gj;
+            cnt = 1.0f;
+        }
+        const int64_t c = t - p.v0 - g0 * kChunk;
+        mine = t >= p.v0 && t < p.v0 + p.V && c >= 0 && c < static_cast<int64_t>(PC) * kChunk;
+        pcol = static_cast<int>(c);
+    }
+#pragma unroll
+    for (int i = tid; i < PC / 4; i += BLOCK) bits[i] = 0u;
+    part = wave_sum(part);
+    cnt = wave_sum(cnt);
+    const uint64_t m = __ballot(mine);
+    if (lane == 0) {
+        red_g[wid] = part;
+        red_n[wid] = cnt;
+        red_c[wid] = __popcll(m);
+    }
+    __syncthreads();
+    float G = red_g[0], n = red_n[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) {
+        G += red_g[w];
+        n += red_n[w];
+    }
+    int base = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        base += w < wid ? red_c[w] : 0;
+        total += red_c[w];
+    }
+    if (mine) {
+        const int rank = __popcll(m & ((1ull << lane) - 1ull));
+        list[base + rank] = make_int2(pcol, __float_as_int(gj));
+        const int ci = pcol / kChunk;
+        atomicOr(&bits[ci >> 2], 1u << ((ci & 3) * 8 + pcol % kChunk));
+    }
+    if (total > 0) __syncthreads();  // uniform: the list and bitmap are complete
+    const int mode = n == 0.0f ? kModeZero : ((rs.flags & kFlagEmptyA) ? kModeNaN : kModeNormal);
+    if (FULL) raw_unpack(raw, x);
+
+    float v[U][kChunk];
+    if (mode == kModeNormal) {
+        const CapArgs ca{p.kx, p.ix};
+        float A, B;
+        row_coeffs<kHeadLogp, CAPA>(rs, G, 0.0f, A, B);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int ci = u * BLOCK + tid;
+            float a[kChunk], s4[kChunk];
+#pragma unroll
+            for (int e = 0; e < kChunk; ++e) {
+                a[e] = cap_value_slope<CAPA>(x[u][e], ca, s4[e]);
+                v[u][e] = grad_elem<kHeadLogp, CAPA>(a[e], s4[e], 0.0f, rs, A, B, p.scx, p.scy);
+            }
+            const uint32_t mark = total > 0 ? (bits[ci >> 2] >> ((ci & 3) * 8)) & 0xffu : 0u;
+            if (mark) {  // rare: a target column in this chunk
+                for (int e = 0; e < kChunk; ++e) {
+                    if (!(mark & (1u << e))) continue;
+                    const int col = ci * kChunk + e;
+                    float h = 0.0f;
+                    for (int j = 0; j < total; ++j) {
+                        const int2 l = list[j];
+                        if (l.x == col) h += __int_as_float(l.y);
+                    }
+                    v[u][e] = target_grad<CAPA>(a[e], s4[e], rs, G, h, p.scx);
+                }
+            }
+        }
+    } else {
+        const float fill = mode == kModeZero ? 0.0f : qnan();
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int e = 0; e < kChunk; ++e) v[u][e] = fill;
+    }
+    store_group<BLOCK, U, S, ALIGNED>(gx, p.V, g0, FULL, v);
+}
+
+template <int U, typename T, int CAPA, bool ALIGNED>
+__global__ __launch_bounds__(kGLanes) void bwd_wide_kernel(BwdParams p, int64_t rbase) {
+    const int64_t row = p.N - 1 - (rbase + static_cast<int64_t>(blockIdx.y));
+    const int64_t g0 = static_cast<int64_t>(blockIdx.x) * (kGLanes * U);
+    if (ALIGNED && g0 + kGLanes * U <= p.V / kChunk)
+        wide_piece<U, T, CAPA, ALIGNED, true>(p, row, g0);
+    else
+        wide_piece<U, T, CAPA, ALIGNED, false>(p, row, g0);
 }
 
 // ------------------------------------------------------------- dispatch
@@ -396,12 +558,29 @@ constexpr int64_t kPieceRowsPerLaunch = 65536;
 
 template <typename T, int HEAD, int CAPX, int CAPY, bool AL>
 inline hipError_t bwd_piece_launch(const BwdParams& p, hipStream_t s) {
-    const int64_t pieces = ((p.V + kChunk - 1) / kChunk + kBwdPieceBlock - 1) / kBwdPieceBlock;
+    constexpr int U = kBwdPieceUnroll;
+    constexpr int64_t pc = static_cast<int64_t>(kBwdPieceBlock) * U;
+    const int64_t pieces = ((p.V + kChunk - 1) / kChunk + pc - 1) / pc;
     for (int64_t r0 = 0; r0 < p.N; r0 += kPieceRowsPerLaunch) {
         const int64_t rows = p.N - r0 < kPieceRowsPerLaunch ? p.N - r0 : kPieceRowsPerLaunch;
         const dim3 grid(static_cast<unsigned>(pieces), static_cast<unsigned>(rows));
-        hipLaunchKernelGGL((bwd_piece_kernel<kBwdPieceBlock, T, HEAD, CAPX, CAPY, AL>), grid,
+        hipLaunchKernelGGL((bwd_piece_kernel<kBwdPieceBlock, U, T, HEAD, CAPX, CAPY, AL>), grid,
                            dim3(kBwdPieceBlock), 0, s, p, r0);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+template <typename T, int CAPX, bool AL>
+inline hipError_t bwd_wide_launch(const BwdParams& p, hipStream_t s) {
+    constexpr int64_t pc = static_cast<int64_t>(kGLanes) * kBwdWideUnroll;
+    const int64_t pieces = ((p.V + kChunk - 1) / kChunk + pc - 1) / pc;
+    for (int64_t r0 = 0; r0 < p.N; r0 += kPieceRowsPerLaunch) {
+        const int64_t rows = p.N - r0 < kPieceRowsPerLaunch ? p.N - r0 : kPieceRowsPerLaunch;
+        const dim3 grid(static_cast<unsigned>(pieces), static_cast<unsigned>(rows));
+        hipLaunchKernelGGL((bwd_wide_kernel<kBwdWideUnroll, T, CAPX, AL>), grid, dim3(kGLanes), 0,
+                           s, p, r0);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -431,6 +610,7 @@ inline hipError_t bwd_dispatch_al(int head, const BwdParams& p0, hipStream_t s) 
             return hipErrorInvalidValue;
     }
     if (p0.k <= kPieceMaxK) return bwd_piece_launch<T, kHeadLogp, CAPX, kCapNone, AL>(p0, s);
+    if (p0.k <= kGLanes) return bwd_wide_launch<T, CAPX, AL>(p0, s);
     BwdParams p = p0;
     if (p.N < kBwdSmallRows) {
         // Few rows: narrow workgroups, each row cut into column segments.

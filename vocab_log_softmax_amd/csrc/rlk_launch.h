@@ -56,6 +56,11 @@ constexpr float kCapFixedMaxScale = 120.0f;
 #ifndef RLK_BWD_PIECE_BLOCK
 #define RLK_BWD_PIECE_BLOCK 256
 #endif
+// Chunks per lane of the wide top-k pieces (logprobs, 4 < k <= 256).
+#ifndef RLK_BWD_WIDE_UNROLL
+#define RLK_BWD_WIDE_UNROLL 4
+#endif
+constexpr int kBwdWideUnroll = RLK_BWD_WIDE_UNROLL;
 #ifndef RLK_FWD_PIPE
 #define RLK_FWD_PIPE 1
 #endif
@@ -65,6 +70,13 @@ constexpr float kCapFixedMaxScale = 120.0f;
 constexpr bool kFwdPipe = RLK_FWD_PIPE;
 constexpr bool kBwdPipe = RLK_BWD_PIPE;
 constexpr int kBwdPieceBlock = RLK_BWD_PIECE_BLOCK;
+// Chunks per lane of a piece.  One (4 KB of bf16 per workgroup) is the
+// fastest for every head, the VALU-heavy capped ones included: two or four
+// amortise the per-piece setup but lengthen each workgroup's life.
+#ifndef RLK_BWD_PIECE_UNROLL
+#define RLK_BWD_PIECE_UNROLL 1
+#endif
+constexpr int kBwdPieceUnroll = RLK_BWD_PIECE_UNROLL;
 // Minimum waves per SIMD requested from the register allocator (0: none).
 #ifndef RLK_WAVES_PER_EU
 #define RLK_WAVES_PER_EU 0
