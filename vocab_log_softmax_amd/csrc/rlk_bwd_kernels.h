@@ -53,22 +53,23 @@ __device__ __forceinline__ void swap_sides(RowStats& rs) {
 //   reverse KL  A = g ln2 / S_a, B = -g (D + ln2 (log2 S_a - log2 S_b)) / S_a
 //                                                   o = 2^ta (A (ta - tb) + B)
 //   forward KL  A = g / S_a, B = g / S_b             o = A 2^ta - B 2^tb
-// (the slope 4 r (1 - r) of the cap has its 4 folded in as well).
+// (with the cap, the slope's constant factor cf = slope_factor is folded in
+// as well).
 template <int HEAD, int CAPA>
-__device__ __forceinline__ void row_coeffs(const RowStats& rs, float G, float g_row, float& A,
-                                           float& B) {
-    constexpr bool C = CAPA != kCapNone;
+__device__ __forceinline__ void row_coeffs(const RowStats& rs, float G, float g_row, float cf,
+                                           float& A, float& B) {
+    const float f = CAPA != kCapNone ? cf : 1.0f;
     float a0 = 0.0f, b0 = 0.0f;
     if (HEAD == kHeadLogp) {
-        a0 = C ? -4.0f * G : -G;
+        a0 = -f * G;
     } else if (HEAD == kHeadEntropy) {
-        a0 = (C ? -4.0f : -1.0f) * g_row * kLn2;
-        b0 = (C ? -4.0f : -1.0f) * g_row * rs.value;
+        a0 = -f * g_row * kLn2;
+        b0 = -f * g_row * rs.value;
     } else if (HEAD == kHeadKLReverse) {
-        a0 = (C ? 4.0f : 1.0f) * g_row * kLn2;
-        b0 = (C ? -4.0f : -1.0f) * g_row * rs.value;
+        a0 = f * g_row * kLn2;
+        b0 = -f * g_row * rs.value;
     } else {
-        a0 = C ? 4.0f * g_row : g_row;
+        a0 = f * g_row;
     }
     const float inv_sa = ex2(-rs.log2Sa);
     A = a0 * inv_sa;
@@ -99,10 +100,10 @@ __device__ __forceinline__ void fixed_refs(RowStats& rs) {
 }
 
 // Gradient of one element from its statistic inputs (a; b for KL), the
-// quarter slope s4 of the cap (cap_value_slope) and the row's record and
+// cap's slope s up to its factor (cap_value_slope) and the row's record and
 // coefficients; the exponent t comes from the forward's own FMA.
 template <int HEAD, int CAPA>
-__device__ __forceinline__ float grad_elem(float a, float s4, float b, const RowStats& rs, float A,
+__device__ __forceinline__ float grad_elem(float a, float s, float b, const RowStats& rs, float A,
                                            float B, float scx, float scy) {
     constexpr bool C = CAPA != kCapNone;
     const float ta = __builtin_fmaf(a, scx, -rs.mLa);
@@ -124,18 +125,18 @@ __device__ __forceinline__ float grad_elem(float a, float s4, float b, const Row
             o = A * ex2(ta) - B * ex2(tb);
         }
     }
-    if (C) o *= s4;  // the slope's 4 is in A, B
+    if (C) o *= s;  // the slope's factor is in A, B
     return o;
 }
 
 // Logprobs gradient at a target column: h - p G (h: the column's summed
-// upstream gradients), times the cap's slope 4 s4.
+// upstream gradients), times the cap's slope cf s.
 template <int CAPA>
-__device__ __forceinline__ float target_grad(float a, float s4, const RowStats& rs, float G,
-                                             float h, float scx) {
+__device__ __forceinline__ float target_grad(float a, float s, float cf, const RowStats& rs,
+                                             float G, float h, float scx) {
     const float pt = ex2(__builtin_fmaf(a, scx, -rs.mLa) - rs.log2Sa);
     const float v = __builtin_fmaf(-pt, G, h);
-    return CAPA != kCapNone ? v * (4.0f * s4) : v;
+    return CAPA != kCapNone ? v * (cf * s) : v;
 }
 
 // Logprobs with wide top-k: one workgroup per (row, column segment), visited
@@ -159,7 +160,8 @@ __global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void bwd_topk_kernel(BwdParams
     const RowStats* stats = static_cast<const RowStats*>(p.stats);
     int* tg = smem_topk;
     float* gg = reinterpret_cast<float*>(smem_topk + p.k);
-    const CapArgs ca{p.kx, p.ix};
+    const CapArgs ca{p.kx, p.ix, p.spx};
+    const float cf = slope_factor<CAPA>(ca);
 
     for (int64_t it = blockIdx.x; it < p.N * p.split; it += gridDim.x) {
         const int64_t rit = it / p.split, seg = it - rit * p.split;
@@ -205,7 +207,7 @@ __global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void bwd_topk_kernel(BwdParams
 
         if (mode == kModeNormal) {
             float A, B;
-            row_coeffs<kHeadLogp, CAPA>(rs, G, 0.0f, A, B);
+            row_coeffs<kHeadLogp, CAPA>(rs, G, 0.0f, cf, A, B);
             for_each_group<BLOCK, U, S, kCapNone, ALIGNED, kBwdPipe>(
                 xa, p.V, CapArgs{},
                 [&](int64_t g0, bool full, const float (&x)[U][kChunk]) {
@@ -239,7 +241,7 @@ __global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void bwd_topk_kernel(BwdParams
                 if (!first) continue;
                 float s4;
                 const float a = cap_value_slope<CAPA>(load_one(xa + t), ca, s4);
-                store_one(gx + t, target_grad<CAPA>(a, s4, rs, G, h, p.scx));
+                store_one(gx + t, target_grad<CAPA>(a, s4, cf, rs, G, h, p.scx));
             }
         } else {
             const float fill = mode == kModeZero ? 0.0f : qnan();
@@ -290,7 +292,8 @@ __device__ __forceinline__ void piece(const BwdParams& p, int64_t row, int64_t g
         tail_values<BLOCK, U, S, kCapNone, ALIGNED>(xa, p.V, nfull, g0, CapArgs{}, x);
         if (KL) tail_values<BLOCK, U, S, CAPB, ALIGNED>(xb, p.V, nfull, g0, cb, b);
     }
-    const CapArgs ca{p.kx, p.ix};
+    const CapArgs ca{p.kx, p.ix, p.spx};
+    const float cf = slope_factor<CAPA>(ca);
 
     RowStats rs = stats[row];
     if (KL && p.swap) swap_sides(rs);
@@ -342,7 +345,7 @@ __device__ __forceinline__ void piece(const BwdParams& p, int64_t row, int64_t g
     if (mode == kModeNormal) {
         const float g_row = (HEAD == kHeadLogp) ? 0.0f : p.g[row];
         float A, B;
-        row_coeffs<HEAD, CAPA>(rs, G, g_row, A, B);
+        row_coeffs<HEAD, CAPA>(rs, G, g_row, cf, A, B);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             float a[kChunk], s4[kChunk];
@@ -370,7 +373,7 @@ __device__ __forceinline__ void piece(const BwdParams& p, int64_t row, int64_t g
                                 h += gs[j];
                                 hit = true;
                             }
-                        if (hit) v[u][e] = target_grad<CAPA>(a[e], s4[e], rs, G, h, p.scx);
+                        if (hit) v[u][e] = target_grad<CAPA>(a[e], s4[e], cf, rs, G, h, p.scx);
                     }
                 }
             }
@@ -498,9 +501,10 @@ __device__ __forceinline__ void wide_piece(const BwdParams& p, int64_t row, int6
 
     float v[U][kChunk];
     if (mode == kModeNormal) {
-        const CapArgs ca{p.kx, p.ix};
+        const CapArgs ca{p.kx, p.ix, p.spx};
+        const float cf = slope_factor<CAPA>(ca);
         float A, B;
-        row_coeffs<kHeadLogp, CAPA>(rs, G, 0.0f, A, B);
+        row_coeffs<kHeadLogp, CAPA>(rs, G, 0.0f, cf, A, B);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int ci = u * BLOCK + tid;
@@ -520,7 +524,7 @@ __device__ __forceinline__ void wide_piece(const BwdParams& p, int64_t row, int6
                         const int2 l = list[j];
                         if (l.x == col) h += __int_as_float(l.y);
                     }
-                    v[u][e] = target_grad<CAPA>(a[e], s4[e], rs, G, h, p.scx);
+                    v[u][e] = target_grad<CAPA>(a[e], s4[e], cf, rs, G, h, p.scx);
                 }
             }
         }

@@ -178,8 +178,9 @@ __device__ __forceinline__ void store_one(_Float16* p, float f) { *p = static_ca
 // y = -c; slope 0 at both).  The absolute error of a is about 1e-7 (online)
 // or 1e-7 sc (fixed); the softmax depends only on absolute errors of y.
 struct CapArgs {
-    float k;    // -2 log2(e) / c
-    float isc;  // fixed form: 1 / sc
+    float k;     // -2 log2(e) / c
+    float isc;   // fixed form: 1 / sc
+    float span;  // fixed form, backward: sc
 };
 
 template <int CAP>
@@ -189,28 +190,35 @@ __device__ __forceinline__ float cap_value(float x, CapArgs c) {
     return x;
 }
 
-// Statistic input and a quarter of the slope, r (1 - r) = (1 - tanh^2) / 4.
-// Fixed form: with q = 2^(-k x) and w = sc / (1 + q) (so a = -w), 1 - r =
-// w / sc and r = q (1 - r) -- the latter is inf * 0 only at x = +inf, where
-// the minimum with 1 gives r = 1 (a NaN x stays NaN through 1 - r).  Neither
-// factor is a difference, so the slope keeps its relative accuracy in both
-// tails, and it is exactly 0 at x = -inf (q = 0) and x = +inf (1 - r = 0).
+// Statistic input a and the slope 1 - tanh^2 up to a factor fixed per cap
+// (slope_factor): s = r (1 - r) in the online form.  Fixed form: with
+// q = 2^(-k x) and w = sc / (1 + q) (so a = -w), sc (1 - r) = w and
+// sc r = q w, so s = (q w) w = r (1 - r) sc^2.  q w is inf * 0 only at
+// x = +inf, where the minimum with sc gives r = 1 (a NaN x stays NaN through
+// w).  Neither factor is a difference, so the slope keeps its relative
+// accuracy in both tails, and it is exactly 0 at x = -inf (q = 0) and at
+// x = +inf (w = 0).
 template <int CAP>
-__device__ __forceinline__ float cap_value_slope(float x, CapArgs c, float& s4) {
+__device__ __forceinline__ float cap_value_slope(float x, CapArgs c, float& s) {
     if (CAP == kCapOnline) {
         const float r = rcp(1.0f + ex2(x * c.k));
-        s4 = __builtin_fmaf(-r, r, r);
+        s = __builtin_fmaf(-r, r, r);
         return r;
     }
     if (CAP == kCapFixed) {
         const float q = ex2(-(x * c.k));
         const float w = rcp(__builtin_fmaf(q, c.isc, c.isc));
-        const float u = w * c.isc;
-        s4 = fminf(q * u, 1.0f) * u;
+        s = fminf(q * w, c.span) * w;
         return -w;
     }
-    s4 = 1.0f;
+    s = 1.0f;
     return x;
+}
+
+// The slope is slope_factor * s: 4 (online form), 4 / sc^2 (fixed form).
+template <int CAP>
+__device__ __forceinline__ float slope_factor(CapArgs c) {
+    return CAP == kCapFixed ? 4.0f * c.isc * c.isc : 4.0f;
 }
 
 // Standalone form, accurate in RELATIVE terms (the output y itself is
