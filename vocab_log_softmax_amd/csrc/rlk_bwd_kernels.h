@@ -391,7 +391,10 @@ __device__ __forceinline__ void piece(const BwdParams& p, int64_t row, int64_t g
 #pragma unroll
             for (int e = 0; e < kChunk; ++e) v[u][e] = fill;
     }
-    store_group<BLOCK, U, S, ALIGNED>(gx, p.V, g0, FULL, v);
+    if (FULL)
+        store_piece<BLOCK, U, S>(gx + g0 * kChunk, v);
+    else
+        store_group<BLOCK, U, S, ALIGNED>(gx, p.V, g0, false, v);
 }
 
 // grid (pieces of a row, rows): consecutive workgroups take consecutive
@@ -535,6 +538,8 @@ __device__ __forceinline__ void wide_piece(const BwdParams& p, int64_t row, int6
 #pragma unroll
             for (int e = 0; e < kChunk; ++e) v[u][e] = fill;
     }
+    // (plain streaming stores: the sc1 policy of store_piece measured slower
+    // for these 16 KB pieces)
     store_group<BLOCK, U, S, ALIGNED>(gx, p.V, g0, FULL, v);
 }
 

@@ -30,6 +30,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "rlk_launch.h"
 
 namespace rlk {
@@ -491,6 +493,40 @@ __device__ __forceinline__ void for_each_group2(const S* __restrict__ ra, const 
         tail_values<BLOCK, U, S, CAPA, ALIGNED>(ra, V, nfull, gi * step, ka, a);
         tail_values<BLOCK, U, S, CAPB, ALIGNED>(rb, V, nfull, gi * step, kb, b);
         f(gi * step, false, a, b);
+    }
+}
+
+// Stores of a full piece (every chunk inside an aligned row) through a buffer
+// resource whose base is the piece's first element, with the sc1 + nt cache
+// policy: system-scope, streaming writes.  On this part a stream of one-shot
+// 4 KB workgroups copies ~3% faster with them than with nt alone (and writes
+// ~5% faster); loads gain nothing from the extra bits.  Offsets are relative
+// to the piece, so rows of any length fit the 32-bit offsets.
+constexpr int kStoreCpol = 16 | 2;  // sc1 | nt
+template <int BLOCK, int U, typename S>
+__device__ __forceinline__ void store_piece(S* __restrict__ piece, const float (&v)[U][kChunk]) {
+    constexpr uint32_t kChunkBytes = kChunk * sizeof(S);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        static_cast<void*>(piece), 0, BLOCK * U * kChunkBytes, 0x00020000);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const uint32_t off = (u * BLOCK + threadIdx.x) * kChunkBytes;
+        if constexpr (sizeof(S) == 4) {
+            const u32x4 a = {__float_as_uint(v[u][0]), __float_as_uint(v[u][1]),
+                             __float_as_uint(v[u][2]), __float_as_uint(v[u][3])};
+            const u32x4 b = {__float_as_uint(v[u][4]), __float_as_uint(v[u][5]),
+                             __float_as_uint(v[u][6]), __float_as_uint(v[u][7])};
+            __builtin_amdgcn_raw_buffer_store_b128(a, rs, off, 0, kStoreCpol);
+            __builtin_amdgcn_raw_buffer_store_b128(b, rs, off + 16, 0, kStoreCpol);
+        } else if constexpr (std::is_same_v<S, uint16_t>) {
+            const u32x4 w = {pack_bf16x2(v[u][0], v[u][1]), pack_bf16x2(v[u][2], v[u][3]),
+                             pack_bf16x2(v[u][4], v[u][5]), pack_bf16x2(v[u][6], v[u][7])};
+            __builtin_amdgcn_raw_buffer_store_b128(w, rs, off, 0, kStoreCpol);
+        } else {
+            const u32x4 w = {pack_f16x2(v[u][0], v[u][1]), pack_f16x2(v[u][2], v[u][3]),
+                             pack_f16x2(v[u][4], v[u][5]), pack_f16x2(v[u][6], v[u][7])};
+            __builtin_amdgcn_raw_buffer_store_b128(w, rs, off, 0, kStoreCpol);
+        }
     }
 }
 
