@@ -22,20 +22,22 @@ def _gen(seed):
     return torch.Generator().manual_seed(seed)
 
 
-@pytest.mark.parametrize("head", ["logp", "entropy", "kl"])
+@pytest.mark.parametrize("head", ["logp", "logp_k9", "entropy", "kl"])
 def test_more_rows_than_one_launch(dev, orc, head):
     N, V = 70_001, 37
     x = (torch.randn(N, V, generator=_gen(1)) * 3).to(torch.bfloat16)
     g = torch.randn(N, generator=_gen(2))
     xd, gd = x.to(dev), g.to(dev)
     x64 = to64(x)
-    if head == "logp":
-        t = torch.randint(0, V, (N, 1), generator=_gen(3))
+    if head.startswith("logp"):
+        k = 9 if head == "logp_k9" else 1   # wide top-k pieces / one-shot pieces
+        t = torch.randint(0, V, (N, k), generator=_gen(3))
         t[::97] = -100
+        gt = torch.randn(N, k, generator=_gen(5))
         out, st = rlk.logp_fwd(xd, t.to(dev))
-        gx = rlk.logp_bwd(xd, t.to(dev), gd[:, None], st)
+        gx = rlk.logp_bwd(xd, t.to(dev), gt.to(dev), st)
         ref_out = orc.logp_fwd(x64, t.numpy())
-        ref_gx = orc.logp_bwd(x64, t.numpy(), to64(g)[:, None])
+        ref_gx = orc.logp_bwd(x64, t.numpy(), to64(gt))
     elif head == "entropy":
         out, st = rlk.entropy_fwd(xd)
         gx = rlk.entropy_bwd(xd, gd, st)

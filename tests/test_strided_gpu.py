@@ -57,8 +57,9 @@ def make_seq(B, T1, V, dtype, seed, dev):
                          ids=["bf16", "f32", "f16"])
 @pytest.mark.parametrize("V", [4096, 32000, 4099])
 @pytest.mark.parametrize("cap", [0.0, 30.0, 50.0])
-def test_sequence_slice_in_place(dev, dtype, V, cap):
-    B, T1, k = 3, 9, 2
+@pytest.mark.parametrize("k", [2, 40])  # one-shot pieces / wide top-k pieces
+def test_sequence_slice_in_place(dev, dtype, V, cap, k):
+    B, T1 = 3, 9
     T = T1 - 1
     x, ref = make_seq(B, T1, V, dtype, V, dev)
     # the position outside the view is poisoned: reading it would leak NaN
@@ -68,6 +69,7 @@ def test_sequence_slice_in_place(dev, dtype, V, cap):
     assert not xv.is_contiguous()
     t = torch.randint(0, V, (B * T, k), generator=_gen(2)).to(dev)
     t[3, 0] = -100
+    t[5, k - 1] = t[5, 0]
     g_t = torch.randn(B * T, k, generator=_gen(3)).to(dev)
     g_r = torch.randn(B * T, generator=_gen(4)).to(dev)
     want = all_heads(xv.reshape(B * T, V).contiguous(), rv.reshape(B * T, V).contiguous(),
