@@ -229,6 +229,9 @@ def main() -> int:
     ap.add_argument("--oracle-rows", type=int, default=8192,
                     help="rows of the workload timed on the CPU oracle")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--oracle-threads", type=int, default=None,
+                    help="host threads of the CPU oracle (default: the process's cores, "
+                         "at most 16)")
     ap.add_argument("--rows", type=int, default=None,
                     help="override the workload's row count N (same recipe, e.g. 32768 rows "
                          "of c2_logp_bf16 for the pages' B200 comparison)")
@@ -379,7 +382,7 @@ def main() -> int:
 
     cpu = None
     if not args.no_cpu_baseline:
-        threads = min(len(os.sched_getaffinity(0)), 16)
+        threads = args.oracle_threads or min(len(os.sched_getaffinity(0)), 16)
         n, dt, passes = run_oracle_sample(w, d, args.oracle_rows, threads,
                                           direction=args.direction)
         sample_bytes = step_bytes * n / N
