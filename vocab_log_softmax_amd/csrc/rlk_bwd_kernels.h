@@ -139,7 +139,7 @@ __device__ __forceinline__ float target_grad(float a, float s, float cf, const R
     return CAPA != kCapNone ? v * (cf * s) : v;
 }
 
-// Logprobs with wide top-k: one workgroup per (row, column segment), visited
+// Logprobs with k > kGLanes: one workgroup per (row, column segment), visited
 // last-first (the end of the forward's stream is what the Infinity Cache
 // still holds).  The k slots are staged in LDS and G is summed in a tree
 // fixed by kGLanes (slot j by lane j mod kGLanes, in order), not by BLOCK;
@@ -258,7 +258,7 @@ __global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void bwd_topk_kernel(BwdParams
 }
 
 // Logprobs calls with at most this many slots per row take the piece kernel
-// (wider ones bwd_topk_kernel).
+// (up to kGLanes slots bwd_wide_kernel, more bwd_topk_kernel).
 constexpr int kPieceMaxK = 4;
 
 // One-shot pieces: every workgroup computes the gradient of U chunks per lane
@@ -557,10 +557,12 @@ __global__ __launch_bounds__(kGLanes) void bwd_wide_kernel(BwdParams p, int64_t 
 //
 // The backward is elementwise given the row record (and G has a fixed tree),
 // so its launch shape does not change any result and is chosen per call:
-// one-shot 256-thread pieces for entropy, KL and logprobs with k <= 4; for
-// wider top-k bwd_topk_kernel with 512-thread workgroups (fewer idle lanes
-// during each row's fix-up), or, for fewer than kBwdSmallRows rows, 256-thread
-// workgroups with the rows cut into column segments.
+// one-shot 256-thread pieces for entropy, KL and logprobs with k <= 4;
+// one-shot wide pieces (256 lanes x kBwdWideUnroll chunks) for logprobs with
+// k <= kGLanes; for wider top-k bwd_topk_kernel with 512-thread workgroups
+// (fewer idle lanes during each row's fix-up), or, for fewer than
+// kBwdSmallRows rows, 256-thread workgroups with the rows cut into column
+// segments.
 
 // Rows per piece launch (the grid's second dimension is limited to 65536).
 constexpr int64_t kPieceRowsPerLaunch = 65536;

@@ -51,8 +51,8 @@ constexpr float kCapFixedMaxScale = 120.0f;
 #define RLK_BWD_UNROLL_TOPK 2
 #endif
 // Backward in one-shot pieces (every workgroup handles BLOCK chunks of one
-// row and exits) for every head except logprobs with more than a few slots,
-// whose row kernel takes the _TOPK shape.
+// row and exits) for every head except logprobs with more than a few slots
+// (wide pieces below; beyond 256 slots the row kernel takes the _TOPK shape).
 #ifndef RLK_BWD_PIECE_BLOCK
 #define RLK_BWD_PIECE_BLOCK 256
 #endif
