@@ -70,7 +70,8 @@ def assert_out(gpu_t: torch.Tensor, ref: np.ndarray, in_dtype, what="out", exact
         ez = np.asarray(exact_zero).reshape(gpu.shape)
         assert (gpu[ez] == 0).all(), f"{what}: structural zeros are not exactly 0"
     fin = np.isfinite(ref)
-    err = np.where(fin, np.abs(gpu - ref), 0.0)
+    with np.errstate(invalid="ignore"):   # inf - inf where both are infinite
+        err = np.where(fin, np.abs(gpu - ref), 0.0)
     if in_dtype in (torch.float32, torch.float16):
         tol = OUT_F32[0] + OUT_F32[1] * np.abs(np.where(fin, ref, 0.0))
     else:
@@ -87,7 +88,8 @@ def assert_grad(gpu_t: torch.Tensor, ref: np.ndarray, what="grad", exact_zero=No
         assert (gpu[ez] == 0).all(), f"{what}: structural zeros are not exactly 0"
     fin = np.isfinite(ref)
     r0 = np.where(fin, ref, 0.0)
-    err = np.where(fin, np.abs(gpu - ref), 0.0)
+    with np.errstate(invalid="ignore"):   # inf - inf where both are infinite
+        err = np.where(fin, np.abs(gpu - ref), 0.0)
     if gpu_t.dtype == torch.float32:
         tol = GRAD_F32[0] + GRAD_F32[1] * np.abs(r0)
     elif gpu_t.dtype == torch.float16:
