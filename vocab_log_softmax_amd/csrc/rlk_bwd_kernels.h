@@ -391,8 +391,10 @@ __device__ __forceinline__ void piece(const BwdParams& p, int64_t row, int64_t g
 #pragma unroll
             for (int e = 0; e < kChunk; ++e) v[u][e] = fill;
     }
-    if (FULL)
-        store_piece<BLOCK, U, S>(gx + g0 * kChunk, v);
+    if (FULL && p.wt)
+        store_piece<BLOCK, U, S, kCpolWriteThrough>(gx + g0 * kChunk, v);
+    else if (FULL)
+        store_piece<BLOCK, U, S, kCpolStream>(gx + g0 * kChunk, v);
     else
         store_group<BLOCK, U, S, ALIGNED>(gx, p.V, g0, false, v);
 }
@@ -568,7 +570,10 @@ __global__ __launch_bounds__(kGLanes) void bwd_wide_kernel(BwdParams p, int64_t 
 constexpr int64_t kPieceRowsPerLaunch = 65536;
 
 template <typename T, int HEAD, int CAPX, int CAPY, bool AL>
-inline hipError_t bwd_piece_launch(const BwdParams& p, hipStream_t s) {
+inline hipError_t bwd_piece_launch(const BwdParams& p0, hipStream_t s) {
+    BwdParams p = p0;
+    p.wt = static_cast<uint64_t>(p.N) * static_cast<uint64_t>(p.V) * T::kBytes >=
+           kWriteThroughBytes;
     constexpr int U = kBwdPieceUnroll;
     constexpr int64_t pc = static_cast<int64_t>(kBwdPieceBlock) * U;
     const int64_t pieces = ((p.V + kChunk - 1) / kChunk + pc - 1) / pc;

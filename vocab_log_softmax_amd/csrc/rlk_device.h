@@ -497,13 +497,12 @@ __device__ __forceinline__ void for_each_group2(const S* __restrict__ ra, const 
 }
 
 // Stores of a full piece (every chunk inside an aligned row) through a buffer
-// resource whose base is the piece's first element, with the sc1 + nt cache
-// policy: system-scope, streaming writes.  On this part a stream of one-shot
-// 4 KB workgroups copies ~3% faster with them than with nt alone (and writes
-// ~5% faster); loads gain nothing from the extra bits.  Offsets are relative
-// to the piece, so rows of any length fit the 32-bit offsets.
-constexpr int kStoreCpol = 16 | 2;  // sc1 | nt
-template <int BLOCK, int U, typename S>
+// resource whose base is the piece's first element, with cache policy CPOL.
+// Offsets are relative to the piece, so rows of any length fit the 32-bit
+// offsets.  Two policies are used (kCpolStream, kCpolWriteThrough below).
+constexpr int kCpolStream = 2;             // nt
+constexpr int kCpolWriteThrough = 16 | 2;  // sc1 | nt: system scope, streaming
+template <int BLOCK, int U, typename S, int CPOL>
 __device__ __forceinline__ void store_piece(S* __restrict__ piece, const float (&v)[U][kChunk]) {
     constexpr uint32_t kChunkBytes = kChunk * sizeof(S);
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
@@ -516,16 +515,16 @@ __device__ __forceinline__ void store_piece(S* __restrict__ piece, const float (
                              __float_as_uint(v[u][2]), __float_as_uint(v[u][3])};
             const u32x4 b = {__float_as_uint(v[u][4]), __float_as_uint(v[u][5]),
                              __float_as_uint(v[u][6]), __float_as_uint(v[u][7])};
-            __builtin_amdgcn_raw_buffer_store_b128(a, rs, off, 0, kStoreCpol);
-            __builtin_amdgcn_raw_buffer_store_b128(b, rs, off + 16, 0, kStoreCpol);
+            __builtin_amdgcn_raw_buffer_store_b128(a, rs, off, 0, CPOL);
+            __builtin_amdgcn_raw_buffer_store_b128(b, rs, off + 16, 0, CPOL);
         } else if constexpr (std::is_same_v<S, uint16_t>) {
             const u32x4 w = {pack_bf16x2(v[u][0], v[u][1]), pack_bf16x2(v[u][2], v[u][3]),
                              pack_bf16x2(v[u][4], v[u][5]), pack_bf16x2(v[u][6], v[u][7])};
-            __builtin_amdgcn_raw_buffer_store_b128(w, rs, off, 0, kStoreCpol);
+            __builtin_amdgcn_raw_buffer_store_b128(w, rs, off, 0, CPOL);
         } else {
             const u32x4 w = {pack_f16x2(v[u][0], v[u][1]), pack_f16x2(v[u][2], v[u][3]),
                              pack_f16x2(v[u][4], v[u][5]), pack_f16x2(v[u][6], v[u][7])};
-            __builtin_amdgcn_raw_buffer_store_b128(w, rs, off, 0, kStoreCpol);
+            __builtin_amdgcn_raw_buffer_store_b128(w, rs, off, 0, CPOL);
         }
     }
 }
