@@ -21,6 +21,7 @@ import argparse
 import ctypes
 import hashlib
 import json
+import math
 import os
 import re
 import sys
@@ -230,8 +231,10 @@ def run_oracle_sample(w, d, max_rows: int, threads: int, min_seconds: float = 1.
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default: at least 50, enough for 0.2 s of work)")
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps first (default: at least 5, enough for 50 ms)")
     ap.add_argument("--workload", default="c2_logp_bf16")
     ap.add_argument("--oracle-rows", type=int, default=8192,
                     help="rows of the workload timed on the CPU oracle")
@@ -294,8 +297,8 @@ def main() -> int:
         out = torch.empty(tg.shape, dtype=torch.float32, device=dev)
         st = rlk.new_stats(rlk.RLK_HEAD_LOGP, N, V, dev)
         gx = torch.empty_like(x)
-        fwd = lambda: rlk.rlk_logp_fwd(x, tg, w.cap, out, st)          # noqa: E731
-        bwd = lambda: rlk.rlk_logp_bwd(x, tg, w.cap, st, g, gx)        # noqa: E731
+        fwd = rlk.prepare(rlk.rlk_logp_fwd, x, tg, w.cap, out, st)
+        bwd = rlk.prepare(rlk.rlk_logp_bwd, x, tg, w.cap, st, g, gx)
         # k <= 4 slots: one-shot pieces; up to 256: wide pieces; wider: the row kernel
         n_in, fwd_name = 1, "fwd1_kernel"
         bwd_name = ("bwd_piece_kernel" if w.k <= 4 else
@@ -305,8 +308,8 @@ def main() -> int:
         out = torch.empty(N, dtype=torch.float32, device=dev)
         st = rlk.new_stats(rlk.RLK_HEAD_ENTROPY, N, V, dev)
         gx = torch.empty_like(x)
-        fwd = lambda: rlk.rlk_entropy_fwd(x, w.cap, out, st)           # noqa: E731
-        bwd = lambda: rlk.rlk_entropy_bwd(x, w.cap, st, g, gx)         # noqa: E731
+        fwd = rlk.prepare(rlk.rlk_entropy_fwd, x, w.cap, out, st)
+        bwd = rlk.prepare(rlk.rlk_entropy_bwd, x, w.cap, st, g, gx)
         n_in, fwd_name, bwd_name = 1, "fwd1_kernel", "bwd_piece_kernel"
     else:
         ref, g = d["ref"], d["grad"]
@@ -314,8 +317,8 @@ def main() -> int:
         st = rlk.new_stats(rlk.RLK_HEAD_KL, N, V, dev)
         gx = torch.empty_like(x)
         kd = args.direction
-        fwd = lambda: rlk.rlk_kl_fwd(x, ref, kd, 0.0, 0.0, out, st)     # noqa: E731
-        bwd = lambda: rlk.rlk_kl_bwd(x, ref, kd, 0.0, 0.0, st, g, gx)   # noqa: E731
+        fwd = rlk.prepare(rlk.rlk_kl_fwd, x, ref, kd, 0.0, 0.0, out, st)
+        bwd = rlk.prepare(rlk.rlk_kl_bwd, x, ref, kd, 0.0, 0.0, st, g, gx)
         n_in, fwd_name, bwd_name = 2, "fwdkl_kernel", "bwd_piece_kernel"
 
     sf, sb = side_bytes(w, N)
@@ -323,13 +326,28 @@ def main() -> int:
     bwd_bytes = (n_in + 1) * N * V * es + sb      # read again, write the gradient once
     step_bytes = fwd_bytes + bwd_bytes
 
-    torch.cuda.synchronize()
-    tw = time.perf_counter()
-    for _ in range(args.warmup):
-        fwd()
-        bwd()
-    torch.cuda.synchronize()
-    warm_ms = (time.perf_counter() - tw) * 1e3 / max(1, args.warmup)
+    # Warm-up.  Without --warmup / --steps both are sized from the step time:
+    # a launch-bound step (microseconds) needs thousands of steps before clocks
+    # and queues settle and for the timed region to outweigh its start-up.
+    def run(n):
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for _ in range(n):
+            fwd()
+            bwd()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t) * 1e3 / max(1, n)
+
+    if args.warmup is not None:
+        warm_ms = run(args.warmup)
+    else:
+        run(5)                   # first launches (code loading, clocks)
+        warm_ms = run(10)        # the step time, from settled launches
+        extra = max(0, math.ceil(50.0 / max(warm_ms, 1e-6)) - 15)
+        run(extra)
+        args.warmup = 15 + extra
+    if args.steps is None:
+        args.steps = max(50, math.ceil(200.0 / max(warm_ms, 1e-6)))
 
     # HIP events on the stream the kernels run on, three per sampled step:
     # before the forward, between forward and backward, after the backward.

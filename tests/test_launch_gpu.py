@@ -96,3 +96,29 @@ def test_graph_capture_replays_equal_eager(dev, cap):
             av = a.contiguous().view(torch.int16 if a.element_size() == 2 else torch.int32)
             wv = w.contiguous().view(torch.int16 if w.element_size() == 2 else torch.int32)
             assert torch.equal(av, wv), f"replay {rep}: output {i} differs from eager"
+
+
+def test_prepared_calls_repeat_the_direct_call(dev):
+    # prepare() marshals once; every call of the result is the same C call
+    N, V, k = 5, 3000, 2
+    x = (torch.randn(N, V, generator=_gen(31)) * 3).to(torch.bfloat16).to(dev)
+    t = torch.randint(0, V, (N, k), generator=_gen(32)).to(dev)
+    g = torch.randn(N, k, generator=_gen(33)).to(dev)
+    lp, st = rlk.logp_fwd(x, t, 20.0)
+    gx = rlk.logp_bwd(x, t, g, st, 20.0)
+    out = torch.full_like(lp, float("nan"))
+    st2 = torch.zeros_like(st)
+    gx2 = torch.full_like(gx, float("nan"))
+    fwd = rlk.prepare(rlk.rlk_logp_fwd, x, t, 20.0, out, st2)
+    bwd = rlk.prepare(rlk.rlk_logp_bwd, x, t, 20.0, st2, g, gx2)
+    for _ in range(3):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+    assert torch.equal(out, lp) and torch.equal(st2, st) and torch.equal(gx2, gx)
+    # the C library still validates each call: a NaN cap is rejected on call
+    bad = rlk.prepare(rlk.rlk_logp_fwd, x, t, float("nan"), out, st2)
+    with pytest.raises(rlk.RLKError):
+        bad()
+    with pytest.raises(ValueError):
+        rlk.prepare(lambda: None)   # makes no library call

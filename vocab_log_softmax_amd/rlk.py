@@ -15,6 +15,7 @@ from __future__ import annotations
 
 import ctypes
 import os
+import threading
 
 import torch
 
@@ -109,11 +110,51 @@ def load_library(path: str = LIB_PATH):
     return lib
 
 
+_prep = threading.local()
+
+
 def _call(name: str, *args) -> None:
+    rec = getattr(_prep, "calls", None)
+    if rec is not None:            # inside prepare(): record instead of calling
+        rec.append((name, args))
+        return
     lib = load_library()
     st = getattr(lib, name)(*args)
     if st != 0:
         raise RLKError(name, st, lib.rlk_last_error().decode())
+
+
+def prepare(fn, *args, **kwargs):
+    """Marshal one call of a raw binding function once; return a callable that
+    repeats exactly that C call.
+
+    ``fn`` is one of the ``rlk_*`` functions of this module and ``args`` its
+    arguments.  The tensor checks, pointer and stream conversions are done
+    here, once; each call of the result only enters the C library (which still
+    validates every argument).  For tight loops over fixed buffers on the
+    current stream, where those per-call conversions would cost more than a
+    small kernel; the buffers must outlive the callable.
+    """
+    _prep.calls = []
+    try:
+        fn(*args, **kwargs)
+        calls = _prep.calls
+    finally:
+        _prep.calls = None
+    if len(calls) != 1:
+        raise ValueError(f"{getattr(fn, '__name__', fn)} did not make exactly one library call")
+    name, cargs = calls[0]
+    lib = load_library()
+    cfn = getattr(lib, name)
+    keep = args  # the tensors whose pointers the call holds
+
+    def call() -> None:
+        st = cfn(*cargs)
+        if st != 0:
+            raise RLKError(name, st, lib.rlk_last_error().decode())
+
+    call.tensors = keep
+    return call
 
 
 # ------------------------------------------------------------ marshalling
