@@ -7,6 +7,8 @@ so the error codes and the empty-input path are testable without a GPU.
 import ctypes
 import os
 import re
+import subprocess
+import sys
 
 import numpy as np
 import pytest
@@ -191,3 +193,19 @@ def test_kl_both_and_reference_gradient_validate(lib):
     assert lib.rlk_kl_bwd_ref_strided(p, p, 1, 8, 10, ctypes.byref(R(4, 40, 10)),
                                       ctypes.byref(R(4, 40, 10)), 0, F(0), F(0), p, p, p,
                                       ctypes.byref(R(4, 20, 5)), None) == SHAPE
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    # no fallback implementation: without librlk.so the binding refuses to load
+    code = ("from vocab_log_softmax_amd import rlk\n"
+            "try:\n"
+            "    rlk.load_library()\n"
+            "except ImportError as e:\n"
+            "    print('ImportError:', e)\n"
+            "    raise SystemExit(3)\n"
+            "raise SystemExit(0)\n")
+    env = dict(os.environ, RLK_LIB=str(tmp_path / "librlk.so"))
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 3, r.stdout + r.stderr
+    assert "no fallback" in r.stdout
