@@ -196,6 +196,30 @@ def test_cap_mode_edge_rows(dev, orc, cap, dtype):
     assert_grad(gH, orc.entropy_bwd(to64(x), to64(gr), cap), "entropy grad", exact_zero=inf_cols)
 
 
+@pytest.mark.parametrize("cap", [1e-7, 1e-5, 200.0], ids=["tiny", "fixed_min", "large"])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+def test_cap_extremes(dev, orc, cap, dtype):
+    """Caps far from the usual 20-50: a tiny cap (running-max form below the
+    fixed form's lower bound; every logit saturates to +-c), one just inside
+    the fixed form's range, and a large cap (y ~ x over the logits' range)."""
+    N, V = 6, 3001
+    x = (torch.randn(N, V, generator=gen(41)) * 3.0).to(dtype)
+    x64 = to64(x)
+    t = torch.randint(0, V, (N, 2), generator=gen(42))
+    gt = torch.randn(N, 2, generator=gen(43))
+    gr = torch.randn(N, generator=gen(44))
+    xd = x.to(dev)
+    lp, st = rlk.logp_fwd(xd, t.to(dev), cap)
+    glp = rlk.logp_bwd(xd, t.to(dev), gt.to(dev), st, cap)
+    H, sh = rlk.entropy_fwd(xd, cap)
+    gH = rlk.entropy_bwd(xd, gr.to(dev), sh, cap)
+    torch.cuda.synchronize()
+    assert_out(lp, orc.logp_fwd(x64, t.numpy(), cap), dtype, "logp")
+    assert_grad(glp, orc.logp_bwd(x64, t.numpy(), to64(gt), cap), "logp grad")
+    assert_out(H, orc.entropy_fwd(x64, cap), dtype, "entropy")
+    assert_grad(gH, orc.entropy_bwd(x64, to64(gr), cap), "entropy grad")
+
+
 def test_entropy_saturated_cap_rows(dev, orc):
     # every logit caps to exactly c: a uniform row, H = log V
     V = 151936

@@ -63,13 +63,16 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // Softcap constants of the row kernels (rlk::CapMode): k = -2 log2(e) / c
 // gives r = 1 / (1 + 2^(k x)); the statistic input is x with scale log2(e)
 // (cap off), r with scale 2 c log2(e) (online form) or t = (y - c) log2(e)
-// itself with scale 1 (fixed form, caps with 2 c log2(e) <=
-// kCapFixedMaxScale), whose kernels also take 1 / (2 c log2(e)).  A forward
-// call, its backward and the shard combine all derive the mode from the same c.
+// itself with scale 1 (fixed form, caps with kCapFixedMinScale <=
+// 2 c log2(e) <= kCapFixedMaxScale), whose kernels also take 1 / (2 c log2(e)).
+// A forward call, its backward and the shard combine all derive the mode from
+// the same c.
 constexpr double kLog2eD = 1.44269504088896340736;
 int cap_mode(float c) {
     if (c == 0.0f) return rlk::kCapNone;
-    return 2.0 * c * kLog2eD <= rlk::kCapFixedMaxScale ? rlk::kCapFixed : rlk::kCapOnline;
+    const double sc = 2.0 * c * kLog2eD;
+    return sc >= rlk::kCapFixedMinScale && sc <= rlk::kCapFixedMaxScale ? rlk::kCapFixed
+                                                                         : rlk::kCapOnline;
 }
 float cap_k(float c) { return c != 0.0f ? static_cast<float>(-2.0 * kLog2eD / c) : 0.0f; }
 float cap_sc(float c) {

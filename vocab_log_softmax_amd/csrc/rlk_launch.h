@@ -25,9 +25,12 @@ enum Head : int {
 //              and a reciprocal, scale 1, reference 0 (no running max).
 // t of the fixed mode lies in [-2 c log2(e), 0], so for caps with
 // 2 c log2(e) <= kCapFixedMaxScale every 2^t is a normal float and the sums
-// need no rescaling; larger caps take the online mode.
+// need no rescaling; larger caps take the online mode.  So do caps with
+// 2 c log2(e) < kCapFixedMinScale: the fixed form's backward scales its slope
+// by 1 / (2 c log2(e))^2, which must stay far from overflow.
 enum CapMode : int { kCapNone = 0, kCapOnline = 1, kCapFixed = 2 };
 constexpr float kCapFixedMaxScale = 120.0f;
+constexpr float kCapFixedMinScale = 1.0f / 65536.0f;
 
 // Launch shape of the forward row kernels: one workgroup per row (grid-stride
 // over rows), each lane consuming groups of U chunks of 8 elements.  These
