@@ -258,7 +258,8 @@ def main() -> int:
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
-              "(rows shard across GPUs with no exchange; see the design notes). "
+              "(rows shard across GPUs with no exchange; vocabulary shards need one "
+              "all-gather of the rlk_*_fwd_partial records before rlk_combine). "
               "Run with --gpus 1.", file=sys.stderr)
         return 2
 

@@ -14,7 +14,7 @@ against closed forms, invariants, brute force on tiny rows, finite differences
 and independent library routines (torch fp64 ``log_softmax``, ``kl_div``,
 autograd).  The one reading with no independent pin (gradient on a
 reverse-KL support-mismatch row: NaN on the policy's support) is marked
-"parity unpinned" there and in the design notes.
+"parity unpinned" there.
 """
 
 from __future__ import annotations

@@ -29,7 +29,7 @@
  *         g * (onehot - softmax)), Behavior changes (targets outside [0, V)
  *         give output 0 and an exactly zero gradient row).
  *
- * Readings where the pages are silent (each also listed in the design notes):
+ * Readings where the pages are silent:
  *   - a target is valid iff 0 <= t < V; any other value is ignored [ZW];
  *   - a logp row with no valid target has output 0 and an all-zero gradient,
  *     even if the row is empty (index handling comes first);

@@ -1,6 +1,6 @@
 """Comparison rules between the HIP path and the fp64 oracle.
 
-Tolerances (fixed for this library; derivations in the design notes):
+Tolerances (fixed for this library; the reason for each is given with it):
   * head outputs (fp32) from fp32 logits: |d| <= 1e-5 + 1e-5 |ref|
     (relative 1e-5, with the 1e-5 absolute floor of the fp32 row of the
     accuracy table on the "Final Logit Softcap" page);

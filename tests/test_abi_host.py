@@ -209,3 +209,9 @@ def test_missing_library_fails_loudly(tmp_path):
                        text=True, timeout=120)
     assert r.returncode == 3, r.stdout + r.stderr
     assert "no fallback" in r.stdout
+
+
+def test_bench_refuses_more_than_one_gpu():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       cwd=ROOT, capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU only" in r.stderr, r.stdout + r.stderr

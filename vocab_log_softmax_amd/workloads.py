@@ -10,7 +10,8 @@ Every tensor is a pure function of (workload, seed, device, row chunking):
 chunks so that peak memory stays bounded for the 10 GB tensors.
 
 Workloads (each takes its distribution from the page it stands in for; the
-pages time random tensors, see the design notes for the recipe):
+pages time random tensors: normal logits whose scale grows with the cap,
+uniform targets, +1000 offset rows):
   c1_logp_fp32      logprobs k=1, fp32 [64, 32000] ~ N(0, 2^2), 4 rows -100
   c2_logp_bf16      logprobs k=1, bf16 [8192, 151936] ~ N(0, 3^2),
                     5% targets -100 and 0.1% targets V+7
