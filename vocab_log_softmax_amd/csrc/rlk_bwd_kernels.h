@@ -139,17 +139,36 @@ __device__ __forceinline__ float target_grad(float a, float s, float cf, const R
     return CAPA != kCapNone ? v * (cf * s) : v;
 }
 
+// Slots of bwd_topk_kernel: the sort keys are padded to a power of two.
+__host__ __device__ inline int topk_pad(int64_t k) {
+    int n = 2;
+    while (n < k) n <<= 1;
+    return n;
+}
+
+// Dynamic LDS of bwd_topk_kernel: kpad 64-bit sort keys, then k fp32 g.
+inline size_t topk_lds_bytes(int64_t k) {
+    return static_cast<size_t>(topk_pad(k)) * sizeof(uint64_t) +
+           static_cast<size_t>(k) * sizeof(float);
+}
+
 // Logprobs with k > kGLanes: one workgroup per (row, column segment), visited
 // last-first (the end of the forward's stream is what the Infinity Cache
 // still holds).  The k slots are staged in LDS and G is summed in a tree
-// fixed by kGLanes (slot j by lane j mod kGLanes, in order), not by BLOCK;
-// after the bulk pass a barrier orders the target columns' one-hot rewrites
-// after the bulk stores of the same addresses.
+// fixed by kGLanes (slot j by lane j mod kGLanes, in order), not by BLOCK.
+// After the bulk pass a barrier orders the target columns' one-hot rewrites
+// after the bulk stores of the same addresses.  The rewrites find duplicate
+// ids by sorting the keys (local column, slot) of the row's local slots in
+// LDS (bitonic, O(k log^2 k) compare-exchanges over the workgroup): the
+// first key of each column's run sums the run's g, which the sort leaves in
+// slot order, and writes the column once.
 template <int BLOCK, int U, typename T, int CAPA, bool ALIGNED>
 __global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void bwd_topk_kernel(BwdParams p) {
     using S = typename T::storage;
     static_assert(BLOCK >= kGLanes, "the G tree needs kGLanes threads");
-    extern __shared__ int smem_topk[];  // int32 local target (-1 ignored, -2 other shard) [k], fp32 g [k]
+    // (local column << 32 | slot) of the local slots, all ones for the rest
+    // and the padding [kpad]; then fp32 g [k]
+    extern __shared__ uint64_t smem_topk[];
     __shared__ float red_g[kGLanes / 64];
     __shared__ float red_n[kGLanes / 64];
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -158,8 +177,10 @@ __global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void bwd_topk_kernel(BwdParams
     const int64_t ngroups = (nchunks + step - 1) / step;
     const int64_t gps = (ngroups + p.split - 1) / p.split;  // groups per column segment
     const RowStats* stats = static_cast<const RowStats*>(p.stats);
-    int* tg = smem_topk;
-    float* gg = reinterpret_cast<float*>(smem_topk + p.k);
+    const int kpad = topk_pad(p.k);
+    constexpr uint64_t kNoKey = ~0ull;
+    uint64_t* keys = smem_topk;
+    float* gg = reinterpret_cast<float*>(smem_topk + kpad);
     const CapArgs ca{p.kx, p.ix, p.spx};
     const float cf = slope_factor<CAPA>(ca);
 
@@ -173,8 +194,8 @@ __global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void bwd_topk_kernel(BwdParams
         RowStats rs = stats[row];
         fixed_refs<CAPA, kCapNone, false>(rs);
 
-        // Stage the slots (valid over the whole row; local to this vocabulary
-        // shard -- plain call: the same -- as its column, else -1 / -2).
+        // Stage the slots: g, and the key of each slot local to this
+        // vocabulary shard (plain call: every valid slot).
         float part = 0.0f, cnt = 0.0f;
         if (tid < kGLanes) {
             for (int64_t j = tid; j < p.k; j += kGLanes) {
@@ -182,7 +203,8 @@ __global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void bwd_topk_kernel(BwdParams
                 const bool valid = t >= 0 && t < p.vtotal;
                 const bool local = t >= p.v0 && t < p.v0 + p.V;
                 const float g = p.g[row * p.k + j];
-                tg[j] = local ? static_cast<int>(t - p.v0) : (valid ? -2 : -1);
+                keys[j] = local ? (static_cast<uint64_t>(t - p.v0) << 32) | static_cast<uint64_t>(j)
+                                : kNoKey;
                 gg[j] = g;
                 if (valid) {
                     part += g;
@@ -190,6 +212,7 @@ __global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void bwd_topk_kernel(BwdParams
                 }
             }
         }
+        for (int j = static_cast<int>(p.k) + tid; j < kpad; j += BLOCK) keys[j] = kNoKey;
         part = wave_sum(part);
         cnt = wave_sum(cnt);
         if (lane == 0 && wid < kGLanes / 64) {
@@ -224,21 +247,35 @@ __global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void bwd_topk_kernel(BwdParams
                     store_group<BLOCK, U, S, ALIGNED>(gx, p.V, g0, full, v);
                 },
                 gbeg, gend);
-            // Target columns of this segment: the bulk value becomes the
-            // one-hot term (first slot of each column sums its duplicates).
-            __syncthreads();
-            for (int64_t j = tid; j < p.k; j += BLOCK) {
-                const int t = tg[j];
-                if (t < 0 || t < cbeg || t >= cend) continue;
-                bool first = true;
-                float h = 0.0f;
-                for (int64_t jj = 0; jj < p.k; ++jj) {
-                    if (tg[jj] == t) {
-                        if (jj < j) first = false;
-                        h += gg[jj];
+            // Sort the keys: a column's slots become one run, in slot order.
+            for (int size = 2; size <= kpad; size <<= 1) {
+                for (int stride = size >> 1; stride > 0; stride >>= 1) {
+                    __syncthreads();
+                    for (int i = tid; i < kpad / 2; i += BLOCK) {
+                        const int lo = 2 * i - (i & (stride - 1)), hi = lo + stride;
+                        const uint64_t a = keys[lo], b = keys[hi];
+                        if ((a > b) == ((lo & size) == 0)) {
+                            keys[lo] = b;
+                            keys[hi] = a;
+                        }
                     }
                 }
-                if (!first) continue;
+            }
+            // (the last barrier of the sort also orders the rewrites after
+            // the bulk stores)
+            __syncthreads();
+            // Target columns of this segment: the bulk value becomes the
+            // one-hot term, written by the first slot of the column's run,
+            // which sums the run's g in slot order.
+            for (int i = tid; i < p.k; i += BLOCK) {
+                const uint64_t key = keys[i];
+                if (key == kNoKey) continue;
+                const int64_t t = static_cast<int64_t>(key >> 32);
+                if (t < cbeg || t >= cend) continue;
+                if (i > 0 && (keys[i - 1] >> 32) == (key >> 32)) continue;
+                float h = 0.0f;
+                for (int r = i; r < p.k && (keys[r] >> 32) == (key >> 32); ++r)
+                    h += gg[static_cast<uint32_t>(keys[r])];
                 float s4;
                 const float a = cap_value_slope<CAPA>(load_one(xa + t), ca, s4);
                 store_one(gx + t, target_grad<CAPA>(a, s4, cf, rs, G, h, p.scx));
@@ -626,7 +663,7 @@ inline hipError_t bwd_wide_launch(const BwdParams& p, hipStream_t s) {
 
 template <int BB, int U, typename T, int CAPX, bool AL>
 inline hipError_t bwd_topk_launch(const BwdParams& p, hipStream_t s) {
-    const size_t lds = static_cast<size_t>(p.k) * (sizeof(int) + sizeof(float));
+    const size_t lds = topk_lds_bytes(p.k);
     hipLaunchKernelGGL((bwd_topk_kernel<BB, U, T, CAPX, AL>), dim3(row_grid(p.N * p.split)),
                        dim3(BB), lds, s, p);
     return hipGetLastError();

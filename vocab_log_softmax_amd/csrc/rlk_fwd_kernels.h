@@ -171,6 +171,9 @@ __device__ __forceinline__ void update_kl2(StatKL2& st, const float (&a)[U][kChu
         }
 }
 
+// Target slots per lane whose loads a logprobs forward issues together.
+constexpr int kTopkBatch = 4;
+
 // Logprobs / entropy forward: one workgroup per row.
 template <int BLOCK, int U, typename T, int HEAD, int CAP, bool ALIGNED>
 __global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void fwd1_kernel(FwdParams p) {
@@ -225,17 +228,36 @@ __global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void fwd1_kernel(FwdParams p) 
             RowStats rs;
             rs.mLa = bc[0];
             rs.log2Sa = bc[1];
-            for (int64_t j = tid; j < p.k; j += BLOCK) {
-                const int64_t t = j == tid ? t0 : p.targets[row * p.k + j];
-                const bool local = t >= p.v0 && t < p.v0 + p.V;
-                float a = 0.0f;
-                if (local) {
-                    a = cap_value<CAP>(j == tid ? xt0 : load_one(x + (t - p.v0)), ca);
+            // Slots beyond the prefetched first one (k > BLOCK), kTopkBatch
+            // per lane at a time: their target loads are issued together,
+            // then their gathers, so a lane waits twice per batch instead of
+            // twice per slot.
+            for (int64_t j0 = tid; j0 < p.k; j0 += static_cast<int64_t>(BLOCK) * kTopkBatch) {
+                int64_t t[kTopkBatch];
+                float xv[kTopkBatch];
+#pragma unroll
+                for (int b = 0; b < kTopkBatch; ++b) {
+                    const int64_t j = j0 + static_cast<int64_t>(b) * BLOCK;
+                    t[b] = j == tid ? t0 : (j < p.k ? p.targets[row * p.k + j] : -1);
                 }
-                if (p.part)
-                    p.tvals[row * p.k + j] = a;  // statistic input of an owned target
-                else
-                    p.out[row * p.k + j] = (t >= 0 && t < p.vtotal) ? target_logp(a, p.scx, rs) : 0.0f;
+#pragma unroll
+                for (int b = 0; b < kTopkBatch; ++b) {
+                    const int64_t j = j0 + static_cast<int64_t>(b) * BLOCK;
+                    const bool local = t[b] >= p.v0 && t[b] < p.v0 + p.V;
+                    xv[b] = j == tid ? xt0 : (local ? load_one(x + (t[b] - p.v0)) : 0.0f);
+                }
+#pragma unroll
+                for (int b = 0; b < kTopkBatch; ++b) {
+                    const int64_t j = j0 + static_cast<int64_t>(b) * BLOCK;
+                    if (j >= p.k) break;
+                    const bool local = t[b] >= p.v0 && t[b] < p.v0 + p.V;
+                    const float a = local ? cap_value<CAP>(xv[b], ca) : 0.0f;
+                    if (p.part)
+                        p.tvals[row * p.k + j] = a;  // statistic input of an owned target
+                    else
+                        p.out[row * p.k + j] =
+                            (t[b] >= 0 && t[b] < p.vtotal) ? target_logp(a, p.scx, rs) : 0.0f;
+                }
             }
         }
         __syncthreads();
