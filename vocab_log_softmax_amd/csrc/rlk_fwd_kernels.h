@@ -171,9 +171,6 @@ __device__ __forceinline__ void update_kl2(StatKL2& st, const float (&a)[U][kChu
         }
 }
 
-// Target slots per lane whose loads a logprobs forward issues together.
-constexpr int kTopkBatch = 4;
-
 // Logprobs / entropy forward: one workgroup per row.
 template <int BLOCK, int U, typename T, int HEAD, int CAP, bool ALIGNED>
 __global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void fwd1_kernel(FwdParams p) {

@@ -100,6 +100,9 @@ constexpr int kBwdBlockSmall = 256;
 constexpr int kBwdUnrollSmall = 1;
 constexpr int64_t kBwdSmallRows = 512;      // below this many rows
 constexpr int64_t kBwdTargetItems = 2048;   // aim for this many (row, segment) items
+// Top-k slots per lane whose target loads and gathers a logprobs forward
+// issues together.
+constexpr int kTopkBatch = 4;
 // Largest grid in workgroups: a dispatch counts work-items in 32 bits, and
 // blocks are at most 1024 threads.
 constexpr int kMaxGrid = (1 << 22) - 1;
