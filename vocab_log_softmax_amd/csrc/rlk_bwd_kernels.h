@@ -162,7 +162,7 @@ inline size_t topk_lds_bytes(int64_t k) {
 // LDS (bitonic, O(k log^2 k) compare-exchanges over the workgroup): the
 // first key of each column's run sums the run's g, which the sort leaves in
 // slot order, and writes the column once.
-template <int BLOCK, int U, typename T, int CAPA, bool ALIGNED>
+template <int BLOCK, int U, typename T, int CAPA, bool ALIGNED, bool NT>
 __global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void bwd_topk_kernel(BwdParams p) {
     using S = typename T::storage;
     static_assert(BLOCK >= kGLanes, "the G tree needs kGLanes threads");
@@ -231,7 +231,7 @@ __global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void bwd_topk_kernel(BwdParams
         if (mode == kModeNormal) {
             float A, B;
             row_coeffs<kHeadLogp, CAPA>(rs, G, 0.0f, cf, A, B);
-            for_each_group<BLOCK, U, S, kCapNone, ALIGNED, kBwdPipe>(
+            for_each_group<BLOCK, U, S, kCapNone, ALIGNED, kBwdPipe, NT>(
                 xa, p.V, CapArgs{},
                 [&](int64_t g0, bool full, const float (&x)[U][kChunk]) {
                     float v[U][kChunk];
@@ -307,7 +307,8 @@ constexpr int kPieceMaxK = 4;
 // with no branch between them.  Logprobs slots (k <= kPieceMaxK) are read by
 // every lane: G is summed in the association of bwd_topk_kernel's tree, and
 // target columns take target_grad, so all backward kernels give the same bits.
-template <int BLOCK, int U, typename T, int HEAD, int CAPA, int CAPB, bool ALIGNED, bool FULL>
+template <int BLOCK, int U, typename T, int HEAD, int CAPA, int CAPB, bool ALIGNED, bool FULL,
+          bool NT>
 __device__ __forceinline__ void piece(const BwdParams& p, int64_t row, int64_t g0) {
     using S = typename T::storage;
     constexpr bool KL = HEAD == kHeadKLReverse || HEAD == kHeadKLForward;
@@ -323,11 +324,11 @@ __device__ __forceinline__ void piece(const BwdParams& p, int64_t row, int64_t g
     const CapArgs cb{p.ky, p.iy};
     const S* __restrict__ xb = KL ? static_cast<const S*>(p.y) + p.my.offset(row) : nullptr;
     if (FULL) {
-        raw_load<BLOCK, U>(xa, g0, rx);
-        if (KL) raw_load<BLOCK, U>(xb, g0, ry);
+        raw_load<BLOCK, U, NT>(xa, g0, rx);
+        if (KL) raw_load<BLOCK, U, NT>(xb, g0, ry);
     } else {
-        tail_values<BLOCK, U, S, kCapNone, ALIGNED>(xa, p.V, nfull, g0, CapArgs{}, x);
-        if (KL) tail_values<BLOCK, U, S, CAPB, ALIGNED>(xb, p.V, nfull, g0, cb, b);
+        tail_values<BLOCK, U, S, kCapNone, ALIGNED, NT>(xa, p.V, nfull, g0, CapArgs{}, x);
+        if (KL) tail_values<BLOCK, U, S, CAPB, ALIGNED, NT>(xb, p.V, nfull, g0, cb, b);
     }
     const CapArgs ca{p.kx, p.ix, p.spx};
     const float cf = slope_factor<CAPA>(ca);
@@ -448,14 +449,14 @@ __device__ __forceinline__ void piece(const BwdParams& p, int64_t row, int64_t g
 // grid (pieces of a row, rows): consecutive workgroups take consecutive
 // pieces of a row, so the chip sweeps the matrix front to back; rows run
 // last-first (see bwd_topk_kernel).
-template <int BLOCK, int U, typename T, int HEAD, int CAPA, int CAPB, bool ALIGNED>
+template <int BLOCK, int U, typename T, int HEAD, int CAPA, int CAPB, bool ALIGNED, bool NT>
 __global__ __launch_bounds__(BLOCK) void bwd_piece_kernel(BwdParams p, int64_t rbase) {
     const int64_t row = p.N - 1 - (rbase + static_cast<int64_t>(blockIdx.y));
     const int64_t g0 = static_cast<int64_t>(blockIdx.x) * (BLOCK * U);  // first chunk
     if (ALIGNED && g0 + BLOCK * U <= p.V / kChunk)
-        piece<BLOCK, U, T, HEAD, CAPA, CAPB, ALIGNED, true>(p, row, g0);
+        piece<BLOCK, U, T, HEAD, CAPA, CAPB, ALIGNED, true, NT>(p, row, g0);
     else
-        piece<BLOCK, U, T, HEAD, CAPA, CAPB, ALIGNED, false>(p, row, g0);
+        piece<BLOCK, U, T, HEAD, CAPA, CAPB, ALIGNED, false, NT>(p, row, g0);
 }
 
 // Logprobs with kPieceMaxK < k <= kGLanes: one-shot pieces of kGLanes lanes
@@ -473,7 +474,7 @@ __global__ __launch_bounds__(BLOCK) void bwd_piece_kernel(BwdParams p, int64_t r
 // FULL: every chunk of the piece lies inside an aligned row, so its loads are
 // raw 16-byte vectors issued back to back without branches (tail_values'
 // per-chunk branches would make the compiler wait for each load in turn).
-template <int U, typename T, int CAPA, bool ALIGNED, bool FULL>
+template <int U, typename T, int CAPA, bool ALIGNED, bool FULL, bool NT>
 __device__ __forceinline__ void wide_piece(const BwdParams& p, int64_t row, int64_t g0) {
     using S = typename T::storage;
     constexpr int BLOCK = kGLanes, NW = kGLanes / 64;
@@ -503,9 +504,9 @@ __device__ __forceinline__ void wide_piece(const BwdParams& p, int64_t row, int6
     RawGroup<S, U> raw;
     float x[U][kChunk];
     if (FULL)
-        raw_load<BLOCK, U>(xa, g0, raw);
+        raw_load<BLOCK, U, NT>(xa, g0, raw);
     else
-        tail_values<BLOCK, U, S, kCapNone, ALIGNED>(xa, p.V, nfull, g0, CapArgs{}, x);
+        tail_values<BLOCK, U, S, kCapNone, ALIGNED, NT>(xa, p.V, nfull, g0, CapArgs{}, x);
     RowStats rs = stats[row];
     fixed_refs<CAPA, kCapNone, false>(rs);
 
@@ -603,14 +604,14 @@ __device__ __forceinline__ void wide_piece(const BwdParams& p, int64_t row, int6
     store_group<BLOCK, U, S, ALIGNED>(gx, p.V, g0, FULL, v);
 }
 
-template <int U, typename T, int CAPA, bool ALIGNED>
+template <int U, typename T, int CAPA, bool ALIGNED, bool NT>
 __global__ __launch_bounds__(kGLanes) void bwd_wide_kernel(BwdParams p, int64_t rbase) {
     const int64_t row = p.N - 1 - (rbase + static_cast<int64_t>(blockIdx.y));
     const int64_t g0 = static_cast<int64_t>(blockIdx.x) * (kGLanes * U);
     if (ALIGNED && g0 + kGLanes * U <= p.V / kChunk)
-        wide_piece<U, T, CAPA, ALIGNED, true>(p, row, g0);
+        wide_piece<U, T, CAPA, ALIGNED, true, NT>(p, row, g0);
     else
-        wide_piece<U, T, CAPA, ALIGNED, false>(p, row, g0);
+        wide_piece<U, T, CAPA, ALIGNED, false, NT>(p, row, g0);
 }
 
 // ------------------------------------------------------------- dispatch
@@ -627,7 +628,7 @@ __global__ __launch_bounds__(kGLanes) void bwd_wide_kernel(BwdParams p, int64_t 
 // Rows per piece launch (the grid's second dimension is limited to 65536).
 constexpr int64_t kPieceRowsPerLaunch = 65536;
 
-template <typename T, int HEAD, int CAPX, int CAPY, bool AL>
+template <typename T, int HEAD, int CAPX, int CAPY, bool AL, bool NT>
 inline hipError_t bwd_piece_launch(const BwdParams& p0, hipStream_t s) {
     BwdParams p = p0;
     p.wt = static_cast<uint64_t>(p.N) * static_cast<uint64_t>(p.V) * T::kBytes >=
@@ -638,7 +639,7 @@ inline hipError_t bwd_piece_launch(const BwdParams& p0, hipStream_t s) {
     for (int64_t r0 = 0; r0 < p.N; r0 += kPieceRowsPerLaunch) {
         const int64_t rows = p.N - r0 < kPieceRowsPerLaunch ? p.N - r0 : kPieceRowsPerLaunch;
         const dim3 grid(static_cast<unsigned>(pieces), static_cast<unsigned>(rows));
-        hipLaunchKernelGGL((bwd_piece_kernel<kBwdPieceBlock, U, T, HEAD, CAPX, CAPY, AL>), grid,
+        hipLaunchKernelGGL((bwd_piece_kernel<kBwdPieceBlock, U, T, HEAD, CAPX, CAPY, AL, NT>), grid,
                            dim3(kBwdPieceBlock), 0, s, p, r0);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -646,14 +647,14 @@ inline hipError_t bwd_piece_launch(const BwdParams& p0, hipStream_t s) {
     return hipSuccess;
 }
 
-template <typename T, int CAPX, bool AL>
+template <typename T, int CAPX, bool AL, bool NT>
 inline hipError_t bwd_wide_launch(const BwdParams& p, hipStream_t s) {
     constexpr int64_t pc = static_cast<int64_t>(kGLanes) * kBwdWideUnroll;
     const int64_t pieces = ((p.V + kChunk - 1) / kChunk + pc - 1) / pc;
     for (int64_t r0 = 0; r0 < p.N; r0 += kPieceRowsPerLaunch) {
         const int64_t rows = p.N - r0 < kPieceRowsPerLaunch ? p.N - r0 : kPieceRowsPerLaunch;
         const dim3 grid(static_cast<unsigned>(pieces), static_cast<unsigned>(rows));
-        hipLaunchKernelGGL((bwd_wide_kernel<kBwdWideUnroll, T, CAPX, AL>), grid, dim3(kGLanes), 0,
+        hipLaunchKernelGGL((bwd_wide_kernel<kBwdWideUnroll, T, CAPX, AL, NT>), grid, dim3(kGLanes), 0,
                            s, p, r0);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -661,30 +662,30 @@ inline hipError_t bwd_wide_launch(const BwdParams& p, hipStream_t s) {
     return hipSuccess;
 }
 
-template <int BB, int U, typename T, int CAPX, bool AL>
+template <int BB, int U, typename T, int CAPX, bool AL, bool NT>
 inline hipError_t bwd_topk_launch(const BwdParams& p, hipStream_t s) {
     const size_t lds = topk_lds_bytes(p.k);
-    hipLaunchKernelGGL((bwd_topk_kernel<BB, U, T, CAPX, AL>), dim3(row_grid(p.N * p.split)),
+    hipLaunchKernelGGL((bwd_topk_kernel<BB, U, T, CAPX, AL, NT>), dim3(row_grid(p.N * p.split)),
                        dim3(BB), lds, s, p);
     return hipGetLastError();
 }
 
-template <typename T, int CAPX, int CAPY, bool AL>
+template <typename T, int CAPX, int CAPY, bool AL, bool NT>
 inline hipError_t bwd_dispatch_al(int head, const BwdParams& p0, hipStream_t s) {
     switch (head) {
         case kHeadEntropy:
-            return bwd_piece_launch<T, kHeadEntropy, CAPX, kCapNone, AL>(p0, s);
+            return bwd_piece_launch<T, kHeadEntropy, CAPX, kCapNone, AL, NT>(p0, s);
         case kHeadKLReverse:
-            return bwd_piece_launch<T, kHeadKLReverse, CAPX, CAPY, AL>(p0, s);
+            return bwd_piece_launch<T, kHeadKLReverse, CAPX, CAPY, AL, NT>(p0, s);
         case kHeadKLForward:
-            return bwd_piece_launch<T, kHeadKLForward, CAPX, CAPY, AL>(p0, s);
+            return bwd_piece_launch<T, kHeadKLForward, CAPX, CAPY, AL, NT>(p0, s);
         case kHeadLogp:
             break;
         default:
             return hipErrorInvalidValue;
     }
-    if (p0.k <= kPieceMaxK) return bwd_piece_launch<T, kHeadLogp, CAPX, kCapNone, AL>(p0, s);
-    if (p0.k <= kGLanes) return bwd_wide_launch<T, CAPX, AL>(p0, s);
+    if (p0.k <= kPieceMaxK) return bwd_piece_launch<T, kHeadLogp, CAPX, kCapNone, AL, NT>(p0, s);
+    if (p0.k <= kGLanes) return bwd_wide_launch<T, CAPX, AL, NT>(p0, s);
     BwdParams p = p0;
     if (p.N < kBwdSmallRows) {
         // Few rows: narrow workgroups, each row cut into column segments.
@@ -692,16 +693,21 @@ inline hipError_t bwd_dispatch_al(int head, const BwdParams& p0, hipStream_t s) 
         const int64_t ngroups = ((p.V + kChunk - 1) / kChunk + step - 1) / step;
         const int64_t split = (kBwdTargetItems + p.N - 1) / p.N;
         p.split = split < ngroups ? split : (ngroups > 0 ? ngroups : 1);
-        return bwd_topk_launch<kBwdBlockSmall, kBwdUnrollSmall, T, CAPX, AL>(p, s);
+        return bwd_topk_launch<kBwdBlockSmall, kBwdUnrollSmall, T, CAPX, AL, NT>(p, s);
     }
     p.split = 1;
-    return bwd_topk_launch<kBwdBlockTopk, kBwdUnrollTopk, T, CAPX, AL>(p, s);
+    return bwd_topk_launch<kBwdBlockTopk, kBwdUnrollTopk, T, CAPX, AL, NT>(p, s);
 }
 
+// Rows that are not 16-byte aligned read every element with ordinary loads,
+// so only aligned rows choose between streaming and cached loads.
 template <typename T, int CAPX, int CAPY>
 inline hipError_t bwd_dispatch_a(int head, bool al, const BwdParams& p, hipStream_t s) {
-    return al ? bwd_dispatch_al<T, CAPX, CAPY, true>(head, p, s)
-              : bwd_dispatch_al<T, CAPX, CAPY, false>(head, p, s);
+    if (!al) return bwd_dispatch_al<T, CAPX, CAPY, false, true>(head, p, s);
+    const bool kl = head == kHeadKLReverse || head == kHeadKLForward;
+    return stream_reads(p.N, p.V, T::kBytes, kl ? 2 : 1)
+               ? bwd_dispatch_al<T, CAPX, CAPY, true, true>(head, p, s)
+               : bwd_dispatch_al<T, CAPX, CAPY, true, false>(head, p, s);
 }
 
 template <typename T, int CAPX>

@@ -83,20 +83,21 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
-// Streaming hints for the bulk row traffic (every logit is touched once per
-// kernel, so caching it only evicts other data).  Compile-time switches.
-#ifndef RLK_NT_LOAD
-#define RLK_NT_LOAD 1
-#endif
+// Cache hints for the bulk row traffic.  Every logit is touched once per
+// kernel: an operand larger than the Infinity Cache streams through
+// non-temporal loads (NT), which keep it from evicting other data, while one
+// that fits is read with ordinary loads, which find what the previous kernel
+// left in the cache (kCachedReadBytes).  Stores are non-temporal (a
+// compile-time switch).
 #ifndef RLK_NT_STORE
 #define RLK_NT_STORE 1
 #endif
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-template <typename V>
+template <bool NT, typename V>
 __device__ __forceinline__ V ld16(const V* p) {
-    if (RLK_NT_LOAD) return __builtin_nontemporal_load(p);
+    if (NT) return __builtin_nontemporal_load(p);
     return *p;
 }
 template <typename V>
@@ -108,21 +109,24 @@ __device__ __forceinline__ void st16(V* p, V v) {
 }
 
 // Load one full chunk of 8 elements from a 16-byte aligned address.
+template <bool NT>
 __device__ __forceinline__ void load_chunk(const float* p, float (&f)[kChunk]) {
-    const f32x4 a = ld16(reinterpret_cast<const f32x4*>(p));
-    const f32x4 b = ld16(reinterpret_cast<const f32x4*>(p) + 1);
+    const f32x4 a = ld16<NT>(reinterpret_cast<const f32x4*>(p));
+    const f32x4 b = ld16<NT>(reinterpret_cast<const f32x4*>(p) + 1);
     f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
     f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
 }
+template <bool NT>
 __device__ __forceinline__ void load_chunk(const uint16_t* p, float (&f)[kChunk]) {
-    const u32x4 w = ld16(reinterpret_cast<const u32x4*>(p));
+    const u32x4 w = ld16<NT>(reinterpret_cast<const u32x4*>(p));
     f[0] = bf16_lo(w.x); f[1] = bf16_hi(w.x);
     f[2] = bf16_lo(w.y); f[3] = bf16_hi(w.y);
     f[4] = bf16_lo(w.z); f[5] = bf16_hi(w.z);
     f[6] = bf16_lo(w.w); f[7] = bf16_hi(w.w);
 }
+template <bool NT>
 __device__ __forceinline__ void load_chunk(const _Float16* p, float (&f)[kChunk]) {
-    const u32x4 w = ld16(reinterpret_cast<const u32x4*>(p));
+    const u32x4 w = ld16<NT>(reinterpret_cast<const u32x4*>(p));
     const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -267,31 +271,31 @@ struct RawGroup<_Float16, U> {
     u32x4 v[U];
 };
 
-template <int BLOCK, int U>
+template <int BLOCK, int U, bool NT>
 __device__ __forceinline__ void raw_load(const uint16_t* __restrict__ row, int64_t g0,
                                          RawGroup<uint16_t, U>& r) {
 #pragma unroll
     for (int u = 0; u < U; ++u)
-        r.v[u] = ld16(reinterpret_cast<const u32x4*>(
+        r.v[u] = ld16<NT>(reinterpret_cast<const u32x4*>(
             row + (g0 + u * BLOCK + (int)threadIdx.x) * kChunk));
 }
-template <int BLOCK, int U>
+template <int BLOCK, int U, bool NT>
 __device__ __forceinline__ void raw_load(const _Float16* __restrict__ row, int64_t g0,
                                          RawGroup<_Float16, U>& r) {
 #pragma unroll
     for (int u = 0; u < U; ++u)
-        r.v[u] = ld16(reinterpret_cast<const u32x4*>(
+        r.v[u] = ld16<NT>(reinterpret_cast<const u32x4*>(
             row + (g0 + u * BLOCK + (int)threadIdx.x) * kChunk));
 }
-template <int BLOCK, int U>
+template <int BLOCK, int U, bool NT>
 __device__ __forceinline__ void raw_load(const float* __restrict__ row, int64_t g0,
                                          RawGroup<float, U>& r) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const f32x4* p =
             reinterpret_cast<const f32x4*>(row + (g0 + u * BLOCK + (int)threadIdx.x) * kChunk);
-        r.v[u][0] = ld16(p);
-        r.v[u][1] = ld16(p + 1);
+        r.v[u][0] = ld16<NT>(p);
+        r.v[u][1] = ld16<NT>(p + 1);
     }
 }
 template <int U>
@@ -333,14 +337,14 @@ __device__ __forceinline__ void raw_unpack(const RawGroup<float, U>& r, float (&
 // exactly 0; consumers clamp t before any 0 * t in tail groups).  With a
 // cap the in-range values are mapped to their statistic input (cap_value)
 // while padding stays -inf.
-template <int BLOCK, int U, typename S, int CAP, bool ALIGNED>
+template <int BLOCK, int U, typename S, int CAP, bool ALIGNED, bool NT>
 __device__ __forceinline__ void tail_values(const S* __restrict__ row, int64_t V, int64_t nfull,
                                             int64_t g0, CapArgs ca, float (&a)[U][kChunk]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int64_t c = g0 + u * BLOCK + (int)threadIdx.x;
         if (ALIGNED && c < nfull) {
-            load_chunk(row + c * kChunk, a[u]);
+            load_chunk<NT>(row + c * kChunk, a[u]);
             if (CAP != kCapNone) {
 #pragma unroll
                 for (int e = 0; e < kChunk; ++e) a[u][e] = cap_value<CAP>(a[u][e], ca);
@@ -385,7 +389,7 @@ __device__ __forceinline__ void fast_values(const RawGroup<S, U>& r, CapArgs ca,
 //
 // gbeg / gend restrict the walk to the groups [gbeg, gend) of the row (a
 // column segment); -1 for gend means "to the end of the row".
-template <int BLOCK, int U, typename S, int CAP, bool ALIGNED, bool PIPE, typename F>
+template <int BLOCK, int U, typename S, int CAP, bool ALIGNED, bool PIPE, bool NT, typename F>
 __device__ __forceinline__ void for_each_group(const S* __restrict__ row, int64_t V, CapArgs k, F&& f,
                                                int64_t gbeg = 0, int64_t gend = -1) {
     const int64_t step = (int64_t)U * BLOCK;
@@ -397,15 +401,15 @@ __device__ __forceinline__ void for_each_group(const S* __restrict__ row, int64_
     int64_t gi = gbeg;
     if (PIPE && gi < nfg) {
         RawGroup<S, U> A, B;
-        raw_load<BLOCK, U>(row, gi * step, A);
+        raw_load<BLOCK, U, NT>(row, gi * step, A);
         for (; gi + 1 < nfg; gi += 2) {
-            raw_load<BLOCK, U>(row, (gi + 1) * step, B);
+            raw_load<BLOCK, U, NT>(row, (gi + 1) * step, B);
             {
                 float a[U][kChunk];
                 fast_values<U, S, CAP>(A, k, a);
                 f(gi * step, true, a);
             }
-            if (gi + 2 < nfg) raw_load<BLOCK, U>(row, (gi + 2) * step, A);
+            if (gi + 2 < nfg) raw_load<BLOCK, U, NT>(row, (gi + 2) * step, A);
             {
                 float a[U][kChunk];
                 fast_values<U, S, CAP>(B, k, a);
@@ -421,7 +425,7 @@ __device__ __forceinline__ void for_each_group(const S* __restrict__ row, int64_
     } else {
         for (; gi < nfg; ++gi) {
             RawGroup<S, U> A;
-            raw_load<BLOCK, U>(row, gi * step, A);
+            raw_load<BLOCK, U, NT>(row, gi * step, A);
             float a[U][kChunk];
             fast_values<U, S, CAP>(A, k, a);
             f(gi * step, true, a);
@@ -429,13 +433,14 @@ __device__ __forceinline__ void for_each_group(const S* __restrict__ row, int64_
     }
     for (; gi < gend; ++gi) {
         float a[U][kChunk];
-        tail_values<BLOCK, U, S, CAP, ALIGNED>(row, V, nfull, gi * step, k, a);
+        tail_values<BLOCK, U, S, CAP, ALIGNED, NT>(row, V, nfull, gi * step, k, a);
         f(gi * step, false, a);
     }
 }
 
 // Same walk over two rows in lockstep (KL: policy and reference).
-template <int BLOCK, int U, typename S, int CAPA, int CAPB, bool ALIGNED, bool PIPE, typename F>
+template <int BLOCK, int U, typename S, int CAPA, int CAPB, bool ALIGNED, bool PIPE, bool NT,
+          typename F>
 __device__ __forceinline__ void for_each_group2(const S* __restrict__ ra, const S* __restrict__ rb,
                                                 int64_t V, CapArgs ka, CapArgs kb, F&& f,
                                                 int64_t gbeg = 0, int64_t gend = -1) {
@@ -448,11 +453,11 @@ __device__ __forceinline__ void for_each_group2(const S* __restrict__ ra, const 
     int64_t gi = gbeg;
     if (PIPE && gi < nfg) {
         RawGroup<S, U> A0, B0, A1, B1;
-        raw_load<BLOCK, U>(ra, gi * step, A0);
-        raw_load<BLOCK, U>(rb, gi * step, B0);
+        raw_load<BLOCK, U, NT>(ra, gi * step, A0);
+        raw_load<BLOCK, U, NT>(rb, gi * step, B0);
         for (; gi + 1 < nfg; gi += 2) {
-            raw_load<BLOCK, U>(ra, (gi + 1) * step, A1);
-            raw_load<BLOCK, U>(rb, (gi + 1) * step, B1);
+            raw_load<BLOCK, U, NT>(ra, (gi + 1) * step, A1);
+            raw_load<BLOCK, U, NT>(rb, (gi + 1) * step, B1);
             {
                 float a[U][kChunk], b[U][kChunk];
                 fast_values<U, S, CAPA>(A0, ka, a);
@@ -460,8 +465,8 @@ __device__ __forceinline__ void for_each_group2(const S* __restrict__ ra, const 
                 f(gi * step, true, a, b);
             }
             if (gi + 2 < nfg) {
-                raw_load<BLOCK, U>(ra, (gi + 2) * step, A0);
-                raw_load<BLOCK, U>(rb, (gi + 2) * step, B0);
+                raw_load<BLOCK, U, NT>(ra, (gi + 2) * step, A0);
+                raw_load<BLOCK, U, NT>(rb, (gi + 2) * step, B0);
             }
             {
                 float a[U][kChunk], b[U][kChunk];
@@ -480,8 +485,8 @@ __device__ __forceinline__ void for_each_group2(const S* __restrict__ ra, const 
     } else {
         for (; gi < nfg; ++gi) {
             RawGroup<S, U> A, B;
-            raw_load<BLOCK, U>(ra, gi * step, A);
-            raw_load<BLOCK, U>(rb, gi * step, B);
+            raw_load<BLOCK, U, NT>(ra, gi * step, A);
+            raw_load<BLOCK, U, NT>(rb, gi * step, B);
             float a[U][kChunk], b[U][kChunk];
             fast_values<U, S, CAPA>(A, ka, a);
             fast_values<U, S, CAPB>(B, kb, b);
@@ -490,8 +495,8 @@ __device__ __forceinline__ void for_each_group2(const S* __restrict__ ra, const 
     }
     for (; gi < gend; ++gi) {
         float a[U][kChunk], b[U][kChunk];
-        tail_values<BLOCK, U, S, CAPA, ALIGNED>(ra, V, nfull, gi * step, ka, a);
-        tail_values<BLOCK, U, S, CAPB, ALIGNED>(rb, V, nfull, gi * step, kb, b);
+        tail_values<BLOCK, U, S, CAPA, ALIGNED, NT>(ra, V, nfull, gi * step, ka, a);
+        tail_values<BLOCK, U, S, CAPB, ALIGNED, NT>(rb, V, nfull, gi * step, kb, b);
         f(gi * step, false, a, b);
     }
 }

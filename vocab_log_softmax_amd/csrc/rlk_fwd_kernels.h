@@ -172,7 +172,7 @@ __device__ __forceinline__ void update_kl2(StatKL2& st, const float (&a)[U][kChu
 }
 
 // Logprobs / entropy forward: one workgroup per row.
-template <int BLOCK, int U, typename T, int HEAD, int CAP, bool ALIGNED>
+template <int BLOCK, int U, typename T, int HEAD, int CAP, bool ALIGNED, bool NT>
 __global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void fwd1_kernel(FwdParams p) {
     using S = typename T::storage;
     constexpr bool WITH_W = HEAD == kHeadEntropy;
@@ -195,7 +195,7 @@ __global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void fwd1_kernel(FwdParams p) 
             if (t0 >= p.v0 && t0 < p.v0 + p.V) xt0 = load_one(x + (t0 - p.v0));
         }
         Stat1 st = stat1_init<FIX>();
-        for_each_group<BLOCK, U, S, CAP, ALIGNED, kFwdPipe>(
+        for_each_group<BLOCK, U, S, CAP, ALIGNED, kFwdPipe, NT>(
             x, p.V, ca,
             [&](int64_t, bool full, const float (&a)[U][kChunk]) {
                 if (full)
@@ -262,7 +262,7 @@ __global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void fwd1_kernel(FwdParams p) 
 }
 
 // KL forward (either direction): one workgroup per row pair.
-template <int BLOCK, int U, typename T, bool REVERSE, int CAPA, int CAPB, bool ALIGNED>
+template <int BLOCK, int U, typename T, bool REVERSE, int CAPA, int CAPB, bool ALIGNED, bool NT>
 __global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void fwdkl_kernel(FwdParams p) {
     constexpr bool FIXA = CAPA == kCapFixed, FIXB = CAPB == kCapFixed;
     using S = typename T::storage;
@@ -274,7 +274,7 @@ __global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void fwdkl_kernel(FwdParams p)
         const S* __restrict__ xa = static_cast<const S*>(p.x) + p.mx.offset(row);
         const S* __restrict__ xb = static_cast<const S*>(p.y) + p.my.offset(row);
         StatKL st = statkl_init<REVERSE, FIXA, FIXB>();
-        for_each_group2<BLOCK, U, S, CAPA, CAPB, ALIGNED, kFwdPipe>(
+        for_each_group2<BLOCK, U, S, CAPA, CAPB, ALIGNED, kFwdPipe, NT>(
             xa, xb, p.V, CapArgs{p.kx, p.ix}, CapArgs{p.ky, p.iy},
             [&](int64_t, bool, const float (&a)[U][kChunk], const float (&b)[U][kChunk]) {
                 update_kl<U, REVERSE, FIXA, FIXB>(st, a, b, p.scx, p.scy);
@@ -300,7 +300,7 @@ __global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void fwdkl_kernel(FwdParams p)
 
 // Both KL directions from one read of the pair: reverse KL to out / stats,
 // forward KL to out2 / stats2, each bit-identical to its one-direction call.
-template <int BLOCK, int U, typename T, int CAPA, int CAPB, bool ALIGNED>
+template <int BLOCK, int U, typename T, int CAPA, int CAPB, bool ALIGNED, bool NT>
 __global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void fwdkl2_kernel(FwdParams p) {
     constexpr bool FIXA = CAPA == kCapFixed, FIXB = CAPB == kCapFixed;
     using S = typename T::storage;
@@ -313,7 +313,7 @@ __global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void fwdkl2_kernel(FwdParams p
         const S* __restrict__ xa = static_cast<const S*>(p.x) + p.mx.offset(row);
         const S* __restrict__ xb = static_cast<const S*>(p.y) + p.my.offset(row);
         StatKL2 st = statkl2_init<FIXA, FIXB>();
-        for_each_group2<BLOCK, U, S, CAPA, CAPB, ALIGNED, kFwdPipe>(
+        for_each_group2<BLOCK, U, S, CAPA, CAPB, ALIGNED, kFwdPipe, NT>(
             xa, xb, p.V, CapArgs{p.kx, p.ix}, CapArgs{p.ky, p.iy},
             [&](int64_t, bool, const float (&a)[U][kChunk], const float (&b)[U][kChunk]) {
                 update_kl2<U, FIXA, FIXB>(st, a, b, p.scx, p.scy);
@@ -338,28 +338,28 @@ __global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void fwdkl2_kernel(FwdParams p
 
 // ------------------------------------------------------------- dispatch
 
-template <typename T, int CAPX, int CAPY, bool AL>
+template <typename T, int CAPX, int CAPY, bool AL, bool NT>
 inline hipError_t fwd_dispatch_head(int head, const FwdParams& p, hipStream_t s) {
     const dim3 grid(row_grid(p.N)), block(kBlock);
     switch (head) {
         case kHeadLogp:
-            hipLaunchKernelGGL((fwd1_kernel<kBlock, kUnroll1, T, kHeadLogp, CAPX, AL>), grid,
+            hipLaunchKernelGGL((fwd1_kernel<kBlock, kUnroll1, T, kHeadLogp, CAPX, AL, NT>), grid,
                                block, 0, s, p);
             break;
         case kHeadEntropy:
-            hipLaunchKernelGGL((fwd1_kernel<kBlock, kUnroll1, T, kHeadEntropy, CAPX, AL>), grid,
+            hipLaunchKernelGGL((fwd1_kernel<kBlock, kUnroll1, T, kHeadEntropy, CAPX, AL, NT>), grid,
                                block, 0, s, p);
             break;
         case kHeadKLReverse:
-            hipLaunchKernelGGL((fwdkl_kernel<kBlock, kUnrollKL, T, true, CAPX, CAPY, AL>), grid,
+            hipLaunchKernelGGL((fwdkl_kernel<kBlock, kUnrollKL, T, true, CAPX, CAPY, AL, NT>), grid,
                                block, 0, s, p);
             break;
         case kHeadKLForward:
-            hipLaunchKernelGGL((fwdkl_kernel<kBlock, kUnrollKL, T, false, CAPX, CAPY, AL>), grid,
+            hipLaunchKernelGGL((fwdkl_kernel<kBlock, kUnrollKL, T, false, CAPX, CAPY, AL, NT>), grid,
                                block, 0, s, p);
             break;
         case kHeadKLBoth:
-            hipLaunchKernelGGL((fwdkl2_kernel<kBlock, kUnrollKL, T, CAPX, CAPY, AL>), grid, block,
+            hipLaunchKernelGGL((fwdkl2_kernel<kBlock, kUnrollKL, T, CAPX, CAPY, AL, NT>), grid, block,
                                0, s, p);
             break;
         default:
@@ -368,10 +368,15 @@ inline hipError_t fwd_dispatch_head(int head, const FwdParams& p, hipStream_t s)
     return hipGetLastError();
 }
 
+// Rows that are not 16-byte aligned read every element with ordinary loads,
+// so only aligned rows choose between streaming and cached loads.
 template <typename T, int CAPX, int CAPY>
 inline hipError_t fwd_dispatch_al(int head, bool al, const FwdParams& p, hipStream_t s) {
-    return al ? fwd_dispatch_head<T, CAPX, CAPY, true>(head, p, s)
-              : fwd_dispatch_head<T, CAPX, CAPY, false>(head, p, s);
+    if (!al) return fwd_dispatch_head<T, CAPX, CAPY, false, true>(head, p, s);
+    const bool kl = head == kHeadKLReverse || head == kHeadKLForward || head == kHeadKLBoth;
+    return stream_reads(p.N, p.V, T::kBytes, kl ? 2 : 1)
+               ? fwd_dispatch_head<T, CAPX, CAPY, true, true>(head, p, s)
+               : fwd_dispatch_head<T, CAPX, CAPY, true, false>(head, p, s);
 }
 
 template <typename T, int CAPX>

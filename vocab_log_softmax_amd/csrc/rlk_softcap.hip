@@ -26,7 +26,7 @@ __global__ __launch_bounds__(kCapBlock) void softcap_fwd_kernel(const void* xv, 
         const int64_t i0 = ch * kChunk;
         float f[kChunk];
         if (ALIGNED && i0 + kChunk <= n) {
-            load_chunk(x + i0, f);
+            load_chunk<true>(x + i0, f);
 #pragma unroll
             for (int e = 0; e < kChunk; ++e) {
                 float s;
@@ -55,8 +55,8 @@ __global__ __launch_bounds__(kCapBlock) void softcap_bwd_kernel(const void* xv, 
         const int64_t i0 = ch * kChunk;
         float f[kChunk], g[kChunk];
         if (ALIGNED && i0 + kChunk <= n) {
-            load_chunk(x + i0, f);
-            load_chunk(gy + i0, g);
+            load_chunk<true>(x + i0, f);
+            load_chunk<true>(gy + i0, g);
 #pragma unroll
             for (int e = 0; e < kChunk; ++e) {
                 float s;
