@@ -92,18 +92,20 @@ def test_batch_invariance(dev, V):
         assert_bitwise(full[k][5:6], single[k], f"single row {k}")
 
 
-def test_batch_invariance_across_load_policy(dev):
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.float16],
+                         ids=["f32", "bf16", "f16"])
+def test_batch_invariance_across_load_policy(dev, dtype):
     # Operands above 256 MiB are read with non-temporal loads, smaller ones
     # with ordinary loads; the rows of a large batch and of a small subset of
     # it must still agree bit for bit.
-    N, V = 1100, 131072                    # bf16: 288 MB per tensor
+    N, V = 1100, 131072                    # 288 MB per tensor in 16 bits
     g = torch.Generator(device=dev).manual_seed(11)
-    x = (torch.randn(N, V, generator=g, device=dev) * 4).to(torch.bfloat16)
-    ref = (x.float() + torch.randn(N, V, generator=g, device=dev) * 0.5).to(torch.bfloat16)
+    x = (torch.randn(N, V, generator=g, device=dev) * 4).to(dtype)
+    ref = (x.float() + torch.randn(N, V, generator=g, device=dev) * 0.5).to(dtype)
     t = torch.randint(0, V, (N, 3), generator=g, device=dev)
     g_t = torch.randn(N, 3, generator=g, device=dev)
     g_r = torch.randn(N, generator=g, device=dev)
-    sub = torch.arange(0, N, 17, device=dev)  # 65 rows: 17 MB
+    sub = torch.arange(0, N, 17, device=dev)  # 65 rows: 17 MB in 16 bits
     for cap in (0.0, 30.0):
         full = run_all(x, ref, t, g_t, g_r, cap)
         part = run_all(x[sub].contiguous(), ref[sub].contiguous(), t[sub].contiguous(),
