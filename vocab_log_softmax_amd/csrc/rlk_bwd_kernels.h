@@ -29,6 +29,9 @@ namespace rlk {
 
 // Lanes that sum the upstream gradient of the k slots (fixed tree).
 constexpr int kGLanes = 256;
+// Longest per-piece slot list that bwd_wide_kernel searches entry by entry;
+// a longer one is sorted first.
+constexpr int kWideScanMax = 16;
 
 // Row modes.
 enum : int { kModeNormal = 0, kModeZero = 1, kModeNaN = 2, kModeMismatch = 3 };
@@ -467,10 +470,13 @@ __global__ __launch_bounds__(BLOCK) void bwd_piece_kernel(BwdParams p, int64_t r
 // (ballot ranks, per-wave offsets) and marked in a bitmap of one byte per
 // chunk; a lane whose chunk has a marked column sums that column's slots from
 // the list in slot order (bwd_topk_kernel's one-hot sum) and writes the
-// target gradient in place of the bulk value.  Every column is computed once
-// and stored once, the data loads are issued first, and the piece exits after
-// its stores: the slot work (k 12-byte records, mostly from L2) is spread
-// over 4 KB U of logits.
+// target gradient in place of the bulk value.  A short list is searched entry
+// by entry; a long one (a small V puts many targets in one piece) is sorted by
+// (column, slot) first, and each marked chunk starts at its first key, so a
+// column costs a few reads instead of a pass over the list.  Every column is
+// computed once and stored once, the data loads are issued first, and the
+// piece exits after its stores: the slot work (k 12-byte records, mostly from
+// L2) is spread over 4 KB U of logits.
 // FULL: every chunk of the piece lies inside an aligned row, so its loads are
 // raw 16-byte vectors issued back to back without branches (tail_values'
 // per-chunk branches would make the compiler wait for each load in turn).
@@ -485,6 +491,11 @@ __device__ __forceinline__ void wide_piece(const BwdParams& p, int64_t row, int6
     // per step measured slower: the kernel then needs 88 VGPRs instead of 80,
     // 5 waves per SIMD instead of 6)
     __shared__ __align__(16) int2 list[kGLanes];
+    // A list longer than kWideScanMax entries (many targets per piece: a small
+    // V or a large k) is searched through its keys (column << 16 | list
+    // index) sorted in LDS and the first sorted position of each marked chunk.
+    __shared__ uint32_t skey[kGLanes];
+    __shared__ uint16_t cstart[PC];
     __shared__ float red_g[NW], red_n[NW];
     __shared__ int red_c[NW];
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -553,6 +564,34 @@ __device__ __forceinline__ void wide_piece(const BwdParams& p, int64_t row, int6
     }
     if (tid >= total && tid < ((total + 3) & ~3)) list[tid] = make_int2(-1, 0);
     if (total > 0) __syncthreads();  // uniform: the list and bitmap are complete
+    const bool sorted = total > kWideScanMax;  // uniform
+    if (sorted) {
+        int pad = 2;
+        while (pad < total) pad <<= 1;
+        if (tid < pad)
+            skey[tid] = tid < total ? (static_cast<uint32_t>(list[tid].x) << 16) |
+                                          static_cast<uint32_t>(tid)
+                                    : 0xffffffffu;
+        for (int size = 2; size <= pad; size <<= 1) {
+            for (int stride = size >> 1; stride > 0; stride >>= 1) {
+                __syncthreads();
+                if (tid < pad / 2) {
+                    const int lo = 2 * tid - (tid & (stride - 1)), hi = lo + stride;
+                    const uint32_t ka = skey[lo], kb = skey[hi];
+                    if ((ka > kb) == ((lo & size) == 0)) {
+                        skey[lo] = kb;
+                        skey[hi] = ka;
+                    }
+                }
+            }
+        }
+        __syncthreads();
+        if (tid < total) {
+            const uint32_t c = skey[tid] >> 19;  // chunk of the key's column
+            if (tid == 0 || (skey[tid - 1] >> 19) != c) cstart[c] = static_cast<uint16_t>(tid);
+        }
+        __syncthreads();
+    }
     const int mode = n == 0.0f ? kModeZero : ((rs.flags & kFlagEmptyA) ? kModeNaN : kModeNormal);
     if (FULL) raw_unpack(raw, x);
 
@@ -565,30 +604,46 @@ __device__ __forceinline__ void wide_piece(const BwdParams& p, int64_t row, int6
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int ci = u * BLOCK + tid;
-            float a[kChunk], s4[kChunk];
 #pragma unroll
             for (int e = 0; e < kChunk; ++e) {
-                a[e] = cap_value_slope<CAPA>(x[u][e], ca, s4[e]);
-                v[u][e] = grad_elem<kHeadLogp, CAPA>(a[e], s4[e], 0.0f, rs, A, B, p.scx, p.scy);
+                float s4;
+                const float a = cap_value_slope<CAPA>(x[u][e], ca, s4);
+                v[u][e] = grad_elem<kHeadLogp, CAPA>(a, s4, 0.0f, rs, A, B, p.scx, p.scy);
             }
+            // (a target column takes its statistic input and slope again
+            // from x: keeping them for all 8 columns costs registers)
             const uint32_t mark = total > 0 ? (bits[ci >> 2] >> ((ci & 3) * 8)) & 0xffu : 0u;
             if (mark) {  // rare: a target column in this chunk
                 for (int e = 0; e < kChunk; ++e) {
                     if (!(mark & (1u << e))) continue;
                     const int col = ci * kChunk + e;
-                    // the matching slots' g in slot order; adding +0 for the
-                    // others leaves every partial sum's bits unchanged (h
-                    // starts at +0 and a sum is never -0 in round-to-nearest)
                     float h = 0.0f;
-                    const int4* l4 = reinterpret_cast<const int4*>(list);
-                    for (int j = 0; j < total; j += 4) {
-                        const int4 l0 = l4[j >> 1], l1 = l4[(j >> 1) + 1];
-                        h += l0.x == col ? __int_as_float(l0.y) : 0.0f;
-                        h += l0.z == col ? __int_as_float(l0.w) : 0.0f;
-                        h += l1.x == col ? __int_as_float(l1.y) : 0.0f;
-                        h += l1.z == col ? __int_as_float(l1.w) : 0.0f;
+                    if (sorted) {
+                        // the chunk's keys follow cstart in (column, slot)
+                        // order: the column's g are summed in slot order
+                        for (int r = cstart[ci]; r < total; ++r) {
+                            const uint32_t key = skey[r];
+                            const int kc = static_cast<int>(key >> 16);
+                            if (kc > col) break;
+                            if (kc == col) h += __int_as_float(list[key & 0xffffu].y);
+                        }
+                    } else {
+                        // the matching slots' g in slot order; adding +0 for
+                        // the others leaves every partial sum's bits unchanged
+                        // (h starts at +0 and a sum is never -0 in
+                        // round-to-nearest)
+                        const int4* l4 = reinterpret_cast<const int4*>(list);
+                        for (int j = 0; j < total; j += 4) {
+                            const int4 l0 = l4[j >> 1], l1 = l4[(j >> 1) + 1];
+                            h += l0.x == col ? __int_as_float(l0.y) : 0.0f;
+                            h += l0.z == col ? __int_as_float(l0.w) : 0.0f;
+                            h += l1.x == col ? __int_as_float(l1.y) : 0.0f;
+                            h += l1.z == col ? __int_as_float(l1.w) : 0.0f;
+                        }
                     }
-                    v[u][e] = target_grad<CAPA>(a[e], s4[e], cf, rs, G, h, p.scx);
+                    float s4;
+                    const float a = cap_value_slope<CAPA>(x[u][e], ca, s4);
+                    v[u][e] = target_grad<CAPA>(a, s4, cf, rs, G, h, p.scx);
                 }
             }
         }
@@ -605,13 +660,28 @@ __device__ __forceinline__ void wide_piece(const BwdParams& p, int64_t row, int6
 }
 
 template <int U, typename T, int CAPA, bool ALIGNED, bool NT>
-__global__ __launch_bounds__(kGLanes) void bwd_wide_kernel(BwdParams p, int64_t rbase) {
+__device__ __forceinline__ void wide_pieces(const BwdParams& p, int64_t rbase) {
     const int64_t row = p.N - 1 - (rbase + static_cast<int64_t>(blockIdx.y));
     const int64_t g0 = static_cast<int64_t>(blockIdx.x) * (kGLanes * U);
     if (ALIGNED && g0 + kGLanes * U <= p.V / kChunk)
         wide_piece<U, T, CAPA, ALIGNED, true, NT>(p, row, g0);
     else
         wide_piece<U, T, CAPA, ALIGNED, false, NT>(p, row, g0);
+}
+
+// Rows with 16-byte aligned starts: held to 80 VGPRs (six waves per SIMD; the
+// compiler's 81 leave five, and top-256 logprobs then measured 4% slower,
+// against 0.6% for the one spilled register).
+template <int U, typename T, int CAPA, bool NT>
+__global__ __launch_bounds__(kGLanes) __attribute__((amdgpu_waves_per_eu(6))) void bwd_wide_kernel(
+    BwdParams p, int64_t rbase) {
+    wide_pieces<U, T, CAPA, true, NT>(p, rbase);
+}
+
+// Other rows (element loads) keep the registers they need.
+template <int U, typename T, int CAPA, bool NT>
+__global__ __launch_bounds__(kGLanes) void bwd_wide_kernel_unaligned(BwdParams p, int64_t rbase) {
+    wide_pieces<U, T, CAPA, false, NT>(p, rbase);
 }
 
 // ------------------------------------------------------------- dispatch
@@ -654,8 +724,12 @@ inline hipError_t bwd_wide_launch(const BwdParams& p, hipStream_t s) {
     for (int64_t r0 = 0; r0 < p.N; r0 += kPieceRowsPerLaunch) {
         const int64_t rows = p.N - r0 < kPieceRowsPerLaunch ? p.N - r0 : kPieceRowsPerLaunch;
         const dim3 grid(static_cast<unsigned>(pieces), static_cast<unsigned>(rows));
-        hipLaunchKernelGGL((bwd_wide_kernel<kBwdWideUnroll, T, CAPX, AL, NT>), grid, dim3(kGLanes), 0,
-                           s, p, r0);
+        if constexpr (AL)
+            hipLaunchKernelGGL((bwd_wide_kernel<kBwdWideUnroll, T, CAPX, NT>), grid, dim3(kGLanes),
+                               0, s, p, r0);
+        else
+            hipLaunchKernelGGL((bwd_wide_kernel_unaligned<kBwdWideUnroll, T, CAPX, NT>), grid,
+                               dim3(kGLanes), 0, s, p, r0);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
