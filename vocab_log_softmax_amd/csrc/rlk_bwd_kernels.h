@@ -326,6 +326,17 @@ __device__ __forceinline__ void piece(const BwdParams& p, int64_t row, int64_t g
     RawGroup<S, U> rx, ry;
     const CapArgs cb{p.ky, p.iy};
     const S* __restrict__ xb = KL ? static_cast<const S*>(p.y) + p.my.offset(row) : nullptr;
+    // A tail piece reads the row's record and upstream gradient first: its
+    // logit loads end in waits (tail_values), and the record's loads would
+    // otherwise each add a round trip after them (the tail piece then took
+    // three times as long as a full one).  Full pieces read them after the
+    // logits, as scalar loads that overlap the logits' latency.
+    RowStats rs;
+    float g_row = 0.0f;
+    if (!FULL) {
+        rs = stats[row];
+        if (HEAD != kHeadLogp) g_row = p.g[row];
+    }
     if (FULL) {
         raw_load<BLOCK, U, NT>(xa, g0, rx);
         if (KL) raw_load<BLOCK, U, NT>(xb, g0, ry);
@@ -336,7 +347,10 @@ __device__ __forceinline__ void piece(const BwdParams& p, int64_t row, int64_t g
     const CapArgs ca{p.kx, p.ix, p.spx};
     const float cf = slope_factor<CAPA>(ca);
 
-    RowStats rs = stats[row];
+    if (FULL) {
+        rs = stats[row];
+        if (HEAD != kHeadLogp) g_row = p.g[row];
+    }
     if (KL && p.swap) swap_sides(rs);
     fixed_refs<CAPA, CAPB, KL>(rs);
 
@@ -390,9 +404,14 @@ __device__ __forceinline__ void piece(const BwdParams& p, int64_t row, int64_t g
         if (KL) fast_values<U, S, CAPB>(ry, cb, b);
     }
 
+    // Entropy and KL compute the bulk values for every row and replace them
+    // afterwards in the rare rows that need others: their mode comes from the
+    // record's flags alone, and with a mode branch around the computation the
+    // compiler moved the logits' loads into it, behind a wait for the flags.
+    // (Logprobs' mode also needs the slots, which are read after the logits.)
+    constexpr bool UNCOND = HEAD != kHeadLogp;
     float v[U][kChunk];
-    if (mode == kModeNormal) {
-        const float g_row = (HEAD == kHeadLogp) ? 0.0f : p.g[row];
+    if (UNCOND || mode == kModeNormal) {
         float A, B;
         row_coeffs<HEAD, CAPA>(rs, G, g_row, cf, A, B);
 #pragma unroll
@@ -428,13 +447,14 @@ __device__ __forceinline__ void piece(const BwdParams& p, int64_t row, int64_t g
                 }
             }
         }
-    } else if (mode == kModeMismatch) {
+    }
+    if (mode == kModeMismatch) {
 #pragma unroll
         for (int u = 0; u < U; ++u)
 #pragma unroll
             for (int e = 0; e < kChunk; ++e)
                 v[u][e] = (CAPA == kCapNone && x[u][e] == neg_inf()) ? 0.0f : qnan();
-    } else {
+    } else if (mode != kModeNormal) {
         const float fill = mode == kModeZero ? 0.0f : qnan();
 #pragma unroll
         for (int u = 0; u < U; ++u)
