@@ -106,8 +106,8 @@ def test_logp_target_on_masked_column(dev, orc):
 
 
 @pytest.mark.parametrize("dtype", DTYPES, ids=DT_IDS)
-@pytest.mark.parametrize("V,k", [(7, 4), (255, 17), (4097, 64), (32768, 256), (2000, 300),
-                                 (20000, 1024), (3000, 4096)])
+@pytest.mark.parametrize("V,k", [(7, 4), (255, 17), (4097, 64), (14000, 64), (32768, 256),
+                                 (2000, 300), (20000, 1024), (3000, 4096)])
 @pytest.mark.parametrize("cap", [0.0, 20.0, 60.0])
 def test_logp_topk(dev, orc, dtype, V, k, cap):
     N = 9

@@ -311,8 +311,9 @@ constexpr int kPieceMaxK = 4;
 // every lane: G is summed in the association of bwd_topk_kernel's tree, and
 // target columns take target_grad, so all backward kernels give the same bits.
 template <int BLOCK, int U, typename T, int HEAD, int CAPA, int CAPB, bool ALIGNED, bool FULL,
-          bool NT>
-__device__ __forceinline__ void piece(const BwdParams& p, int64_t row, int64_t g0) {
+          bool NT, bool CUT = false>
+__device__ __forceinline__ void piece(const BwdParams& p, int64_t row, int64_t g0,
+                                      int64_t cut = 0) {
     using S = typename T::storage;
     constexpr bool KL = HEAD == kHeadKLReverse || HEAD == kHeadKLForward;
     const int64_t nfull = p.V / kChunk;
@@ -461,12 +462,13 @@ __device__ __forceinline__ void piece(const BwdParams& p, int64_t row, int64_t g
 #pragma unroll
             for (int e = 0; e < kChunk; ++e) v[u][e] = fill;
     }
+    const uint32_t skip = CUT ? static_cast<uint32_t>(cut - g0) : 0u;
     if (FULL && p.wt)
-        store_piece<BLOCK, U, S, kCpolWriteThrough>(gx + g0 * kChunk, v);
+        store_piece<BLOCK, U, S, kCpolWriteThrough, CUT>(gx + g0 * kChunk, v, skip);
     else if (FULL)
-        store_piece<BLOCK, U, S, kCpolStream>(gx + g0 * kChunk, v);
+        store_piece<BLOCK, U, S, kCpolStream, CUT>(gx + g0 * kChunk, v, skip);
     else
-        store_group<BLOCK, U, S, ALIGNED>(gx, p.V, g0, false, v);
+        store_group<BLOCK, U, S, ALIGNED, CUT>(gx, p.V, g0, false, v, cut);
 }
 
 // grid (pieces of a row, rows): consecutive workgroups take consecutive
@@ -480,6 +482,19 @@ __global__ __launch_bounds__(BLOCK) void bwd_piece_kernel(BwdParams p, int64_t r
         piece<BLOCK, U, T, HEAD, CAPA, CAPB, ALIGNED, true, NT>(p, row, g0);
     else
         piece<BLOCK, U, T, HEAD, CAPA, CAPB, ALIGNED, false, NT>(p, row, g0);
+}
+
+// The last piece of each row (one workgroup per row, grid (1, rows)), moved
+// back to end at the row's end: it takes the full-piece path, recomputes the
+// columns it shares with the piece before it and stores only its own.  Used
+// for aligned rows of whole chunks whose tail is at least half a piece (see
+// last_piece_apart).
+template <int BLOCK, int U, typename T, int HEAD, int CAPA, int CAPB, bool NT>
+__global__ __launch_bounds__(BLOCK) void bwd_last_piece_kernel(BwdParams p, int64_t rbase) {
+    const int64_t row = p.N - 1 - (rbase + static_cast<int64_t>(blockIdx.y));
+    const int64_t nfull = p.V / kChunk;
+    const int64_t cut = nfull / (BLOCK * U) * (BLOCK * U);
+    piece<BLOCK, U, T, HEAD, CAPA, CAPB, true, true, NT, true>(p, row, nfull - BLOCK * U, cut);
 }
 
 // Logprobs with kPieceMaxK < k <= kGLanes: one-shot pieces of kGLanes lanes
@@ -500,8 +515,9 @@ __global__ __launch_bounds__(BLOCK) void bwd_piece_kernel(BwdParams p, int64_t r
 // FULL: every chunk of the piece lies inside an aligned row, so its loads are
 // raw 16-byte vectors issued back to back without branches (tail_values'
 // per-chunk branches would make the compiler wait for each load in turn).
-template <int U, typename T, int CAPA, bool ALIGNED, bool FULL, bool NT>
-__device__ __forceinline__ void wide_piece(const BwdParams& p, int64_t row, int64_t g0) {
+template <int U, typename T, int CAPA, bool ALIGNED, bool FULL, bool NT, bool CUT = false>
+__device__ __forceinline__ void wide_piece(const BwdParams& p, int64_t row, int64_t g0,
+                                           int64_t cut = 0) {
     using S = typename T::storage;
     constexpr int BLOCK = kGLanes, NW = kGLanes / 64;
     constexpr int PC = BLOCK * U;  // chunks per piece
@@ -676,7 +692,7 @@ __device__ __forceinline__ void wide_piece(const BwdParams& p, int64_t row, int6
     }
     // (plain streaming stores: the sc1 policy of store_piece measured slower
     // for these 16 KB pieces)
-    store_group<BLOCK, U, S, ALIGNED>(gx, p.V, g0, FULL, v);
+    store_group<BLOCK, U, S, ALIGNED, CUT>(gx, p.V, g0, FULL, v, cut);
 }
 
 template <int U, typename T, int CAPA, bool ALIGNED, bool NT>
@@ -704,6 +720,16 @@ __global__ __launch_bounds__(kGLanes) void bwd_wide_kernel_unaligned(BwdParams p
     wide_pieces<U, T, CAPA, false, NT>(p, rbase);
 }
 
+// The last wide piece of each row, as bwd_last_piece_kernel.
+template <int U, typename T, int CAPA, bool NT>
+__global__ __launch_bounds__(kGLanes) __attribute__((amdgpu_waves_per_eu(6))) void
+bwd_wide_last_kernel(BwdParams p, int64_t rbase) {
+    const int64_t row = p.N - 1 - (rbase + static_cast<int64_t>(blockIdx.y));
+    const int64_t nfull = p.V / kChunk;
+    const int64_t cut = nfull / (kGLanes * U) * (kGLanes * U);
+    wide_piece<U, T, CAPA, true, true, NT, true>(p, row, nfull - kGLanes * U, cut);
+}
+
 // ------------------------------------------------------------- dispatch
 //
 // The backward is elementwise given the row record (and G has a fixed tree),
@@ -718,6 +744,21 @@ __global__ __launch_bounds__(kGLanes) void bwd_wide_kernel_unaligned(BwdParams p
 // Rows per piece launch (the grid's second dimension is limited to 65536).
 constexpr int64_t kPieceRowsPerLaunch = 65536;
 
+// Whether the last piece of each row (pc chunks per piece) runs apart, moved
+// back to end at the row's end (bwd_last_piece_kernel), in a second launch:
+// for aligned rows of whole chunks, fewer than 16 pieces long, whose tail is
+// at least half a piece, in a call of at least 64 MiB of logits.  The tail
+// path would cost about three full pieces (branching loads); with a shorter
+// tail the recomputed shared part, in a longer row or a smaller call the
+// second launch cost more than that (logprobs bf16 backward, k = 1
+// [16384, 32000]: 378 -> 332 us, k = 4: 482 -> 332 us; but [4096, 128256],
+// 62 pieces: 308 us either way, and fp32 [64, 32000]: 5.5 -> 8.4 us).
+inline bool last_piece_apart(bool aligned, int64_t N, int64_t V, int64_t esize, int64_t pc) {
+    const int64_t nfull = V / kChunk;
+    return aligned && V % kChunk == 0 && nfull >= pc && nfull / pc < 16 &&
+           2 * (nfull % pc) >= pc && N * V * esize >= (int64_t(64) << 20);
+}
+
 template <typename T, int HEAD, int CAPX, int CAPY, bool AL, bool NT>
 inline hipError_t bwd_piece_launch(const BwdParams& p0, hipStream_t s) {
     BwdParams p = p0;
@@ -725,14 +766,24 @@ inline hipError_t bwd_piece_launch(const BwdParams& p0, hipStream_t s) {
            kWriteThroughBytes;
     constexpr int U = kBwdPieceUnroll;
     constexpr int64_t pc = static_cast<int64_t>(kBwdPieceBlock) * U;
-    const int64_t pieces = ((p.V + kChunk - 1) / kChunk + pc - 1) / pc;
+    const bool apart = last_piece_apart(AL, p.N, p.V, T::kBytes, pc);
+    const int64_t pieces = apart ? p.V / kChunk / pc : ((p.V + kChunk - 1) / kChunk + pc - 1) / pc;
     for (int64_t r0 = 0; r0 < p.N; r0 += kPieceRowsPerLaunch) {
         const int64_t rows = p.N - r0 < kPieceRowsPerLaunch ? p.N - r0 : kPieceRowsPerLaunch;
         const dim3 grid(static_cast<unsigned>(pieces), static_cast<unsigned>(rows));
         hipLaunchKernelGGL((bwd_piece_kernel<kBwdPieceBlock, U, T, HEAD, CAPX, CAPY, AL, NT>), grid,
                            dim3(kBwdPieceBlock), 0, s, p, r0);
-        const hipError_t e = hipGetLastError();
+        hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
+        if constexpr (AL) {
+            if (apart) {
+                hipLaunchKernelGGL(
+                    (bwd_last_piece_kernel<kBwdPieceBlock, U, T, HEAD, CAPX, CAPY, NT>),
+                    dim3(1, static_cast<unsigned>(rows)), dim3(kBwdPieceBlock), 0, s, p, r0);
+                e = hipGetLastError();
+                if (e != hipSuccess) return e;
+            }
+        }
     }
     return hipSuccess;
 }
@@ -740,7 +791,8 @@ inline hipError_t bwd_piece_launch(const BwdParams& p0, hipStream_t s) {
 template <typename T, int CAPX, bool AL, bool NT>
 inline hipError_t bwd_wide_launch(const BwdParams& p, hipStream_t s) {
     constexpr int64_t pc = static_cast<int64_t>(kGLanes) * kBwdWideUnroll;
-    const int64_t pieces = ((p.V + kChunk - 1) / kChunk + pc - 1) / pc;
+    const bool apart = last_piece_apart(AL, p.N, p.V, T::kBytes, pc);
+    const int64_t pieces = apart ? p.V / kChunk / pc : ((p.V + kChunk - 1) / kChunk + pc - 1) / pc;
     for (int64_t r0 = 0; r0 < p.N; r0 += kPieceRowsPerLaunch) {
         const int64_t rows = p.N - r0 < kPieceRowsPerLaunch ? p.N - r0 : kPieceRowsPerLaunch;
         const dim3 grid(static_cast<unsigned>(pieces), static_cast<unsigned>(rows));
@@ -750,8 +802,17 @@ inline hipError_t bwd_wide_launch(const BwdParams& p, hipStream_t s) {
         else
             hipLaunchKernelGGL((bwd_wide_kernel_unaligned<kBwdWideUnroll, T, CAPX, NT>), grid,
                                dim3(kGLanes), 0, s, p, r0);
-        const hipError_t e = hipGetLastError();
+        hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
+        if constexpr (AL) {
+            if (apart) {
+                hipLaunchKernelGGL((bwd_wide_last_kernel<kBwdWideUnroll, T, CAPX, NT>),
+                                   dim3(1, static_cast<unsigned>(rows)), dim3(kGLanes), 0, s, p,
+                                   r0);
+                e = hipGetLastError();
+                if (e != hipSuccess) return e;
+            }
+        }
     }
     return hipSuccess;
 }

@@ -507,14 +507,19 @@ __device__ __forceinline__ void for_each_group2(const S* __restrict__ ra, const 
 // offsets.  Two policies are used (kCpolStream, kCpolWriteThrough below).
 constexpr int kCpolStream = 2;             // nt
 constexpr int kCpolWriteThrough = 16 | 2;  // sc1 | nt: system scope, streaming
-template <int BLOCK, int U, typename S, int CPOL>
-__device__ __forceinline__ void store_piece(S* __restrict__ piece, const float (&v)[U][kChunk]) {
+// With CUT, the first `skip` chunks of the piece are not stored: their offset
+// is the end of the buffer, where its range check drops the stores.
+template <int BLOCK, int U, typename S, int CPOL, bool CUT = false>
+__device__ __forceinline__ void store_piece(S* __restrict__ piece, const float (&v)[U][kChunk],
+                                            uint32_t skip = 0) {
     constexpr uint32_t kChunkBytes = kChunk * sizeof(S);
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        static_cast<void*>(piece), 0, BLOCK * U * kChunkBytes, 0x00020000);
+    constexpr uint32_t kBytes = BLOCK * U * kChunkBytes;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(static_cast<void*>(piece), 0, kBytes, 0x00020000);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const uint32_t off = (u * BLOCK + threadIdx.x) * kChunkBytes;
+        const uint32_t ci = u * BLOCK + threadIdx.x;
+        const uint32_t off = (!CUT || ci >= skip) ? ci * kChunkBytes : kBytes;
         if constexpr (sizeof(S) == 4) {
             const u32x4 a = {__float_as_uint(v[u][0]), __float_as_uint(v[u][1]),
                              __float_as_uint(v[u][2]), __float_as_uint(v[u][3])};
@@ -537,13 +542,15 @@ __device__ __forceinline__ void store_piece(S* __restrict__ piece, const float (
 // Store a group of results.  Full aligned groups use 16-byte stores; in
 // other groups, whole in-range chunks of an aligned row still do, and the
 // remaining elements are stored one by one (nothing beyond V is written).
-template <int BLOCK, int U, typename S, bool ALIGNED>
+// With CUT, chunks before `cut` are not stored.
+template <int BLOCK, int U, typename S, bool ALIGNED, bool CUT = false>
 __device__ __forceinline__ void store_group(S* __restrict__ row, int64_t V, int64_t g0, bool full,
-                                            const float (&v)[U][kChunk]) {
+                                            const float (&v)[U][kChunk], int64_t cut = 0) {
     const int64_t nfull = V / kChunk;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int64_t c = g0 + u * BLOCK + (int)threadIdx.x;
+        if (CUT && c < cut) continue;
         if (ALIGNED && (full || c < nfull)) {
             store_chunk(row + c * kChunk, v[u]);
         } else {
