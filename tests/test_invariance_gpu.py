@@ -115,6 +115,57 @@ def test_batch_invariance_across_load_policy(dev, dtype):
         del full, part
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "f16"])
+def test_cap_table_and_computed_odd_form_agree(dev, dtype):
+    # Under the fixed cap, long rows of 16-bit logits read their statistic
+    # inputs from an LDS table once a call has 1024 rows or more and compute
+    # them below that; fp32 logits always compute them.  Rows wide enough for
+    # the odd form in both heads (logprobs from 196608 columns), a call of
+    # 1030 rows (table kernel, aligned and misaligned), a 65-row subset and
+    # its fp32 copy (computed) must agree bit for bit, record and gradient
+    # included.
+    N, V = 1030, 196616
+    g = torch.Generator(device=dev).manual_seed(23)
+    x = (torch.randn(N, V, generator=g, device=dev) * 4).to(dtype)
+    x[3, :1000] = float("inf")
+    x[4, 5:9] = float("-inf")
+    t = torch.randint(0, V, (N, 3), generator=g, device=dev)
+    g_t = torch.randn(N, 3, generator=g, device=dev)
+    g_r = torch.randn(N, generator=g, device=dev)
+    sub = torch.arange(0, N, 16, device=dev)
+    buf = torch.empty(N * V + 1, dtype=dtype, device=dev)
+    xm = buf[1:].view(N, V)
+    xm.copy_(x)
+    cap = 20.0
+
+    def heads(xx, tt, gt, gr):
+        lp, st = rlk.logp_fwd(xx, tt, cap)
+        h, sh = rlk.entropy_fwd(xx, cap)
+        n = xx.shape[0]
+        out = {"logp": lp, "logp_rec": st.view(n, -1), "ent": h, "ent_rec": sh.view(n, -1),
+               "logp_grad": rlk.logp_bwd(xx, tt, gt, st, cap),
+               "ent_grad": rlk.entropy_bwd(xx, gr, sh, cap)}
+        torch.cuda.synchronize()
+        return out
+
+    full = heads(x, t, g_t, g_r)
+    mis = heads(xm, t, g_t, g_r)
+    for k in full:
+        assert_bitwise(mis[k], full[k], f"misaligned {k}")
+    del mis
+    part = heads(x[sub].contiguous(), t[sub].contiguous(), g_t[sub].contiguous(),
+                 g_r[sub].contiguous())
+    wide = heads(x[sub].float(), t[sub].contiguous(), g_t[sub].contiguous(),
+                 g_r[sub].contiguous())
+    for k in full:
+        assert_bitwise(full[k][sub], part[k], f"subset {k}")
+        if k.endswith("grad"):
+            assert_bitwise(part[k], wide[k].to(dtype), f"fp32 copy {k}")
+        else:
+            assert_bitwise(part[k], wide[k], f"fp32 copy {k}")
+    assert torch.isfinite(full["logp"][:5]).all() and torch.isfinite(full["ent"][:5]).all()
+
+
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.float16],
                          ids=["f32", "bf16", "f16"])
 @pytest.mark.parametrize("V,pad", [(4096, 8), (4099, 5), (151936, 64)])

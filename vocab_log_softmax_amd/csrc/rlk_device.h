@@ -187,12 +187,43 @@ struct CapArgs {
     float k;     // -2 log2(e) / c
     float isc;   // fixed form: 1 / sc
     float span;  // fixed form, backward: sc
+    const float* tab = nullptr;  // table forms: sc/2 + t(|x|) by 16-bit magnitude (LDS)
+    float half = 0.0f;           // odd forms: sc/2
 };
+
+// Table forms.  With w(x) = sc / (1 + 2^(-k x)), w(x) + w(-x) = sc, so
+// t(x) + sc/2 = sc/2 - w(x) is odd in x: its value at |x| with the sign bit
+// of x.  hi16 holds the 16-bit pattern in bits 31..16; a NaN pattern reads
+// a NaN entry, +-inf read +-sc/2.
+// The magnitude of m with the sign bit of s.
+__device__ __forceinline__ float with_sign(float m, uint32_t s) {
+    return __uint_as_float((s & 0x80000000u) | (__float_as_uint(m) & 0x7fffffffu));
+}
+__device__ __forceinline__ float tab_lookup(const float* tab, uint32_t hi16) {
+    return with_sign(tab[(hi16 >> 16) & 0x7fffu], hi16);
+}
+template <typename S>
+__device__ __forceinline__ float from_bits16(uint32_t b);
+template <>
+__device__ __forceinline__ float from_bits16<uint16_t>(uint32_t b) {
+    return __uint_as_float(b << 16);
+}
+template <>
+__device__ __forceinline__ float from_bits16<_Float16>(uint32_t b) {
+    return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(b)));
+}
 
 template <int CAP>
 __device__ __forceinline__ float cap_value(float x, CapArgs c) {
     if (CAP == kCapOnline) return rcp(1.0f + ex2(x * c.k));
     if (CAP == kCapFixed) return -rcp(__builtin_fmaf(ex2(-(x * c.k)), c.isc, c.isc));
+    if (CAP == kCapFixedOdd)
+        return with_sign(c.half + cap_value<kCapFixed>(fabsf(x), c), __float_as_uint(x));
+    // x is a bf16 / fp16 value widened to float: back to its 16-bit pattern
+    if (CAP == kCapTableB) return tab_lookup(c.tab, __float_as_uint(x));
+    if (CAP == kCapTableH)
+        return tab_lookup(c.tab, static_cast<uint32_t>(__builtin_bit_cast(
+                                     uint16_t, static_cast<_Float16>(x))) << 16);
     return x;
 }
 
@@ -271,13 +302,21 @@ struct RawGroup<_Float16, U> {
     u32x4 v[U];
 };
 
+// Lane of the calling thread among the BLOCK threads that walk one row (a
+// workgroup may walk several rows side by side, BLOCK threads each).
+template <int BLOCK>
+__device__ __forceinline__ int row_lane() {
+    static_assert((BLOCK & (BLOCK - 1)) == 0, "BLOCK must be a power of two");
+    return static_cast<int>(threadIdx.x) & (BLOCK - 1);
+}
+
 template <int BLOCK, int U, bool NT>
 __device__ __forceinline__ void raw_load(const uint16_t* __restrict__ row, int64_t g0,
                                          RawGroup<uint16_t, U>& r) {
 #pragma unroll
     for (int u = 0; u < U; ++u)
         r.v[u] = ld16<NT>(reinterpret_cast<const u32x4*>(
-            row + (g0 + u * BLOCK + (int)threadIdx.x) * kChunk));
+            row + (g0 + u * BLOCK + row_lane<BLOCK>()) * kChunk));
 }
 template <int BLOCK, int U, bool NT>
 __device__ __forceinline__ void raw_load(const _Float16* __restrict__ row, int64_t g0,
@@ -285,7 +324,7 @@ __device__ __forceinline__ void raw_load(const _Float16* __restrict__ row, int64
 #pragma unroll
     for (int u = 0; u < U; ++u)
         r.v[u] = ld16<NT>(reinterpret_cast<const u32x4*>(
-            row + (g0 + u * BLOCK + (int)threadIdx.x) * kChunk));
+            row + (g0 + u * BLOCK + row_lane<BLOCK>()) * kChunk));
 }
 template <int BLOCK, int U, bool NT>
 __device__ __forceinline__ void raw_load(const float* __restrict__ row, int64_t g0,
@@ -293,7 +332,7 @@ __device__ __forceinline__ void raw_load(const float* __restrict__ row, int64_t 
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const f32x4* p =
-            reinterpret_cast<const f32x4*>(row + (g0 + u * BLOCK + (int)threadIdx.x) * kChunk);
+            reinterpret_cast<const f32x4*>(row + (g0 + u * BLOCK + row_lane<BLOCK>()) * kChunk);
         r.v[u][0] = ld16<NT>(p);
         r.v[u][1] = ld16<NT>(p + 1);
     }
@@ -342,7 +381,7 @@ __device__ __forceinline__ void tail_values(const S* __restrict__ row, int64_t V
                                             int64_t g0, CapArgs ca, float (&a)[U][kChunk]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const int64_t c = g0 + u * BLOCK + (int)threadIdx.x;
+        const int64_t c = g0 + u * BLOCK + row_lane<BLOCK>();
         if (ALIGNED && c < nfull) {
             load_chunk<NT>(row + c * kChunk, a[u]);
             if (CAP != kCapNone) {
@@ -372,6 +411,20 @@ __device__ __forceinline__ void tail_values(const S* __restrict__ row, int64_t V
 template <int U, typename S, int CAP>
 __device__ __forceinline__ void fast_values(const RawGroup<S, U>& r, CapArgs ca,
                                             float (&a)[U][kChunk]) {
+    if constexpr (CAP == kCapTableB || CAP == kCapTableH) {
+        static_assert(sizeof(S) == 2, "table forms read 16-bit logits");
+        // straight from the packed words: element 2i in the low half
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint32_t ws[4] = {r.v[u].x, r.v[u].y, r.v[u].z, r.v[u].w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                a[u][2 * i] = tab_lookup(ca.tab, ws[i] << 16);
+                a[u][2 * i + 1] = tab_lookup(ca.tab, ws[i]);
+            }
+        }
+        return;
+    }
     raw_unpack(r, a);
     if (CAP != kCapNone) {
 #pragma unroll

@@ -172,13 +172,18 @@ __device__ __forceinline__ void update_kl2(StatKL2& st, const float (&a)[U][kChu
 }
 
 // Logprobs / entropy forward: one workgroup per row.
-template <int BLOCK, int U, typename T, int HEAD, int CAP, bool ALIGNED, bool NT>
+template <int BLOCK, int U, typename T, int HEAD, int CAP, bool ALIGNED, bool NT, bool ODD = false>
 __global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void fwd1_kernel(FwdParams p) {
     using S = typename T::storage;
     constexpr bool WITH_W = HEAD == kHeadEntropy;
     constexpr bool FIX = CAP == kCapFixed;
     constexpr bool CLAMP = WITH_W && CAP == kCapNone;  // full groups; tail groups always clamp
-    const CapArgs ca{p.kx, p.ix};
+    // ODD: the fixed form's statistics take the odd form (reference -sc/2),
+    // the same bits as fwd1_tab_kernel's table; targets keep the direct form
+    static_assert(!ODD || FIX, "the odd form is a form of the fixed cap");
+    constexpr int CAPS = ODD ? kCapFixedOdd : CAP;
+    CapArgs ca{p.kx, p.ix};
+    if (ODD) ca.half = 0.5f / p.ix;
     constexpr int NW = BLOCK / 64;
     __shared__ Stat1 red[NW];
     __shared__ float bc[2];
@@ -195,7 +200,8 @@ __global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void fwd1_kernel(FwdParams p) 
             if (t0 >= p.v0 && t0 < p.v0 + p.V) xt0 = load_one(x + (t0 - p.v0));
         }
         Stat1 st = stat1_init<FIX>();
-        for_each_group<BLOCK, U, S, CAP, ALIGNED, kFwdPipe, NT>(
+        if (ODD) st.mL = -ca.half;
+        for_each_group<BLOCK, U, S, CAPS, ALIGNED, kFwdPipe, NT>(
             x, p.V, ca,
             [&](int64_t, bool full, const float (&a)[U][kChunk]) {
                 if (full)
@@ -262,6 +268,122 @@ __global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void fwd1_kernel(FwdParams p) 
 }
 
 // KL forward (either direction): one workgroup per row pair.
+// Logprobs / entropy forward of 16-bit logits under the fixed-form cap.  A
+// 16-bit logit has 2^15 magnitudes and t(x) + sc/2 is odd in x (tab_lookup),
+// so a 128 KB LDS table of sc/2 + t(|x|), built once per workgroup, and the
+// logit's sign bit give every statistic input, shifted by sc/2 (reference
+// -sc/2), where the direct form spends an exponential, an FMA and a
+// reciprocal per logit.  Every path of the row walk (full, tail and
+// unaligned groups) reads the table, so a row's values do not depend on how
+// it is laid out or batched.  The table fills a CU's LDS: one workgroup of
+// kTabRows x BLOCK threads walks up to kTabRows rows side by side (rpw,
+// fewer when N is small so that the rows still spread over the CUs), each
+// row as fwd1_kernel walks it (its own BLOCK threads, waves and reduction),
+// so the bits do not depend on rpw.  The targets' values keep the direct
+// form (target_logp subtracts the record's reference).
+template <int U, typename T, int HEAD, bool ALIGNED, bool NT>
+__global__ __launch_bounds__(kTabRows* kBlock) void fwd1_tab_kernel(FwdParams p, int rpw) {
+    constexpr int BLOCK = kBlock;
+    using S = typename T::storage;
+    static_assert(sizeof(S) == 2, "table forms read 16-bit logits");
+    constexpr int TAB = std::is_same<S, uint16_t>::value ? kCapTableB : kCapTableH;
+    constexpr bool WITH_W = HEAD == kHeadEntropy;
+    constexpr int NW = BLOCK / 64;
+    __shared__ float tab[kTabSize];
+    __shared__ Stat1 red[kTabRows][NW];
+    __shared__ float bc[kTabRows][2];
+    const int sub = threadIdx.x / BLOCK, tid = threadIdx.x % BLOCK, lane = tid & 63,
+              wid = tid >> 6;
+    CapArgs cf{p.kx, p.ix};
+    const float half = 0.5f / p.ix;
+    cf.half = half;
+    // Where 2^(-k |x|) overflows (nearly half of the bf16 magnitudes) the
+    // direct form gives -1 / inf = -0 and the entry is exactly sc/2: those
+    // entries skip the exponential and the reciprocal (same bits).
+    for (int i = threadIdx.x; i < kTabSize; i += kTabRows * BLOCK) {
+        const float v = from_bits16<S>(static_cast<uint32_t>(i));
+        tab[i] = -(v * cf.k) >= 128.0f ? half : half + cap_value<kCapFixed>(v, cf);
+    }
+    CapArgs ct = cf;
+    ct.tab = tab;
+    __syncthreads();
+    RowStats* stats = static_cast<RowStats*>(p.stats);
+    for (int64_t base = static_cast<int64_t>(blockIdx.x) * rpw; base < p.N;
+         base += static_cast<int64_t>(gridDim.x) * rpw) {
+        const int64_t row = base + sub;
+        const bool live = sub < rpw && row < p.N;
+        const S* __restrict__ x = static_cast<const S*>(p.x) + p.mx.offset(live ? row : 0);
+        int64_t t0 = -1;
+        float xt0 = 0.0f;
+        if (live) {
+            if (HEAD == kHeadLogp && tid < p.k) {
+                t0 = p.targets[row * p.k + tid];
+                if (t0 >= p.v0 && t0 < p.v0 + p.V) xt0 = load_one(x + (t0 - p.v0));
+            }
+            Stat1 st{0.0f, -half, 0.0f, 0.0f};
+            for_each_group<BLOCK, U, S, TAB, ALIGNED, kFwdPipe, NT>(
+                x, p.V, ct, [&](int64_t, bool full, const float (&a)[U][kChunk]) {
+                    if (full)
+                        update1<U, WITH_W, false, true>(st, a, p.scx);
+                    else
+                        update1<U, WITH_W, WITH_W, true>(st, a, p.scx);
+                });
+            st = wave_reduce<WITH_W>(st);
+            if (lane == 0) red[sub][wid] = st;
+        }
+        __syncthreads();
+        if (live && tid == 0) {
+            Stat1 r = red[sub][0];
+#pragma unroll
+            for (int w = 1; w < NW; ++w) r = stat1_merge<WITH_W>(r, red[sub][w]);
+            if (p.part) {
+                static_cast<PartialRec*>(p.part)[row] = to_partial(r);
+            } else {
+                const RowStats rs = finalize1<WITH_W>(r);
+                if (HEAD == kHeadEntropy) p.out[row] = rs.value;
+                stats[row] = rs;
+                bc[sub][0] = rs.mLa;
+                bc[sub][1] = rs.log2Sa;
+            }
+        }
+        // A row's red / bc entries are written again only after the next
+        // pass's first barrier, which every reader of them has passed.
+        __syncthreads();
+        if (live && HEAD == kHeadLogp) {
+            RowStats rs;
+            rs.mLa = bc[sub][0];
+            rs.log2Sa = bc[sub][1];
+            for (int64_t j0 = tid; j0 < p.k; j0 += static_cast<int64_t>(BLOCK) * kTopkBatch) {
+                int64_t t[kTopkBatch];
+                float xv[kTopkBatch];
+#pragma unroll
+                for (int b = 0; b < kTopkBatch; ++b) {
+                    const int64_t j = j0 + static_cast<int64_t>(b) * BLOCK;
+                    t[b] = j == tid ? t0 : (j < p.k ? p.targets[row * p.k + j] : -1);
+                }
+#pragma unroll
+                for (int b = 0; b < kTopkBatch; ++b) {
+                    const int64_t j = j0 + static_cast<int64_t>(b) * BLOCK;
+                    const bool local = t[b] >= p.v0 && t[b] < p.v0 + p.V;
+                    xv[b] = j == tid ? xt0 : (local ? load_one(x + (t[b] - p.v0)) : 0.0f);
+                }
+#pragma unroll
+                for (int b = 0; b < kTopkBatch; ++b) {
+                    const int64_t j = j0 + static_cast<int64_t>(b) * BLOCK;
+                    if (j >= p.k) break;
+                    const bool local = t[b] >= p.v0 && t[b] < p.v0 + p.V;
+                    const float a = local ? cap_value<kCapFixed>(xv[b], cf) : 0.0f;
+                    if (p.part)
+                        p.tvals[row * p.k + j] = a;
+                    else
+                        p.out[row * p.k + j] =
+                            (t[b] >= 0 && t[b] < p.vtotal) ? target_logp(a, p.scx, rs) : 0.0f;
+                }
+            }
+        }
+    }
+}
+
 template <int BLOCK, int U, typename T, bool REVERSE, int CAPA, int CAPB, bool ALIGNED, bool NT>
 __global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void fwdkl_kernel(FwdParams p) {
     constexpr bool FIXA = CAPA == kCapFixed, FIXB = CAPB == kCapFixed;
@@ -338,17 +460,45 @@ __global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void fwdkl2_kernel(FwdParams p
 
 // ------------------------------------------------------------- dispatch
 
+// Logprobs / entropy forward.  Under the fixed cap, rows of at least
+// odd_form_min_cols(HEAD) columns take the odd form: 16-bit logits from the
+// LDS table once there are kTabRows rows per CU, else (and fp32) computed;
+// the two give the same bits, so the choice may follow N.  Which form a row
+// takes depends on its width, head and cap only, never on N or its layout.
+template <typename T, int HEAD, int CAP, bool AL, bool NT>
+inline void fwd1_launch(const FwdParams& p, hipStream_t s) {
+    const dim3 grid(row_grid(p.N)), block(kBlock);
+    if constexpr (CAP == kCapFixed) {
+        if (kUseCapTable && p.V >= odd_form_min_cols(HEAD)) {
+            if constexpr (T::kBytes == 2) {
+                if (p.N >= static_cast<int64_t>(kTabRows) * kTabGrid) {
+                    // rows per workgroup: kTabRows once every CU has a row
+                    const int64_t rpw64 = (p.N + kTabGrid - 1) / kTabGrid;
+                    const int rpw = static_cast<int>(rpw64 < kTabRows ? rpw64 : kTabRows);
+                    const int64_t wgs = (p.N + rpw - 1) / rpw;
+                    hipLaunchKernelGGL((fwd1_tab_kernel<kUnroll1, T, HEAD, AL, NT>),
+                                       dim3(static_cast<int>(wgs < kTabGrid ? wgs : kTabGrid)),
+                                       dim3(kTabRows * kBlock), 0, s, p, rpw);
+                    return;
+                }
+            }
+            hipLaunchKernelGGL((fwd1_kernel<kBlock, kUnroll1, T, HEAD, CAP, AL, NT, true>), grid,
+                               block, 0, s, p);
+            return;
+        }
+    }
+    hipLaunchKernelGGL((fwd1_kernel<kBlock, kUnroll1, T, HEAD, CAP, AL, NT>), grid, block, 0, s, p);
+}
+
 template <typename T, int CAPX, int CAPY, bool AL, bool NT>
 inline hipError_t fwd_dispatch_head(int head, const FwdParams& p, hipStream_t s) {
     const dim3 grid(row_grid(p.N)), block(kBlock);
     switch (head) {
         case kHeadLogp:
-            hipLaunchKernelGGL((fwd1_kernel<kBlock, kUnroll1, T, kHeadLogp, CAPX, AL, NT>), grid,
-                               block, 0, s, p);
+            fwd1_launch<T, kHeadLogp, CAPX, AL, NT>(p, s);
             break;
         case kHeadEntropy:
-            hipLaunchKernelGGL((fwd1_kernel<kBlock, kUnroll1, T, kHeadEntropy, CAPX, AL, NT>), grid,
-                               block, 0, s, p);
+            fwd1_launch<T, kHeadEntropy, CAPX, AL, NT>(p, s);
             break;
         case kHeadKLReverse:
             hipLaunchKernelGGL((fwdkl_kernel<kBlock, kUnrollKL, T, true, CAPX, CAPY, AL, NT>), grid,

@@ -29,6 +29,29 @@ enum Head : int {
 // 2 c log2(e) < kCapFixedMinScale: the fixed form's backward scales its slope
 // by 1 / (2 c log2(e))^2, which must stay far from overflow.
 enum CapMode : int { kCapNone = 0, kCapOnline = 1, kCapFixed = 2 };
+// Device-side forms of kCapFixed in the logprobs / entropy forward (never
+// passed in from the host): the statistic input is t + sc/2, odd in x, with
+// the reference at -sc/2 instead of 0 -- computed as sc/2 + t(|x|) with the
+// sign of x (kCapFixedOdd), or read from an LDS table of sc/2 + t(|x|) over
+// the 2^15 magnitudes of bf16 / fp16 bit patterns (fwd1_tab_kernel).  The
+// two give the same bits for the same value, whatever its dtype.
+enum CapFormMode : int { kCapTableB = 3, kCapTableH = 4, kCapFixedOdd = 5 };
+constexpr int kTabSize = 1 << 15;  // 16-bit magnitudes
+constexpr int kTabRows = 4;        // rows side by side in one table workgroup
+constexpr int kTabGrid = 256;      // table workgroups at most: one per CU
+#ifndef RLK_CAP_TABLE
+#define RLK_CAP_TABLE 1
+#endif
+constexpr bool kUseCapTable = RLK_CAP_TABLE != 0;
+// Row widths from which the fixed cap's logprobs / entropy forward takes the
+// odd form (measured on bf16 rows: the table kernel walks kTabRows rows in
+// lockstep per CU, which pays only for long rows; entropy spends more VALU
+// per logit than logprobs and gains from shorter rows on).
+constexpr int64_t kOddMinColsEntropy = 65536;
+constexpr int64_t kOddMinColsLogp = 196608;
+inline int64_t odd_form_min_cols(int head) {
+    return head == kHeadEntropy ? kOddMinColsEntropy : kOddMinColsLogp;
+}
 constexpr float kCapFixedMaxScale = 120.0f;
 constexpr float kCapFixedMinScale = 1.0f / 65536.0f;
 
