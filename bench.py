@@ -177,6 +177,22 @@ def time_softcap(name: str, dev, torch, reps: int = 50) -> dict:
     return out
 
 
+def fwd1_name(w, N, V, es):
+    """Which single-tensor forward kernel the library launches for this call.
+
+    Mirrors the dispatch rule: under the fixed-form cap (2 c log2 e within
+    [2^-16, 120]), rows of at least 65536 columns (entropy) or 196608
+    (logprobs) take the odd form, read from the LDS table for 16-bit logits
+    once the call has 1024 rows; only the kernel's name is taken from here.
+    """
+    sc = 2.0 * w.cap / math.log(2.0) if w.cap > 0 else 0.0
+    fixed = 2.0 ** -16 <= sc <= 120.0
+    min_cols = 65536 if w.head == "entropy" else 196608
+    if fixed and es == 2 and V >= min_cols and N >= 1024:
+        return "fwd1_tab_kernel"
+    return "fwd1_kernel"
+
+
 def side_bytes(w, N):
     """Per-step bytes of the per-row side arrays (targets, grads, outputs, stats)."""
     k = w.k
@@ -301,7 +317,7 @@ def main() -> int:
         fwd = rlk.prepare(rlk.rlk_logp_fwd, x, tg, w.cap, out, st)
         bwd = rlk.prepare(rlk.rlk_logp_bwd, x, tg, w.cap, st, g, gx)
         # k <= 4 slots: one-shot pieces; up to 256: wide pieces; wider: the row kernel
-        n_in, fwd_name = 1, "fwd1_kernel"
+        n_in, fwd_name = 1, fwd1_name(w, N, V, es)
         bwd_name = ("bwd_piece_kernel" if w.k <= 4 else
                     "bwd_wide_kernel" if w.k <= 256 else "bwd_topk_kernel")
     elif w.head == "entropy":
@@ -311,7 +327,7 @@ def main() -> int:
         gx = torch.empty_like(x)
         fwd = rlk.prepare(rlk.rlk_entropy_fwd, x, w.cap, out, st)
         bwd = rlk.prepare(rlk.rlk_entropy_bwd, x, w.cap, st, g, gx)
-        n_in, fwd_name, bwd_name = 1, "fwd1_kernel", "bwd_piece_kernel"
+        n_in, fwd_name, bwd_name = 1, fwd1_name(w, N, V, es), "bwd_piece_kernel"
     else:
         ref, g = d["ref"], d["grad"]
         out = torch.empty(N, dtype=torch.float32, device=dev)
