@@ -228,3 +228,66 @@ def test_shard_backward_equals_plain_backward_columns(dev):
         rlk.rlk_logp_bwd_shard(x[:, b0:b1], b0, V, t, 0.0, st, g, gs)
         torch.cuda.synchronize()
         assert torch.equal(_bits(gs), _bits(want[:, b0:b1])), (b0, b1)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "f16"])
+def test_table_forward_partials(dev, dtype):
+    # Shards wide enough for the fixed cap's odd form in both heads: in a
+    # call of 1030 rows the LDS-table forward writes the partial records, in
+    # a 65-row subset the computed form does.  Records, target inputs and
+    # combined heads agree bit for bit; one shard's combine equals the plain
+    # call bit for bit; two shards match the plain call.
+    N, W, k, cap = 1030, 196616, 3, 20.0
+    V = 2 * W
+    g = torch.Generator(device=dev).manual_seed(31)
+    x = (torch.randn(N, V, generator=g, device=dev) * 4).to(dtype)
+    t = torch.randint(-2, V + 2, (N, k), generator=g, device=dev)
+    bounds = [0, W, V]
+    sub = torch.arange(0, N, 16, device=dev)
+
+    def run(xx, tt):
+        n = xx.shape[0]
+        parts = rlk.new_partials(2, n, dev)
+        eparts = rlk.new_partials(2, n, dev)
+        tv = torch.empty(2, n, k, dtype=torch.float32, device=dev)
+        for s in range(2):
+            xs = xx[:, bounds[s]:bounds[s + 1]]
+            rlk.rlk_logp_fwd_partial(xs, bounds[s], V, tt, cap, parts[s], tv[s])
+            rlk.rlk_entropy_fwd_partial(xs, cap, eparts[s])
+        lp = torch.empty(n, k, dtype=torch.float32, device=dev)
+        st = rlk.new_stats(rlk.RLK_HEAD_LOGP, n, V, dev)
+        rlk.rlk_combine(rlk.RLK_HEAD_LOGP, 0, bounds, parts, tt, tv, cap, lp, st)
+        h = torch.empty(n, dtype=torch.float32, device=dev)
+        sh = rlk.new_stats(rlk.RLK_HEAD_ENTROPY, n, V, dev)
+        rlk.rlk_combine(rlk.RLK_HEAD_ENTROPY, 0, bounds, eparts, None, None, cap, h, sh)
+        torch.cuda.synchronize()
+        return {"parts": parts[:, :n * 32].reshape(2, n, 32), "eparts": eparts[:, :n * 32].reshape(2, n, 32),
+                "tv": tv, "lp": lp, "st": st.view(n, -1), "h": h, "sh": sh.view(n, -1)}
+
+    full = run(x, t)
+    part = run(x[sub].contiguous(), t[sub].contiguous())
+    for key in full:
+        a = full[key][:, sub] if key in ("parts", "eparts", "tv") else full[key][sub]
+        assert torch.equal(_bits(a), _bits(part[key])), key
+    lp0, _ = rlk.logp_fwd(x, t, cap)
+    h0, _ = rlk.entropy_fwd(x, cap)
+    torch.testing.assert_close(full["lp"], lp0, rtol=0, atol=2e-4)
+    torch.testing.assert_close(full["h"], h0, rtol=1e-5, atol=1e-5)
+    del full, part
+
+    x1 = x[:, :W].contiguous()
+    t1 = torch.randint(0, W, (N, k), generator=g, device=dev)
+    want_lp, want_st = rlk.logp_fwd(x1, t1, cap)
+    parts = rlk.new_partials(1, N, dev)
+    tv = torch.empty(1, N, k, dtype=torch.float32, device=dev)
+    rlk.rlk_logp_fwd_partial(x1, 0, W, t1, cap, parts[0], tv[0])
+    lp = torch.empty(N, k, dtype=torch.float32, device=dev)
+    st = rlk.new_stats(rlk.RLK_HEAD_LOGP, N, W, dev)
+    rlk.rlk_combine(rlk.RLK_HEAD_LOGP, 0, [0, W], parts, t1, tv, cap, lp, st)
+    assert torch.equal(_bits(lp), _bits(want_lp)) and torch.equal(_bits(st), _bits(want_st))
+    want_h, want_sh = rlk.entropy_fwd(x1, cap)
+    rlk.rlk_entropy_fwd_partial(x1, cap, parts[0])
+    h = torch.empty(N, dtype=torch.float32, device=dev)
+    sh = rlk.new_stats(rlk.RLK_HEAD_ENTROPY, N, W, dev)
+    rlk.rlk_combine(rlk.RLK_HEAD_ENTROPY, 0, [0, W], parts, None, None, cap, h, sh)
+    assert torch.equal(_bits(h), _bits(want_h)) and torch.equal(_bits(sh), _bits(want_sh))
