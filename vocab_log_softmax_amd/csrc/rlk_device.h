@@ -302,37 +302,40 @@ struct RawGroup<_Float16, U> {
     u32x4 v[U];
 };
 
-// Lane of the calling thread among the BLOCK threads that walk one row (a
-// workgroup may walk several rows side by side, BLOCK threads each).
-template <int BLOCK>
+// Lane of the calling thread among the BLOCK threads that walk one row.
+// MULTI: the workgroup walks several rows side by side, BLOCK threads each
+// (the table forward); otherwise the workgroup is BLOCK threads.
+template <int BLOCK, bool MULTI>
 __device__ __forceinline__ int row_lane() {
     static_assert((BLOCK & (BLOCK - 1)) == 0, "BLOCK must be a power of two");
-    return static_cast<int>(threadIdx.x) & (BLOCK - 1);
+    return MULTI ? static_cast<int>(threadIdx.x) & (BLOCK - 1) : static_cast<int>(threadIdx.x);
 }
+// The table forms run in the multi-row workgroup.
+constexpr bool multi_row(int CAP) { return CAP == kCapTableB || CAP == kCapTableH; }
 
-template <int BLOCK, int U, bool NT>
+template <int BLOCK, int U, bool NT, bool MULTI = false>
 __device__ __forceinline__ void raw_load(const uint16_t* __restrict__ row, int64_t g0,
                                          RawGroup<uint16_t, U>& r) {
 #pragma unroll
     for (int u = 0; u < U; ++u)
         r.v[u] = ld16<NT>(reinterpret_cast<const u32x4*>(
-            row + (g0 + u * BLOCK + row_lane<BLOCK>()) * kChunk));
+            row + (g0 + u * BLOCK + row_lane<BLOCK, MULTI>()) * kChunk));
 }
-template <int BLOCK, int U, bool NT>
+template <int BLOCK, int U, bool NT, bool MULTI = false>
 __device__ __forceinline__ void raw_load(const _Float16* __restrict__ row, int64_t g0,
                                          RawGroup<_Float16, U>& r) {
 #pragma unroll
     for (int u = 0; u < U; ++u)
         r.v[u] = ld16<NT>(reinterpret_cast<const u32x4*>(
-            row + (g0 + u * BLOCK + row_lane<BLOCK>()) * kChunk));
+            row + (g0 + u * BLOCK + row_lane<BLOCK, MULTI>()) * kChunk));
 }
-template <int BLOCK, int U, bool NT>
+template <int BLOCK, int U, bool NT, bool MULTI = false>
 __device__ __forceinline__ void raw_load(const float* __restrict__ row, int64_t g0,
                                          RawGroup<float, U>& r) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const f32x4* p =
-            reinterpret_cast<const f32x4*>(row + (g0 + u * BLOCK + row_lane<BLOCK>()) * kChunk);
+            reinterpret_cast<const f32x4*>(row + (g0 + u * BLOCK + row_lane<BLOCK, MULTI>()) * kChunk);
         r.v[u][0] = ld16<NT>(p);
         r.v[u][1] = ld16<NT>(p + 1);
     }
@@ -381,7 +384,7 @@ __device__ __forceinline__ void tail_values(const S* __restrict__ row, int64_t V
                                             int64_t g0, CapArgs ca, float (&a)[U][kChunk]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const int64_t c = g0 + u * BLOCK + row_lane<BLOCK>();
+        const int64_t c = g0 + u * BLOCK + row_lane<BLOCK, multi_row(CAP)>();
         if (ALIGNED && c < nfull) {
             load_chunk<NT>(row + c * kChunk, a[u]);
             if (CAP != kCapNone) {
@@ -454,15 +457,15 @@ __device__ __forceinline__ void for_each_group(const S* __restrict__ row, int64_
     int64_t gi = gbeg;
     if (PIPE && gi < nfg) {
         RawGroup<S, U> A, B;
-        raw_load<BLOCK, U, NT>(row, gi * step, A);
+        raw_load<BLOCK, U, NT, multi_row(CAP)>(row, gi * step, A);
         for (; gi + 1 < nfg; gi += 2) {
-            raw_load<BLOCK, U, NT>(row, (gi + 1) * step, B);
+            raw_load<BLOCK, U, NT, multi_row(CAP)>(row, (gi + 1) * step, B);
             {
                 float a[U][kChunk];
                 fast_values<U, S, CAP>(A, k, a);
                 f(gi * step, true, a);
             }
-            if (gi + 2 < nfg) raw_load<BLOCK, U, NT>(row, (gi + 2) * step, A);
+            if (gi + 2 < nfg) raw_load<BLOCK, U, NT, multi_row(CAP)>(row, (gi + 2) * step, A);
             {
                 float a[U][kChunk];
                 fast_values<U, S, CAP>(B, k, a);
@@ -478,7 +481,7 @@ __device__ __forceinline__ void for_each_group(const S* __restrict__ row, int64_
     } else {
         for (; gi < nfg; ++gi) {
             RawGroup<S, U> A;
-            raw_load<BLOCK, U, NT>(row, gi * step, A);
+            raw_load<BLOCK, U, NT, multi_row(CAP)>(row, gi * step, A);
             float a[U][kChunk];
             fast_values<U, S, CAP>(A, k, a);
             f(gi * step, true, a);
