@@ -346,8 +346,9 @@ __global__ __launch_bounds__(kTabRows* kBlock) void fwd1_tab_kernel(FwdParams p,
                 bc[sub][1] = rs.log2Sa;
             }
         }
-        // A row's red / bc entries are written again only after the next
-        // pass's first barrier, which every reader of them has passed.
+        // Next pass: red[sub] is rewritten after this barrier, which its
+        // reader (tid 0) passes after reading it; bc[sub] after the next
+        // pass's first barrier, which its readers pass after reading it.
         __syncthreads();
         if (live && HEAD == kHeadLogp) {
             RowStats rs;
