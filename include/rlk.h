@@ -105,7 +105,8 @@ int rlk_abi_version(void);
 
 /* Bytes of the per-row forward->backward record for `head` (N rows of
  * width V); the caller allocates it in device memory.  The layout is
- * private to the library.  Returns 0 for N <= 0 or an unknown head. */
+ * private to the library.  Returns 0 for N <= 0, an unknown head, or a
+ * size that does not fit size_t. */
 size_t rlk_stats_bytes(rlk_head head, int64_t N, int64_t V);
 
 /* Static text of a status code. */
@@ -270,7 +271,8 @@ rlk_status rlk_kl_bwd_ref_strided(const void* policy, const void* ref, rlk_dtype
  *      record.  A one-shard combine gives bitwise the plain forward. */
 #define RLK_MAX_SHARDS 64
 
-/* Bytes of N partial records (32 per row). */
+/* Bytes of N partial records (32 per row); 0 for N <= 0 or a size that
+ * does not fit size_t. */
 size_t rlk_partial_bytes(int64_t N);
 
 rlk_status rlk_logp_fwd_partial(const void* logits, rlk_dtype dtype, int64_t N, int64_t V_shard,

@@ -156,7 +156,7 @@ int rlk_abi_version(void) { return RLK_ABI_VERSION; }
 
 size_t rlk_stats_bytes(rlk_head head, int64_t N, int64_t V) {
     (void)V;
-    if (N <= 0) return 0;
+    if (N <= 0 || static_cast<uint64_t>(N) > SIZE_MAX / 32u) return 0;
     if (head != RLK_HEAD_LOGP && head != RLK_HEAD_ENTROPY && head != RLK_HEAD_KL) return 0;
     return static_cast<size_t>(N) * 32u;
 }
@@ -230,7 +230,7 @@ rlk_status check_rows(const rlk_rows* r, int64_t N, int64_t V, int64_t es, const
     const int64_t T = r->rows_per_batch, sb = r->batch_stride, st = r->row_stride;
     if (T < 1) return fail(RLK_ERR_SHAPE, "%s: rows_per_batch must be >= 1", name);
     if (sb < 0 || st < 0) return fail(RLK_ERR_SHAPE, "%s: strides must be >= 0", name);
-    const int64_t B = N > 0 ? (N + T - 1) / T : 0;
+    const int64_t B = N > 0 ? (N - 1) / T + 1 : 0;  // batches (no N + T - 1 overflow)
     if (N > 0) {
         // the last element touched: (B-1) sb + (min(N,T)-1) st + V - 1 must fit
         const int64_t tmax = (N < T ? N : T) - 1;
@@ -729,7 +729,10 @@ rlk_status rlk_kl_bwd_ref_strided(const void* policy, const void* ref, rlk_dtype
 
 // ------------------------------------------------- vocabulary shards
 
-size_t rlk_partial_bytes(int64_t N) { return N > 0 ? static_cast<size_t>(N) * 32u : 0u; }
+size_t rlk_partial_bytes(int64_t N) {
+    if (N <= 0 || static_cast<uint64_t>(N) > SIZE_MAX / 32u) return 0;
+    return static_cast<size_t>(N) * 32u;
+}
 
 rlk_status rlk_logp_fwd_partial(const void* logits, rlk_dtype dtype, int64_t N, int64_t V_shard,
                                 int64_t ld, int64_t v0, int64_t V_total, const int64_t* targets,
