@@ -1,16 +1,26 @@
 #!/usr/bin/env python3
-"""Benchmark: fused logprobs forward + backward on one MI355X.
+"""Benchmark: the fused log-softmax heads forward + backward on one MI355X.
 
-A step is one forward + backward pass of the hot path over one batch: the
-single-read row statistics with the target gather (rlk_logp_fwd), then the
-fused zero-workspace backward (rlk_logp_bwd), on the logprobs k=1 workload
-bf16 logits [8192, 151936] (seeded synthetic inputs, already resident in HBM).
+A step is one forward + backward pass of the hot path over one batch of a
+workload: the single-read row statistics with the head outputs (rlk_*_fwd),
+then the fused zero-workspace backward (rlk_*_bwd), on seeded synthetic inputs
+already resident in HBM.  By default every workload is timed in this one
+process:
 
-Prints ONE JSON line with the throughput in algorithmic GB/s (every logit
-read once by the forward, read once and written once by the backward, plus the
-per-row side arrays), the dominant kernel's roofline figures measured with HIP
-events on the launch stream, and the fp64 CPU oracle timed on a bounded sample
-of the same workload on the host cores.
+  c1_logp_fp32      logprobs k=1, fp32 [64, 32000]
+  c2_logp_bf16      logprobs k=1, bf16 [8192, 151936]
+  c3_kl_bf16        reverse KL and forward KL (timed apart), bf16 [8192, 75968] x 2
+  c4_entropy_cap30  entropy with softcap 30, bf16 [32768, 151936]   (headline)
+  c5_topk_cap20     top-256 logprobs with softcap 20, bf16 [2048, 262144],
+                    plus the standalone softcap on bf16 [2, 3, 262144]
+
+Prints ONE JSON line.  Its top-level figures are the headline workload's (the
+largest one that fits one GPU): throughput in algorithmic GB/s (each logit
+read once by the forward, read once and written once by the backward, plus
+the per-row side arrays), the dominant kernel's roofline figures measured with
+HIP events on the launch stream, and the fp64 CPU oracle timed on a bounded
+sample of the same workload on the host cores.  ``configs`` holds the same
+figures for every workload; ``provenance`` the build, device and software.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -23,6 +33,7 @@ import hashlib
 import json
 import math
 import os
+import platform
 import re
 import sys
 import time
@@ -32,6 +43,16 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "fwd+bwd ms and HBM GB/s (% of 8 TB/s) for logp/entropy/KL at N x V"
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "vocab_log_softmax_amd", "csrc")
+BUILD_INFO = os.path.join(ROOT, "vocab_log_softmax_amd", "build_info.json")
+HEADLINE = "c4_entropy_cap30"
+# (workload, KL direction) in the order they are timed
+ALL_RUNS = [("c1_logp_fp32", 0), ("c2_logp_bf16", 0), ("c3_kl_bf16", 0), ("c3_kl_bf16", 1),
+            ("c4_entropy_cap30", 0), ("c5_topk_cap20", 0)]
+# The oracle sample of each workload: at most this many logits per tensor
+# (fp64 copies on the host), repeated until it has run for ORACLE_SECONDS.
+ORACLE_MAX_ELEMS = 1 << 28
+ORACLE_SECONDS = 2.0
+ORACLE_MAX_THREADS = 16
 
 
 def kernel_source_hash() -> str:
@@ -76,10 +97,7 @@ class HipEvents:
     DISABLE_SYSTEM_FENCE = 0x20000000  # hipEventDisableSystemFence
 
     def __init__(self, n: int, torch):
-        lib_dir = os.path.join(os.path.dirname(torch.__file__), "lib")
-        path = os.path.join(lib_dir, "libamdhip64.so")
-        # same soname as the runtime torch loaded -> the same instance
-        self.hip = ctypes.CDLL(path if os.path.exists(path) else "libamdhip64.so.7")
+        self.hip = hip_runtime(torch)
         self.ev = [ctypes.c_void_p() for _ in range(n)]
         for e in self.ev:
             if self.hip.hipEventCreateWithFlags(ctypes.byref(e),
@@ -98,6 +116,49 @@ class HipEvents:
     def close(self) -> None:
         for e in self.ev:
             self.hip.hipEventDestroy(e)
+
+
+def hip_runtime(torch):
+    """The HIP runtime library torch loaded (same soname -> same instance)."""
+    lib_dir = os.path.join(os.path.dirname(torch.__file__), "lib")
+    path = os.path.join(lib_dir, "libamdhip64.so")
+    return ctypes.CDLL(path if os.path.exists(path) else "libamdhip64.so.7")
+
+
+def provenance(torch, dev) -> dict:
+    """Where a record comes from: build, sources, device, software, host."""
+    info: dict = {"source_hash": kernel_source_hash()}
+    try:
+        with open(BUILD_INFO) as f:
+            bi = json.load(f)
+        info["git_commit"] = bi.get("git_commit")
+        info["git_dirty"] = bi.get("git_dirty")
+        info["library_built_from_sources"] = bi.get("source_hash")
+        info["library_matches_sources"] = bi.get("source_hash") == info["source_hash"]
+    except (OSError, ValueError):
+        info["git_commit"] = None
+        info["library_matches_sources"] = None
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            info["rocm"] = f.read().strip()
+    except OSError:
+        info["rocm"] = None
+    info["torch"] = torch.__version__
+    info["torch_hip"] = getattr(torch.version, "hip", None)
+    hip = hip_runtime(torch)
+    v = ctypes.c_int()
+    if hip.hipRuntimeGetVersion(ctypes.byref(v)) == 0:
+        info["hip_runtime_version"] = v.value
+    if hip.hipDriverGetVersion(ctypes.byref(v)) == 0:
+        info["hip_driver_version"] = v.value
+    p = torch.cuda.get_device_properties(dev)
+    info["device"] = p.name
+    info["arch"] = getattr(p, "gcnArchName", None)
+    info["compute_units"] = p.multi_processor_count
+    info["device_memory_gib"] = round(p.total_memory / 2**30, 1)
+    info["host"] = {"cpu_count": os.cpu_count(), "affinity_cores": len(os.sched_getaffinity(0)),
+                    "machine": platform.machine(), "python": platform.python_version()}
+    return info
 
 
 def measure_ceilings(w, dev, torch) -> dict:
@@ -146,9 +207,10 @@ def measure_ceilings(w, dev, torch) -> dict:
     return {"ceilings": out, "workload": w.name}
 
 
-def time_softcap(name: str, dev, torch, reps: int = 50) -> dict:
+def time_softcap(name: str, dev, torch, reps: int = 200) -> dict:
     """The standalone softcap forward (y fp32) and backward on the workload's
-    softcap tensor: mean kernel time over `reps` launches, HIP events."""
+    softcap tensor: mean kernel time over `reps` back-to-back launches, HIP
+    events."""
     from vocab_log_softmax_amd import rlk, workloads
 
     w = workloads.WORKLOADS[name]
@@ -157,11 +219,12 @@ def time_softcap(name: str, dev, torch, reps: int = 50) -> dict:
     gx = torch.empty_like(x)
     n, es = x.numel(), x.element_size()
     raw = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
-    out = {"shape": list(x.shape), "dtype": str(x.dtype).replace("torch.", ""), "cap": w.cap}
-    for what, fn, nbytes in (("fwd", lambda: rlk.rlk_softcap_fwd(x, y, w.cap), n * (es + 4)),
-                             ("bwd", lambda: rlk.rlk_softcap_bwd(x, gy, gx, w.cap),
-                              n * (es + 4 + es))):
-        for _ in range(5):
+    out = {"shape": list(x.shape), "dtype": str(x.dtype).replace("torch.", ""), "cap": w.cap,
+           "reps": reps}
+    fwd = rlk.prepare(rlk.rlk_softcap_fwd, x, y, w.cap)
+    bwd = rlk.prepare(rlk.rlk_softcap_bwd, x, gy, gx, w.cap)
+    for what, fn, nbytes in (("fwd", fwd, n * (es + 4)), ("bwd", bwd, n * (es + 4 + es))):
+        for _ in range(20):
             fn()
         ev = HipEvents(2, torch)
         torch.cuda.synchronize()
@@ -174,6 +237,10 @@ def time_softcap(name: str, dev, torch, reps: int = 50) -> dict:
         ev.close()
         out[what] = {"us": round(ms * 1e3, 2), "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
                      "bytes": nbytes}
+    tot = out["fwd"]["us"] + out["bwd"]["us"]
+    out["fwd+bwd_us"] = round(tot, 2)
+    out["GB/s"] = round((out["fwd"]["bytes"] + out["bwd"]["bytes"]) / (tot * 1e-6) / 1e9, 1)
+    out["frac_of_hbm_peak"] = round(out["GB/s"] / HBM_PEAK_GBS, 4)
     return out
 
 
@@ -205,18 +272,19 @@ def side_bytes(w, N):
     return fwd, bwd
 
 
-def run_oracle_sample(w, d, max_rows: int, threads: int, min_seconds: float = 1.0,
-                      direction: int = 0):
-    """Time the fp64 oracle's fwd+bwd on the first max_rows rows (host cores).
+def oracle_baseline(w, d, direction: int, step_bytes: int, threads: int) -> dict:
+    """The fp64 oracle's fwd+bwd on the first rows of the same inputs.
 
-    A sample that takes less than min_seconds is repeated (up to 1000 times)
-    and the mean time of one pass is returned with the pass count.
+    At most ORACLE_MAX_ELEMS logits per tensor; the pass is repeated until
+    ORACLE_SECONDS have elapsed (at most 1000 passes) and the mean time of
+    one pass is reported, scaled to GB/s of the workload's algorithmic bytes.
     """
     import oracle
 
     orc = oracle.get()
     orc.set_threads(threads)
-    n = min(max_rows, d["N"])
+    N, V = d["N"], d["V"]
+    n = max(1, min(N, ORACLE_MAX_ELEMS // V))
     x = d["logits"][:n].double().cpu().numpy()
     g = d["grad"][:n].double().cpu().numpy()
     t = d["targets"][:n].cpu().numpy() if w.head == "logp" else None
@@ -239,30 +307,214 @@ def run_oracle_sample(w, d, max_rows: int, threads: int, min_seconds: float = 1.
         one_pass()
         passes += 1
         dt = time.perf_counter() - t0
-        if dt >= min_seconds or passes >= 1000:
+        if dt >= ORACLE_SECONDS or passes >= 1000:
             break
-    return n, dt / passes, passes
+    per_pass = dt / passes
+    return {"value": round(step_bytes * n / N / per_pass / 1e9, 4), "unit": "GB/s",
+            "cores": threads, "kind": "oracle",
+            "host_cpu_count": os.cpu_count(), "host_affinity_cores": len(os.sched_getaffinity(0)),
+            "sample": f"fp64 oracle fwd+bwd (OpenMP, {threads} threads) on the first {n} of {N} "
+                      f"rows of the same workload ({n * V} logits per tensor): "
+                      f"{per_pass:.4f} s per pass, mean of {passes} "
+                      f"pass{'es' if passes > 1 else ''} ({dt:.1f} s)"}
+
+
+def setup_workload(name, direction, dev, torch, rows=None):
+    """Inputs, outputs and pre-marshalled fwd / bwd calls of one workload."""
+    from vocab_log_softmax_amd import rlk, workloads
+
+    w = workloads.WORKLOADS[name]
+    d = workloads.make_inputs(name, dev, N=rows)
+    x = d["logits"]
+    N, V = x.shape
+    es = x.element_size()
+    gx = torch.empty_like(x)
+    if w.head == "logp":
+        tg, g = d["targets"], d["grad"]
+        out = torch.empty(tg.shape, dtype=torch.float32, device=dev)
+        st = rlk.new_stats(rlk.RLK_HEAD_LOGP, N, V, dev)
+        fwd = rlk.prepare(rlk.rlk_logp_fwd, x, tg, w.cap, out, st)
+        bwd = rlk.prepare(rlk.rlk_logp_bwd, x, tg, w.cap, st, g, gx)
+        # k <= 4 slots: one-shot pieces; up to 256: wide pieces; wider: the row kernel
+        n_in, fwd_name = 1, fwd1_name(w, N, V, es)
+        bwd_name = ("bwd_piece_kernel" if w.k <= 4 else
+                    "bwd_wide_kernel" if w.k <= 256 else "bwd_topk_kernel")
+    elif w.head == "entropy":
+        g = d["grad"]
+        out = torch.empty(N, dtype=torch.float32, device=dev)
+        st = rlk.new_stats(rlk.RLK_HEAD_ENTROPY, N, V, dev)
+        fwd = rlk.prepare(rlk.rlk_entropy_fwd, x, w.cap, out, st)
+        bwd = rlk.prepare(rlk.rlk_entropy_bwd, x, w.cap, st, g, gx)
+        n_in, fwd_name, bwd_name = 1, fwd1_name(w, N, V, es), "bwd_piece_kernel"
+    else:
+        ref, g = d["ref"], d["grad"]
+        out = torch.empty(N, dtype=torch.float32, device=dev)
+        st = rlk.new_stats(rlk.RLK_HEAD_KL, N, V, dev)
+        fwd = rlk.prepare(rlk.rlk_kl_fwd, x, ref, direction, 0.0, 0.0, out, st)
+        bwd = rlk.prepare(rlk.rlk_kl_bwd, x, ref, direction, 0.0, 0.0, st, g, gx)
+        n_in, fwd_name, bwd_name = 2, "fwdkl_kernel", "bwd_piece_kernel"
+    sf, sb = side_bytes(w, N)
+    fwd_bytes = n_in * N * V * es + sf            # read every input logit once
+    bwd_bytes = (n_in + 1) * N * V * es + sb      # read again, write the gradient once
+    desc = (f"{name}: {w.head} fwd+bwd, {'bf16' if es == 2 else 'fp32'} logits [{N}, {V}]"
+            + (f" x 2" if w.head == "kl" else "")
+            + (f", k={w.k}" if w.head == "logp" else "")
+            + ((", forward KL(ref||policy)" if direction else ", reverse KL(policy||ref)")
+               if w.head == "kl" else "")
+            + (f", softcap {w.cap:g}" if w.cap else ""))
+    keep = (x, gx, out, st, d)
+    return dict(w=w, d=d, N=N, V=V, es=es, fwd=fwd, bwd=bwd, fwd_name=fwd_name,
+                bwd_name=bwd_name, fwd_bytes=fwd_bytes, bwd_bytes=bwd_bytes, desc=desc,
+                keep=keep)
+
+
+def time_steps(fwd, bwd, stream, torch, steps=None, warmup=None, cold=False, dev=None) -> dict:
+    """Warm up, then time `steps` back-to-back fwd+bwd steps (wall clock) with
+    HIP events around the forward and the backward of sampled steps.
+
+    Without explicit counts both are sized from the step time: a
+    launch-bound step (microseconds) needs thousands of steps before clocks
+    and queues settle and for the timed region to outweigh its start-up
+    (warm-up >= 50 ms, timed region >= 0.2 s, at least 50 steps).
+    """
+    def run(n):
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for _ in range(n):
+            fwd()
+            bwd()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t) * 1e3 / max(1, n)
+
+    if warmup is not None:
+        warm_ms = run(warmup)
+    else:
+        run(5)                   # first launches (code loading, clocks)
+        warm_ms = run(10)        # the step time, from settled launches
+        extra = max(0, math.ceil(50.0 / max(warm_ms, 1e-6)) - 15)
+        run(extra)
+        warmup = 15 + extra
+    if steps is None:
+        steps = max(50, math.ceil(200.0 / max(warm_ms, 1e-6)))
+
+    # Three events per sampled step: before the forward, between forward and
+    # backward, after the backward.  Every step is sampled unless a step is
+    # so short (launch-bound) that the markers would show in its wall time;
+    # then every tenth step is.
+    stride = 1 if (warm_ms > 0.2 or cold) else 10
+    sampled = list(range(0, steps, stride))
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev) if cold else None
+    ev = HipEvents(3 * len(sampled), torch)
+    raw = ctypes.c_void_p(stream.cuda_stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    j = 0
+    for i in range(steps):
+        if flush is not None:
+            flush.fill_(float(i))
+        if i % stride == 0:
+            ev.record(3 * j, raw)
+            fwd()
+            ev.record(3 * j + 1, raw)
+            bwd()
+            ev.record(3 * j + 2, raw)
+            j += 1
+        else:
+            fwd()
+            bwd()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    fwd_ms = sum(ev.elapsed_ms(3 * j, 3 * j + 1) for j in range(len(sampled))) / len(sampled)
+    bwd_ms = sum(ev.elapsed_ms(3 * j + 1, 3 * j + 2) for j in range(len(sampled))) / len(sampled)
+    ev.close()
+    del flush
+    ms_per_step = wall * 1e3 / steps
+    if cold:  # the flush is not part of a step: the kernels' event time
+        ms_per_step = fwd_ms + bwd_ms
+    return dict(steps=steps, warmup=warmup, ms_per_step=ms_per_step, fwd_ms=fwd_ms,
+                bwd_ms=bwd_ms, event_timed_steps=len(sampled))
+
+
+def run_workload(name, direction, dev, torch, args, steps=None, warmup=None) -> dict:
+    """Time one workload; returns its record (and the roofline of its
+    dominant kernel)."""
+    s = setup_workload(name, direction, dev, torch, rows=args.rows)
+    stream = torch.cuda.current_stream(dev)
+    tm = time_steps(s["fwd"], s["bwd"], stream, torch, steps=steps, warmup=warmup,
+                    cold=args.cold, dev=dev)
+    step_bytes = s["fwd_bytes"] + s["bwd_bytes"]
+    value = step_bytes / (tm["ms_per_step"] * 1e-3) / 1e9
+    fwd_gbs = s["fwd_bytes"] / (tm["fwd_ms"] * 1e-3) / 1e9
+    bwd_gbs = s["bwd_bytes"] / (tm["bwd_ms"] * 1e-3) / 1e9
+    wname = name if args.rows is None else None
+    t_bwd = traffic_from_profiles(wname, s["bwd_name"]) if wname else None
+    # the dominant kernel: the one with the longer event time
+    dom_bwd = tm["bwd_ms"] >= tm["fwd_ms"]
+    k_name, k_ms, k_bytes, k_gbs = ((s["bwd_name"], tm["bwd_ms"], s["bwd_bytes"], bwd_gbs)
+                                    if dom_bwd else
+                                    (s["fwd_name"], tm["fwd_ms"], s["fwd_bytes"], fwd_gbs))
+    other = ((s["fwd_name"], "forward", tm["fwd_ms"], s["fwd_bytes"], fwd_gbs) if dom_bwd else
+             (s["bwd_name"], "backward", tm["bwd_ms"], s["bwd_bytes"], bwd_gbs))
+    head = s["w"].head
+    roofline = {
+        "bound": "hbm",
+        "kernel": f"{k_name} ({head} {'backward' if dom_bwd else 'forward'})",
+        "achieved": round(k_gbs, 1),
+        "peak": HBM_PEAK_GBS,
+        "unit": "GB/s",
+        "frac": round(k_gbs / HBM_PEAK_GBS, 4),
+        "traffic": t_bwd if dom_bwd else None,
+        "algorithmic_bytes_per_launch": k_bytes,
+        "avg_launch_ms": round(k_ms, 4),
+        "event_timed_steps": tm["event_timed_steps"],
+        "second_kernel": {"kernel": f"{other[0]} ({head} {other[1]})",
+                          "avg_launch_ms": round(other[2], 4), "achieved": round(other[4], 1),
+                          "frac": round(other[4] / HBM_PEAK_GBS, 4),
+                          "algorithmic_bytes_per_launch": other[3]},
+    }
+    rec = {
+        "workload": s["desc"], "N": s["N"], "V": s["V"],
+        "logits_dtype": "bf16" if s["es"] == 2 else "fp32", "seed": s["w"].seed,
+        "steps": tm["steps"], "warmup": tm["warmup"],
+        "ms_per_step": round(tm["ms_per_step"], 5),
+        "fwd_ms": round(tm["fwd_ms"], 5), "bwd_ms": round(tm["bwd_ms"], 5),
+        "GB/s": round(value, 1), "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "fwd_GB/s": round(fwd_gbs, 1), "bwd_GB/s": round(bwd_gbs, 1),
+        "algorithmic_bytes_per_step": step_bytes,
+        "traffic_ratio_bwd": (round(t_bwd / s["bwd_bytes"], 4) if t_bwd else None),
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        threads = args.oracle_threads or min(len(os.sched_getaffinity(0)), ORACLE_MAX_THREADS)
+        rec["cpu_baseline"] = oracle_baseline(s["w"], s["d"], direction, step_bytes, threads)
+    if "softcap_shape" in s["w"].extra and args.rows is None:
+        rec["softcap_standalone"] = time_softcap(name, dev, torch)
+    del s
+    torch.cuda.empty_cache()
+    return rec
 
 
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None,
-                    help="timed steps (default: at least 50, enough for 0.2 s of work)")
+                    help="timed steps of the headline workload (default: at least 50, enough "
+                         "for 0.2 s of work; the other workloads always size their own)")
     ap.add_argument("--warmup", type=int, default=None,
                     help="untimed steps first (default: at least 5, enough for 50 ms)")
-    ap.add_argument("--workload", default="c2_logp_bf16")
-    ap.add_argument("--oracle-rows", type=int, default=8192,
-                    help="rows of the workload timed on the CPU oracle")
+    ap.add_argument("--workload", default=None,
+                    help="time this workload only (default: every workload, headline "
+                         f"{HEADLINE})")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--oracle-threads", type=int, default=None,
                     help="host threads of the CPU oracle (default: the process's cores, "
-                         "at most 16)")
+                         f"at most {ORACLE_MAX_THREADS})")
     ap.add_argument("--rows", type=int, default=None,
-                    help="override the workload's row count N (same recipe, e.g. 32768 rows "
-                         "of c2_logp_bf16 for the pages' B200 comparison)")
+                    help="with --workload: override the row count N (same recipe, e.g. 32768 "
+                         "rows of c2_logp_bf16 for the pages' B200 comparison)")
     ap.add_argument("--direction", type=int, default=0, choices=(0, 1),
-                    help="KL workloads: 0 reverse KL(policy||ref), 1 forward KL(ref||policy)")
+                    help="with a KL --workload: 0 reverse KL(policy||ref), 1 forward "
+                         "KL(ref||policy)")
     ap.add_argument("--cold", action="store_true",
                     help="write a 1 GiB buffer before every step (flushes the 256 MB Infinity "
                          "Cache and the L2s) and time the two kernels with events only")
@@ -277,6 +529,9 @@ def main() -> int:
               "(rows shard across GPUs with no exchange; vocabulary shards need one "
               "all-gather of the rlk_*_fwd_partial records before rlk_combine). "
               "Run with --gpus 1.", file=sys.stderr)
+        return 2
+    if args.rows is not None and args.workload is None:
+        print("--rows needs --workload", file=sys.stderr)
         return 2
 
     import torch
@@ -299,149 +554,39 @@ def main() -> int:
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes_each_way": src.numel(), "launches": 3}))
         return 0
-    w = workloads.WORKLOADS[args.workload]
     if args.ceilings:
+        w = workloads.WORKLOADS[args.workload or HEADLINE]
         print(json.dumps(measure_ceilings(w, dev, torch)))
         return 0
-    d = workloads.make_inputs(args.workload, dev, N=args.rows)
-    x = d["logits"]
-    N, V = x.shape
-    es = x.element_size()
-    stream = torch.cuda.current_stream(dev)
 
-    if w.head == "logp":
-        tg, g = d["targets"], d["grad"]
-        out = torch.empty(tg.shape, dtype=torch.float32, device=dev)
-        st = rlk.new_stats(rlk.RLK_HEAD_LOGP, N, V, dev)
-        gx = torch.empty_like(x)
-        fwd = rlk.prepare(rlk.rlk_logp_fwd, x, tg, w.cap, out, st)
-        bwd = rlk.prepare(rlk.rlk_logp_bwd, x, tg, w.cap, st, g, gx)
-        # k <= 4 slots: one-shot pieces; up to 256: wide pieces; wider: the row kernel
-        n_in, fwd_name = 1, fwd1_name(w, N, V, es)
-        bwd_name = ("bwd_piece_kernel" if w.k <= 4 else
-                    "bwd_wide_kernel" if w.k <= 256 else "bwd_topk_kernel")
-    elif w.head == "entropy":
-        g = d["grad"]
-        out = torch.empty(N, dtype=torch.float32, device=dev)
-        st = rlk.new_stats(rlk.RLK_HEAD_ENTROPY, N, V, dev)
-        gx = torch.empty_like(x)
-        fwd = rlk.prepare(rlk.rlk_entropy_fwd, x, w.cap, out, st)
-        bwd = rlk.prepare(rlk.rlk_entropy_bwd, x, w.cap, st, g, gx)
-        n_in, fwd_name, bwd_name = 1, fwd1_name(w, N, V, es), "bwd_piece_kernel"
+    if args.workload is not None:
+        runs = [(args.workload, args.direction)]
+        headline = runs[0]
     else:
-        ref, g = d["ref"], d["grad"]
-        out = torch.empty(N, dtype=torch.float32, device=dev)
-        st = rlk.new_stats(rlk.RLK_HEAD_KL, N, V, dev)
-        gx = torch.empty_like(x)
-        kd = args.direction
-        fwd = rlk.prepare(rlk.rlk_kl_fwd, x, ref, kd, 0.0, 0.0, out, st)
-        bwd = rlk.prepare(rlk.rlk_kl_bwd, x, ref, kd, 0.0, 0.0, st, g, gx)
-        n_in, fwd_name, bwd_name = 2, "fwdkl_kernel", "bwd_piece_kernel"
-
-    sf, sb = side_bytes(w, N)
-    fwd_bytes = n_in * N * V * es + sf            # read every input logit once
-    bwd_bytes = (n_in + 1) * N * V * es + sb      # read again, write the gradient once
-    step_bytes = fwd_bytes + bwd_bytes
-
-    # Warm-up.  Without --warmup / --steps both are sized from the step time:
-    # a launch-bound step (microseconds) needs thousands of steps before clocks
-    # and queues settle and for the timed region to outweigh its start-up.
-    def run(n):
-        torch.cuda.synchronize()
-        t = time.perf_counter()
-        for _ in range(n):
-            fwd()
-            bwd()
-        torch.cuda.synchronize()
-        return (time.perf_counter() - t) * 1e3 / max(1, n)
-
-    if args.warmup is not None:
-        warm_ms = run(args.warmup)
-    else:
-        run(5)                   # first launches (code loading, clocks)
-        warm_ms = run(10)        # the step time, from settled launches
-        extra = max(0, math.ceil(50.0 / max(warm_ms, 1e-6)) - 15)
-        run(extra)
-        args.warmup = 15 + extra
-    if args.steps is None:
-        args.steps = max(50, math.ceil(200.0 / max(warm_ms, 1e-6)))
-
-    # HIP events on the stream the kernels run on, three per sampled step:
-    # before the forward, between forward and backward, after the backward.
-    # Every step is sampled unless a step is so short (launch-bound) that the
-    # event markers themselves would show in its wall time; then every
-    # tenth step is.
-    stride = 1 if (warm_ms > 0.2 or args.cold) else 10
-    sampled = list(range(0, args.steps, stride))
-    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev) if args.cold else None
-    ev = HipEvents(3 * len(sampled), torch)
-    raw = ctypes.c_void_p(stream.cuda_stream)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    j = 0
-    for i in range(args.steps):
-        if flush is not None:
-            flush.fill_(float(i))
-        if i % stride == 0:
-            ev.record(3 * j, raw)
-            fwd()
-            ev.record(3 * j + 1, raw)
-            bwd()
-            ev.record(3 * j + 2, raw)
-            j += 1
-        else:
-            fwd()
-            bwd()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    fwd_ms = sum(ev.elapsed_ms(3 * j, 3 * j + 1) for j in range(len(sampled))) / len(sampled)
-    bwd_ms = sum(ev.elapsed_ms(3 * j + 1, 3 * j + 2) for j in range(len(sampled))) / len(sampled)
-    ev.close()
-    ms_per_step = wall * 1e3 / args.steps
-    if args.cold:  # the flush is not part of a step: the kernels' event time
-        ms_per_step = fwd_ms + bwd_ms
-    value = step_bytes / (ms_per_step * 1e-3) / 1e9
-
-    bwd_gbs = bwd_bytes / (bwd_ms * 1e-3) / 1e9
-    fwd_gbs = fwd_bytes / (fwd_ms * 1e-3) / 1e9
-    traffic = traffic_from_profiles(args.workload, bwd_name)
-    roofline = {
-        "bound": "hbm",
-        "kernel": f"{bwd_name} ({w.head} backward)",
-        "achieved": round(bwd_gbs, 1),
-        "peak": HBM_PEAK_GBS,
-        "unit": "GB/s",
-        "frac": round(bwd_gbs / HBM_PEAK_GBS, 4),
-        "traffic": traffic,
-        "algorithmic_bytes_per_launch": bwd_bytes,
-        "avg_launch_ms": round(bwd_ms, 4),
-        "event_timed_steps": len(sampled),
-        "second_kernel": {"kernel": f"{fwd_name} ({w.head} forward)", "avg_launch_ms":
-                          round(fwd_ms, 4), "achieved": round(fwd_gbs, 1),
-                          "frac": round(fwd_gbs / HBM_PEAK_GBS, 4),
-                          "algorithmic_bytes_per_launch": fwd_bytes},
-    }
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        threads = args.oracle_threads or min(len(os.sched_getaffinity(0)), 16)
-        n, dt, passes = run_oracle_sample(w, d, args.oracle_rows, threads,
-                                          direction=args.direction)
-        sample_bytes = step_bytes * n / N
-        cpu = {"value": round(sample_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
-               "kind": "oracle",
-               "sample": f"fp64 oracle fwd+bwd on the first {n} of {N} rows of the same "
-                         f"workload ({n * V} logits per tensor), {dt:.3f} s wall per pass, "
-                         f"mean of {passes} pass{'es' if passes > 1 else ''}"}
-
+        runs = ALL_RUNS
+        headline = (HEADLINE, 0)
+    configs = {}
+    for name, direction in runs:
+        is_head = (name, direction) == headline
+        rec = run_workload(name, direction, dev, torch, args,
+                           steps=args.steps if is_head else None,
+                           warmup=args.warmup if is_head else None)
+        key = name + ({0: "_reverse", 1: "_forward"}[direction]
+                      if workloads.WORKLOADS[name].head == "kl" else "")
+        configs[key] = rec
+        print(f"[bench] {key}: {rec['ms_per_step']:.5f} ms/step, {rec['GB/s']} GB/s "
+              f"({100 * rec['frac_of_hbm_peak']:.1f}% of 8 TB/s)", file=sys.stderr, flush=True)
+    hkey = headline[0] + ({0: "_reverse", 1: "_forward"}[headline[1]]
+                          if workloads.WORKLOADS[headline[0]].head == "kl" else "")
+    h = configs[hkey]
     result = {
         "metric": METRIC,
-        "value": round(value, 1),
+        "value": h["GB/s"],
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "steps": h["steps"],
+        "warmup": h["warmup"],
+        "ms_per_step": round(h["ms_per_step"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -450,21 +595,19 @@ def main() -> int:
         "timing": ("cold: 1 GiB written before every step, step = forward + backward event time"
                    if args.cold else "warm: back-to-back steps, wall clock"),
         "config": {
-            "workload": f"{args.workload}" + (f" (N overridden to {N})" if args.rows else "")
-                        + f": {w.head} fwd+bwd, "
-                        f"{'bf16' if es == 2 else 'fp32'} logits [{N}, {V}]"
-                        + (f", k={w.k}" if w.head == "logp" else "")
-                        + ((", forward KL(ref||policy)" if args.direction else
-                            ", reverse KL(policy||ref)") if w.head == "kl" else "")
-                        + (f", softcap {w.cap:g}" if w.cap else ""),
-            "N": N, "V": V, "logits_dtype": "bf16" if es == 2 else "fp32",
-            "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
-            "algorithmic_bytes_per_step": step_bytes,
+            "workload": h["workload"] + (f" (N overridden to {h['N']})" if args.rows else ""),
+            "N": h["N"], "V": h["V"], "logits_dtype": h["logits_dtype"],
+            "frac_of_hbm_peak": h["frac_of_hbm_peak"],
+            "algorithmic_bytes_per_step": h["algorithmic_bytes_per_step"],
+            "fwd_ms": h["fwd_ms"], "bwd_ms": h["bwd_ms"],
         },
-        "roofline": roofline,
-        "cpu_baseline": cpu,
-        **({"softcap_standalone": time_softcap(args.workload, dev, torch)}
-           if "softcap_shape" in w.extra else {}),
+        "roofline": h["roofline"],
+        "cpu_baseline": h.get("cpu_baseline"),
+        "configs": {k: {kk: vv for kk, vv in v.items() if kk != "roofline"}
+                    | {"dominant_kernel": v["roofline"]["kernel"],
+                       "dominant_kernel_frac": v["roofline"]["frac"]}
+                    for k, v in configs.items()},
+        "provenance": provenance(torch, dev),
     }
     print(json.dumps(result), flush=True)
     return 0

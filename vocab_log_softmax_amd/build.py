@@ -20,6 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "librlk.so")
+BUILD_INFO = os.path.join(PKG, "build_info.json")
 # Bandwidth probes for the benchmark's ceiling report (not part of the ABI).
 CEILING_SRC = os.path.join(PKG, "ceiling", "ceiling.hip")
 CEILING_LIB = os.path.join(PKG, "ceiling", "libceiling.so")
@@ -53,6 +54,38 @@ def _compile(src: str, build_dir: str = BUILD_DIR, defines=()) -> str:
     return obj
 
 
+def source_hash() -> str:
+    """Hash of the kernel and host sources (the same rule as bench.py's)."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(CSRC)):
+        if f.endswith((".hip", ".h", ".cpp")):
+            with open(os.path.join(CSRC, f), "rb") as fh:
+                h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def write_build_info() -> None:
+    """Record which commit and sources the library was built from.
+
+    The GPU runs see the tree without its git metadata; the benchmark reports
+    this file's commit, dirty flag and source hash as its provenance.
+    """
+    import json
+
+    def git(*a):
+        r = subprocess.run(["git", "-C", ROOT, *a], capture_output=True, text=True)
+        return r.stdout.strip() if r.returncode == 0 else None
+
+    status = git("status", "--porcelain", "--untracked-files=no")
+    info = {"git_commit": git("rev-parse", "HEAD"),
+            "git_dirty": None if status is None else bool(status),
+            "source_hash": source_hash(), "arch": ARCH}
+    with open(BUILD_INFO, "w") as f:
+        json.dump(info, f)
+
+
 def build(verbose: bool = True, out_path: str = LIB_PATH, defines=(), build_dir=BUILD_DIR) -> str:
     """Compile every source and link librlk.so; returns its path.
 
@@ -68,6 +101,8 @@ def build(verbose: bool = True, out_path: str = LIB_PATH, defines=(), build_dir=
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
     os.replace(tmp, out_path)
+    if out_path == LIB_PATH and not defines:
+        write_build_info()
     if verbose:
         print(f"built {out_path}")
     return out_path
