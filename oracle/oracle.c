@@ -22,8 +22,9 @@
  *         (DeepSpeed pull request 8838): Changes (logprobs / entropy / KL
  *         heads, top-k one-hot terms), Tests (masked vocabulary, all -inf
  *         rows, support mismatch, duplicate / ignored top-k ids), and the
- *         review comment "Suggested change: read each logit once" (entropy
- *         H = log S - W/S, KL closed form, support-mismatch rule).
+ *         review comment proposing a single pass over the logits for the
+ *         entropy and KL forward (entropy H = log S - W/S, KL closed form,
+ *         support-mismatch rule).
  *   [ZW]  "perf(logp): fused zero-workspace backward for the generic CUDA
  *         fused logp" (RL-Kernel pull request 495): Summary (gradient
  *         g * (onehot - softmax)), Behavior changes (targets outside [0, V)

@@ -1,10 +1,10 @@
 // rlk_fwd_kernels.h -- forward row kernels: one read of each logit, online
 // statistics, head outputs and the per-row record for the backward.
 //
-// Single-read statistics follow the review comment "Suggested change: read
-// each logit once in the entropy / KL forward" on "Add Triton kernels for
-// vocab-parallel logprobs, entropy and KL" (DeepSpeed pull request 8838):
-// the running max, the sum of exponentials and a probability-weighted sum of
+// Single-read statistics follow the review comment on the entropy / KL
+// forward of "Add Triton kernels for vocab-parallel logprobs, entropy and
+// KL" (DeepSpeed pull request 8838), which proposes a single pass over the
+// logits in place of the first version's two: the running max, the sum of exponentials and a probability-weighted sum of
 // centred logits, all rescaled when the max grows, give
 //   entropy  H = log S - W / S,
 //   KL(A||B) = W / S_A - log S_A + log S_B,
