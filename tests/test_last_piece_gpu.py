@@ -17,8 +17,9 @@ cases sit on the far side of that switch: V = 32000 (4000 chunks: 15 full
     logp", RL-Kernel pull request 495, Tests: agreement with fp64 across V);
   * checks that a 4-row subset of the same rows, a call far below 64 MiB
     that takes the ordinary tail path, gives bit-identical outputs and
-    gradients (the same pull request's Summary: deterministic and
-    batch-invariant).
+    gradients, and so does the subset at a misaligned base, which reads
+    every element on its own and stores element by element (the same pull
+    request's Summary: deterministic and batch-invariant).
 """
 
 import numpy as np
@@ -74,6 +75,15 @@ def check_subset_bits(full_out, full_gx, sub_out, sub_gx, rows, what):
     assert torch.equal(a, b), f"{what}: gradients of a row subset differ from the full call"
 
 
+def misaligned(t):
+    """A copy of t whose base is one element past a 16-byte boundary."""
+    buf = torch.empty(t.numel() + 8, dtype=t.dtype, device=t.device)
+    m = buf[1:1 + t.numel()].view(t.shape)
+    m.copy_(t)
+    assert m.data_ptr() % 16 != 0
+    return m
+
+
 def logits(dev, dtype, N, std, seed):
     return (torch.randn(N, V, generator=dgen(dev, seed), device=dev) * std).to(dtype)
 
@@ -122,12 +132,13 @@ def test_logp_last_piece(dev, orc, dtype, N, k, cap):
         print(f"logp k={k} cap={cap}: {strict_bf16_misses(gx[ri], refg)} elements beyond 4e-3")
     sub = [0, 3, 6, N - 1]
     si = torch.tensor(sub, device=dev)
-    xs, ts, gss = x[si].contiguous(), td[si].contiguous(), gd[si].contiguous()
+    ts, gss = td[si].contiguous(), gd[si].contiguous()
     assert not last_piece_apart(len(sub), V, es, PIECE_CHUNKS if k <= 4 else WIDE_CHUNKS)
-    so, sst = rlk.logp_fwd(xs, ts, cap)
-    sg = rlk.logp_bwd(xs, ts, gss, sst, cap)
-    torch.cuda.synchronize()
-    check_subset_bits(out, gx, so, sg, sub, f"logp k={k}")
+    for xs in (x[si].contiguous(), misaligned(x[si])):
+        so, sst = rlk.logp_fwd(xs, ts, cap)
+        sg = rlk.logp_bwd(xs, ts, gss, sst, cap)
+        torch.cuda.synchronize()
+        check_subset_bits(out, gx, so, sg, sub, f"logp k={k}, base % 16 = {xs.data_ptr() % 16}")
 
 
 @pytest.mark.parametrize("cap", [0.0, 30.0])
@@ -156,11 +167,12 @@ def test_entropy_last_piece(dev, orc, dtype, N, cap):
         print(f"entropy cap={cap}: {strict_bf16_misses(gx[ri], refg)} elements beyond 4e-3")
     sub = [0, 11, 12, N - 1]
     si = torch.tensor(sub, device=dev)
-    xs, gs = x[si].contiguous(), g[si].contiguous()
-    sh, sst = rlk.entropy_fwd(xs, cap)
-    sg = rlk.entropy_bwd(xs, gs, sst, cap)
-    torch.cuda.synchronize()
-    check_subset_bits(H, gx, sh, sg, sub, "entropy")
+    gs = g[si].contiguous()
+    for xs in (x[si].contiguous(), misaligned(x[si])):
+        sh, sst = rlk.entropy_fwd(xs, cap)
+        sg = rlk.entropy_bwd(xs, gs, sst, cap)
+        torch.cuda.synchronize()
+        check_subset_bits(H, gx, sh, sg, sub, f"entropy, base % 16 = {xs.data_ptr() % 16}")
 
 
 @pytest.mark.parametrize("direction", [0, 1], ids=["rev", "fwd"])
@@ -196,10 +208,12 @@ def test_kl_last_piece(dev, orc, dtype, N, cap, direction):
               f"beyond 4e-3")
     sub = [0, 8, 10, N - 1]
     si = torch.tensor(sub, device=dev)
-    sa, sb, sgv = a[si].contiguous(), b[si].contiguous(), g[si].contiguous()
-    sD, sst = rlk.kl_fwd(sa, sb, direction, cap, cap)
-    sgp = rlk.kl_bwd(sa, sb, sgv, sst, direction, cap, cap)
-    sgr = rlk.kl_bwd_ref(sa, sb, sgv, sst, direction, cap, cap)
-    torch.cuda.synchronize()
-    check_subset_bits(D, gp, sD, sgp, sub, "kl policy")
-    check_subset_bits(D, gr, sD, sgr, sub, "kl reference")
+    sgv = g[si].contiguous()
+    for sa, sb in ((a[si].contiguous(), b[si].contiguous()), (misaligned(a[si]), misaligned(b[si]))):
+        sD, sst = rlk.kl_fwd(sa, sb, direction, cap, cap)
+        sgp = rlk.kl_bwd(sa, sb, sgv, sst, direction, cap, cap)
+        sgr = rlk.kl_bwd_ref(sa, sb, sgv, sst, direction, cap, cap)
+        torch.cuda.synchronize()
+        al = sa.data_ptr() % 16
+        check_subset_bits(D, gp, sD, sgp, sub, f"kl policy, base % 16 = {al}")
+        check_subset_bits(D, gr, sD, sgr, sub, f"kl reference, base % 16 = {al}")
