@@ -64,8 +64,10 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_from_profiles(workload: str, kernel: str):
-    """HBM bytes per launch from a committed rocprofv3 --pmc summary, or None.
+def traffic_from_profiles(workload: str, kernel: str, which: str = "bwd"):
+    """HBM bytes per launch of the workload's backward (or forward, which =
+    "fwd") from the committed rocprofv3 --pmc summary named after its
+    backward kernel, or None.
 
     The summary must name the same kernel sources (hash) as this tree; a
     changed kernel makes its counters stale.
@@ -74,9 +76,10 @@ def traffic_from_profiles(workload: str, kernel: str):
     if not os.path.exists(path):
         return None
     txt = open(path).read()
+    pre = "fwd_" if which == "fwd" else ""
     m_hash = re.search(r"^source_hash:\s*(\S+)", txt, re.M)
-    m_rd = re.search(r"^hbm_read_bytes_per_launch:\s*([0-9.eE+]+)", txt, re.M)
-    m_wr = re.search(r"^hbm_write_bytes_per_launch:\s*([0-9.eE+]+)", txt, re.M)
+    m_rd = re.search(rf"^{pre}hbm_read_bytes_per_launch:\s*([0-9.eE+]+)", txt, re.M)
+    m_wr = re.search(rf"^{pre}hbm_write_bytes_per_launch:\s*([0-9.eE+]+)", txt, re.M)
     if not (m_hash and m_rd and m_wr) or m_hash.group(1) != kernel_source_hash():
         return None
     return float(m_rd.group(1)) + float(m_wr.group(1))
@@ -205,6 +208,84 @@ def measure_ceilings(w, dev, torch) -> dict:
         out[name] = {"ms": round(ms, 4), "GB/s": round(passes * bytes_ / (ms * 1e-3) / 1e9, 1)}
     ev.close()
     return {"ceilings": out, "workload": w.name}
+
+
+def measure_launch_floor(dev, torch) -> dict:
+    """Latency probes at the logprobs fp32 [64, 32000] size (libceiling.so):
+    back-to-back launch intervals of empty kernels, a one-workgroup-per-row
+    read with every load in flight, the same with the row kernels' online
+    fold and with their epilogue, the fold split over four workgroups per
+    row, the backward's one-shot pieces, and pairs of them; beside them the
+    library's own forward, backward and step on the workload.  Each figure is
+    the best of 5 runs of 500 back-to-back launches (HIP events, mean per
+    launch); the probes are launched from a C loop, the library through its
+    binding (about 3 us of host time per call, under the GPU time here)."""
+    from vocab_log_softmax_amd import build as B
+    from vocab_log_softmax_amd import rlk, workloads
+
+    if not os.path.exists(B.CEILING_LIB):
+        raise SystemExit(f"{B.CEILING_LIB} is missing: run __graft_entry__.build()")
+    lib = ctypes.CDLL(B.CEILING_LIB)
+    lib.launch_floor_run.argtypes = [ctypes.c_int] * 3 + [ctypes.c_void_p] * 6
+    lib.launch_floor_run.restype = ctypes.c_int
+    R, C = lib.launch_floor_rows(), lib.launch_floor_cols()
+    d = workloads.make_inputs("c1_logp_fp32", dev)
+    x = d["logits"]
+    assert tuple(x.shape) == (R, C) and x.dtype == torch.float32
+    y = torch.empty_like(x)
+    tg = d["targets"].reshape(-1).contiguous()
+    stats = torch.empty(R * 8, dtype=torch.float32, device=dev)
+    out = torch.empty(256, dtype=torch.float32, device=dev)
+    raw = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    ev = HipEvents(2, torch)
+
+    def probe(a, b=-1):
+        def run(reps):
+            rc = lib.launch_floor_run(a, b, reps, x.data_ptr(), y.data_ptr(), tg.data_ptr(),
+                                      stats.data_ptr(), out.data_ptr(), raw)
+            if rc != 0:
+                raise RuntimeError(f"launch_floor_run({a}, {b}) failed: {rc}")
+        return run
+
+    def best_us(run, reps=500):
+        run(50)
+        best = float("inf")
+        for _ in range(5):
+            torch.cuda.synchronize()
+            ev.record(0, raw)
+            run(reps)
+            ev.record(1, raw)
+            torch.cuda.synchronize()
+            best = min(best, ev.elapsed_ms(0, 1) * 1e3 / reps)
+        return round(best, 2)
+
+    names = ["empty, 64 workgroups", "empty, 1024 workgroups",
+             "row read, one workgroup per row, every load in flight",
+             "row read + online fold", "row read + fold + forward epilogue",
+             "fold split over 4 workgroups per row", "backward-shaped one-shot pieces (copy)"]
+    res = {n: best_us(probe(k)) for k, n in enumerate(names)}
+    res["pair: empty + empty"] = best_us(probe(0, 1))
+    res["pair: read + fold + epilogue, then one-shot pieces"] = best_us(probe(4, 6))
+    tg2, g = d["targets"], d["grad"]
+    lp = torch.empty(tg2.shape, dtype=torch.float32, device=dev)
+    st = rlk.new_stats(rlk.RLK_HEAD_LOGP, R, C, dev)
+    gx = torch.empty_like(x)
+    fwd = rlk.prepare(rlk.rlk_logp_fwd, x, tg2, 0.0, lp, st)
+    bwd = rlk.prepare(rlk.rlk_logp_bwd, x, tg2, 0.0, st, g, gx)
+    def loop(*fns):  # the library through its Python binding (host-side ~3 us per call)
+        def run(reps):
+            for _ in range(reps):
+                for f in fns:
+                    f()
+        return run
+
+    res["library: logprobs forward"] = best_us(loop(fwd))
+    res["library: logprobs backward"] = best_us(loop(bwd))
+    res["library: forward + backward step"] = best_us(loop(fwd, bwd))
+    ev.close()
+    return {"launch_floor_us": res, "shape": [R, C], "dtype": "fp32",
+            "method": "best of 5 x 500 back-to-back launches, HIP events, mean per launch; "
+                      "probes launched from a C loop"}
 
 
 def time_softcap(name: str, dev, torch, reps: int = 200) -> dict:
@@ -446,8 +527,12 @@ def run_workload(name, direction, dev, torch, args, steps=None, warmup=None) -> 
     value = step_bytes / (tm["ms_per_step"] * 1e-3) / 1e9
     fwd_gbs = s["fwd_bytes"] / (tm["fwd_ms"] * 1e-3) / 1e9
     bwd_gbs = s["bwd_bytes"] / (tm["bwd_ms"] * 1e-3) / 1e9
-    wname = name if args.rows is None else None
-    t_bwd = traffic_from_profiles(wname, s["bwd_name"]) if wname else None
+    # traffic summaries are per workload (and per direction for KL)
+    pkey = None
+    if args.rows is None:
+        pkey = name + ({0: "_reverse", 1: "_forward"}[direction] if s["w"].head == "kl" else "")
+    t_bwd = traffic_from_profiles(pkey, s["bwd_name"]) if pkey else None
+    t_fwd = traffic_from_profiles(pkey, s["bwd_name"], "fwd") if pkey else None
     # the dominant kernel: the one with the longer event time
     dom_bwd = tm["bwd_ms"] >= tm["fwd_ms"]
     k_name, k_ms, k_bytes, k_gbs = ((s["bwd_name"], tm["bwd_ms"], s["bwd_bytes"], bwd_gbs)
@@ -463,7 +548,7 @@ def run_workload(name, direction, dev, torch, args, steps=None, warmup=None) -> 
         "peak": HBM_PEAK_GBS,
         "unit": "GB/s",
         "frac": round(k_gbs / HBM_PEAK_GBS, 4),
-        "traffic": t_bwd if dom_bwd else None,
+        "traffic": t_bwd if dom_bwd else t_fwd,
         "algorithmic_bytes_per_launch": k_bytes,
         "avg_launch_ms": round(k_ms, 4),
         "event_timed_steps": tm["event_timed_steps"],
@@ -481,6 +566,7 @@ def run_workload(name, direction, dev, torch, args, steps=None, warmup=None) -> 
         "GB/s": round(value, 1), "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "fwd_GB/s": round(fwd_gbs, 1), "bwd_GB/s": round(bwd_gbs, 1),
         "algorithmic_bytes_per_step": step_bytes,
+        "traffic_ratio_fwd": (round(t_fwd / s["fwd_bytes"], 4) if t_fwd else None),
         "traffic_ratio_bwd": (round(t_bwd / s["bwd_bytes"], 4) if t_bwd else None),
         "roofline": roofline,
     }
@@ -520,6 +606,8 @@ def main() -> int:
                          "Cache and the L2s) and time the two kernels with events only")
     ap.add_argument("--ceilings", action="store_true",
                     help="only measure the read / write / copy ceilings at the workload's size")
+    ap.add_argument("--launch-floor", action="store_true",
+                    help="only measure the launch-latency probes at the fp32 [64, 32000] size")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain device copy of a known size (counter calibration)")
     args = ap.parse_args()
@@ -553,6 +641,9 @@ def main() -> int:
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes_each_way": src.numel(), "launches": 3}))
+        return 0
+    if args.launch_floor:
+        print(json.dumps(measure_launch_floor(dev, torch)))
         return 0
     if args.ceilings:
         w = workloads.WORKLOADS[args.workload or HEADLINE]

@@ -21,8 +21,10 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "librlk.so")
 BUILD_INFO = os.path.join(PKG, "build_info.json")
-# Bandwidth probes for the benchmark's ceiling report (not part of the ABI).
-CEILING_SRC = os.path.join(PKG, "ceiling", "ceiling.hip")
+# Bandwidth and launch-latency probes for the benchmark's ceiling reports
+# (not part of the ABI).
+CEILING_SRCS = [os.path.join(PKG, "ceiling", "ceiling.hip"),
+                os.path.join(PKG, "ceiling", "launch_floor.hip")]
 CEILING_LIB = os.path.join(PKG, "ceiling", "libceiling.so")
 
 SOURCES = ["rlk_fwd_f32.hip", "rlk_fwd_bf16.hip", "rlk_fwd_f16.hip",
@@ -109,11 +111,12 @@ def build(verbose: bool = True, out_path: str = LIB_PATH, defines=(), build_dir=
 
 
 def build_ceiling(verbose: bool = True) -> str:
-    """Compile the bandwidth probes into libceiling.so (benchmark only)."""
+    """Compile the bandwidth and launch-latency probes into libceiling.so
+    (benchmark only)."""
     os.makedirs(BUILD_DIR, exist_ok=True)
-    obj = _compile(CEILING_SRC, BUILD_DIR)
+    objs = [_compile(src, BUILD_DIR) for src in CEILING_SRCS]
     tmp = CEILING_LIB + ".tmp"
-    r = subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", obj, "-o", tmp],
+    r = subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp],
                        capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")

@@ -1,0 +1,223 @@
+// launch_floor.hip -- latency probes at the size of the logprobs fp32
+// [64, 32000] workload (8 MB of logits), where a forward + backward pair
+// takes about one launch interval per kernel: what an empty launch costs
+// back to back on one stream, and what the row walk, its fold and its
+// epilogue add on top.  Measurement infrastructure only (linked into
+// libceiling.so, loaded by the benchmark); every index stays inside the
+// [64, 32000] buffers.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+constexpr int kRows = 64, kCols = 32000, kChunks = kCols / 8;  // chunks of 8 floats
+constexpr int kPer = (kChunks + 255) / 256;                   // chunks per lane (16)
+constexpr float kL2e = 1.44269504088896340736f;
+
+__global__ __launch_bounds__(256) void empty_kernel(float* out) {
+    if (threadIdx.x == 1023) out[0] = 1.0f;  // never true for 256 threads
+}
+
+// Every chunk of lane tid (tid, tid + 256, ...) loaded before any use; the
+// chunk index is clamped to the row, so the loads carry no branch.
+__device__ __forceinline__ void load_row(const float* __restrict__ row, f32x4 (&v)[kPer][2]) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        int c = static_cast<int>(threadIdx.x) + i * 256;
+        c = c < kChunks ? c : kChunks - 1;
+        v[i][0] = *reinterpret_cast<const f32x4*>(row + c * 8);
+        v[i][1] = *reinterpret_cast<const f32x4*>(row + c * 8 + 4);
+    }
+}
+
+// The online fold of the row kernels on values already in registers: a
+// running max per group of 4 chunks, t = x log2(e) - mL, S += 2^t.
+template <int PER>
+__device__ __forceinline__ void fold(const f32x4 (&v)[PER][2], float& m, float& mL, float& S) {
+#pragma unroll
+    for (int g = 0; g < PER / 4; ++g) {
+        float gm = m;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const f32x4 a = v[g * 4 + u][0], b = v[g * 4 + u][1];
+            gm = fmaxf(gm, fmaxf(fmaxf(fmaxf(a.x, a.y), fmaxf(a.z, a.w)),
+                                 fmaxf(fmaxf(b.x, b.y), fmaxf(b.z, b.w))));
+        }
+        if (gm > m) {
+            const float nl = gm * kL2e;
+            S *= __builtin_amdgcn_exp2f(mL - nl);
+            m = gm;
+            mL = nl;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const f32x4 a = v[g * 4 + u][0], b = v[g * 4 + u][1];
+            const float e[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+            for (int k = 0; k < 8; ++k) S += __builtin_amdgcn_exp2f(__builtin_fmaf(e[k], kL2e, -mL));
+        }
+    }
+}
+
+__device__ __forceinline__ float plain_sum(float s) {
+    for (int o = 32; o; o >>= 1) s += __shfl_xor(s, o, 64);
+    __shared__ float r[4];
+    if ((threadIdx.x & 63) == 0) r[threadIdx.x >> 6] = s;
+    __syncthreads();
+    return r[0] + r[1] + r[2] + r[3];
+}
+
+// one 256-thread workgroup per row, every load in flight at once
+__global__ __launch_bounds__(256) void row_read(const float* __restrict__ x, float* out) {
+    f32x4 v[kPer][2];
+    load_row(x + static_cast<int64_t>(blockIdx.x) * kCols, v);
+    float s = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i)
+        s += v[i][0].x + v[i][0].y + v[i][0].z + v[i][0].w + v[i][1].x + v[i][1].y + v[i][1].z +
+             v[i][1].w;
+    s = plain_sum(s);
+    if (threadIdx.x == 0) out[blockIdx.x] = s;
+}
+
+// ... plus the online fold of every element
+__global__ __launch_bounds__(256) void row_fold(const float* __restrict__ x, float* out) {
+    f32x4 v[kPer][2];
+    load_row(x + static_cast<int64_t>(blockIdx.x) * kCols, v);
+    float m = -__builtin_inff(), mL = 0.0f, S = 0.0f;
+    fold<kPer>(v, m, mL, S);
+    const float s = plain_sum(S + mL);
+    if (threadIdx.x == 0) out[blockIdx.x] = s;
+}
+
+// ... plus the epilogue of the forward row kernels: a wave64 butterfly that
+// merges (m, mL, S), the fold over the four waves, log2, a 32-byte row
+// record, and one target's log-probability gathered from the row
+__global__ __launch_bounds__(256) void row_fold_epilogue(const float* __restrict__ x,
+                                                         const int64_t* __restrict__ targets,
+                                                         float* __restrict__ stats,
+                                                         float* __restrict__ out) {
+    const float* row = x + static_cast<int64_t>(blockIdx.x) * kCols;
+    int64_t t0 = -1;
+    if (threadIdx.x == 0) t0 = targets[blockIdx.x];
+    f32x4 v[kPer][2];
+    load_row(row, v);
+    float xt = 0.0f;
+    if (t0 >= 0 && t0 < kCols) xt = row[t0];
+    float m = -__builtin_inff(), mL = 0.0f, S = 0.0f;
+    fold<kPer>(v, m, mL, S);
+    for (int o = 32; o; o >>= 1) {
+        const float om = __shfl_xor(m, o, 64), oL = __shfl_xor(mL, o, 64), oS = __shfl_xor(S, o, 64);
+        const bool big = m >= om;
+        const float nL = big ? mL : oL;
+        S = S * __builtin_amdgcn_exp2f(mL - nL) + oS * __builtin_amdgcn_exp2f(oL - nL);
+        m = big ? m : om;
+        mL = nL;
+    }
+    __shared__ float red[4][3];
+    __shared__ float bc[2];
+    if ((threadIdx.x & 63) == 0) {
+        red[threadIdx.x >> 6][0] = m;
+        red[threadIdx.x >> 6][1] = mL;
+        red[threadIdx.x >> 6][2] = S;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float M = red[0][0], ML = red[0][1], SS = red[0][2];
+        for (int w = 1; w < 4; ++w) {
+            const bool big = M >= red[w][0];
+            const float nL = big ? ML : red[w][1];
+            SS = SS * __builtin_amdgcn_exp2f(ML - nL) + red[w][2] * __builtin_amdgcn_exp2f(red[w][1] - nL);
+            M = big ? M : red[w][0];
+            ML = nL;
+        }
+        const float l2 = log2f(SS);
+        f32x4* st = reinterpret_cast<f32x4*>(stats + static_cast<int64_t>(blockIdx.x) * 8);
+        st[0] = f32x4{ML, l2, 0.0f, 0.0f};
+        st[1] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        bc[0] = ML;
+        bc[1] = l2;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) out[blockIdx.x] = (xt * kL2e - bc[0] - bc[1]) * 0.69314718f;
+}
+
+// four workgroups per row, each folding a quarter of every lane's chunks
+// (a different reduction tree: the lower bound of splitting a row's fold)
+__global__ __launch_bounds__(256) void row_fold_quarter(const float* __restrict__ x, float* out) {
+    const int row = blockIdx.x / 4, q = blockIdx.x % 4;
+    const float* rp = x + static_cast<int64_t>(row) * kCols;
+    f32x4 v[kPer / 4][2];
+#pragma unroll
+    for (int i = 0; i < kPer / 4; ++i) {
+        int c = static_cast<int>(threadIdx.x) + (q * (kPer / 4) + i) * 256;
+        c = c < kChunks ? c : kChunks - 1;
+        v[i][0] = *reinterpret_cast<const f32x4*>(rp + c * 8);
+        v[i][1] = *reinterpret_cast<const f32x4*>(rp + c * 8 + 4);
+    }
+    float m = -__builtin_inff(), mL = 0.0f, S = 0.0f;
+    fold<kPer / 4>(v, m, mL, S);
+    const float s = plain_sum(S + mL);
+    if (threadIdx.x == 0) out[blockIdx.x] = s;
+}
+
+// one-shot pieces of the backward's shape: grid (16, 64), one chunk per lane,
+// read, scale, streaming store
+__global__ __launch_bounds__(256) void copy_pieces(const float* __restrict__ x,
+                                                   float* __restrict__ y) {
+    const int c = blockIdx.x * 256 + threadIdx.x;
+    if (c >= kChunks) return;
+    const int64_t off = static_cast<int64_t>(blockIdx.y) * kCols + c * 8;
+    const f32x4* p = reinterpret_cast<const f32x4*>(x + off);
+    const f32x4 a = p[0], b = p[1];
+    f32x4* q = reinterpret_cast<f32x4*>(y + off);
+    __builtin_nontemporal_store(a * 2.0f, q);
+    __builtin_nontemporal_store(b * 2.0f, q + 1);
+}
+
+}  // namespace
+
+extern "C" {
+
+// Shape of the probes' buffers: x and y [64, 32000] fp32, targets [64] int64,
+// stats [64, 8] fp32, out [256] fp32.
+int launch_floor_rows(void) { return kRows; }
+int launch_floor_cols(void) { return kCols; }
+
+// Launch probe kind_a, then (if kind_b >= 0) probe kind_b, `reps` times in a
+// row on `stream`, from this host loop (a launch per call from Python would
+// time the interpreter, not the GPU).  Kinds: 0 empty (64 workgroups),
+// 1 empty (1024 workgroups), 2 row_read, 3 row_fold, 4 row_fold_epilogue,
+// 5 row_fold_quarter, 6 copy_pieces.  Returns 0, -1 for an unknown kind, or
+// the first launch error.
+static int launch_one(int kind, const float* x, float* y, const int64_t* targets, float* stats,
+                      float* out, hipStream_t s) {
+    switch (kind) {
+        case 0: hipLaunchKernelGGL(empty_kernel, dim3(kRows), dim3(256), 0, s, out); break;
+        case 1: hipLaunchKernelGGL(empty_kernel, dim3(1024), dim3(256), 0, s, out); break;
+        case 2: hipLaunchKernelGGL(row_read, dim3(kRows), dim3(256), 0, s, x, out); break;
+        case 3: hipLaunchKernelGGL(row_fold, dim3(kRows), dim3(256), 0, s, x, out); break;
+        case 4:
+            hipLaunchKernelGGL(row_fold_epilogue, dim3(kRows), dim3(256), 0, s, x, targets, stats,
+                               out);
+            break;
+        case 5: hipLaunchKernelGGL(row_fold_quarter, dim3(kRows * 4), dim3(256), 0, s, x, out); break;
+        case 6: hipLaunchKernelGGL(copy_pieces, dim3(16, kRows), dim3(256), 0, s, x, y); break;
+        default: return -1;
+    }
+    return static_cast<int>(hipGetLastError());
+}
+
+int launch_floor_run(int kind_a, int kind_b, int reps, const float* x, float* y,
+                     const int64_t* targets, float* stats, float* out, void* stream) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    for (int r = 0; r < reps; ++r) {
+        int rc = launch_one(kind_a, x, y, targets, stats, out, s);
+        if (rc == 0 && kind_b >= 0) rc = launch_one(kind_b, x, y, targets, stats, out, s);
+        if (rc != 0) return rc;
+    }
+    return 0;
+}
+
+}  // extern "C"
