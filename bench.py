@@ -215,7 +215,8 @@ def measure_launch_floor(dev, torch) -> dict:
     back-to-back launch intervals of empty kernels, a one-workgroup-per-row
     read with every load in flight, the same with the row kernels' online
     fold and with their epilogue, the fold split over four workgroups per
-    row, the backward's one-shot pieces, and pairs of them; beside them the
+    row (alone, and with a last-arriver combine and the epilogue in the same
+    launch), the backward's one-shot pieces, and pairs of them; beside them the
     library's own forward, backward and step on the workload.  Each figure is
     the best of 5 runs of 500 back-to-back launches (HIP events, mean per
     launch); the probes are launched from a C loop, the library through its
@@ -262,10 +263,12 @@ def measure_launch_floor(dev, torch) -> dict:
     names = ["empty, 64 workgroups", "empty, 1024 workgroups",
              "row read, one workgroup per row, every load in flight",
              "row read + online fold", "row read + fold + forward epilogue",
-             "fold split over 4 workgroups per row", "backward-shaped one-shot pieces (copy)"]
+             "fold split over 4 workgroups per row", "backward-shaped one-shot pieces (copy)",
+             "fold split over 4 workgroups per row + last-arriver combine and epilogue"]
     res = {n: best_us(probe(k)) for k, n in enumerate(names)}
     res["pair: empty + empty"] = best_us(probe(0, 1))
     res["pair: read + fold + epilogue, then one-shot pieces"] = best_us(probe(4, 6))
+    res["pair: split + combine, then one-shot pieces"] = best_us(probe(7, 6))
     tg2, g = d["targets"], d["grad"]
     lp = torch.empty(tg2.shape, dtype=torch.float32, device=dev)
     st = rlk.new_stats(rlk.RLK_HEAD_LOGP, R, C, dev)

@@ -162,6 +162,78 @@ __global__ __launch_bounds__(256) void row_fold_quarter(const float* __restrict_
     if (threadIdx.x == 0) out[blockIdx.x] = s;
 }
 
+// The fold split over four workgroups per row with the combine in the same
+// launch: each workgroup reduces its quarter like the row kernels' epilogue,
+// publishes (mL, S), and the last of the row's four to arrive (an acq_rel
+// counter per row, reset by that workgroup) merges the four in quarter order
+// and writes the record and the target's log-probability.  Nothing waits, so
+// every workgroup ends whatever the others do.
+__device__ int split_count[kRows];
+__device__ float split_part[kRows][4][2];
+
+__global__ __launch_bounds__(256) void row_split_combine(const float* __restrict__ x,
+                                                         const int64_t* __restrict__ targets,
+                                                         float* __restrict__ stats,
+                                                         float* __restrict__ out) {
+    const int row = blockIdx.x / 4, q = blockIdx.x % 4;
+    const float* rp = x + static_cast<int64_t>(row) * kCols;
+    f32x4 v[kPer / 4][2];
+#pragma unroll
+    for (int i = 0; i < kPer / 4; ++i) {
+        int c = static_cast<int>(threadIdx.x) + (q * (kPer / 4) + i) * 256;
+        c = c < kChunks ? c : kChunks - 1;
+        v[i][0] = *reinterpret_cast<const f32x4*>(rp + c * 8);
+        v[i][1] = *reinterpret_cast<const f32x4*>(rp + c * 8 + 4);
+    }
+    float m = -__builtin_inff(), mL = 0.0f, S = 0.0f;
+    fold<kPer / 4>(v, m, mL, S);
+    for (int o = 32; o; o >>= 1) {
+        const float om = __shfl_xor(m, o, 64), oL = __shfl_xor(mL, o, 64), oS = __shfl_xor(S, o, 64);
+        const bool big = m >= om;
+        const float nL = big ? mL : oL;
+        S = S * __builtin_amdgcn_exp2f(mL - nL) + oS * __builtin_amdgcn_exp2f(oL - nL);
+        m = big ? m : om;
+        mL = nL;
+    }
+    __shared__ float red[4][2];
+    __shared__ int last;
+    if ((threadIdx.x & 63) == 0) {
+        red[threadIdx.x >> 6][0] = mL;
+        red[threadIdx.x >> 6][1] = S;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float ML = red[0][0], SS = red[0][1];
+        for (int w = 1; w < 4; ++w) {
+            const float nL = ML >= red[w][0] ? ML : red[w][0];
+            SS = SS * __builtin_amdgcn_exp2f(ML - nL) + red[w][1] * __builtin_amdgcn_exp2f(red[w][0] - nL);
+            ML = nL;
+        }
+        split_part[row][q][0] = ML;
+        split_part[row][q][1] = SS;
+        const int before = __hip_atomic_fetch_add(&split_count[row], 1, __ATOMIC_ACQ_REL,
+                                                  __HIP_MEMORY_SCOPE_AGENT);
+        last = before == 3;
+    }
+    __syncthreads();
+    if (!last || threadIdx.x != 0) return;
+    const int64_t t0 = targets[row];
+    const float xt = (t0 >= 0 && t0 < kCols) ? rp[t0] : 0.0f;
+    float ML = split_part[row][0][0], SS = split_part[row][0][1];
+    for (int j = 1; j < 4; ++j) {
+        const float oL = split_part[row][j][0], oS = split_part[row][j][1];
+        const float nL = ML >= oL ? ML : oL;
+        SS = SS * __builtin_amdgcn_exp2f(ML - nL) + oS * __builtin_amdgcn_exp2f(oL - nL);
+        ML = nL;
+    }
+    __hip_atomic_store(&split_count[row], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const float l2 = log2f(SS);
+    f32x4* st = reinterpret_cast<f32x4*>(stats + static_cast<int64_t>(row) * 8);
+    st[0] = f32x4{ML, l2, 0.0f, 0.0f};
+    st[1] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    out[row] = (xt * kL2e - ML - l2) * 0.69314718f;
+}
+
 // one-shot pieces of the backward's shape: grid (16, 64), one chunk per lane,
 // read, scale, streaming store
 __global__ __launch_bounds__(256) void copy_pieces(const float* __restrict__ x,
@@ -189,8 +261,8 @@ int launch_floor_cols(void) { return kCols; }
 // row on `stream`, from this host loop (a launch per call from Python would
 // time the interpreter, not the GPU).  Kinds: 0 empty (64 workgroups),
 // 1 empty (1024 workgroups), 2 row_read, 3 row_fold, 4 row_fold_epilogue,
-// 5 row_fold_quarter, 6 copy_pieces.  Returns 0, -1 for an unknown kind, or
-// the first launch error.
+// 5 row_fold_quarter, 6 copy_pieces, 7 row_split_combine.  Returns 0, -1 for an
+// unknown kind, or the first launch error.
 static int launch_one(int kind, const float* x, float* y, const int64_t* targets, float* stats,
                       float* out, hipStream_t s) {
     switch (kind) {
@@ -204,6 +276,10 @@ static int launch_one(int kind, const float* x, float* y, const int64_t* targets
             break;
         case 5: hipLaunchKernelGGL(row_fold_quarter, dim3(kRows * 4), dim3(256), 0, s, x, out); break;
         case 6: hipLaunchKernelGGL(copy_pieces, dim3(16, kRows), dim3(256), 0, s, x, y); break;
+        case 7:
+            hipLaunchKernelGGL(row_split_combine, dim3(kRows * 4), dim3(256), 0, s, x, targets,
+                               stats, out);
+            break;
         default: return -1;
     }
     return static_cast<int>(hipGetLastError());
