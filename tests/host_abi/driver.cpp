@@ -151,7 +151,7 @@ static void test_logp() {
             EXPECT_LAUNCH(0, rlk_logp_bwd(x, d, N, V, ld, t, k, cap, st, g, gx, nullptr));
             CHECK(g_log.kind == stub::kBwd && g_log.bwd.mg.st == V && g_log.bwd.k == k);
             if (want == rlk::kCapFixed)
-                CHECK(std::fabs(g_log.bwd.spx / (2.0 * cap * 1.4426950408889634) - 1.0) < 1e-6);
+                CHECK(std::fabs(g_log.bwd.ix * 2.0 * cap * 1.4426950408889634 - 1.0) < 1e-6);
         }
         // the row stride decides the alignment: ld = 1033 is not 16-byte aligned
         EXPECT_LAUNCH(0, rlk_logp_fwd(x, d, N, V, 1033, t, k, 0.0f, out, st, nullptr));

@@ -85,9 +85,6 @@ float cap_sc(float c) {
 float cap_isc(float c) {
     return cap_mode(c) == rlk::kCapFixed ? static_cast<float>(1.0 / (2.0 * c * kLog2eD)) : 0.0f;
 }
-float cap_span(float c) {
-    return cap_mode(c) == rlk::kCapFixed ? static_cast<float>(2.0 * c * kLog2eD) : 0.0f;
-}
 
 // Device that owns `ptr` (device or managed memory only).
 rlk_status pointer_device(const void* ptr, const char* name, int* dev) {
@@ -309,7 +306,6 @@ rlk_status logp_bwd_impl(const void* logits, rlk_dtype dtype, int64_t N, int64_t
     p.kx = cap_k(softcap);
     p.scx = cap_sc(softcap);
     p.ix = cap_isc(softcap);
-    p.spx = cap_span(softcap);
     p.stats = stats;
     p.g = grad_logp;
     p.gx = grad_logits;
@@ -371,7 +367,6 @@ rlk_status entropy_bwd_impl(const void* logits, rlk_dtype dtype, int64_t N, int6
     p.kx = cap_k(softcap);
     p.scx = cap_sc(softcap);
     p.ix = cap_isc(softcap);
-    p.spx = cap_span(softcap);
     p.stats = stats;
     p.g = grad_entropy;
     p.gx = grad_logits;
@@ -456,10 +451,8 @@ rlk_status kl_bwd_impl(const void* policy, const void* ref, rlk_dtype dtype, int
     p.ky = cap_k(cy);
     p.scx = cap_sc(cx);
     p.ix = cap_isc(cx);
-    p.spx = cap_span(cx);
     p.scy = cap_sc(cy);
     p.iy = cap_isc(cy);
-    p.spy = cap_span(cy);
     p.stats = stats;
     p.swap = wrt_ref ? 1 : 0;
     p.g = grad_kl;
@@ -909,7 +902,6 @@ rlk_status rlk_logp_bwd_shard(const void* logits, rlk_dtype dtype, int64_t N, in
     p.kx = cap_k(softcap);
     p.scx = cap_sc(softcap);
     p.ix = cap_isc(softcap);
-    p.spx = cap_span(softcap);
     p.stats = stats;
     p.g = grad_logp;
     p.gx = grad_logits;

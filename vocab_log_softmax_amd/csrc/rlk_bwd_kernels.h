@@ -36,6 +36,21 @@ constexpr int kWideScanMax = 16;
 // Row modes.
 enum : int { kModeNormal = 0, kModeZero = 1, kModeNaN = 2, kModeMismatch = 3 };
 
+// Which flags a record can carry, by the cap forms of its sides.  Every
+// forward starts a fixed-form side's reference at 0, so that side is never
+// empty (an all-NaN row of it yields NaN values through the arithmetic);
+// a capped logit is never -inf, so reverse KL flags no support mismatch
+// when both sides are capped.  The backward tests only the flags that can
+// be set.
+template <int CAP>
+constexpr bool can_be_empty() {
+    return CAP != kCapFixed;
+}
+template <int CAPA, int CAPB>
+constexpr bool can_mismatch() {
+    return CAPA == kCapNone || CAPB == kCapNone;
+}
+
 // The record with its a and b sides exchanged (gradient w.r.t. the KL
 // reference: the operands are exchanged too).
 __device__ __forceinline__ void swap_sides(RowStats& rs) {
@@ -102,6 +117,16 @@ __device__ __forceinline__ void fixed_refs(RowStats& rs) {
     }
 }
 
+// A gradient as the rounded fp32 value it is.  The empty asm operand hides
+// how it was computed from the conversion to a 16-bit gradient, which the
+// compiler would otherwise fuse with a last product on some store paths
+// (v_fma_mix: one rounding instead of two) and not on others, so that the
+// bits would depend on the path.  It emits no instruction.
+__device__ __forceinline__ float rounded(float v) {
+    __asm__("" : "+v"(v));
+    return v;
+}
+
 // Gradient of one element from its statistic inputs (a; b for KL), the
 // cap's slope s up to its factor (cap_value_slope) and the row's record and
 // coefficients; the exponent t comes from the forward's own FMA.
@@ -129,7 +154,7 @@ __device__ __forceinline__ float grad_elem(float a, float s, float b, const RowS
         }
     }
     if (C) o *= s;  // the slope's factor is in A, B
-    return o;
+    return rounded(o);
 }
 
 // Logprobs gradient at a target column: h - p G (h: the column's summed
@@ -139,7 +164,7 @@ __device__ __forceinline__ float target_grad(float a, float s, float cf, const R
                                              float G, float h, float scx) {
     const float pt = ex2(__builtin_fmaf(a, scx, -rs.mLa) - rs.log2Sa);
     const float v = __builtin_fmaf(-pt, G, h);
-    return CAPA != kCapNone ? v * (cf * s) : v;
+    return rounded(CAPA != kCapNone ? v * (cf * s) : v);
 }
 
 // Slots of bwd_topk_kernel: the sort keys are padded to a power of two.
@@ -184,7 +209,7 @@ __global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void bwd_topk_kernel(BwdParams
     constexpr uint64_t kNoKey = ~0ull;
     uint64_t* keys = smem_topk;
     float* gg = reinterpret_cast<float*>(smem_topk + kpad);
-    const CapArgs ca{p.kx, p.ix, p.spx};
+    const CapArgs ca{p.kx, p.ix, CAPA == kCapFixed ? fixed_span(p.ix) : 0.0f};
     const float cf = slope_factor<CAPA>(ca);
 
     for (int64_t it = blockIdx.x; it < p.N * p.split; it += gridDim.x) {
@@ -229,7 +254,9 @@ __global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void bwd_topk_kernel(BwdParams
             G += red_g[w];
             n += red_n[w];
         }
-        const int mode = n == 0.0f ? kModeZero : ((rs.flags & kFlagEmptyA) ? kModeNaN : kModeNormal);
+        const int mode = n == 0.0f ? kModeZero
+                         : (can_be_empty<CAPA>() && (rs.flags & kFlagEmptyA)) ? kModeNaN
+                                                                               : kModeNormal;
 
         if (mode == kModeNormal) {
             float A, B;
@@ -345,7 +372,7 @@ __device__ __forceinline__ void piece(const BwdParams& p, int64_t row, int64_t g
         tail_values<BLOCK, U, S, kCapNone, ALIGNED, NT>(xa, p.V, nfull, g0, CapArgs{}, x);
         if (KL) tail_values<BLOCK, U, S, CAPB, ALIGNED, NT>(xb, p.V, nfull, g0, cb, b);
     }
-    const CapArgs ca{p.kx, p.ix, p.spx};
+    const CapArgs ca{p.kx, p.ix, CAPA == kCapFixed ? fixed_span(p.ix) : 0.0f};
     const float cf = slope_factor<CAPA>(ca);
 
     if (FULL) {
@@ -390,14 +417,17 @@ __device__ __forceinline__ void piece(const BwdParams& p, int64_t row, int64_t g
         G = (sv[0] + sv[2]) + (sv[1] + sv[3]);
         if (nvalid == 0)
             mode = kModeZero;
-        else if (rs.flags & kFlagEmptyA)
+        else if (can_be_empty<CAPA>() && (rs.flags & kFlagEmptyA))
             mode = kModeNaN;
     } else if (HEAD == kHeadEntropy) {
-        if (rs.flags & kFlagEmptyA) mode = kModeNaN;
+        if (can_be_empty<CAPA>() && (rs.flags & kFlagEmptyA)) mode = kModeNaN;
     } else {
-        if (rs.flags & (kFlagEmptyA | kFlagEmptyB))
+        // (the reference gradient exchanges the sides: both are tested)
+        if ((can_be_empty<CAPA>() || can_be_empty<CAPB>()) &&
+            (rs.flags & (kFlagEmptyA | kFlagEmptyB)))
             mode = kModeNaN;
-        else if (HEAD == kHeadKLReverse && (rs.flags & kFlagMismatch))
+        else if (HEAD == kHeadKLReverse && can_mismatch<CAPA, CAPB>() &&
+                 (rs.flags & kFlagMismatch))
             mode = kModeMismatch;
     }
     if (FULL) {
@@ -628,12 +658,14 @@ __device__ __forceinline__ void wide_piece(const BwdParams& p, int64_t row, int6
         }
         __syncthreads();
     }
-    const int mode = n == 0.0f ? kModeZero : ((rs.flags & kFlagEmptyA) ? kModeNaN : kModeNormal);
+    const int mode = n == 0.0f ? kModeZero
+                     : (can_be_empty<CAPA>() && (rs.flags & kFlagEmptyA)) ? kModeNaN
+                                                                           : kModeNormal;
     if (FULL) raw_unpack(raw, x);
 
     float v[U][kChunk];
     if (mode == kModeNormal) {
-        const CapArgs ca{p.kx, p.ix, p.spx};
+        const CapArgs ca{p.kx, p.ix, CAPA == kCapFixed ? fixed_span(p.ix) : 0.0f};
         const float cf = slope_factor<CAPA>(ca);
         float A, B;
         row_coeffs<kHeadLogp, CAPA>(rs, G, 0.0f, cf, A, B);

@@ -186,7 +186,7 @@ __device__ __forceinline__ void store_one(_Float16* p, float f) { *p = static_ca
 struct CapArgs {
     float k;     // -2 log2(e) / c
     float isc;   // fixed form: 1 / sc
-    float span;  // fixed form, backward: sc
+    float span;  // fixed form, backward: w where 2^(-k x) = 0, i.e. rcp(isc) (fixed_span)
     const float* tab = nullptr;  // table forms: sc/2 + t(|x|) by 16-bit magnitude (LDS)
     float half = 0.0f;           // odd forms: sc/2
 };
@@ -230,11 +230,12 @@ __device__ __forceinline__ float cap_value(float x, CapArgs c) {
 // Statistic input a and the slope 1 - tanh^2 up to a factor fixed per cap
 // (slope_factor): s = r (1 - r) in the online form.  Fixed form: with
 // q = 2^(-k x) and w = sc / (1 + q) (so a = -w), sc (1 - r) = w and
-// sc r = q w, so s = (q w) w = r (1 - r) sc^2.  q w is inf * 0 only at
-// x = +inf, where the minimum with sc gives r = 1 (a NaN x stays NaN through
-// w).  Neither factor is a difference, so the slope keeps its relative
-// accuracy in both tails, and it is exactly 0 at x = -inf (q = 0) and at
-// x = +inf (w = 0).
+// sc r = sc - w, so s = (sc - w) w = r (1 - r) sc^2, with sc taken as the
+// very w of q = 0 (c.span = fixed_span): s is exactly 0 at x = -inf
+// (q = 0, w = span) and at x = +inf (q = inf, w = 0), and a NaN x stays NaN
+// through w.  Towards x = -inf the difference keeps its absolute accuracy
+// (about 2^-23 sc^2 in s, 2^-21 in the slope), not a relative one; the
+// gradient's error bounds are absolute there.
 template <int CAP>
 __device__ __forceinline__ float cap_value_slope(float x, CapArgs c, float& s) {
     if (CAP == kCapOnline) {
@@ -245,12 +246,16 @@ __device__ __forceinline__ float cap_value_slope(float x, CapArgs c, float& s) {
     if (CAP == kCapFixed) {
         const float q = ex2(-(x * c.k));
         const float w = rcp(__builtin_fmaf(q, c.isc, c.isc));
-        s = fminf(q * w, c.span) * w;
+        s = (c.span - w) * w;
         return -w;
     }
     s = 1.0f;
     return x;
 }
+
+// The fixed form's span for cap_value_slope: its w at q = 0, by the same
+// reciprocal, so that the slope vanishes exactly there.
+__device__ __forceinline__ float fixed_span(float isc) { return rcp(__builtin_fmaf(0.0f, isc, isc)); }
 
 // The slope is slope_factor * s: 4 (online form), 4 / sc^2 (fixed form).
 template <int CAP>

@@ -190,7 +190,6 @@ struct BwdParams {
     const int64_t* targets;
     int64_t k;
     float kx, ky, scx, scy, ix, iy;
-    float spx, spy;  // fixed cap: 2 c log2(e), the span of its t (else unused)
     const void* stats;
     const float* g;  // upstream gradient: [N, k] (logp) or [N]
     void* gx;        // gradient w.r.t. x, [N, V] contiguous, logits dtype
