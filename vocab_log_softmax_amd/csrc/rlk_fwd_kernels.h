@@ -302,7 +302,7 @@ __global__ __launch_bounds__(kTabRows* kBlock) void fwd1_tab_kernel(FwdParams p,
     // entries skip the exponential and the reciprocal (same bits).
     for (int i = threadIdx.x; i < kTabSize; i += kTabRows * BLOCK) {
         const float v = from_bits16<S>(static_cast<uint32_t>(i));
-        tab[i] = -(v * cf.k) >= 128.0f ? half : half + cap_value<kCapFixed>(v, cf);
+        tab[i] = tab_entry(-(v * cf.k) >= 128.0f ? half : half + cap_value<kCapFixed>(v, cf));
     }
     CapArgs ct = cf;
     ct.tab = tab;
