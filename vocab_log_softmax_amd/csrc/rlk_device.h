@@ -354,7 +354,8 @@ __device__ __forceinline__ void raw_load(const float* __restrict__ row, int64_t 
 // keeps it in scalar registers), its range the group's bytes, and each lane
 // adds a 32-bit offset, so a group costs no 64-bit vector address arithmetic
 // (the KL forward's loop lost 2% of its VALU instructions).  The policy bit
-// nt (2) is the non-temporal load's.  The backward's one-shot pieces keep
+// nt (2) is the non-temporal load's; a range shorter than the group (bytes)
+// reads 0 beyond it.  The backward's one-shot pieces keep
 // raw_load's global loads, with which they measured faster (logprobs
 // backward, bf16 [8192, 151936]: 743 us against 761 us).
 template <typename S>
@@ -364,11 +365,13 @@ __device__ __forceinline__ void* wave_base(const S* p) {
     const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32));
     return reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
 }
-template <int BLOCK, int U, bool MULTI, typename S>
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t group_rsrc(const S* row, int64_t g0) {
-    constexpr int kGroupBytes = BLOCK * U * kChunk * static_cast<int>(sizeof(S));
-    return __builtin_amdgcn_make_buffer_rsrc(wave_base(row + g0 * kChunk), 0, kGroupBytes,
-                                             0x00020000);
+template <int BLOCK, int U, typename S>
+constexpr int group_bytes() {
+    return BLOCK * U * kChunk * static_cast<int>(sizeof(S));
+}
+template <typename S>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t group_rsrc(const S* row, int64_t g0, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(wave_base(row + g0 * kChunk), 0, bytes, 0x00020000);
 }
 template <int BLOCK, bool MULTI, typename S>
 __device__ __forceinline__ int lane_offset(int u) {
@@ -376,8 +379,9 @@ __device__ __forceinline__ int lane_offset(int u) {
 }
 template <int BLOCK, int U, bool NT, bool MULTI = false>
 __device__ __forceinline__ void raw_load_walk(const uint16_t* __restrict__ row, int64_t g0,
-                                         RawGroup<uint16_t, U>& r) {
-    const __amdgpu_buffer_rsrc_t rs = group_rsrc<BLOCK, U, MULTI>(row, g0);
+                                              RawGroup<uint16_t, U>& r,
+                                              int bytes = group_bytes<BLOCK, U, uint16_t>()) {
+    const __amdgpu_buffer_rsrc_t rs = group_rsrc(row, g0, bytes);
 #pragma unroll
     for (int u = 0; u < U; ++u)
         r.v[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
@@ -386,8 +390,9 @@ __device__ __forceinline__ void raw_load_walk(const uint16_t* __restrict__ row, 
 }
 template <int BLOCK, int U, bool NT, bool MULTI = false>
 __device__ __forceinline__ void raw_load_walk(const _Float16* __restrict__ row, int64_t g0,
-                                         RawGroup<_Float16, U>& r) {
-    const __amdgpu_buffer_rsrc_t rs = group_rsrc<BLOCK, U, MULTI>(row, g0);
+                                              RawGroup<_Float16, U>& r,
+                                              int bytes = group_bytes<BLOCK, U, _Float16>()) {
+    const __amdgpu_buffer_rsrc_t rs = group_rsrc(row, g0, bytes);
 #pragma unroll
     for (int u = 0; u < U; ++u)
         r.v[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
@@ -396,8 +401,9 @@ __device__ __forceinline__ void raw_load_walk(const _Float16* __restrict__ row, 
 }
 template <int BLOCK, int U, bool NT, bool MULTI = false>
 __device__ __forceinline__ void raw_load_walk(const float* __restrict__ row, int64_t g0,
-                                         RawGroup<float, U>& r) {
-    const __amdgpu_buffer_rsrc_t rs = group_rsrc<BLOCK, U, MULTI>(row, g0);
+                                              RawGroup<float, U>& r,
+                                              int bytes = group_bytes<BLOCK, U, float>()) {
+    const __amdgpu_buffer_rsrc_t rs = group_rsrc(row, g0, bytes);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int off = lane_offset<BLOCK, MULTI, float>(u);
@@ -510,49 +516,88 @@ __device__ __forceinline__ void fast_values(const RawGroup<S, U>& r, CapArgs ca,
 // flight while the current group is consumed.  The order in which f sees the
 // groups, and the values, are the same for every path.
 //
+// The last group of an aligned row of whole chunks (V a multiple of 8) that
+// does not fill a group is read the same way, through a resource that ends
+// at the row's end: its chunks are each wholly inside the row or wholly
+// beyond it (read as 0, then set to -inf, as tail_values does), so it is
+// prefetched behind the last full group instead of being loaded after it,
+// and f receives the values tail_values would give (full = false).  (The
+// two-row walk below keeps tail_values for that group: the prefetch took
+// the KL forward from 116 to 136 VGPRs and measured 1.4% slower.)
+//
 // gbeg / gend restrict the walk to the groups [gbeg, gend) of the row (a
 // column segment); -1 for gend means "to the end of the row".
+template <int BLOCK, int U, bool MULTI>
+__device__ __forceinline__ void beyond_row(int64_t g0, int64_t nchunks, float (&a)[U][kChunk]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+        if (g0 + u * BLOCK + row_lane<BLOCK, MULTI>() >= nchunks) {
+#pragma unroll
+            for (int e = 0; e < kChunk; ++e) a[u][e] = neg_inf();
+        }
+}
 template <int BLOCK, int U, typename S, int CAP, bool ALIGNED, bool PIPE, bool NT, typename F>
 __device__ __forceinline__ void for_each_group(const S* __restrict__ row, int64_t V, CapArgs k, F&& f,
                                                int64_t gbeg = 0, int64_t gend = -1) {
+    constexpr bool MULTI = multi_row(CAP);
     const int64_t step = (int64_t)U * BLOCK;
     const int64_t nchunks = (V + kChunk - 1) / kChunk, nfull = V / kChunk;
     const int64_t ngroups = (nchunks + step - 1) / step;
     if (gend < 0 || gend > ngroups) gend = ngroups;
     const int64_t nfg_row = ALIGNED ? nfull / step : 0;  // full aligned groups of the row
     const int64_t nfg = nfg_row < gend ? nfg_row : gend;
+    // the row's last group, partial, read like a full one
+    const bool last_raw =
+        ALIGNED && nfull == nchunks && nfg_row < ngroups && gend == ngroups && gbeg <= nfg_row;
+    const int64_t nraw = nfg + (last_raw ? 1 : 0);
+    const int last_bytes =
+        last_raw ? static_cast<int>((nchunks - nfg_row * step) * kChunk * sizeof(S)) : 0;
+    auto load = [&](int64_t g, RawGroup<S, U>& r) {
+        if (g < nfg)
+            raw_load_walk<BLOCK, U, NT, MULTI>(row, g * step, r);
+        else
+            raw_load_walk<BLOCK, U, NT, MULTI>(row, g * step, r, last_bytes);
+    };
+    auto full = [&](int64_t g, const RawGroup<S, U>& r) {
+        float a[U][kChunk];
+        fast_values<U, S, CAP>(r, k, a);
+        f(g * step, true, a);
+    };
+    auto last = [&](int64_t g, const RawGroup<S, U>& r) {
+        float a[U][kChunk];
+        fast_values<U, S, CAP>(r, k, a);
+        beyond_row<BLOCK, U, MULTI>(g * step, nchunks, a);
+        f(g * step, false, a);
+    };
     int64_t gi = gbeg;
-    if (PIPE && gi < nfg) {
+    if (PIPE && gi < nraw) {
         RawGroup<S, U> A, B;
-        raw_load_walk<BLOCK, U, NT, multi_row(CAP)>(row, gi * step, A);
+        load(gi, A);
         for (; gi + 1 < nfg; gi += 2) {
-            raw_load_walk<BLOCK, U, NT, multi_row(CAP)>(row, (gi + 1) * step, B);
-            {
-                float a[U][kChunk];
-                fast_values<U, S, CAP>(A, k, a);
-                f(gi * step, true, a);
-            }
-            if (gi + 2 < nfg)
-                raw_load_walk<BLOCK, U, NT, multi_row(CAP)>(row, (gi + 2) * step, A);
-            {
-                float a[U][kChunk];
-                fast_values<U, S, CAP>(B, k, a);
-                f((gi + 1) * step, true, a);
-            }
+            load(gi + 1, B);
+            full(gi, A);
+            if (gi + 2 < nraw) load(gi + 2, A);
+            full(gi + 1, B);
         }
-        if (gi < nfg) {
-            float a[U][kChunk];
-            fast_values<U, S, CAP>(A, k, a);
-            f(gi * step, true, a);
+        if (gi + 1 == nfg) {  // one full group left (in A); the last one behind it
+            if (last_raw) load(nfg, B);
+            full(gi, A);
+            ++gi;
+        } else if (last_raw) {  // gi == nfg: the last group is in A
+            B = A;
+        }
+        if (last_raw) {
+            last(gi, B);
             ++gi;
         }
     } else {
-        for (; gi < nfg; ++gi) {
+        for (; gi < nraw; ++gi) {
             RawGroup<S, U> A;
-            raw_load_walk<BLOCK, U, NT, multi_row(CAP)>(row, gi * step, A);
-            float a[U][kChunk];
-            fast_values<U, S, CAP>(A, k, a);
-            f(gi * step, true, a);
+            load(gi, A);
+            if (gi < nfg)
+                full(gi, A);
+            else
+                last(gi, A);
         }
     }
     for (; gi < gend; ++gi) {
