@@ -217,10 +217,12 @@ def measure_launch_floor(dev, torch) -> dict:
     fold and with their epilogue, the fold split over four workgroups per
     row (alone, and with a last-arriver combine and the epilogue in the same
     launch), the backward's one-shot pieces, and pairs of them; beside them the
-    library's own forward, backward and step on the workload.  Each figure is
-    the best of 5 runs of 500 back-to-back launches (HIP events, mean per
-    launch); the probes are launched from a C loop, the library through its
-    binding (about 3 us of host time per call, under the GPU time here)."""
+    library's own forward, backward and step on the workload; and the empty
+    pair and the library's step replayed from HIP graphs of 10 steps.  Each
+    figure is the best of 5 runs of 500 back-to-back launches or steps (HIP
+    events, mean per launch or step); the probes are launched from a C loop,
+    the library through its binding (about 3 us of host time per call, under
+    the GPU time here)."""
     from vocab_log_softmax_amd import build as B
     from vocab_log_softmax_amd import rlk, workloads
 
@@ -248,8 +250,8 @@ def measure_launch_floor(dev, torch) -> dict:
                 raise RuntimeError(f"launch_floor_run({a}, {b}) failed: {rc}")
         return run
 
-    def best_us(run, reps=500):
-        run(50)
+    def best_us(run, reps=500, per=1):
+        run(max(1, reps // 10))
         best = float("inf")
         for _ in range(5):
             torch.cuda.synchronize()
@@ -257,7 +259,7 @@ def measure_launch_floor(dev, torch) -> dict:
             run(reps)
             ev.record(1, raw)
             torch.cuda.synchronize()
-            best = min(best, ev.elapsed_ms(0, 1) * 1e3 / reps)
+            best = min(best, ev.elapsed_ms(0, 1) * 1e3 / reps / per)
         return round(best, 2)
 
     names = ["empty, 64 workgroups", "empty, 1024 workgroups",
@@ -285,10 +287,61 @@ def measure_launch_floor(dev, torch) -> dict:
     res["library: logprobs forward"] = best_us(loop(fwd))
     res["library: logprobs backward"] = best_us(loop(bwd))
     res["library: forward + backward step"] = best_us(loop(fwd, bwd))
+
+    # The same pairs from HIP graphs of G steps (one graph launch per G
+    # steps): dependent kernels without a stream launch each.  Every replay
+    # of the library's graph is compared bit for bit with the eager step,
+    # with eager work between the replays.
+    G = 10
+
+    def graph(capture):
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            capture()
+        return gr
+
+    def empty_pairs():
+        cs = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+        rc = lib.launch_floor_run(0, 0, G, x.data_ptr(), y.data_ptr(), tg.data_ptr(),
+                                  stats.data_ptr(), out.data_ptr(), cs)
+        if rc != 0:
+            raise RuntimeError(f"launch_floor_run under capture failed: {rc}")
+
+    def library_steps():
+        f = rlk.prepare(rlk.rlk_logp_fwd, x, tg2, 0.0, lp, st)
+        b = rlk.prepare(rlk.rlk_logp_bwd, x, tg2, 0.0, st, g, gx)
+        for _ in range(G):
+            f()
+            b()
+
+    g_empty, g_lib = graph(empty_pairs), graph(library_steps)
+    fwd()
+    bwd()
+    torch.cuda.synchronize()
+    ref_lp, ref_gx = lp.clone(), gx.view(torch.int32).clone()
+    for _ in range(3):
+        lp.zero_()
+        gx.zero_()
+        g_lib.replay()
+        torch.cuda.synchronize()
+        if not (torch.equal(lp, ref_lp) and torch.equal(gx.view(torch.int32), ref_gx)):
+            raise RuntimeError("a graph replay differs from the eager step")
+        fwd()
+        bwd()
+        torch.cuda.synchronize()
+
+    def replays(gr):
+        def run(reps):
+            for _ in range(reps):
+                gr.replay()
+        return run
+
+    res[f"graph of {G} pairs: empty + empty, per pair"] = best_us(replays(g_empty), 50, G)
+    res[f"graph of {G} library steps: per step"] = best_us(replays(g_lib), 50, G)
     ev.close()
     return {"launch_floor_us": res, "shape": [R, C], "dtype": "fp32",
-            "method": "best of 5 x 500 back-to-back launches, HIP events, mean per launch; "
-                      "probes launched from a C loop"}
+            "method": "best of 5 x 500 back-to-back launches (or graph-replayed steps), HIP "
+                      "events, mean per launch or step; probes launched from a C loop"}
 
 
 def time_softcap(name: str, dev, torch, reps: int = 200) -> dict:
