@@ -45,6 +45,11 @@
  *     caller's current device is restored afterwards.  Calls are
  *     asynchronous on `stream` (0 = the null stream); faults inside a kernel
  *     surface at the caller's next synchronisation.
+ *   - A call enqueues kernel launches on `stream` and nothing else (no
+ *     allocation, synchronisation, memset or copy), so calls may be captured
+ *     into a HIP graph with hipStreamBeginCapture and replayed; a replay
+ *     reads the captured buffers' current contents and gives the bits of an
+ *     eager call on them.
  *   - A *_bwd call must receive the `stats` buffer written by the matching
  *     *_fwd call with identical inputs and arguments, ordered after it (same
  *     stream, or after a synchronisation).
