@@ -344,6 +344,45 @@ def measure_launch_floor(dev, torch) -> dict:
                       "events, mean per launch or step; probes launched from a C loop"}
 
 
+def measure_issue_rate(dev, torch) -> dict:
+    """VALU issue rates (libceiling.so): wave64 FMA, v_exp_f32 and v_rcp_f32
+    with 8 independent chains per lane at 8 waves per SIMD (2048 workgroups
+    of 256 threads on 256 CUs).  Reported as cycles per wave instruction per
+    SIMD at the 2.4 GHz peak engine clock, best of 5 launches each."""
+    from vocab_log_softmax_amd import build as B
+
+    if not os.path.exists(B.CEILING_LIB):
+        raise SystemExit(f"{B.CEILING_LIB} is missing: run __graft_entry__.build()")
+    lib = ctypes.CDLL(B.CEILING_LIB)
+    lib.issue_rate_run.argtypes = [ctypes.c_int] * 3 + [ctypes.c_void_p] * 2
+    lib.issue_rate_run.restype = ctypes.c_int
+    blocks, iters = 2048, 4096
+    out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    raw = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    ev = HipEvents(2, torch)
+    simds = torch.cuda.get_device_properties(dev).multi_processor_count * 4
+    wave_instr = blocks * 4 * iters * lib.issue_rate_chains()  # per launch
+    res = {}
+    for op, name in enumerate(("fma", "exp2", "rcp")):
+        best = float("inf")
+        for _ in range(6):
+            torch.cuda.synchronize()
+            ev.record(0, raw)
+            rc = lib.issue_rate_run(op, blocks, iters, ctypes.c_void_p(out.data_ptr()), raw)
+            ev.record(1, raw)
+            torch.cuda.synchronize()
+            if rc != 0:
+                raise RuntimeError(f"issue_rate_run({op}) failed: {rc}")
+            best = min(best, ev.elapsed_ms(0, 1))
+        cycles = best * 1e-3 * 2.4e9 * simds / wave_instr
+        res[name] = {"ms": round(best, 4), "cycles_per_wave_instr_per_simd": round(cycles, 2)}
+    ev.close()
+    res["transcendental_vs_fma"] = round(res["exp2"]["cycles_per_wave_instr_per_simd"] /
+                                         res["fma"]["cycles_per_wave_instr_per_simd"], 2)
+    return {"issue_rate": res, "workgroups": blocks, "iterations": iters,
+            "chains_per_lane": lib.issue_rate_chains(), "simds": simds}
+
+
 def time_softcap(name: str, dev, torch, reps: int = 200) -> dict:
     """The standalone softcap forward (y fp32) and backward on the workload's
     softcap tensor: mean kernel time over `reps` back-to-back launches, HIP
@@ -664,6 +703,8 @@ def main() -> int:
                     help="only measure the read / write / copy ceilings at the workload's size")
     ap.add_argument("--launch-floor", action="store_true",
                     help="only measure the launch-latency probes at the fp32 [64, 32000] size")
+    ap.add_argument("--issue-rate", action="store_true",
+                    help="only measure the VALU issue rates of FMA, exp2 and rcp")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain device copy of a known size (counter calibration)")
     args = ap.parse_args()
@@ -700,6 +741,9 @@ def main() -> int:
         return 0
     if args.launch_floor:
         print(json.dumps(measure_launch_floor(dev, torch)))
+        return 0
+    if args.issue_rate:
+        print(json.dumps(measure_issue_rate(dev, torch)))
         return 0
     if args.ceilings:
         w = workloads.WORKLOADS[args.workload or HEADLINE]

@@ -24,7 +24,8 @@ BUILD_INFO = os.path.join(PKG, "build_info.json")
 # Bandwidth and launch-latency probes for the benchmark's ceiling reports
 # (not part of the ABI).
 CEILING_SRCS = [os.path.join(PKG, "ceiling", "ceiling.hip"),
-                os.path.join(PKG, "ceiling", "launch_floor.hip")]
+                os.path.join(PKG, "ceiling", "launch_floor.hip"),
+                os.path.join(PKG, "ceiling", "issue_rate.hip")]
 CEILING_LIB = os.path.join(PKG, "ceiling", "libceiling.so")
 
 SOURCES = ["rlk_fwd_f32.hip", "rlk_fwd_bf16.hip", "rlk_fwd_f16.hip",
