@@ -346,9 +346,9 @@ def measure_launch_floor(dev, torch) -> dict:
 
 def measure_issue_rate(dev, torch) -> dict:
     """VALU issue rates (libceiling.so): wave64 FMA, v_exp_f32 and v_rcp_f32
-    with 8 independent chains per lane at 8 waves per SIMD (2048 workgroups
-    of 256 threads on 256 CUs).  Reported as cycles per wave instruction per
-    SIMD at the 2.4 GHz peak engine clock, best of 5 launches each."""
+    with 8 independent chains per lane at 4, 8 and 16 waves per SIMD
+    (256-thread workgroups).  Reported as cycles per wave instruction per
+    SIMD at the 2.4 GHz peak engine clock, best of 6 launches each."""
     from vocab_log_softmax_amd import build as B
 
     if not os.path.exists(B.CEILING_LIB):
@@ -356,31 +356,35 @@ def measure_issue_rate(dev, torch) -> dict:
     lib = ctypes.CDLL(B.CEILING_LIB)
     lib.issue_rate_run.argtypes = [ctypes.c_int] * 3 + [ctypes.c_void_p] * 2
     lib.issue_rate_run.restype = ctypes.c_int
-    blocks, iters = 2048, 4096
-    out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    iters = 4096
+    simds = torch.cuda.get_device_properties(dev).multi_processor_count * 4
+    out = torch.empty(4 * simds * 256, dtype=torch.float32, device=dev)
     raw = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
     ev = HipEvents(2, torch)
-    simds = torch.cuda.get_device_properties(dev).multi_processor_count * 4
-    wave_instr = blocks * 4 * iters * lib.issue_rate_chains()  # per launch
     res = {}
-    for op, name in enumerate(("fma", "exp2", "rcp")):
-        best = float("inf")
-        for _ in range(6):
-            torch.cuda.synchronize()
-            ev.record(0, raw)
-            rc = lib.issue_rate_run(op, blocks, iters, ctypes.c_void_p(out.data_ptr()), raw)
-            ev.record(1, raw)
-            torch.cuda.synchronize()
-            if rc != 0:
-                raise RuntimeError(f"issue_rate_run({op}) failed: {rc}")
-            best = min(best, ev.elapsed_ms(0, 1))
-        cycles = best * 1e-3 * 2.4e9 * simds / wave_instr
-        res[name] = {"ms": round(best, 4), "cycles_per_wave_instr_per_simd": round(cycles, 2)}
+    for waves in (4, 8, 16):  # waves per SIMD: 256-thread workgroups of 4 waves
+        blocks = waves * simds // 4
+        wave_instr = blocks * 4 * iters * lib.issue_rate_chains()  # per launch
+        r = {}
+        for op, name in enumerate(("fma", "exp2", "rcp")):
+            best = float("inf")
+            for _ in range(6):
+                torch.cuda.synchronize()
+                ev.record(0, raw)
+                rc = lib.issue_rate_run(op, blocks, iters, ctypes.c_void_p(out.data_ptr()), raw)
+                ev.record(1, raw)
+                torch.cuda.synchronize()
+                if rc != 0:
+                    raise RuntimeError(f"issue_rate_run({op}) failed: {rc}")
+                best = min(best, ev.elapsed_ms(0, 1))
+            cycles = best * 1e-3 * 2.4e9 * simds / wave_instr
+            r[name] = {"ms": round(best, 4), "cycles_per_wave_instr_per_simd": round(cycles, 2)}
+        r["transcendental_vs_fma"] = round(r["exp2"]["cycles_per_wave_instr_per_simd"] /
+                                           r["fma"]["cycles_per_wave_instr_per_simd"], 2)
+        res[f"{waves}_waves_per_simd"] = r
     ev.close()
-    res["transcendental_vs_fma"] = round(res["exp2"]["cycles_per_wave_instr_per_simd"] /
-                                         res["fma"]["cycles_per_wave_instr_per_simd"], 2)
-    return {"issue_rate": res, "workgroups": blocks, "iterations": iters,
-            "chains_per_lane": lib.issue_rate_chains(), "simds": simds}
+    return {"issue_rate": res, "iterations": iters, "chains_per_lane": lib.issue_rate_chains(),
+            "simds": simds}
 
 
 def time_softcap(name: str, dev, torch, reps: int = 200) -> dict:
