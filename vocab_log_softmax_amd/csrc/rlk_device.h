@@ -258,9 +258,7 @@ __device__ __forceinline__ float cap_value_slope(float x, CapArgs c, float& s) {
 
 // The fixed form's span for cap_value_slope: its w at q = 0, by the same
 // reciprocal, so that the slope vanishes exactly there.
-__device__ __forceinline__ float fixed_span(float isc) {
-    return rcp(__builtin_fmaf(0.0f, isc, isc));
-}
+__device__ __forceinline__ float fixed_span(float isc) { return rcp(__builtin_fmaf(0.0f, isc, isc)); }
 
 // The slope is slope_factor * s: 4 (online form), 4 / sc^2 (fixed form).
 template <int CAP>
