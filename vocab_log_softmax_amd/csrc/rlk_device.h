@@ -552,11 +552,11 @@ __device__ __forceinline__ void for_each_group(const S* __restrict__ row, int64_
     const int64_t nraw = nfg + (last_raw ? 1 : 0);
     const int last_bytes =
         last_raw ? static_cast<int>((nchunks - nfg_row * step) * kChunk * sizeof(S)) : 0;
+    // (g beyond the walk: a resource of no bytes, which reads 0 and touches
+    // no memory; see the loop below)
     auto load = [&](int64_t g, RawGroup<S, U>& r) {
-        if (g < nfg)
-            raw_load_walk<BLOCK, U, NT, MULTI>(row, g * step, r);
-        else
-            raw_load_walk<BLOCK, U, NT, MULTI>(row, g * step, r, last_bytes);
+        raw_load_walk<BLOCK, U, NT, MULTI>(
+            row, g * step, r, g < nfg ? group_bytes<BLOCK, U, S>() : (g < nraw ? last_bytes : 0));
     };
     auto full = [&](int64_t g, const RawGroup<S, U>& r) {
         float a[U][kChunk];
@@ -573,10 +573,18 @@ __device__ __forceinline__ void for_each_group(const S* __restrict__ row, int64_
     if (PIPE && gi < nraw) {
         RawGroup<S, U> A, B;
         load(gi, A);
+        // The next-but-one group is loaded unconditionally (an empty range
+        // past the walk): behind a branch, the compiler's wait for the
+        // current group merged both paths and also waited for the loads
+        // just issued.  The scheduling barriers keep each group's loads
+        // ahead of the other group's consumption, which the scheduler
+        // otherwise hoisted above them: two groups stay in flight.
         for (; gi + 1 < nfg; gi += 2) {
             load(gi + 1, B);
+            __builtin_amdgcn_sched_barrier(0);
             full(gi, A);
-            if (gi + 2 < nraw) load(gi + 2, A);
+            load(gi + 2, A);
+            __builtin_amdgcn_sched_barrier(0);
             full(gi + 1, B);
         }
         if (gi + 1 == nfg) {  // one full group left (in A); the last one behind it
@@ -624,19 +632,21 @@ __device__ __forceinline__ void for_each_group2(const S* __restrict__ ra, const 
         RawGroup<S, U> A0, B0, A1, B1;
         raw_load_walk<BLOCK, U, NT>(ra, gi * step, A0);
         raw_load_walk<BLOCK, U, NT>(rb, gi * step, B0);
+        // unconditional loads and scheduling barriers as in for_each_group
         for (; gi + 1 < nfg; gi += 2) {
             raw_load_walk<BLOCK, U, NT>(ra, (gi + 1) * step, A1);
             raw_load_walk<BLOCK, U, NT>(rb, (gi + 1) * step, B1);
+            __builtin_amdgcn_sched_barrier(0);
             {
                 float a[U][kChunk], b[U][kChunk];
                 fast_values<U, S, CAPA>(A0, ka, a);
                 fast_values<U, S, CAPB>(B0, kb, b);
                 f(gi * step, true, a, b);
             }
-            if (gi + 2 < nfg) {
-                raw_load_walk<BLOCK, U, NT>(ra, (gi + 2) * step, A0);
-                raw_load_walk<BLOCK, U, NT>(rb, (gi + 2) * step, B0);
-            }
+            const int next = gi + 2 < nfg ? group_bytes<BLOCK, U, S>() : 0;
+            raw_load_walk<BLOCK, U, NT>(ra, (gi + 2) * step, A0, next);
+            raw_load_walk<BLOCK, U, NT>(rb, (gi + 2) * step, B0, next);
+            __builtin_amdgcn_sched_barrier(0);
             {
                 float a[U][kChunk], b[U][kChunk];
                 fast_values<U, S, CAPA>(A1, ka, a);
