@@ -169,8 +169,9 @@ def measure_ceilings(w, dev, torch) -> dict:
 
     Read-only, write-only and copy streams of 16-byte nontemporal accesses,
     grid-stride and row by row (one workgroup per row of V logits, as the
-    library's kernels stream); median of 15 timed launches after 3 warm-up
-    launches, HIP events on the current stream.
+    library's kernels stream), and reads by one-shot workgroups that each
+    fold one 16, 32 or 64 KB piece of a row; median of 15 timed launches
+    after 3 warm-up launches, HIP events on the current stream.
     """
     from vocab_log_softmax_amd import build as B
 
@@ -189,7 +190,8 @@ def measure_ceilings(w, dev, torch) -> dict:
     ev = HipEvents(2 * 15, torch)
     out = {"bytes_per_tensor": bytes_, "row_bytes": row_bytes}
     kinds = {"read_grid_stride": (0, 1), "write_grid_stride": (1, 1), "copy_grid_stride": (2, 2),
-             "read_rows": (3, 1), "copy_rows": (4, 2)}
+             "read_rows": (3, 1), "copy_rows": (4, 2), "read_pieces_16k": (5, 1),
+             "read_pieces_32k": (6, 1), "read_pieces_64k": (7, 1)}
     for name, (kind, passes) in kinds.items():
         def run():
             rc = lib.ceiling_run(kind, src.data_ptr(), dst.data_ptr(), bytes_, row_bytes,

@@ -213,6 +213,54 @@ def test_half_dtypes_equal_fp32_of_same_values(dev, dtype, cap):
             assert_bitwise(b[k], f[k], f"{dtype} vs fp32 output {k}")
 
 
+def _layout_targets(N, V, k, seed):
+    """Target ids on the edges of the backward's lane layouts: for the lane
+    t of a 2048-column slot (one 256-lane chunk slot), the last column of its
+    first four and the first of its next four (16-bit: one chunk; fp32 full
+    pieces: quads t and 256 + t, 1024 columns apart), slot and piece
+    boundaries, duplicates, the row's tail and, for k > 4, uniform fill."""
+    g = _gen(seed)
+    t = torch.randint(0, V, (N, k), generator=g)
+    full = V // 2048 * 2048
+    for r in range(N):
+        lane = (37 * r) % 256
+        slot = r % (full // 2048)
+        base = slot * 2048
+        edge = [base + 4 * lane + 3, base + 1024 + 4 * lane, base + 4 * lane + 4,
+                base + 1024 + 4 * lane + 3, base + 2047, base, full + (r % (V - full))]
+        for j in range(min(k, len(edge))):
+            t[r, j] = edge[j]
+        if k >= 4:
+            t[r, k - 1] = t[r, 0]  # duplicate
+    if k > 8:
+        t[:, k // 2: k // 2 + k // 8] = t[:, : k // 8]
+    t[::7, 1] = -100
+    return t
+
+
+@pytest.mark.parametrize("k", [4, 16, 256])
+@pytest.mark.parametrize("cap", [0.0, 20.0])
+def test_fp32_piece_layout_matches_bf16(dev, k, cap):
+    # fp32 full backward pieces hold two 16-byte quads 1024 columns apart per
+    # lane and chunk slot, 16-bit ones one chunk: the bf16 gradient must still
+    # be the round-to-nearest-even of the fp32 one at every column, target
+    # columns included (k = 4: one-shot pieces; 16 and 256: wide pieces, whose
+    # slot lists are scanned, or sorted when a piece holds more than 16).
+    N, V = 300, 16680
+    x = (torch.randn(N, V, generator=_gen(71)) * (10.0 if cap else 3.0)).to(torch.bfloat16)
+    t = _layout_targets(N, V, k, 72 + k)
+    g_t = torch.randn(N, k, generator=_gen(73))
+    x, t, g_t = x.to(dev), t.to(dev), g_t.to(dev)
+    lp_b, st_b = rlk.logp_fwd(x, t, cap)
+    gx_b = rlk.logp_bwd(x, t, g_t, st_b, cap)
+    xf = x.float()
+    lp_f, st_f = rlk.logp_fwd(xf, t, cap)
+    gx_f = rlk.logp_bwd(xf, t, g_t, st_f, cap)
+    torch.cuda.synchronize()
+    assert_bitwise(lp_b, lp_f, f"logp k={k}")
+    assert_bitwise(gx_b, gx_f.to(torch.bfloat16), f"grad k={k}")
+
+
 def test_outputs_independent_of_stats_buffer_history(dev):
     # the forward record is fully rewritten: garbage in the buffer changes nothing
     x, ref, t, g_t, g_r = make(6, 5000, torch.bfloat16, 3, dev)

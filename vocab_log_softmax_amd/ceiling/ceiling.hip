@@ -5,7 +5,8 @@
 //     (T = grid x block), the usual streaming probe;
 //   * rows: one workgroup per row of `row_bytes`, lanes striding the row as
 //     the library's kernels do (reads: 256 threads, 4 words per lane in
-//     flight; copies: 1024 threads, 8 words per lane in flight).
+//     flight; copies: 1024 threads, 8 words per lane in flight);
+//   * pieces: one-shot workgroups that each read one piece of a row.
 // Measurement infrastructure only (built as libceiling.so, loaded by the
 // benchmark); every access is bounds-checked against the buffer or the row.
 #include <hip/hip_runtime.h>
@@ -83,6 +84,41 @@ __global__ __launch_bounds__(BS) void copy_rows(const u32x4* __restrict__ a,
     }
 }
 
+// One-shot read pieces: workgroup (x, y) reads piece x (BS x U words) of row
+// y with every load in flight, folds it and writes one 16-byte word per piece
+// (a segment record), then exits; consecutive workgroups take consecutive
+// pieces of a row, so the chip sweeps the buffer front to back.
+template <int BS, int U>
+__global__ __launch_bounds__(BS) void read_pieces(const u32x4* __restrict__ a, int64_t rows,
+                                                  int64_t row16, u32x4* __restrict__ rec) {
+    __shared__ uint32_t red[BS / 64];
+    const int64_t npc = (row16 + (int64_t)BS * U - 1) / ((int64_t)BS * U);
+    for (int64_t r = blockIdx.y; r < rows; r += gridDim.y) {
+        const u32x4* ra = a + r * row16;
+        const int64_t c0 = (int64_t)blockIdx.x * BS * U + threadIdx.x;
+        u32x4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t c = c0 + (int64_t)u * BS;
+            v[u] = c < row16 ? __builtin_nontemporal_load(ra + c) : u32x4{0u, 0u, 0u, 0u};
+        }
+        uint32_t acc = 0;
+#pragma unroll
+        for (int u = 0; u < U; ++u) acc += v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
+        if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            uint32_t t = 0;
+#pragma unroll
+            for (int w = 0; w < BS / 64; ++w) t += red[w];
+            rec[r * npc + blockIdx.x] = u32x4{t, 0u, 0u, 0u};
+        }
+        __syncthreads();
+    }
+}
+
 int grid_of(int64_t n) { return static_cast<int>(n < 1 ? 1 : (n < (1 << 20) ? n : (1 << 20))); }
 
 }  // namespace
@@ -90,8 +126,10 @@ int grid_of(int64_t n) { return static_cast<int>(n < 1 ? 1 : (n < (1 << 20) ? n 
 extern "C" {
 
 // kind: 0 read grid-stride, 1 write grid-stride, 2 copy grid-stride,
-//       3 read rows, 4 copy rows.  bytes and row_bytes are multiples of 16;
-// src / dst hold `bytes` (dst unused by reads); sink holds 4 bytes.
+//       3 read rows, 4 copy rows, 5 / 6 / 7 read pieces of 16 / 32 / 64 KB
+//       (one 16-byte record per piece written to dst).  bytes and row_bytes
+// are multiples of 16; src / dst hold `bytes` (dst unused by the other
+// reads); sink holds 4 bytes.
 // Returns 0 on success, 1 on bad arguments, 2 if the launch failed.
 int ceiling_run(int kind, const void* src, void* dst, int64_t bytes, int64_t row_bytes,
                 void* sink, void* stream) {
@@ -123,6 +161,25 @@ int ceiling_run(int kind, const void* src, void* dst, int64_t bytes, int64_t row
             else
                 hipLaunchKernelGGL((copy_rows<1024, 8>), dim3(grid_of(rows)), dim3(1024), 0, s, a,
                                    b, rows, row16);
+            break;
+        }
+        case 5:
+        case 6:
+        case 7: {
+            if (row_bytes <= 0 || row_bytes % 16 != 0 || bytes % row_bytes != 0) return 1;
+            const int64_t rows = bytes / row_bytes, row16 = row_bytes / 16;
+            const int U = kind == 5 ? 4 : (kind == 6 ? 8 : 16);
+            const int64_t npc = (row16 + 256 * U - 1) / (256 * U);
+            // records: rows x npc words, at most one per 1024 words of src
+            if (npc > (1 << 20) || rows * npc > n16) return 1;
+            const dim3 g(static_cast<unsigned>(npc),
+                         static_cast<unsigned>(rows < 65535 ? rows : 65535));
+            if (kind == 5)
+                hipLaunchKernelGGL((read_pieces<256, 4>), g, dim3(256), 0, s, a, rows, row16, b);
+            else if (kind == 6)
+                hipLaunchKernelGGL((read_pieces<256, 8>), g, dim3(256), 0, s, a, rows, row16, b);
+            else
+                hipLaunchKernelGGL((read_pieces<256, 16>), g, dim3(256), 0, s, a, rows, row16, b);
             break;
         }
         default:

@@ -456,20 +456,25 @@ __device__ __forceinline__ void piece(const BwdParams& p, int64_t row, int64_t g
             }
             if (HEAD == kHeadLogp && hit) {
                 // one-hot terms: a slot whose column falls in this lane's chunk
-                // (most pieces hold no target column and skip this)
-                const int64_t col0 = (g0 + u * BLOCK + (int)threadIdx.x) * kChunk;
+                // (most pieces hold no target column and skip this); values
+                // 0..3 sit at columns lo.., 4..7 at hi.. (piece_col)
+                constexpr bool Q = piece_quads<S, FULL>();
+                const int64_t lo = piece_col<BLOCK, Q>(g0, u, threadIdx.x, 0);
+                const int64_t hi = piece_col<BLOCK, Q>(g0, u, threadIdx.x, 4);
                 bool any = false;
 #pragma unroll
                 for (int j = 0; j < kPieceMaxK; ++j)
-                    any |= tl[j] >= col0 && tl[j] < col0 + kChunk;
+                    any |= Q ? (tl[j] >= lo && tl[j] < lo + 4) || (tl[j] >= hi && tl[j] < hi + 4)
+                             : tl[j] >= lo && tl[j] < lo + kChunk;
                 if (any) {
 #pragma unroll
                     for (int e = 0; e < kChunk; ++e) {
+                        const int64_t col = e < 4 ? lo + e : hi + (e - 4);
                         float h = 0.0f;
                         bool match = false;
 #pragma unroll
                         for (int j = 0; j < kPieceMaxK; ++j)
-                            if (tl[j] == col0 + e) {
+                            if (tl[j] == col) {
                                 h += gs[j];
                                 match = true;
                             }
@@ -552,14 +557,15 @@ __device__ __forceinline__ void wide_piece(const BwdParams& p, int64_t row, int6
     constexpr int BLOCK = kGLanes, NW = kGLanes / 64;
     constexpr int PC = BLOCK * U;  // chunks per piece
     __shared__ uint32_t bits[PC / 4];
-    // (column in the piece, g as bits) in slot order, padded to a multiple of
-    // 4 entries with (-1, +0) so that the search reads 4 entries per step (8
-    // per step measured slower: the kernel then needs 88 VGPRs instead of 80,
-    // 5 waves per SIMD instead of 6)
+    // (the column's lane-order index in the piece, piece_slot; g as bits) in
+    // slot order, padded to a multiple of 4 entries with (-1, +0) so that the
+    // search reads 4 entries per step (8 per step measured slower: the kernel
+    // then needs 88 VGPRs instead of 80, 5 waves per SIMD instead of 6)
     __shared__ __align__(16) int2 list[kGLanes];
     // A list longer than kWideScanMax entries (many targets per piece: a small
-    // V or a large k) is searched through its keys (column << 16 | list
-    // index) sorted in LDS and the first sorted position of each marked chunk.
+    // V or a large k) is searched through its keys (lane-order index << 16 |
+    // list index) sorted in LDS and the first sorted position of each marked
+    // chunk.
     __shared__ uint32_t skey[kGLanes];
     __shared__ uint16_t cstart[PC];
     __shared__ float red_g[NW], red_n[NW];
@@ -597,7 +603,8 @@ __device__ __forceinline__ void wide_piece(const BwdParams& p, int64_t row, int6
         }
         const int64_t c = t - p.v0 - g0 * kChunk;
         mine = t >= p.v0 && t < p.v0 + p.V && c >= 0 && c < static_cast<int64_t>(PC) * kChunk;
-        pcol = static_cast<int>(c);
+        // the list and bitmap index values in lane order (piece_slot)
+        pcol = piece_slot<BLOCK, piece_quads<S, FULL>()>(static_cast<int>(c));
     }
 #pragma unroll
     for (int i = tid; i < PC / 4; i += BLOCK) bits[i] = 0u;
@@ -724,7 +731,11 @@ __device__ __forceinline__ void wide_piece(const BwdParams& p, int64_t row, int6
     }
     // (plain streaming stores: the sc1 policy of store_piece measured slower
     // for these 16 KB pieces)
-    store_group<BLOCK, U, S, ALIGNED, CUT>(gx, p.V, g0, FULL, v, cut);
+    if constexpr (piece_quads<S, FULL>())
+        store_piece<BLOCK, U, S, kCpolStream, CUT>(gx + g0 * kChunk, v,
+                                                   CUT ? static_cast<uint32_t>(cut - g0) : 0u);
+    else
+        store_group<BLOCK, U, S, ALIGNED, CUT>(gx, p.V, g0, FULL, v, cut);
 }
 
 template <int U, typename T, int CAPA, bool ALIGNED, bool NT>

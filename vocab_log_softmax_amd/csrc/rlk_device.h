@@ -337,16 +337,48 @@ __device__ __forceinline__ void raw_load(const _Float16* __restrict__ row, int64
         r.v[u] = ld16<NT>(reinterpret_cast<const u32x4*>(
             row + (g0 + u * BLOCK + row_lane<BLOCK, MULTI>()) * kChunk));
 }
+// fp32 pieces hold quads: chunk slot u of lane t is quads t and BLOCK + t of
+// the slot's BLOCK chunks (piece_col), so that each load covers 1 KB per wave.
 template <int BLOCK, int U, bool NT, bool MULTI = false>
 __device__ __forceinline__ void raw_load(const float* __restrict__ row, int64_t g0,
                                          RawGroup<float, U>& r) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const f32x4* p =
-            reinterpret_cast<const f32x4*>(row + (g0 + u * BLOCK + row_lane<BLOCK, MULTI>()) * kChunk);
+        const f32x4* p = reinterpret_cast<const f32x4*>(row + (g0 + u * BLOCK) * kChunk) +
+                         row_lane<BLOCK, MULTI>();
         r.v[u][0] = ld16<NT>(p);
-        r.v[u][1] = ld16<NT>(p + 1);
+        r.v[u][1] = ld16<NT>(p + BLOCK);
     }
+}
+
+// Column (from the piece's first chunk g0) of value e of chunk slot u that
+// lane t holds in a one-shot backward piece.  16-bit logits: chunk g0 + u
+// BLOCK + t, its 8 values side by side.  fp32 logits in a full piece (QUADS):
+// values 0..3 are quad t and values 4..7 quad BLOCK + t of the slot's 2 BLOCK
+// quads, so each of a wave's two 16-byte loads or stores per slot covers 1 KB
+// contiguous; a chunk's two quads side by side would make each store write
+// every other 16 bytes (the fp32 backward then moved 3.3x fewer bytes per
+// second).  Partial pieces keep the chunk layout (tail_values, store_group).
+template <int BLOCK, bool QUADS>
+__device__ __forceinline__ int64_t piece_col(int64_t g0, int u, int t, int e) {
+    if (QUADS) {
+        const int64_t q0 = (g0 + static_cast<int64_t>(u) * BLOCK) * kChunk + 4 * t;
+        return e < 4 ? q0 + e : q0 + 4 * BLOCK + (e - 4);
+    }
+    return (g0 + static_cast<int64_t>(u) * BLOCK + t) * kChunk + e;
+}
+template <typename S, bool FULL>
+constexpr bool piece_quads() {
+    return FULL && sizeof(S) == 4;
+}
+// Inverse of piece_col: the lane-order index (u BLOCK + t) kChunk + e of the
+// value at column c of the piece (0 <= c < BLOCK U kChunk).
+template <int BLOCK, bool QUADS>
+__device__ __forceinline__ int piece_slot(int c) {
+    if (!QUADS) return c;
+    const int q = c >> 2, r = q % (2 * BLOCK);
+    const int half = r >= BLOCK ? 1 : 0;
+    return ((q / (2 * BLOCK)) * BLOCK + (r - half * BLOCK)) * kChunk + half * 4 + (c & 3);
 }
 // The row walks (for_each_group, for_each_group2) read their full groups
 // through a buffer resource per group: its base is the group's first byte,
@@ -687,7 +719,8 @@ __device__ __forceinline__ void for_each_group2(const S* __restrict__ ra, const 
 constexpr int kCpolStream = 2;             // nt
 constexpr int kCpolWriteThrough = 16 | 2;  // sc1 | nt: system scope, streaming
 // With CUT, the first `skip` chunks of the piece are not stored: their offset
-// is the end of the buffer, where its range check drops the stores.
+// is the end of the buffer, where its range check drops the stores.  fp32
+// pieces are stored in quads (piece_col).
 template <int BLOCK, int U, typename S, int CPOL, bool CUT = false>
 __device__ __forceinline__ void store_piece(S* __restrict__ piece, const float (&v)[U][kChunk],
                                             uint32_t skip = 0) {
@@ -697,22 +730,28 @@ __device__ __forceinline__ void store_piece(S* __restrict__ piece, const float (
         __builtin_amdgcn_make_buffer_rsrc(static_cast<void*>(piece), 0, kBytes, 0x00020000);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const uint32_t ci = u * BLOCK + threadIdx.x;
-        const uint32_t off = (!CUT || ci >= skip) ? ci * kChunkBytes : kBytes;
         if constexpr (sizeof(S) == 4) {
+            // quads 2 u BLOCK + t and (2 u + 1) BLOCK + t; with CUT the
+            // first 2 skip quads are dropped
+            const uint32_t q0 = 2 * u * BLOCK + threadIdx.x, q1 = q0 + BLOCK;
+            const uint32_t off0 = (!CUT || q0 >= 2 * skip) ? q0 * 16u : kBytes;
+            const uint32_t off1 = (!CUT || q1 >= 2 * skip) ? q1 * 16u : kBytes;
             const u32x4 a = {__float_as_uint(v[u][0]), __float_as_uint(v[u][1]),
                              __float_as_uint(v[u][2]), __float_as_uint(v[u][3])};
             const u32x4 b = {__float_as_uint(v[u][4]), __float_as_uint(v[u][5]),
                              __float_as_uint(v[u][6]), __float_as_uint(v[u][7])};
-            __builtin_amdgcn_raw_buffer_store_b128(a, rs, off, 0, CPOL);
-            __builtin_amdgcn_raw_buffer_store_b128(b, rs, off + 16, 0, CPOL);
-        } else if constexpr (std::is_same_v<S, uint16_t>) {
-            const u32x4 w = {pack_bf16x2(v[u][0], v[u][1]), pack_bf16x2(v[u][2], v[u][3]),
-                             pack_bf16x2(v[u][4], v[u][5]), pack_bf16x2(v[u][6], v[u][7])};
-            __builtin_amdgcn_raw_buffer_store_b128(w, rs, off, 0, CPOL);
+            __builtin_amdgcn_raw_buffer_store_b128(a, rs, off0, 0, CPOL);
+            __builtin_amdgcn_raw_buffer_store_b128(b, rs, off1, 0, CPOL);
         } else {
-            const u32x4 w = {pack_f16x2(v[u][0], v[u][1]), pack_f16x2(v[u][2], v[u][3]),
-                             pack_f16x2(v[u][4], v[u][5]), pack_f16x2(v[u][6], v[u][7])};
+            const uint32_t ci = u * BLOCK + threadIdx.x;
+            const uint32_t off = (!CUT || ci >= skip) ? ci * kChunkBytes : kBytes;
+            u32x4 w;
+            if constexpr (std::is_same_v<S, uint16_t>)
+                w = u32x4{pack_bf16x2(v[u][0], v[u][1]), pack_bf16x2(v[u][2], v[u][3]),
+                          pack_bf16x2(v[u][4], v[u][5]), pack_bf16x2(v[u][6], v[u][7])};
+            else
+                w = u32x4{pack_f16x2(v[u][0], v[u][1]), pack_f16x2(v[u][2], v[u][3]),
+                          pack_f16x2(v[u][4], v[u][5]), pack_f16x2(v[u][6], v[u][7])};
             __builtin_amdgcn_raw_buffer_store_b128(w, rs, off, 0, CPOL);
         }
     }
