@@ -274,6 +274,12 @@ __global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void bwd_topk_kernel(BwdParams
                             v[u][e] = grad_elem<kHeadLogp, CAPA>(a, s4, 0.0f, rs, A, B, p.scx,
                                                                  p.scy);
                         }
+                    if constexpr (sizeof(S) == 4 && ALIGNED) {
+                        if (full) {  // uniform: the walk's full groups
+                            store_walk_f32<BLOCK, U>(gx, g0, v);
+                            return;
+                        }
+                    }
                     store_group<BLOCK, U, S, ALIGNED>(gx, p.V, g0, full, v);
                 },
                 gbeg, gend);

@@ -431,18 +431,45 @@ __device__ __forceinline__ void raw_load_walk(const _Float16* __restrict__ row, 
                                                rs, lane_offset<BLOCK, MULTI, _Float16>(u), 0,
                                                NT ? 2 : 0));
 }
+// fp32 walks.  A lane's chunk is 32 bytes, so its two halves side by side
+// would make each of the wave's two loads read every other 16 bytes over
+// 2 KB (a read-only probe over fp32 rows: 5.7 TB/s against 7.0 TB/s for
+// contiguous 16-byte words).  Instead each load reads 1 KB of the wave's 64
+// chunks contiguous: the first load chunks 0..31, lanes 0..31 their first
+// and lanes 32..63 their second halves, the second load chunks 32..63 alike.
+// One lane-32 swap per dword (raw_unpack of a WalkF32) then gives every lane
+// both halves of its own chunk, the element-to-lane map of the 16-bit walks
+// (so fp32 and 16-bit rows of the same values still give the same bits).
+// Every lane of the wave takes part (whole waves walk a row).
+template <int U>
+struct WalkF32 {
+    f32x4 v[U][2];
+};
+template <typename S, int U>
+struct WalkGroupT {
+    using type = RawGroup<S, U>;
+};
+template <int U>
+struct WalkGroupT<float, U> {
+    using type = WalkF32<U>;
+};
+template <typename S, int U>
+using WalkGroup = typename WalkGroupT<S, U>::type;
 template <int BLOCK, int U, bool NT, bool MULTI = false>
 __device__ __forceinline__ void raw_load_walk(const float* __restrict__ row, int64_t g0,
-                                              RawGroup<float, U>& r,
+                                              WalkF32<U>& r,
                                               int bytes = group_bytes<BLOCK, U, float>()) {
     const __amdgpu_buffer_rsrc_t rs = group_rsrc(row, g0, bytes);
+    const int t = row_lane<BLOCK, MULTI>(), l = t & 63;
+    // chunk (t - l) + (l & 31) of the slot, half l >> 5; then 32 chunks on
+    const int lane_off = ((t - l) + (l & 31)) * kChunk * 4 + (l >> 5) * 16;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const int off = lane_offset<BLOCK, MULTI, float>(u);
+        const int off = u * BLOCK * kChunk * 4 + lane_off;
         r.v[u][0] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
                                                   rs, off, 0, NT ? 2 : 0));
         r.v[u][1] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                  rs, off + 16, 0, NT ? 2 : 0));
+                                                  rs, off + 32 * kChunk * 4, 0, NT ? 2 : 0));
     }
 }
 template <int U>
@@ -474,6 +501,25 @@ __device__ __forceinline__ void raw_unpack(const RawGroup<float, U>& r, float (&
     for (int u = 0; u < U; ++u) {
         a[u][0] = r.v[u][0].x; a[u][1] = r.v[u][0].y; a[u][2] = r.v[u][0].z; a[u][3] = r.v[u][0].w;
         a[u][4] = r.v[u][1].x; a[u][5] = r.v[u][1].y; a[u][6] = r.v[u][1].z; a[u][7] = r.v[u][1].w;
+    }
+}
+// Lane m < 32 loaded the first half of chunk m and lane m + 32 its second
+// half (first load); lane m - 32 the first and lane m the second half of
+// chunk m >= 32 (second load): the swap of lanes 32..63 of the first with
+// lanes 0..31 of the second gives each lane its chunk's halves in order.
+template <int U>
+__device__ __forceinline__ void raw_unpack(const WalkF32<U>& r, float (&a)[U][kChunk]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const float p[4] = {r.v[u][0].x, r.v[u][0].y, r.v[u][0].z, r.v[u][0].w};
+        const float q[4] = {r.v[u][1].x, r.v[u][1].y, r.v[u][1].z, r.v[u][1].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const auto w = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[i]),
+                                                            __float_as_uint(q[i]), false, false);
+            a[u][i] = __uint_as_float(w[0]);
+            a[u][4 + i] = __uint_as_float(w[1]);
+        }
     }
 }
 // Values of one group that is not a full aligned group (the row's tail, or
@@ -516,9 +562,9 @@ __device__ __forceinline__ void tail_values(const S* __restrict__ row, int64_t V
     }
 }
 // Fast-group counterpart: unpack the raw vectors (and apply the cap).
-template <int U, typename S, int CAP>
-__device__ __forceinline__ void fast_values(const RawGroup<S, U>& r, CapArgs ca,
-                                            float (&a)[U][kChunk]) {
+// G: RawGroup (pieces) or WalkGroup (row walks).
+template <int U, typename S, int CAP, typename G>
+__device__ __forceinline__ void fast_values(const G& r, CapArgs ca, float (&a)[U][kChunk]) {
     if constexpr (CAP == kCapTableB || CAP == kCapTableH) {
         static_assert(sizeof(S) == 2, "table forms read 16-bit logits");
         // straight from the packed words: element 2i in the low half
@@ -586,16 +632,16 @@ __device__ __forceinline__ void for_each_group(const S* __restrict__ row, int64_
         last_raw ? static_cast<int>((nchunks - nfg_row * step) * kChunk * sizeof(S)) : 0;
     // (g beyond the walk: a resource of no bytes, which reads 0 and touches
     // no memory; see the loop below)
-    auto load = [&](int64_t g, RawGroup<S, U>& r) {
+    auto load = [&](int64_t g, WalkGroup<S, U>& r) {
         raw_load_walk<BLOCK, U, NT, MULTI>(
             row, g * step, r, g < nfg ? group_bytes<BLOCK, U, S>() : (g < nraw ? last_bytes : 0));
     };
-    auto full = [&](int64_t g, const RawGroup<S, U>& r) {
+    auto full = [&](int64_t g, const WalkGroup<S, U>& r) {
         float a[U][kChunk];
         fast_values<U, S, CAP>(r, k, a);
         f(g * step, true, a);
     };
-    auto last = [&](int64_t g, const RawGroup<S, U>& r) {
+    auto last = [&](int64_t g, const WalkGroup<S, U>& r) {
         float a[U][kChunk];
         fast_values<U, S, CAP>(r, k, a);
         beyond_row<BLOCK, U, MULTI>(g * step, nchunks, a);
@@ -603,7 +649,7 @@ __device__ __forceinline__ void for_each_group(const S* __restrict__ row, int64_
     };
     int64_t gi = gbeg;
     if (PIPE && gi < nraw) {
-        RawGroup<S, U> A, B;
+        WalkGroup<S, U> A, B;
         load(gi, A);
         // The next-but-one group is loaded unconditionally (an empty range
         // past the walk): behind a branch, the compiler's wait for the
@@ -632,7 +678,7 @@ __device__ __forceinline__ void for_each_group(const S* __restrict__ row, int64_
         }
     } else {
         for (; gi < nraw; ++gi) {
-            RawGroup<S, U> A;
+            WalkGroup<S, U> A;
             load(gi, A);
             if (gi < nfg)
                 full(gi, A);
@@ -661,7 +707,7 @@ __device__ __forceinline__ void for_each_group2(const S* __restrict__ ra, const 
     const int64_t nfg = nfg_row < gend ? nfg_row : gend;
     int64_t gi = gbeg;
     if (PIPE && gi < nfg) {
-        RawGroup<S, U> A0, B0, A1, B1;
+        WalkGroup<S, U> A0, B0, A1, B1;
         raw_load_walk<BLOCK, U, NT>(ra, gi * step, A0);
         raw_load_walk<BLOCK, U, NT>(rb, gi * step, B0);
         // unconditional loads and scheduling barriers as in for_each_group
@@ -695,7 +741,7 @@ __device__ __forceinline__ void for_each_group2(const S* __restrict__ ra, const 
         }
     } else {
         for (; gi < nfg; ++gi) {
-            RawGroup<S, U> A, B;
+            WalkGroup<S, U> A, B;
             raw_load_walk<BLOCK, U, NT>(ra, gi * step, A);
             raw_load_walk<BLOCK, U, NT>(rb, gi * step, B);
             float a[U][kChunk], b[U][kChunk];
@@ -754,6 +800,35 @@ __device__ __forceinline__ void store_piece(S* __restrict__ piece, const float (
                           pack_f16x2(v[u][4], v[u][5]), pack_f16x2(v[u][6], v[u][7])};
             __builtin_amdgcn_raw_buffer_store_b128(w, rs, off, 0, CPOL);
         }
+    }
+}
+
+// Stores of a full fp32 group of a row walk in the layout of its loads
+// (raw_load_walk): the lane-32 swap undoes raw_unpack's, so each of the
+// wave's two stores per chunk slot writes 1 KB contiguous.  Every lane of
+// the wave takes part.
+template <int BLOCK, int U>
+__device__ __forceinline__ void store_walk_f32(float* __restrict__ row, int64_t g0,
+                                               const float (&v)[U][kChunk]) {
+    const __amdgpu_buffer_rsrc_t rs = group_rsrc(row, g0, group_bytes<BLOCK, U, float>());
+    const int t = row_lane<BLOCK, false>(), l = t & 63;
+    const int lane_off = ((t - l) + (l & 31)) * kChunk * 4 + (l >> 5) * 16;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        uint32_t p[4], q[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const auto w = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[u][i]),
+                                                            __float_as_uint(v[u][4 + i]), false,
+                                                            false);
+            p[i] = w[0];
+            q[i] = w[1];
+        }
+        const int off = u * BLOCK * kChunk * 4 + lane_off;
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4{p[0], p[1], p[2], p[3]}, rs, off, 0,
+                                               RLK_NT_STORE ? 2 : 0);
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4{q[0], q[1], q[2], q[3]}, rs,
+                                               off + 32 * kChunk * 4, 0, RLK_NT_STORE ? 2 : 0);
     }
 }
 
