@@ -293,7 +293,7 @@ def test_kl_self_is_zero(dev):
 
 @pytest.mark.parametrize("xdt", DTYPES, ids=["x_" + i for i in DT_IDS])
 @pytest.mark.parametrize("ydt", DTYPES, ids=["y_" + i for i in DT_IDS])
-@pytest.mark.parametrize("n", [1, 7, 8, 1025, 6 * 262144])
+@pytest.mark.parametrize("n", [1, 7, 8, 1025, 6921, 6 * 262144])
 @pytest.mark.parametrize("cap", [20.0, 30.0])
 def test_softcap(dev, orc, xdt, ydt, n, cap):
     g = gen(n)
