@@ -817,11 +817,13 @@ inline hipError_t bwd_piece_launch(const BwdParams& p0, hipStream_t s) {
     constexpr int64_t pc = static_cast<int64_t>(kBwdPieceBlock) * U;
     const bool apart = last_piece_apart(AL, p.N, p.V, T::kBytes, pc);
     const int64_t pieces = apart ? p.V / kChunk / pc : ((p.V + kChunk - 1) / kChunk + pc - 1) / pc;
+    constexpr bool KL = HEAD == kHeadKLReverse || HEAD == kHeadKLForward;
+    const unsigned lds = lds_for_wgs_per_cu(piece_wgs_per_cu<T::kBytes, KL>());
     for (int64_t r0 = 0; r0 < p.N; r0 += kPieceRowsPerLaunch) {
         const int64_t rows = p.N - r0 < kPieceRowsPerLaunch ? p.N - r0 : kPieceRowsPerLaunch;
         const dim3 grid(static_cast<unsigned>(pieces), static_cast<unsigned>(rows));
         hipLaunchKernelGGL((bwd_piece_kernel<kBwdPieceBlock, U, T, HEAD, CAPX, CAPY, AL, NT>), grid,
-                           dim3(kBwdPieceBlock), 0, s, p, r0);
+                           dim3(kBwdPieceBlock), lds, s, p, r0);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         if constexpr (AL) {
@@ -847,7 +849,7 @@ inline hipError_t bwd_wide_launch(const BwdParams& p, hipStream_t s) {
         const dim3 grid(static_cast<unsigned>(pieces), static_cast<unsigned>(rows));
         if constexpr (AL)
             hipLaunchKernelGGL((bwd_wide_kernel<kBwdWideUnroll, T, CAPX, NT>), grid, dim3(kGLanes),
-                               0, s, p, r0);
+                               lds_for_wgs_per_cu(wide_wgs_per_cu<T::kBytes>()), s, p, r0);
         else
             hipLaunchKernelGGL((bwd_wide_kernel_unaligned<kBwdWideUnroll, T, CAPX, NT>), grid,
                                dim3(kGLanes), 0, s, p, r0);

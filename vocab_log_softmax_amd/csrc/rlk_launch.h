@@ -117,6 +117,36 @@ constexpr int kUnroll1 = RLK_UNROLL1;    // forward, single-tensor heads
 constexpr int kUnrollKL = RLK_UNROLL_KL;  // forward, KL (two tensors per group)
 constexpr int kBwdBlockTopk = RLK_BWD_BLOCK_TOPK;  // logprobs backward with wide top-k
 constexpr int kBwdUnrollTopk = RLK_BWD_UNROLL_TOPK;
+// Resident one-shot pieces per CU.  A piece issues all its loads at once, so
+// the pieces resident on a CU set its bytes in flight, and past a point more
+// of them only add DRAM conflicts.  Measured on the read+write stream
+// (bf16 / fp32 [.., 151936] logprobs and entropy, KL [.., 75968]; 256 lanes x
+// 16 bytes of each operand per piece): moving 8 KB per piece (16-bit
+// logprobs, entropy) is best with all the 8 the registers allow (6: +10%);
+// 12 KB (16-bit KL) with 6 (-2 to -3%); 16 and 24 KB (fp32) with 4 (logprobs
+// -10%, KL -3 to -5%).  The limit is set by dynamic LDS that the kernel does
+// not use.
+constexpr int kLdsPerCu = 160 * 1024;  // LDS per CU
+constexpr int kLdsGranule = 512;       // its allocation unit
+inline unsigned lds_for_wgs_per_cu(int w) {
+    // the least multiple of the granule of which w + 1 do not fit
+    return w >= 8 ? 0u
+                  : static_cast<unsigned>((kLdsPerCu / (w + 1) / kLdsGranule + 1) * kLdsGranule);
+}
+template <int ESIZE, bool KL>
+constexpr int piece_wgs_per_cu() {
+    return ESIZE == 4 ? 4 : (KL ? 6 : 8);
+}
+// Wide top-k pieces (16 KB of 16-bit logits read and written, 32 KB of fp32):
+// the capped 16-bit backward needs every resident wave for its arithmetic
+// (top-256 + cap 20, bf16 [2048, 262144]: 5 per CU +9%); fp32 ones are best
+// with 2 per CU (k = 64, fp32 [2048, 151936]: -11%; top-256 + cap 20, fp32
+// [1024, 262144]: -5%).  (Their static LDS only adds to the dynamic part.)
+template <int ESIZE>
+constexpr int wide_wgs_per_cu() {
+    return ESIZE == 4 ? 2 : 8;
+}
+
 // Few rows: a narrow shape whose rows are also split into column segments,
 // so that there are enough workgroups to cover the chip.
 constexpr int kBwdBlockSmall = 256;
