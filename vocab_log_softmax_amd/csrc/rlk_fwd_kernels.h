@@ -191,19 +191,30 @@ __global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void fwd1_kernel(FwdParams p) 
     RowStats* stats = static_cast<RowStats*>(p.stats);
     for (int64_t row = blockIdx.x; row < p.N; row += gridDim.x) {
         const S* __restrict__ x = static_cast<const S*>(p.x) + p.mx.offset(row);
-        // Prefetch this lane's first target slot and its logit (if this
-        // shard owns the column).
+        // This lane's first target slot, read now; its logit (if this shard
+        // owns the column) is gathered once the walk's first group has
+        // arrived (gather_first), behind the loads then in flight: gathered
+        // here, its address would hold back the row's first loads by a
+        // memory round trip.
         int64_t t0 = -1;
         float xt0 = 0.0f;
-        if (HEAD == kHeadLogp && tid < p.k) {
-            t0 = p.targets[row * p.k + tid];
-            if (t0 >= p.v0 && t0 < p.v0 + p.V) xt0 = load_one(x + (t0 - p.v0));
-        }
+        if (HEAD == kHeadLogp && tid < p.k) t0 = p.targets[row * p.k + tid];
+        bool gathered = HEAD != kHeadLogp;
+        auto gather_first = [&]() {
+            if (gathered) return;
+            gathered = true;
+            // (the empty asm keeps the address arithmetic here: hoisted out
+            // of the walk, its wait for t0 held back the next group's loads)
+            int64_t t = t0;
+            __asm__ volatile("" : "+v"(t));
+            if (tid < p.k && t >= p.v0 && t < p.v0 + p.V) xt0 = load_one(x + (t - p.v0));
+        };
         Stat1 st = stat1_init<FIX>();
         if (ODD) st.mL = -ca.half;
         for_each_group<BLOCK, U, S, CAPS, ALIGNED, kFwdPipe, NT>(
             x, p.V, ca,
             [&](int64_t, bool full, const float (&a)[U][kChunk]) {
+                gather_first();
                 if (full)
                     update1<U, WITH_W, CLAMP, FIX>(st, a, p.scx);
                 else
@@ -316,13 +327,20 @@ __global__ __launch_bounds__(kTabRows* kBlock) void fwd1_tab_kernel(FwdParams p,
         int64_t t0 = -1;
         float xt0 = 0.0f;
         if (live) {
-            if (HEAD == kHeadLogp && tid < p.k) {
-                t0 = p.targets[row * p.k + tid];
-                if (t0 >= p.v0 && t0 < p.v0 + p.V) xt0 = load_one(x + (t0 - p.v0));
-            }
+            // (the target's logit is gathered behind the first group, as in
+            // fwd1_kernel)
+            if (HEAD == kHeadLogp && tid < p.k) t0 = p.targets[row * p.k + tid];
+            bool gathered = HEAD != kHeadLogp;
             Stat1 st{0.0f, -half, 0.0f, 0.0f};
             for_each_group<BLOCK, U, S, TAB, ALIGNED, kFwdPipe, NT>(
                 x, p.V, ct, [&](int64_t, bool full, const float (&a)[U][kChunk]) {
+                    if (!gathered) {
+                        gathered = true;
+                        int64_t t = t0;
+                        __asm__ volatile("" : "+v"(t));
+                        if (tid < p.k && t >= p.v0 && t < p.v0 + p.V)
+                            xt0 = load_one(x + (t - p.v0));
+                    }
                     if (full)
                         update1<U, WITH_W, false, true>(st, a, p.scx);
                     else
