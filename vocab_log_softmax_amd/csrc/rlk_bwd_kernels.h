@@ -562,7 +562,10 @@ __device__ __forceinline__ void wide_piece(const BwdParams& p, int64_t row, int6
     using S = typename T::storage;
     constexpr int BLOCK = kGLanes, NW = kGLanes / 64;
     constexpr int PC = BLOCK * U;  // chunks per piece
-    __shared__ uint32_t bits[PC / 4];
+    // one byte per chunk, lane-major: word t holds lane t's U chunks (byte
+    // u: the columns of chunk slot u marked), so a lane reads its marks once
+    static_assert(U <= 4, "a lane's chunk marks fill one word");
+    __shared__ uint32_t bits[BLOCK];
     // (the column's lane-order index in the piece, piece_slot; g as bits) in
     // slot order, padded to a multiple of 4 entries with (-1, +0) so that the
     // search reads 4 entries per step (8 per step measured slower: the kernel
@@ -612,8 +615,7 @@ __device__ __forceinline__ void wide_piece(const BwdParams& p, int64_t row, int6
         // the list and bitmap index values in lane order (piece_slot)
         pcol = piece_slot<BLOCK, piece_quads<S, FULL>()>(static_cast<int>(c));
     }
-#pragma unroll
-    for (int i = tid; i < PC / 4; i += BLOCK) bits[i] = 0u;
+    bits[tid] = 0u;
     part = wave_sum(part);
     cnt = wave_sum(cnt);
     const uint64_t m = __ballot(mine);
@@ -639,7 +641,7 @@ __device__ __forceinline__ void wide_piece(const BwdParams& p, int64_t row, int6
         const int rank = __popcll(m & ((1ull << lane) - 1ull));
         list[base + rank] = make_int2(pcol, __float_as_int(gj));
         const int ci = pcol / kChunk;
-        atomicOr(&bits[ci >> 2], 1u << ((ci & 3) * 8 + pcol % kChunk));
+        atomicOr(&bits[ci % BLOCK], 1u << ((ci / BLOCK) * 8 + pcol % kChunk));
     }
     if (tid >= total && tid < ((total + 3) & ~3)) list[tid] = make_int2(-1, 0);
     if (total > 0) __syncthreads();  // uniform: the list and bitmap are complete
@@ -682,6 +684,7 @@ __device__ __forceinline__ void wide_piece(const BwdParams& p, int64_t row, int6
         const float cf = slope_factor<CAPA>(ca);
         float A, B;
         row_coeffs<kHeadLogp, CAPA>(rs, G, 0.0f, cf, A, B);
+        const uint32_t marks = total > 0 ? bits[tid] : 0u;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int ci = u * BLOCK + tid;
@@ -693,7 +696,7 @@ __device__ __forceinline__ void wide_piece(const BwdParams& p, int64_t row, int6
             }
             // (a target column takes its statistic input and slope again
             // from x: keeping them for all 8 columns costs registers)
-            const uint32_t mark = total > 0 ? (bits[ci >> 2] >> ((ci & 3) * 8)) & 0xffu : 0u;
+            const uint32_t mark = (marks >> (u * 8)) & 0xffu;
             if (mark) {  // rare: a target column in this chunk
                 for (int e = 0; e < kChunk; ++e) {
                     if (!(mark & (1u << e))) continue;
