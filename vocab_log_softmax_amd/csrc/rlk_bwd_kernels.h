@@ -698,8 +698,12 @@ __device__ __forceinline__ void wide_piece(const BwdParams& p, int64_t row, int6
             // from x: keeping them for all 8 columns costs registers)
             const uint32_t mark = (marks >> (u * 8)) & 0xffu;
             if (mark) {  // rare: a target column in this chunk
-                for (int e = 0; e < kChunk; ++e) {
-                    if (!(mark & (1u << e))) continue;
+                // one pass per marked column (its value picked by selects),
+                // not a test of all 8 with the search repeated in each
+                uint32_t mk = mark;
+                do {
+                    const int e = __builtin_ctz(mk);
+                    mk &= mk - 1u;
                     const int col = ci * kChunk + e;
                     float h = 0.0f;
                     if (sorted) {
@@ -725,10 +729,15 @@ __device__ __forceinline__ void wide_piece(const BwdParams& p, int64_t row, int6
                             h += l1.z == col ? __int_as_float(l1.w) : 0.0f;
                         }
                     }
+                    float xe = x[u][0];
+#pragma unroll
+                    for (int i = 1; i < kChunk; ++i) xe = e == i ? x[u][i] : xe;
                     float s4;
-                    const float a = cap_value_slope<CAPA>(x[u][e], ca, s4);
-                    v[u][e] = target_grad<CAPA>(a, s4, cf, rs, G, h, p.scx);
-                }
+                    const float a = cap_value_slope<CAPA>(xe, ca, s4);
+                    const float tg = target_grad<CAPA>(a, s4, cf, rs, G, h, p.scx);
+#pragma unroll
+                    for (int i = 0; i < kChunk; ++i) v[u][i] = e == i ? tg : v[u][i];
+                } while (mk);
             }
         }
     } else {
