@@ -123,9 +123,9 @@ constexpr int kBwdUnrollTopk = RLK_BWD_UNROLL_TOPK;
 // (bf16 / fp32 [.., 151936] logprobs and entropy, KL [.., 75968]; 256 lanes x
 // 16 bytes of each operand per piece): moving 8 KB per piece (16-bit
 // logprobs, entropy) is best with all the 8 the registers allow (6: +10%);
-// 12 KB (16-bit KL) with 6 (-2 to -3%); 16 and 24 KB (fp32) with 4 (logprobs
-// -10%, KL -3 to -5%).  The limit is set by dynamic LDS that the kernel does
-// not use.
+// 12 KB (16-bit KL) with 6 (-2 to -3%; 7: +1%); 16 KB (fp32 logprobs,
+// entropy) with 4 (-10%); 24 KB (fp32 KL) with 3 (-5 to -7%).  The limit is
+// set by dynamic LDS that the kernel does not use.
 constexpr int kLdsPerCu = 160 * 1024;  // LDS per CU
 constexpr int kLdsGranule = 512;       // its allocation unit
 inline unsigned lds_for_wgs_per_cu(int w) {
@@ -135,7 +135,7 @@ inline unsigned lds_for_wgs_per_cu(int w) {
 }
 template <int ESIZE, bool KL>
 constexpr int piece_wgs_per_cu() {
-    return ESIZE == 4 ? 4 : (KL ? 6 : 8);
+    return ESIZE == 4 ? (KL ? 3 : 4) : (KL ? 6 : 8);
 }
 // Wide top-k pieces (16 KB of 16-bit logits read and written, 32 KB of fp32):
 // the capped 16-bit backward needs every resident wave for its arithmetic
