@@ -556,29 +556,51 @@ __global__ __launch_bounds__(BLOCK) void bwd_last_piece_kernel(BwdParams p, int6
 // FULL: every chunk of the piece lies inside an aligned row, so its loads are
 // raw 16-byte vectors issued back to back without branches (tail_values'
 // per-chunk branches would make the compiler wait for each load in turn).
-template <int U, typename T, int CAPA, bool ALIGNED, bool FULL, bool NT, bool CUT = false>
-__device__ __forceinline__ void wide_piece(const BwdParams& p, int64_t row, int64_t g0,
-                                           int64_t cut = 0) {
-    using S = typename T::storage;
-    constexpr int BLOCK = kGLanes, NW = kGLanes / 64;
-    constexpr int PC = BLOCK * U;  // chunks per piece
+// LDS of a wide piece, declared once per kernel (the full and tail forms of
+// the piece are two instantiations of wide_piece and share it).
+template <int U>
+struct WideLds {
+    static constexpr int NW = kGLanes / 64, PC = kGLanes * U;
     // one byte per chunk, lane-major: word t holds lane t's U chunks (byte
     // u: the columns of chunk slot u marked), so a lane reads its marks once
-    static_assert(U <= 4, "a lane's chunk marks fill one word");
-    __shared__ uint32_t bits[BLOCK];
+    uint32_t bits[kGLanes];
     // (the column's lane-order index in the piece, piece_slot; g as bits) in
     // slot order, padded to a multiple of 4 entries with (-1, +0) so that the
     // search reads 4 entries per step (8 per step measured slower: the kernel
     // then needs 88 VGPRs instead of 80, 5 waves per SIMD instead of 6)
-    __shared__ __align__(16) int2 list[kGLanes];
+    alignas(16) int2 list[kGLanes];
     // A list longer than kWideScanMax entries (many targets per piece: a small
     // V or a large k) is searched through its keys (lane-order index << 16 |
     // list index) sorted in LDS and the first sorted position of each marked
     // chunk.
-    __shared__ uint32_t skey[kGLanes];
-    __shared__ uint16_t cstart[PC];
-    __shared__ float red_g[NW], red_n[NW];
-    __shared__ int red_c[NW];
+    uint32_t skey[kGLanes];
+    uint16_t cstart[PC];
+    // A short list without repeated columns (no duplicate ids in the piece,
+    // the common case) is not searched: each marked column's list position
+    // sits in head (written only for marked columns, so never cleared)
+    uint8_t head[PC * kChunk];
+    int dup;  // some column is marked by more than one slot
+    float red_g[NW], red_n[NW];
+    int red_c[NW];
+};
+
+template <int U, typename T, int CAPA, bool ALIGNED, bool FULL, bool NT, bool CUT = false>
+__device__ __forceinline__ void wide_piece(const BwdParams& p, WideLds<U>& L, int64_t row,
+                                           int64_t g0, int64_t cut = 0) {
+    using S = typename T::storage;
+    constexpr int BLOCK = kGLanes, NW = kGLanes / 64;
+    constexpr int PC = BLOCK * U;  // chunks per piece
+    static_assert(U <= 4, "a lane's chunk marks fill one word");
+    static_assert(kGLanes <= 256, "list positions fit head's bytes");
+    uint32_t(&bits)[kGLanes] = L.bits;
+    int2(&list)[kGLanes] = L.list;
+    uint32_t(&skey)[kGLanes] = L.skey;
+    uint16_t(&cstart)[PC] = L.cstart;
+    uint8_t(&head)[PC * kChunk] = L.head;
+    int& dup = L.dup;
+    float(&red_g)[NW] = L.red_g;
+    float(&red_n)[NW] = L.red_n;
+    int(&red_c)[NW] = L.red_c;
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int64_t nfull = p.V / kChunk;
     const RowStats* stats = static_cast<const RowStats*>(p.stats);
@@ -616,6 +638,7 @@ __device__ __forceinline__ void wide_piece(const BwdParams& p, int64_t row, int6
         pcol = piece_slot<BLOCK, piece_quads<S, FULL>()>(static_cast<int>(c));
     }
     bits[tid] = 0u;
+    if (tid == 0) dup = 0;
     part = wave_sum(part);
     cnt = wave_sum(cnt);
     const uint64_t m = __ballot(mine);
@@ -640,8 +663,10 @@ __device__ __forceinline__ void wide_piece(const BwdParams& p, int64_t row, int6
     if (mine) {
         const int rank = __popcll(m & ((1ull << lane) - 1ull));
         list[base + rank] = make_int2(pcol, __float_as_int(gj));
+        head[pcol] = static_cast<uint8_t>(base + rank);
         const int ci = pcol / kChunk;
-        atomicOr(&bits[ci % BLOCK], 1u << ((ci / BLOCK) * 8 + pcol % kChunk));
+        const uint32_t bit = 1u << ((ci / BLOCK) * 8 + pcol % kChunk);
+        if (atomicOr(&bits[ci % BLOCK], bit) & bit) dup = 1;
     }
     if (tid >= total && tid < ((total + 3) & ~3)) list[tid] = make_int2(-1, 0);
     if (total > 0) __syncthreads();  // uniform: the list and bitmap are complete
@@ -706,7 +731,11 @@ __device__ __forceinline__ void wide_piece(const BwdParams& p, int64_t row, int6
                     mk &= mk - 1u;
                     const int col = ci * kChunk + e;
                     float h = 0.0f;
-                    if (sorted) {
+                    if (!sorted && !dup) {
+                        // the column's one slot (h = +0 + g, as the scan
+                        // below would sum it)
+                        h += __int_as_float(list[head[col]].y);
+                    } else if (sorted) {
                         // the chunk's keys follow cstart in (column, slot)
                         // order: the column's g are summed in slot order
                         for (int r = cstart[ci]; r < total; ++r) {
@@ -760,17 +789,18 @@ template <int U, typename T, int CAPA, bool ALIGNED, bool NT>
 __device__ __forceinline__ void wide_pieces(const BwdParams& p, int64_t rbase) {
     const int64_t row = p.N - 1 - (rbase + static_cast<int64_t>(blockIdx.y));
     const int64_t g0 = static_cast<int64_t>(blockIdx.x) * (kGLanes * U);
+    __shared__ WideLds<U> L;
     if (ALIGNED && g0 + kGLanes * U <= p.V / kChunk)
-        wide_piece<U, T, CAPA, ALIGNED, true, NT>(p, row, g0);
+        wide_piece<U, T, CAPA, ALIGNED, true, NT>(p, L, row, g0);
     else
-        wide_piece<U, T, CAPA, ALIGNED, false, NT>(p, row, g0);
+        wide_piece<U, T, CAPA, ALIGNED, false, NT>(p, L, row, g0);
 }
 
-// Rows with 16-byte aligned starts: held to 80 VGPRs (six waves per SIMD; the
-// compiler's 81 leave five, and top-256 logprobs then measured 4% slower,
-// against 0.6% for the one spilled register).
+// Rows with 16-byte aligned starts: held to 72 VGPRs, seven waves per SIMD
+// (top-256 + cap 20 bf16 [2048, 262144]: 418 -> 399 us against six waves at
+// 76 VGPRs; eight waves spill and were slower for k = 16 and 64).
 template <int U, typename T, int CAPA, bool NT>
-__global__ __launch_bounds__(kGLanes) __attribute__((amdgpu_waves_per_eu(6))) void bwd_wide_kernel(
+__global__ __launch_bounds__(kGLanes) __attribute__((amdgpu_waves_per_eu(7))) void bwd_wide_kernel(
     BwdParams p, int64_t rbase) {
     wide_pieces<U, T, CAPA, true, NT>(p, rbase);
 }
@@ -788,7 +818,8 @@ bwd_wide_last_kernel(BwdParams p, int64_t rbase) {
     const int64_t row = p.N - 1 - (rbase + static_cast<int64_t>(blockIdx.y));
     const int64_t nfull = p.V / kChunk;
     const int64_t cut = nfull / (kGLanes * U) * (kGLanes * U);
-    wide_piece<U, T, CAPA, true, true, NT, true>(p, row, nfull - kGLanes * U, cut);
+    __shared__ WideLds<U> L;
+    wide_piece<U, T, CAPA, true, true, NT, true>(p, L, row, nfull - kGLanes * U, cut);
 }
 
 // ------------------------------------------------------------- dispatch
