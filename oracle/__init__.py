@@ -12,9 +12,11 @@ fp32 tensor converted with ``.double()`` is exact) and returns fp64 results.
 Parity pins: every function here is pinned by ``tests/test_oracle_pins.py``
 against closed forms, invariants, brute force on tiny rows, finite differences
 and independent library routines (torch fp64 ``log_softmax``, ``kl_div``,
-autograd).  The one reading with no independent pin (gradient on a
-reverse-KL support-mismatch row: NaN on the policy's support) is marked
-"parity unpinned" there.
+autograd).  The gradient on a reverse-KL support-mismatch row (NaN on the
+policy's support, 0 off it) is pinned by the limit of finite rows, up to the
+NaN marker; its one corner without a pin (the reference masks all of the
+policy's support, where the finite gradients converge) is marked "parity
+unpinned" there.
 """
 
 from __future__ import annotations

@@ -451,6 +451,54 @@ def pin_kl_mismatch_and_empty(orc):
     assert np.isnan(gr[0]).all() and np.isnan(gr[2:]).all()
 
 
+def pin_kl_mismatch_limit(orc):
+    """The reverse-KL gradient on a support-mismatch row as the limit of
+    finite rows.  Replace the reference's -inf logits by -M: the row is then
+    an ordinary one, whose gradient the autograd and finite-difference pins
+    fix.  As M grows, KL grows like P_m M (P_m: the policy's mass on the
+    columns the reference masks) and the gradient on the policy's support
+    diverges like M (g p_v (1 - P_m) M on the masked columns, -g p_v P_m M on
+    the others), so no finite value is right there, while a column off the
+    policy's support (policy logit -inf) has p_v = 0 and a gradient of
+    exactly 0 at every M.  The mismatch row must therefore be non-finite on
+    the support (the oracle's class for it is NaN, the same marker as for
+    the other rows without a defined gradient) and exactly 0 off it.  (When
+    the reference masks all of the policy's support, P_m = 1, the finite
+    gradients converge instead; rows here keep P_m < 1.)"""
+    r = rng(25)
+    V = 10
+    a = r.normal(0, 1, (2, V))
+    b = r.normal(0, 1, (2, V))
+    a[0, 8:] = -np.inf               # off the policy's support
+    b[0, [0, 1, 9]] = -np.inf        # 0, 1: the mismatch; 9: masked on both sides
+    a[1, 0] = -np.inf
+    b[1, [3, 4, 5]] = -np.inf
+    g = np.array([1.3, -0.7])
+    assert (orc.kl_fwd(a, b, 0) == np.inf).all()
+    gr = orc.kl_bwd(a, b, g, 0)
+    off = ~np.isfinite(a)
+    masked = ~np.isfinite(b) & ~off
+    pa = np.where(off, 0.0, np.exp(a - np.log(np.exp(np.where(off, -np.inf, a)).sum(-1,
+                                                                                   keepdims=True))))
+    pm = (pa * masked).sum(-1, keepdims=True)
+    assert ((pm > 0) & (pm < 1)).all()
+    rate = g[:, None] * pa * np.where(masked, 1.0 - pm, -pm)   # d grad / dM
+    # Past M ~ 40 the finite row's gradient is affine in M up to terms of
+    # e^-M, so its slope between two values of M is the rate itself.
+    prev = None
+    for M in (1e3, 1e4, 1e5, 1e6):
+        gm = orc.kl_bwd(a, np.where(np.isfinite(b), b, -M), g, 0)
+        assert np.isfinite(gm).all()
+        assert (gm[off] == 0).all(), "a column off the support has a zero gradient at every M"
+        on = gm[~off]
+        if prev is not None:
+            close((on - prev[1]) / (M - prev[0]), rate[~off], 1e-8, 1e-12, f"slope at M={M:g}")
+            assert (np.abs(on) > np.abs(prev[1])).all(), "the support's gradient grows with M"
+        prev = (M, on)
+    assert (gr[off] == 0).all(), "mismatch row: zero off the policy's support"
+    assert np.isnan(gr[~off]).all(), "mismatch row: non-finite (NaN) on the policy's support"
+
+
 def pin_kl_masked_policy(orc):
     r = rng(21)
     a = _masked_rows(r, 4, 60, 3.0)

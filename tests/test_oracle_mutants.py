@@ -44,6 +44,11 @@ MUTANTS = {
     "kl_direction_ignored": ("dir == ORC_KL_REVERSE ? row_kl(&P, &R, V) : row_kl(&R, &P, V)",
                              "row_kl(&P, &R, V)"),
     "reverse_kl_grad_D_dropped": ("((P.logp[v] - R.logp[v]) - D)", "((P.logp[v] - R.logp[v]))"),
+    "reverse_kl_mismatch_nan_off_support": (
+        "if (P.logp[v] == -INFINITY)\n                    gr[v] = 0.0;\n"
+        "                else if (D == INFINITY)\n                    gr[v] = NAN;",
+        "if (D == INFINITY)\n                    gr[v] = NAN;\n"
+        "                else if (P.logp[v] == -INFINITY)\n                    gr[v] = 0.0;"),
     "forward_kl_grad_sign": ("(P.p[v] - R.p[v])", "(R.p[v] - P.p[v])"),
     "forward_kl_grad_slope_dropped": ("g[i] * (P.p[v] - R.p[v]) * P.s[v];",
                                       "g[i] * (P.p[v] - R.p[v]);"),
