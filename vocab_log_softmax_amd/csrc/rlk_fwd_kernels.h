@@ -171,6 +171,19 @@ __device__ __forceinline__ void update_kl2(StatKL2& st, const float (&a)[U][kChu
         }
 }
 
+// One target slot's output: the statistic input of a target this shard owns
+// (shard call) or the slot's logprob, 0 for a target outside [0, V).
+template <int CAP>
+__device__ __forceinline__ void slot_out(const FwdParams& p, int64_t row, int64_t j, int64_t t,
+                                         float xv, CapArgs ca, const RowStats& rs) {
+    const bool local = t >= p.v0 && t < p.v0 + p.V;
+    const float a = local ? cap_value<CAP>(xv, ca) : 0.0f;
+    if (p.part)
+        p.tvals[row * p.k + j] = a;
+    else
+        p.out[row * p.k + j] = (t >= 0 && t < p.vtotal) ? target_logp(a, p.scx, rs) : 0.0f;
+}
+
 // Logprobs / entropy forward: one workgroup per row.
 template <int BLOCK, int U, typename T, int HEAD, int CAP, bool ALIGNED, bool NT, bool ODD = false>
 __global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void fwd1_kernel(FwdParams p) {
@@ -220,6 +233,9 @@ __global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void fwd1_kernel(FwdParams p) 
                 else
                     update1<U, WITH_W, WITH_W, FIX>(st, a, p.scx);
             });
+        // The gathered logit is waited for here, where the walk's own loads
+        // have arrived, and not at its use below, behind the record's store.
+        if (HEAD == kHeadLogp) __asm__ volatile("" : "+v"(xt0));
         st = wave_reduce<WITH_W>(st);
         if (lane == 0) red[wid] = st;
         __syncthreads();
@@ -242,35 +258,36 @@ __global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void fwd1_kernel(FwdParams p) 
             RowStats rs;
             rs.mLa = bc[0];
             rs.log2Sa = bc[1];
-            // Slots beyond the prefetched first one (k > BLOCK), kTopkBatch
-            // per lane at a time: their target loads are issued together,
-            // then their gathers, so a lane waits twice per batch instead of
-            // twice per slot.
-            for (int64_t j0 = tid; j0 < p.k; j0 += static_cast<int64_t>(BLOCK) * kTopkBatch) {
-                int64_t t[kTopkBatch];
-                float xv[kTopkBatch];
+            if (p.k <= BLOCK) {
+                // Every slot is a lane's prefetched first one: no load here,
+                // hence no wait, which would also wait for the record's store
+                // above (one counter covers loads and stores).
+                if (tid < p.k) slot_out<CAP>(p, row, tid, t0, xt0, ca, rs);
+            } else {
+                // Slots beyond the prefetched first one, kTopkBatch per lane
+                // at a time: their target loads are issued together, then
+                // their gathers, so a lane waits twice per batch instead of
+                // twice per slot.
+                for (int64_t j0 = tid; j0 < p.k; j0 += static_cast<int64_t>(BLOCK) * kTopkBatch) {
+                    int64_t t[kTopkBatch];
+                    float xv[kTopkBatch];
 #pragma unroll
-                for (int b = 0; b < kTopkBatch; ++b) {
-                    const int64_t j = j0 + static_cast<int64_t>(b) * BLOCK;
-                    t[b] = j == tid ? t0 : (j < p.k ? p.targets[row * p.k + j] : -1);
-                }
+                    for (int b = 0; b < kTopkBatch; ++b) {
+                        const int64_t j = j0 + static_cast<int64_t>(b) * BLOCK;
+                        t[b] = j == tid ? t0 : (j < p.k ? p.targets[row * p.k + j] : -1);
+                    }
 #pragma unroll
-                for (int b = 0; b < kTopkBatch; ++b) {
-                    const int64_t j = j0 + static_cast<int64_t>(b) * BLOCK;
-                    const bool local = t[b] >= p.v0 && t[b] < p.v0 + p.V;
-                    xv[b] = j == tid ? xt0 : (local ? load_one(x + (t[b] - p.v0)) : 0.0f);
-                }
+                    for (int b = 0; b < kTopkBatch; ++b) {
+                        const int64_t j = j0 + static_cast<int64_t>(b) * BLOCK;
+                        const bool local = t[b] >= p.v0 && t[b] < p.v0 + p.V;
+                        xv[b] = j == tid ? xt0 : (local ? load_one(x + (t[b] - p.v0)) : 0.0f);
+                    }
 #pragma unroll
-                for (int b = 0; b < kTopkBatch; ++b) {
-                    const int64_t j = j0 + static_cast<int64_t>(b) * BLOCK;
-                    if (j >= p.k) break;
-                    const bool local = t[b] >= p.v0 && t[b] < p.v0 + p.V;
-                    const float a = local ? cap_value<CAP>(xv[b], ca) : 0.0f;
-                    if (p.part)
-                        p.tvals[row * p.k + j] = a;  // statistic input of an owned target
-                    else
-                        p.out[row * p.k + j] =
-                            (t[b] >= 0 && t[b] < p.vtotal) ? target_logp(a, p.scx, rs) : 0.0f;
+                    for (int b = 0; b < kTopkBatch; ++b) {
+                        const int64_t j = j0 + static_cast<int64_t>(b) * BLOCK;
+                        if (j >= p.k) break;
+                        slot_out<CAP>(p, row, j, t[b], xv[b], ca, rs);
+                    }
                 }
             }
         }
@@ -346,6 +363,7 @@ __global__ __launch_bounds__(kTabRows* kBlock) void fwd1_tab_kernel(FwdParams p,
                     else
                         update1<U, WITH_W, WITH_W, true>(st, a, p.scx);
                 });
+            if (HEAD == kHeadLogp) __asm__ volatile("" : "+v"(xt0));  // (as in fwd1_kernel)
             st = wave_reduce<WITH_W>(st);
             if (lane == 0) red[sub][wid] = st;
         }
@@ -372,31 +390,30 @@ __global__ __launch_bounds__(kTabRows* kBlock) void fwd1_tab_kernel(FwdParams p,
             RowStats rs;
             rs.mLa = bc[sub][0];
             rs.log2Sa = bc[sub][1];
-            for (int64_t j0 = tid; j0 < p.k; j0 += static_cast<int64_t>(BLOCK) * kTopkBatch) {
-                int64_t t[kTopkBatch];
-                float xv[kTopkBatch];
+            if (p.k <= BLOCK) {
+                // (as in fwd1_kernel: no load, no wait)
+                if (tid < p.k) slot_out<kCapFixed>(p, row, tid, t0, xt0, cf, rs);
+            } else {
+                for (int64_t j0 = tid; j0 < p.k; j0 += static_cast<int64_t>(BLOCK) * kTopkBatch) {
+                    int64_t t[kTopkBatch];
+                    float xv[kTopkBatch];
 #pragma unroll
-                for (int b = 0; b < kTopkBatch; ++b) {
-                    const int64_t j = j0 + static_cast<int64_t>(b) * BLOCK;
-                    t[b] = j == tid ? t0 : (j < p.k ? p.targets[row * p.k + j] : -1);
-                }
+                    for (int b = 0; b < kTopkBatch; ++b) {
+                        const int64_t j = j0 + static_cast<int64_t>(b) * BLOCK;
+                        t[b] = j == tid ? t0 : (j < p.k ? p.targets[row * p.k + j] : -1);
+                    }
 #pragma unroll
-                for (int b = 0; b < kTopkBatch; ++b) {
-                    const int64_t j = j0 + static_cast<int64_t>(b) * BLOCK;
-                    const bool local = t[b] >= p.v0 && t[b] < p.v0 + p.V;
-                    xv[b] = j == tid ? xt0 : (local ? load_one(x + (t[b] - p.v0)) : 0.0f);
-                }
+                    for (int b = 0; b < kTopkBatch; ++b) {
+                        const int64_t j = j0 + static_cast<int64_t>(b) * BLOCK;
+                        const bool local = t[b] >= p.v0 && t[b] < p.v0 + p.V;
+                        xv[b] = j == tid ? xt0 : (local ? load_one(x + (t[b] - p.v0)) : 0.0f);
+                    }
 #pragma unroll
-                for (int b = 0; b < kTopkBatch; ++b) {
-                    const int64_t j = j0 + static_cast<int64_t>(b) * BLOCK;
-                    if (j >= p.k) break;
-                    const bool local = t[b] >= p.v0 && t[b] < p.v0 + p.V;
-                    const float a = local ? cap_value<kCapFixed>(xv[b], cf) : 0.0f;
-                    if (p.part)
-                        p.tvals[row * p.k + j] = a;
-                    else
-                        p.out[row * p.k + j] =
-                            (t[b] >= 0 && t[b] < p.vtotal) ? target_logp(a, p.scx, rs) : 0.0f;
+                    for (int b = 0; b < kTopkBatch; ++b) {
+                        const int64_t j = j0 + static_cast<int64_t>(b) * BLOCK;
+                        if (j >= p.k) break;
+                        slot_out<kCapFixed>(p, row, j, t[b], xv[b], cf, rs);
+                    }
                 }
             }
         }
