@@ -967,18 +967,49 @@ __device__ __forceinline__ float shfl_xor(float v, int mask) {
     return __shfl_xor(v, mask, 64);
 }
 
+// Wave64 butterflies on lane moves that stay in registers: DPP quad
+// permutations (lane ^ 1, lane ^ 2), the half-row and row mirrors (lane i
+// with 7 - i and 15 - i: after the steps before, the same pairs of partial
+// results as lane ^ 4 and lane ^ 8) and the 16- and 32-lane swaps.  Each step
+// combines two values with a commutative operation, so every lane ends with
+// the same bits.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <typename OP>
+__device__ __forceinline__ float wave_fold(float v, OP op) {
+    v = op(v, dpp_move<0xB1>(v));   // quad_perm [1, 0, 3, 2]
+    v = op(v, dpp_move<0x4E>(v));   // quad_perm [2, 3, 0, 1]
+    v = op(v, dpp_move<0x141>(v));  // row_half_mirror
+    v = op(v, dpp_move<0x140>(v));  // row_mirror
+    const auto h = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                    false);
+    v = op(__uint_as_float(h[0]), __uint_as_float(h[1]));
+    const auto w = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                    false);
+    return op(__uint_as_float(w[0]), __uint_as_float(w[1]));
+}
+
+// A wave's state: the maximum first (with its reference: mL = m * scale
+// grows with m), then each lane's sums rescaled to it once, then plain
+// sums.  Two butterflies of max and add replace a chain of rescaling merges
+// (each step waiting for a shuffle, an exponential and its products); the
+// tree is fixed, so the result is the same for every batch.
 template <bool WITH_W>
 __device__ __forceinline__ Stat1 wave_reduce(Stat1 s) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        Stat1 o;
-        o.m = shfl_xor(s.m, off);
-        o.mL = shfl_xor(s.mL, off);
-        o.S = shfl_xor(s.S, off);
-        o.W = WITH_W ? shfl_xor(s.W, off) : 0.0f;
-        s = stat1_merge<WITH_W>(s, o);
-    }
-    return s;
+    const auto mx = [](float a, float b) { return fmaxf(a, b); };
+    const auto add = [](float a, float b) { return a + b; };
+    const bool empty = s.m == neg_inf();
+    const float M = wave_fold(s.m, mx);
+    const float ML = wave_fold(empty ? neg_inf() : s.mL, mx);
+    if (M == neg_inf()) return s;  // every lane empty (the same in all lanes)
+    const float d = s.mL - ML;     // <= 0
+    const float sc = empty ? 0.0f : ex2(d);
+    const float S = wave_fold(s.S * sc, add);
+    const float W = WITH_W ? wave_fold(empty ? 0.0f : sc * __builtin_fmaf(d, s.S, s.W), add)
+                           : 0.0f;
+    return {M, ML, S, W};
 }
 
 template <bool REVERSE>
