@@ -1012,41 +1012,71 @@ __device__ __forceinline__ Stat1 wave_reduce(Stat1 s) {
     return {M, ML, S, W};
 }
 
+// A wave's KL state, as wave_reduce: both sides' maxima and the flag first,
+// then each lane's sums rescaled once (a lane with an empty side carries no
+// W, as in statkl_merge), then plain sums.
+struct KLScale {
+    bool ea, eb;
+    float da, db, sa, sb;
+};
+__device__ __forceinline__ KLScale kl_scale(float ma, float mLa, float mb, float mLb, float& MLa,
+                                            float& MLb) {
+    const auto mx = [](float a, float b) { return fmaxf(a, b); };
+    KLScale k;
+    k.ea = ma == neg_inf();
+    k.eb = mb == neg_inf();
+    MLa = wave_fold(k.ea ? neg_inf() : mLa, mx);
+    MLb = wave_fold(k.eb ? neg_inf() : mLb, mx);
+    k.da = k.ea ? 0.0f : mLa - MLa;
+    k.db = k.eb ? 0.0f : mLb - MLb;
+    k.sa = k.ea ? 0.0f : ex2(k.da);
+    k.sb = k.eb ? 0.0f : ex2(k.db);
+    return k;
+}
+template <bool REVERSE>
+__device__ __forceinline__ float kl_w(const KLScale& k, float Sa, float Sb, float W) {
+    if (k.ea || k.eb) return 0.0f;
+    return REVERSE ? k.sa * __builtin_fmaf(k.da - k.db, Sa, W)
+                   : k.sb * __builtin_fmaf(k.db - k.da, Sb, W);
+}
 template <bool REVERSE>
 __device__ __forceinline__ StatKL wave_reduce_kl(StatKL s) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        StatKL o;
-        o.ma = shfl_xor(s.ma, off);
-        o.mLa = shfl_xor(s.mLa, off);
-        o.Sa = shfl_xor(s.Sa, off);
-        o.mb = shfl_xor(s.mb, off);
-        o.mLb = shfl_xor(s.mLb, off);
-        o.Sb = shfl_xor(s.Sb, off);
-        o.W = shfl_xor(s.W, off);
-        o.flag = shfl_xor(s.flag, off);
-        s = statkl_merge<REVERSE>(s, o);
-    }
-    return s;
+    const auto mx = [](float a, float b) { return fmaxf(a, b); };
+    const auto mn = [](float a, float b) { return fminf(a, b); };
+    const auto add = [](float a, float b) { return a + b; };
+    float MLa, MLb;
+    const KLScale k = kl_scale(s.ma, s.mLa, s.mb, s.mLb, MLa, MLb);
+    StatKL o;
+    o.ma = wave_fold(s.ma, mx);
+    o.mb = wave_fold(s.mb, mx);
+    o.mLa = o.ma == neg_inf() ? s.mLa : MLa;  // (every lane empty: its own, the same)
+    o.mLb = o.mb == neg_inf() ? s.mLb : MLb;
+    o.flag = REVERSE ? wave_fold(s.flag, mx) : wave_fold(s.flag, mn);
+    o.Sa = wave_fold(s.Sa * k.sa, add);
+    o.Sb = wave_fold(s.Sb * k.sb, add);
+    o.W = wave_fold(kl_w<REVERSE>(k, s.Sa, s.Sb, s.W), add);
+    return o;
 }
 
+// Both directions: the very operations of wave_reduce_kl for each.
 __device__ __forceinline__ StatKL2 wave_reduce_kl2(StatKL2 s) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        StatKL2 o;
-        o.ma = shfl_xor(s.ma, off);
-        o.mLa = shfl_xor(s.mLa, off);
-        o.Sa = shfl_xor(s.Sa, off);
-        o.mb = shfl_xor(s.mb, off);
-        o.mLb = shfl_xor(s.mLb, off);
-        o.Sb = shfl_xor(s.Sb, off);
-        o.Wr = shfl_xor(s.Wr, off);
-        o.Wf = shfl_xor(s.Wf, off);
-        o.fmax = shfl_xor(s.fmax, off);
-        o.fmin = shfl_xor(s.fmin, off);
-        s = statkl2_merge(s, o);
-    }
-    return s;
+    const auto mx = [](float a, float b) { return fmaxf(a, b); };
+    const auto mn = [](float a, float b) { return fminf(a, b); };
+    const auto add = [](float a, float b) { return a + b; };
+    float MLa, MLb;
+    const KLScale k = kl_scale(s.ma, s.mLa, s.mb, s.mLb, MLa, MLb);
+    StatKL2 o;
+    o.ma = wave_fold(s.ma, mx);
+    o.mb = wave_fold(s.mb, mx);
+    o.mLa = o.ma == neg_inf() ? s.mLa : MLa;
+    o.mLb = o.mb == neg_inf() ? s.mLb : MLb;
+    o.fmax = wave_fold(s.fmax, mx);
+    o.fmin = wave_fold(s.fmin, mn);
+    o.Sa = wave_fold(s.Sa * k.sa, add);
+    o.Sb = wave_fold(s.Sb * k.sb, add);
+    o.Wr = wave_fold(kl_w<true>(k, s.Sa, s.Sb, s.Wr), add);
+    o.Wf = wave_fold(kl_w<false>(k, s.Sa, s.Sb, s.Wf), add);
+    return o;
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
