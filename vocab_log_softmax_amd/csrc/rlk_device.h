@@ -996,20 +996,41 @@ __device__ __forceinline__ float wave_fold(float v, OP op) {
 // sums.  Two butterflies of max and add replace a chain of rescaling merges
 // (each step waiting for a shuffle, an exponential and its products); the
 // tree is fixed, so the result is the same for every batch.
-template <bool WITH_W>
-__device__ __forceinline__ Stat1 wave_reduce(Stat1 s) {
+// The first N lanes of each group of N (N = 1, 2, 4, 8 or 16) folded with
+// the first steps of wave_fold.
+template <int N, typename OP>
+__device__ __forceinline__ float lanes_fold(float v, OP op) {
+    static_assert(N == 1 || N == 2 || N == 4 || N == 8 || N == 16, "a power of two up to a row");
+    if (N >= 2) v = op(v, dpp_move<0xB1>(v));
+    if (N >= 4) v = op(v, dpp_move<0x4E>(v));
+    if (N >= 8) v = op(v, dpp_move<0x141>(v));
+    if (N >= 16) v = op(v, dpp_move<0x140>(v));
+    return v;
+}
+template <bool WITH_W, typename FOLD>
+__device__ __forceinline__ Stat1 stat1_fold(Stat1 s, FOLD fold) {
     const auto mx = [](float a, float b) { return fmaxf(a, b); };
     const auto add = [](float a, float b) { return a + b; };
     const bool empty = s.m == neg_inf();
-    const float M = wave_fold(s.m, mx);
-    const float ML = wave_fold(empty ? neg_inf() : s.mL, mx);
-    if (M == neg_inf()) return s;  // every lane empty (the same in all lanes)
+    const float M = fold(s.m, mx);
+    const float ML = fold(empty ? neg_inf() : s.mL, mx);
+    if (M == neg_inf()) return s;  // every lane folded is empty (and holds the same)
     const float d = s.mL - ML;     // <= 0
     const float sc = empty ? 0.0f : ex2(d);
-    const float S = wave_fold(s.S * sc, add);
-    const float W = WITH_W ? wave_fold(empty ? 0.0f : sc * __builtin_fmaf(d, s.S, s.W), add)
-                           : 0.0f;
+    const float S = fold(s.S * sc, add);
+    const float W = WITH_W ? fold(empty ? 0.0f : sc * __builtin_fmaf(d, s.S, s.W), add) : 0.0f;
     return {M, ML, S, W};
+}
+template <bool WITH_W>
+__device__ __forceinline__ Stat1 wave_reduce(Stat1 s) {
+    return stat1_fold<WITH_W>(s, [](float v, auto op) { return wave_fold(v, op); });
+}
+// The NW waves' states of a workgroup (red[0..NW)), combined the same way
+// by the first NW lanes of the wave that calls it (lane 0 holds the result).
+template <int NW, bool WITH_W>
+__device__ __forceinline__ Stat1 waves_reduce(const Stat1* red, int lane) {
+    return stat1_fold<WITH_W>(red[lane & (NW - 1)],
+                              [](float v, auto op) { return lanes_fold<NW>(v, op); });
 }
 
 // A wave's KL state, as wave_reduce: both sides' maxima and the flag first,

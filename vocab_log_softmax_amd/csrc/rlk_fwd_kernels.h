@@ -239,10 +239,9 @@ __global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void fwd1_kernel(FwdParams p) 
         st = wave_reduce<WITH_W>(st);
         if (lane == 0) red[wid] = st;
         __syncthreads();
+        Stat1 r{};
+        if (wid == 0) r = waves_reduce<NW, WITH_W>(red, lane);
         if (tid == 0) {
-            Stat1 r = red[0];
-#pragma unroll
-            for (int w = 1; w < NW; ++w) r = stat1_merge<WITH_W>(r, red[w]);
             if (p.part) {
                 static_cast<PartialRec*>(p.part)[row] = to_partial(r);
             } else {
@@ -368,10 +367,9 @@ __global__ __launch_bounds__(kTabRows* kBlock) void fwd1_tab_kernel(FwdParams p,
             if (lane == 0) red[sub][wid] = st;
         }
         __syncthreads();
+        Stat1 r{};
+        if (live && wid == 0) r = waves_reduce<NW, WITH_W>(red[sub], lane);
         if (live && tid == 0) {
-            Stat1 r = red[sub][0];
-#pragma unroll
-            for (int w = 1; w < NW; ++w) r = stat1_merge<WITH_W>(r, red[sub][w]);
             if (p.part) {
                 static_cast<PartialRec*>(p.part)[row] = to_partial(r);
             } else {
@@ -383,8 +381,8 @@ __global__ __launch_bounds__(kTabRows* kBlock) void fwd1_tab_kernel(FwdParams p,
             }
         }
         // Next pass: red[sub] is rewritten after this barrier, which its
-        // reader (tid 0) passes after reading it; bc[sub] after the next
-        // pass's first barrier, which its readers pass after reading it.
+        // readers (wave 0 of the row) pass after reading it; bc[sub] after the
+        // next pass's first barrier, which its readers pass after reading it.
         __syncthreads();
         if (live && HEAD == kHeadLogp) {
             RowStats rs;
