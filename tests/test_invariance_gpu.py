@@ -238,16 +238,17 @@ def _layout_targets(N, V, k, seed):
     return t
 
 
-@pytest.mark.parametrize("k,N", [(4, 300), (16, 300), (256, 300), (300, 300), (300, 600)])
+@pytest.mark.parametrize("k,N", [(4, 300), (8, 300), (16, 300), (256, 300), (300, 300),
+                                 (300, 600)])
 @pytest.mark.parametrize("cap", [0.0, 20.0])
 def test_fp32_piece_layout_matches_bf16(dev, k, N, cap):
     # fp32 full backward pieces hold two 16-byte quads 1024 columns apart per
     # lane and chunk slot, and fp32 row walks load and store each chunk's
     # halves through a lane swap; 16-bit ones hold one chunk.  The bf16
     # gradient must still be the round-to-nearest-even of the fp32 one at
-    # every column, target columns included (k = 4: one-shot pieces; 16 and
-    # 256: wide pieces, whose slot lists are scanned, or sorted when a piece
-    # holds more than 16; 300: the top-k row kernel, in column segments for
+    # every column, target columns included (k = 4: one-shot pieces; 8:
+    # half-size wide pieces; 16 and 256: wide pieces, whose slot lists are
+    # scanned, or sorted when a piece holds more than 16; 300: the top-k row kernel, in column segments for
     # 300 rows and one workgroup per row for 600).
     V = 16680
     x = (torch.randn(N, V, generator=_gen(71)) * (10.0 if cap else 3.0)).to(torch.bfloat16)

@@ -6,7 +6,8 @@ of its own (moved back to end at the row's end, storing only the columns the
 full pieces did not).  Smaller calls take the ordinary tail path.  These
 cases sit on the far side of that switch: V = 32000 (4000 chunks: 15 full
 256-chunk pieces and a 160-chunk tail; 3 full 1024-chunk wide pieces and a
-928-chunk tail) at 600 to 4200 rows.  Each case
+928-chunk tail, or, for k = 16, 7 full 512-chunk half-size wide pieces and
+a 416-chunk tail) at 600 to 4200 rows.  Each case
 
   * asserts that the shape meets the switch's condition (a mirror of the
     rule the library applies, ``last_piece_apart``), so the test provably
@@ -34,6 +35,15 @@ pytestmark = pytest.mark.gpu
 V = 32000
 PIECE_CHUNKS = 256    # one-shot piece: 256 lanes x 1 chunk (entropy, KL, logprobs k <= 4)
 WIDE_CHUNKS = 1024    # wide piece: 256 lanes x 4 chunks (logprobs 4 < k <= 256)
+
+
+def piece_chunks(k, V):
+    """Chunks per backward piece for logprobs with k slots (the library's
+    rule): one-shot pieces up to 4 slots; wide pieces above, half-size where
+    a full wide piece would hold at most 5 targets on average."""
+    if k <= 4:
+        return PIECE_CHUNKS
+    return WIDE_CHUNKS // 2 if k * WIDE_CHUNKS * 8 <= 5 * V else WIDE_CHUNKS
 
 
 def last_piece_apart(N, V, esize, pc):
@@ -88,14 +98,14 @@ def logits(dev, dtype, N, std, seed):
     return (torch.randn(N, V, generator=dgen(dev, seed), device=dev) * std).to(dtype)
 
 
-@pytest.mark.parametrize("k", [1, 4, 64])
+@pytest.mark.parametrize("k", [1, 4, 16, 64])
 @pytest.mark.parametrize("cap", [0.0, 30.0])
 @pytest.mark.parametrize("dtype,N", SHAPES, ids=SHAPE_IDS)
 def test_logp_last_piece(dev, orc, dtype, N, k, cap):
-    if N == 4200 and (k == 4 or cap):
+    if N == 4200 and (k in (4, 16) or cap):
         pytest.skip("the 4200-row shape covers k = 1 and 64 without a cap")
     es = torch.tensor([], dtype=dtype).element_size()
-    assert last_piece_apart(N, V, es, PIECE_CHUNKS if k <= 4 else WIDE_CHUNKS)
+    assert last_piece_apart(N, V, es, piece_chunks(k, V))
     x = logits(dev, dtype, N, 15.0 if cap else 3.0, 100 + k)
     x[7] += 1000.0
     t = torch.randint(0, V, (N, k), generator=cgen(k))
@@ -110,18 +120,21 @@ def test_logp_last_piece(dev, orc, dtype, N, k, cap):
     # Targets on both sides of the cut of the moved-back last piece: it
     # recomputes chunks [nfull - pc, pc * (nfull // pc)) and stores from
     # chunk pc * (nfull // pc) on (wide pieces: columns 23808..24575 and
-    # 24576.., one-shot pieces 29952..30719 and 30720..).
+    # 24576..; half-size wide pieces 27904..28671 and 28672..; one-shot
+    # pieces 29952..30719 and 30720..).
     t[5, 0] = V - 1
     t[6, 0] = 24575
     t[8, 0] = 24576
     t[9, 0] = 30719
     t[10, 0] = 30720
+    t[11, 0] = 28671
+    t[12, 0] = 28672
     g = torch.randn(N, k, generator=cgen(k + 2))
     td, gd = t.to(dev), g.to(dev)
     out, st = rlk.logp_fwd(x, td, cap)
     gx = rlk.logp_bwd(x, td, gd, st, cap)
     torch.cuda.synchronize()
-    rows = sample(N, [1, 2, 3, 5, 6, 7, 8, 9, 10], seed=k)
+    rows = sample(N, [1, 2, 3, 5, 6, 7, 8, 9, 10, 11, 12], seed=k)
     ri = torch.tensor(rows, device=dev)
     x64, t_np, g64 = to64(x[ri]), t[rows].numpy(), to64(g[rows])
     ref, refg = orc.logp_fwd(x64, t_np, cap), orc.logp_bwd(x64, t_np, g64, cap)
@@ -133,7 +146,7 @@ def test_logp_last_piece(dev, orc, dtype, N, k, cap):
     sub = [0, 3, 6, N - 1]
     si = torch.tensor(sub, device=dev)
     ts, gss = td[si].contiguous(), gd[si].contiguous()
-    assert not last_piece_apart(len(sub), V, es, PIECE_CHUNKS if k <= 4 else WIDE_CHUNKS)
+    assert not last_piece_apart(len(sub), V, es, piece_chunks(k, V))
     for xs in (x[si].contiguous(), misaligned(x[si])):
         so, sst = rlk.logp_fwd(xs, ts, cap)
         sg = rlk.logp_bwd(xs, ts, gss, sst, cap)

@@ -827,11 +827,16 @@ bwd_wide_last_kernel(BwdParams p, int64_t rbase) {
 // The backward is elementwise given the row record (and G has a fixed tree),
 // so its launch shape does not change any result and is chosen per call:
 // one-shot 256-thread pieces for entropy, KL and logprobs with k <= 4;
-// one-shot wide pieces (256 lanes x kBwdWideUnroll chunks) for logprobs with
-// k <= kGLanes; for wider top-k bwd_topk_kernel with 512-thread workgroups
+// one-shot wide pieces (256 lanes x kBwdWideUnroll chunks, half that where a
+// piece would hold few targets) for logprobs with k <= kGLanes; for wider top-k bwd_topk_kernel with 512-thread workgroups
 // (fewer idle lanes during each row's fix-up), or, for fewer than
 // kBwdSmallRows rows, 256-thread workgroups with the rows cut into column
 // segments.
+
+// Targets per full wide piece (on average) up to which the half-size pieces
+// are used.
+constexpr int64_t kWideFewTargets = 5;
+constexpr int kBwdWideUnrollHalf = kBwdWideUnroll > 1 ? kBwdWideUnroll / 2 : 1;
 
 // Rows per piece launch (the grid's second dimension is limited to 65536).
 constexpr int64_t kPieceRowsPerLaunch = 65536;
@@ -882,25 +887,25 @@ inline hipError_t bwd_piece_launch(const BwdParams& p0, hipStream_t s) {
     return hipSuccess;
 }
 
-template <typename T, int CAPX, bool AL, bool NT>
+template <int U, typename T, int CAPX, bool AL, bool NT>
 inline hipError_t bwd_wide_launch(const BwdParams& p, hipStream_t s) {
-    constexpr int64_t pc = static_cast<int64_t>(kGLanes) * kBwdWideUnroll;
+    constexpr int64_t pc = static_cast<int64_t>(kGLanes) * U;
     const bool apart = last_piece_apart(AL, p.N, p.V, T::kBytes, pc);
     const int64_t pieces = apart ? p.V / kChunk / pc : ((p.V + kChunk - 1) / kChunk + pc - 1) / pc;
     for (int64_t r0 = 0; r0 < p.N; r0 += kPieceRowsPerLaunch) {
         const int64_t rows = p.N - r0 < kPieceRowsPerLaunch ? p.N - r0 : kPieceRowsPerLaunch;
         const dim3 grid(static_cast<unsigned>(pieces), static_cast<unsigned>(rows));
         if constexpr (AL)
-            hipLaunchKernelGGL((bwd_wide_kernel<kBwdWideUnroll, T, CAPX, NT>), grid, dim3(kGLanes),
+            hipLaunchKernelGGL((bwd_wide_kernel<U, T, CAPX, NT>), grid, dim3(kGLanes),
                                lds_for_wgs_per_cu(wide_wgs_per_cu<T::kBytes>()), s, p, r0);
         else
-            hipLaunchKernelGGL((bwd_wide_kernel_unaligned<kBwdWideUnroll, T, CAPX, NT>), grid,
+            hipLaunchKernelGGL((bwd_wide_kernel_unaligned<U, T, CAPX, NT>), grid,
                                dim3(kGLanes), 0, s, p, r0);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         if constexpr (AL) {
             if (apart) {
-                hipLaunchKernelGGL((bwd_wide_last_kernel<kBwdWideUnroll, T, CAPX, NT>),
+                hipLaunchKernelGGL((bwd_wide_last_kernel<U, T, CAPX, NT>),
                                    dim3(1, static_cast<unsigned>(rows)), dim3(kGLanes), 0, s, p,
                                    r0);
                 e = hipGetLastError();
@@ -934,7 +939,15 @@ inline hipError_t bwd_dispatch_al(int head, const BwdParams& p0, hipStream_t s) 
             return hipErrorInvalidValue;
     }
     if (p0.k <= kPieceMaxK) return bwd_piece_launch<T, kHeadLogp, CAPX, kCapNone, AL, NT>(p0, s);
-    if (p0.k <= kGLanes) return bwd_wide_launch<T, CAPX, AL, NT>(p0, s);
+    if (p0.k <= kGLanes) {
+        // Half-size pieces where a full one would hold few targets: their
+        // slot staging then costs less than the shorter pieces stream faster
+        // (k = 16 at [4096, 32000] -5%, k = 64 at [8192, 151936] -4%; with 8
+        // targets per full piece, c5's shape, +8%).
+        if (p0.k * kGLanes * kBwdWideUnroll * kChunk <= kWideFewTargets * p0.V)
+            return bwd_wide_launch<kBwdWideUnrollHalf, T, CAPX, AL, NT>(p0, s);
+        return bwd_wide_launch<kBwdWideUnroll, T, CAPX, AL, NT>(p0, s);
+    }
     BwdParams p = p0;
     if (p.N < kBwdSmallRows) {
         // Few rows: narrow workgroups, each row cut into column segments.
