@@ -1040,14 +1040,15 @@ struct KLScale {
     bool ea, eb;
     float da, db, sa, sb;
 };
+template <typename FOLD>
 __device__ __forceinline__ KLScale kl_scale(float ma, float mLa, float mb, float mLb, float& MLa,
-                                            float& MLb) {
+                                            float& MLb, FOLD fold) {
     const auto mx = [](float a, float b) { return fmaxf(a, b); };
     KLScale k;
     k.ea = ma == neg_inf();
     k.eb = mb == neg_inf();
-    MLa = wave_fold(k.ea ? neg_inf() : mLa, mx);
-    MLb = wave_fold(k.eb ? neg_inf() : mLb, mx);
+    MLa = fold(k.ea ? neg_inf() : mLa, mx);
+    MLb = fold(k.eb ? neg_inf() : mLb, mx);
     k.da = k.ea ? 0.0f : mLa - MLa;
     k.db = k.eb ? 0.0f : mLb - MLb;
     k.sa = k.ea ? 0.0f : ex2(k.da);
@@ -1060,44 +1061,62 @@ __device__ __forceinline__ float kl_w(const KLScale& k, float Sa, float Sb, floa
     return REVERSE ? k.sa * __builtin_fmaf(k.da - k.db, Sa, W)
                    : k.sb * __builtin_fmaf(k.db - k.da, Sb, W);
 }
-template <bool REVERSE>
-__device__ __forceinline__ StatKL wave_reduce_kl(StatKL s) {
+template <bool REVERSE, typename FOLD>
+__device__ __forceinline__ StatKL statkl_fold(StatKL s, FOLD fold) {
     const auto mx = [](float a, float b) { return fmaxf(a, b); };
     const auto mn = [](float a, float b) { return fminf(a, b); };
     const auto add = [](float a, float b) { return a + b; };
     float MLa, MLb;
-    const KLScale k = kl_scale(s.ma, s.mLa, s.mb, s.mLb, MLa, MLb);
+    const KLScale k = kl_scale(s.ma, s.mLa, s.mb, s.mLb, MLa, MLb, fold);
     StatKL o;
-    o.ma = wave_fold(s.ma, mx);
-    o.mb = wave_fold(s.mb, mx);
+    o.ma = fold(s.ma, mx);
+    o.mb = fold(s.mb, mx);
     o.mLa = o.ma == neg_inf() ? s.mLa : MLa;  // (every lane empty: its own, the same)
     o.mLb = o.mb == neg_inf() ? s.mLb : MLb;
-    o.flag = REVERSE ? wave_fold(s.flag, mx) : wave_fold(s.flag, mn);
-    o.Sa = wave_fold(s.Sa * k.sa, add);
-    o.Sb = wave_fold(s.Sb * k.sb, add);
-    o.W = wave_fold(kl_w<REVERSE>(k, s.Sa, s.Sb, s.W), add);
+    o.flag = REVERSE ? fold(s.flag, mx) : fold(s.flag, mn);
+    o.Sa = fold(s.Sa * k.sa, add);
+    o.Sb = fold(s.Sb * k.sb, add);
+    o.W = fold(kl_w<REVERSE>(k, s.Sa, s.Sb, s.W), add);
     return o;
 }
+template <bool REVERSE>
+__device__ __forceinline__ StatKL wave_reduce_kl(StatKL s) {
+    return statkl_fold<REVERSE>(s, [](float v, auto op) { return wave_fold(v, op); });
+}
+template <int NW, bool REVERSE>
+__device__ __forceinline__ StatKL waves_reduce_kl(const StatKL* red, int lane) {
+    return statkl_fold<REVERSE>(red[lane & (NW - 1)],
+                                [](float v, auto op) { return lanes_fold<NW>(v, op); });
+}
 
-// Both directions: the very operations of wave_reduce_kl for each.
-__device__ __forceinline__ StatKL2 wave_reduce_kl2(StatKL2 s) {
+// Both directions: the very operations of statkl_fold for each.
+template <typename FOLD>
+__device__ __forceinline__ StatKL2 statkl2_fold(StatKL2 s, FOLD fold) {
     const auto mx = [](float a, float b) { return fmaxf(a, b); };
     const auto mn = [](float a, float b) { return fminf(a, b); };
     const auto add = [](float a, float b) { return a + b; };
     float MLa, MLb;
-    const KLScale k = kl_scale(s.ma, s.mLa, s.mb, s.mLb, MLa, MLb);
+    const KLScale k = kl_scale(s.ma, s.mLa, s.mb, s.mLb, MLa, MLb, fold);
     StatKL2 o;
-    o.ma = wave_fold(s.ma, mx);
-    o.mb = wave_fold(s.mb, mx);
+    o.ma = fold(s.ma, mx);
+    o.mb = fold(s.mb, mx);
     o.mLa = o.ma == neg_inf() ? s.mLa : MLa;
     o.mLb = o.mb == neg_inf() ? s.mLb : MLb;
-    o.fmax = wave_fold(s.fmax, mx);
-    o.fmin = wave_fold(s.fmin, mn);
-    o.Sa = wave_fold(s.Sa * k.sa, add);
-    o.Sb = wave_fold(s.Sb * k.sb, add);
-    o.Wr = wave_fold(kl_w<true>(k, s.Sa, s.Sb, s.Wr), add);
-    o.Wf = wave_fold(kl_w<false>(k, s.Sa, s.Sb, s.Wf), add);
+    o.fmax = fold(s.fmax, mx);
+    o.fmin = fold(s.fmin, mn);
+    o.Sa = fold(s.Sa * k.sa, add);
+    o.Sb = fold(s.Sb * k.sb, add);
+    o.Wr = fold(kl_w<true>(k, s.Sa, s.Sb, s.Wr), add);
+    o.Wf = fold(kl_w<false>(k, s.Sa, s.Sb, s.Wf), add);
     return o;
+}
+__device__ __forceinline__ StatKL2 wave_reduce_kl2(StatKL2 s) {
+    return statkl2_fold(s, [](float v, auto op) { return wave_fold(v, op); });
+}
+template <int NW>
+__device__ __forceinline__ StatKL2 waves_reduce_kl2(const StatKL2* red, int lane) {
+    return statkl2_fold(red[lane & (NW - 1)],
+                        [](float v, auto op) { return lanes_fold<NW>(v, op); });
 }
 
 __device__ __forceinline__ float wave_sum(float v) {

@@ -438,10 +438,9 @@ __global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void fwdkl_kernel(FwdParams p)
         st = wave_reduce_kl<REVERSE>(st);
         if (lane == 0) red[wid] = st;
         __syncthreads();
+        StatKL r{};
+        if (wid == 0) r = waves_reduce_kl<NW, REVERSE>(red, lane);
         if (tid == 0) {
-            StatKL r = red[0];
-#pragma unroll
-            for (int w = 1; w < NW; ++w) r = statkl_merge<REVERSE>(r, red[w]);
             if (p.part) {
                 static_cast<PartialRec*>(p.part)[row] = to_partial(r);
             } else {
@@ -477,10 +476,9 @@ __global__ __launch_bounds__(BLOCK) RLK_OCCUPANCY void fwdkl2_kernel(FwdParams p
         st = wave_reduce_kl2(st);
         if (lane == 0) red[wid] = st;
         __syncthreads();
+        StatKL2 r{};
+        if (wid == 0) r = waves_reduce_kl2<NW>(red, lane);
         if (tid == 0) {
-            StatKL2 r = red[0];
-#pragma unroll
-            for (int w = 1; w < NW; ++w) r = statkl2_merge(r, red[w]);
             const RowStats rr = finalize_kl<true>(kl_view_rev(r));
             const RowStats rf = finalize_kl<false>(kl_view_fwd(r));
             stats[row] = rr;
